@@ -1,0 +1,185 @@
+"""Pins of oracle/score.py: brute-force drop-one recomputation, the drop-set
+identity, exhaustive optimal subsets, and scipy's max filter."""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.ndimage import maximum_filter1d
+
+from oracle import perturbation_scores, group_scores, max_pool, row_positions
+from oracle.score import max_pool_fast, score_workload
+from tests import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(seed, R, n, d, scale_k=1.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((R, d)), scale_k * rng.standard_normal((n, d)),
+            rng.standard_normal((n, d)))
+
+
+@pytest.mark.parametrize("seed,R,n,d,causal", [
+    (0, 1, 12, 4, False), (1, 4, 64, 8, True), (2, 3, 33, 5, False), (3, 4, 20, 8, True),
+])
+def test_drop_one_bruteforce(seed, R, n, d, causal):
+    # [DK] §3.2: removing only token j moves the output by
+    # alpha_j/(1-alpha_j) * ||o - v_j||.  Brute force recomputes attention
+    # without token j for every row and sums the squared moves.
+    q, k, v = _rand(seed, R, n, d, scale_k=2.0)
+    scale = 1 / np.sqrt(d)
+    pos = row_positions(n, R) if causal else None
+    ref = np.zeros(n)
+    for r in range(R):
+        pert = bf.drop_one_perturbation(q[r], k, v, scale, None if pos is None else pos[r])
+        ref += pert ** 2
+    got = perturbation_scores(q, k, v, pos, scale, explicit=True)
+    got_id = perturbation_scores(q, k, v, pos, scale, explicit=False)
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-12 * ref.max())
+    assert np.allclose(got_id, ref, rtol=1e-8, atol=1e-14)
+
+
+def test_group_and_window_sum_bruteforce():
+    # the group score sums the window rows of every q-head of the group
+    rng = np.random.default_rng(7)
+    Hq, Hkv, w, n, d = 4, 2, 3, 24, 8
+    g = Hq // Hkv
+    q_win = rng.standard_normal((Hq, w, d))
+    k = rng.standard_normal((n, d)) * 1.5
+    v = rng.standard_normal((n, d))
+    scale = 1 / np.sqrt(d)
+    for h in range(Hkv):
+        got = group_scores(q_win, k, v, h, g, scale, causal=True)
+        ref = np.zeros(n)
+        for qh in range(h * g, (h + 1) * g):
+            for i in range(w):
+                pos = n - w + i
+                ref += bf.drop_one_perturbation(q_win[qh, i], k, v, scale, pos) ** 2
+        assert np.allclose(got, ref, rtol=1e-10)
+
+
+def test_dominant_key_uses_sum_of_others():
+    # alpha -> 1: 1 - alpha is formed from the other weights, so the score of
+    # the dominant key is still exact where 1 - alpha would cancel.
+    n, d = 16, 4
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    k[5] = np.array([60.0, 0, 0, 0])   # logit 60: others have weight ~e^-60
+    got = perturbation_scores(q, k, v, None, 1.0, explicit=True)
+    ref = bf.drop_one_perturbation(q[0], k, v, 1.0, None) ** 2
+    assert np.isfinite(got).all()
+    assert np.isclose(got[5], ref[5], rtol=1e-6)
+
+
+def test_single_visible_key_contributes_zero():
+    # causal row at position 0 sees only key 0
+    n, d = 6, 4
+    q, k, v = _rand(5, n, n, d)
+    got = perturbation_scores(q, k, v, row_positions(n, n), 0.5, explicit=True)
+    row0 = perturbation_scores(q[:1], k, v, np.array([0]), 0.5, explicit=True)
+    assert np.all(row0 == 0.0)
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_drop_set_identity(seed):
+    # [DK] §3.2: ||Delta(J)|| = ||sum_{i in J} p_i (o - v_i)|| / (1 - P_J)
+    rng = np.random.default_rng(100 + seed)
+    n, d = 20, 6
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((n, d)) * 1.5
+    v = rng.standard_normal((n, d))
+    lg = k @ q
+    p = np.exp(lg - lg.max())
+    p /= p.sum()
+    o = p @ v
+    for _ in range(10):
+        J = rng.choice(n, size=rng.integers(1, n - 1), replace=False)
+        closed = np.linalg.norm((p[J][:, None] * (o - v[J])).sum(0)) / (1 - p[J].sum())
+        assert np.isclose(bf.drop_set_perturbation(q, k, v, 1.0, J), closed, rtol=1e-10)
+
+
+def test_single_query_score_is_squared_drop_one_and_same_ranking():
+    # w = 1, one head: the score is the squared single-token perturbation and
+    # ranks like the unsquared proxy ([DK] §3.3)
+    q, k, v = _rand(21, 1, 50, 8, scale_k=2.0)
+    got = perturbation_scores(q, k, v, None, 0.35, explicit=True)
+    pert = bf.drop_one_perturbation(q[0], k, v, 0.35, None)
+    assert np.allclose(got, pert ** 2, rtol=1e-10)
+    assert (np.argsort(got, kind="stable") == np.argsort(pert, kind="stable")).all()
+
+
+def test_proxy_against_exhaustive_optimum():
+    # exact combinatorial problem ([DK] §3.2 (Exact); [PI] Problem 1) by
+    # exhaustive search for n = 12; the proxy can never beat the optimum.
+    rng = np.random.default_rng(2024)
+    ratios = []
+    for _ in range(20):
+        n, d, kev = 12, 4, 4
+        q = rng.standard_normal(d)
+        k = rng.standard_normal((n, d)) * 1.5
+        v = rng.standard_normal((n, d))
+        sc = perturbation_scores(q[None], k, v, None, 1.0, explicit=True)
+        J_hat = np.argsort(sc, kind="stable")[:kev]
+        f_hat = bf.drop_set_perturbation(q, k, v, 1.0, J_hat)
+        f_opt, _ = bf.best_subset(q, k, v, 1.0, kev)
+        assert f_hat >= f_opt - 1e-12
+        ratios.append(f_hat / f_opt if f_opt > 0 else 1.0)
+    assert np.median(ratios) < 3.0      # context only: the page reports ~1.16 on real activations
+
+
+@pytest.mark.parametrize("vals,has_partition", [
+    ([3, 1, 1, 2, 2, 1], True), ([1, 2, 3, 4, 5, 7], True), ([1, 1, 1, 4], False), ([2, 2, 2, 7], False),
+])
+def test_partition_special_case(vals, has_partition):
+    # [PI] §3 / App. B: d=1, K=Q=1, keep half of the entries; an eviction with
+    # zero error exists iff the values have an equal-sum split.
+    n = len(vals)
+    q = np.ones(1)
+    k = np.ones((n, 1))
+    v = np.array(vals, dtype=float)[:, None]
+    f_opt, _ = bf.best_subset(q, k, v, 1.0, n // 2)
+    assert (f_opt < 1e-12) == has_partition
+
+
+@pytest.mark.parametrize("kernel", [1, 3, 7, 9])
+def test_max_pool_against_scipy(kernel):
+    rng = np.random.default_rng(kernel)
+    s = rng.standard_normal(101)
+    ref = maximum_filter1d(s, size=kernel, mode="constant", cval=-np.inf)
+    assert np.array_equal(max_pool(s, kernel), ref)
+    assert np.array_equal(max_pool_fast(s, kernel), ref)
+
+
+def test_ragged_workload_layout():
+    # per-sequence scoring on the [Hkv][T] layout equals scoring each
+    # sequence alone
+    rng = np.random.default_rng(3)
+    S, Hq, Hkv, w, d = 2, 2, 1, 3, 4
+    lens = [10, 17]
+    off = np.array([0, 10, 27])
+    q = rng.standard_normal((S, Hq, w, d))
+    k = rng.standard_normal((Hkv, 27, d))
+    v = rng.standard_normal((Hkv, 27, d))
+    got = score_workload(q, k, v, off, Hq, Hkv, 0.5, True, 3)
+    for s in range(S):
+        a, b = off[s], off[s + 1]
+        ref = max_pool(group_scores(q[s], k[0, a:b], v[0, a:b], 0, 2, 0.5, True), 3)
+        assert np.allclose(got[0, a:b], ref, rtol=1e-14)
+
+
+def test_value_norm_example_ordering():
+    # research-topic note: weight 0.05 with value norm 10 contributes 5x the
+    # output of weight 0.20 with value norm 0.5.  The single-token
+    # perturbation ranks the two tokens the same way.
+    ex = json.load(open(os.path.join(GOLDEN, "value_norm_example.json")))
+    a, b = ex["a"], ex["b"]
+    assert np.isclose(a["alpha"] * a["value_norm"] / (b["alpha"] * b["value_norm"]), ex["ratio"])
+    # o = 0: perturbation alpha/(1-alpha) * ||v||
+    pa = a["alpha"] / (1 - a["alpha"]) * a["value_norm"]
+    pb = b["alpha"] / (1 - b["alpha"]) * b["value_norm"]
+    assert pa > pb

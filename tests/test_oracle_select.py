@@ -1,0 +1,204 @@
+"""Pins of oracle/select.py and oracle/philox.py."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import (topk_select, proposal, expected_distinct, expected_samples_search,
+                    inclusion_prob, sample_select, philox4x64_10, uniform53)
+from oracle.select import STATUS_NOCONV, select_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- top-k
+def _topk_bruteforce(s, B):
+    # pure-python ranking: larger value first, NaN after every number,
+    # ties -> lower index
+    def rank_key(j):
+        x = s[j]
+        return (1, 0.0, j) if np.isnan(x) else (0, -x, j)
+    order = sorted(range(len(s)), key=rank_key)
+    return sorted(order[:B])
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_topk_against_python_sort(seed):
+    rng = np.random.default_rng(seed)
+    s = np.round(rng.standard_normal(300), 1).astype(np.float32)   # many exact ties
+    s[rng.choice(300, 5, replace=False)] = np.nan
+    s[rng.choice(300, 3, replace=False)] = -np.inf
+    for B in (0, 1, 17, 150, 295, 300):
+        assert list(topk_select(s, B)) == _topk_bruteforce(list(s.astype(float)), B)
+
+
+def test_topk_ties_lower_index():
+    s = np.array([1.0, 3.0, 3.0, 2.0, 3.0, 0.5])
+    assert list(topk_select(s, 2)) == [1, 2]
+    assert list(topk_select(s, 4)) == [1, 2, 3, 4]
+    assert list(topk_select(np.array([np.nan, 1.0, np.nan]), 2)) == [0, 1]
+
+
+# ---------------------------------------------------------------- E[J(m)]
+@pytest.mark.parametrize("seed", range(3))
+def test_expected_distinct_monte_carlo(seed):
+    # [PI] App. F, Eq. 24 against direct simulation of m draws with replacement
+    rng = np.random.default_rng(seed)
+    n = 24
+    pi = rng.dirichlet(np.full(n, 0.3))
+    for m in (1, 5, 30, 200):
+        trials = 100000
+        draws = rng.choice(n, size=(trials, m), p=pi)
+        distinct = np.array([len(np.unique(r)) for r in draws[:2000]])
+        # full trial count via a vectorised membership count
+        seen = np.zeros((trials, n), dtype=bool)
+        seen[np.repeat(np.arange(trials), m), draws.ravel()] = True
+        distinct = seen.sum(1)
+        sigma = distinct.std() / np.sqrt(trials)
+        assert abs(distinct.mean() - expected_distinct(pi, m)) < 4 * sigma + 1e-12
+
+
+def test_expected_distinct_monotone_unit_increments():
+    # [PI] App. F, Eq. 27-31: nondecreasing in m, increments at most 1, and
+    # the increment equals sum_i (1 - pi_i)^m pi_i
+    rng = np.random.default_rng(9)
+    pi = rng.dirichlet(np.full(200, 0.2))
+    e = np.array([expected_distinct(pi, m) for m in range(0, 400)])
+    inc = np.diff(e)
+    assert np.all(inc >= -1e-12) and np.all(inc <= 1 + 1e-12)
+    closed = np.array([np.sum((1 - pi) ** m * pi) for m in range(0, 399)])
+    assert np.allclose(inc, closed, atol=1e-10)
+
+
+@pytest.mark.parametrize("target", [1, 10, 57, 150, 199])
+def test_algorithm2_lands_in_band(target):
+    rng = np.random.default_rng(target)
+    pi = rng.dirichlet(np.full(200, 0.5))
+    m, st = expected_samples_search(pi, float(target))
+    assert st == 0
+    assert abs(expected_distinct(pi, m) - target) <= 0.5
+
+
+def test_algorithm2_not_converged_flag():
+    pi = np.full(100, 1e-16)
+    pi[0] = 1 - 99e-16
+    m, st = expected_samples_search(pi, 90.0)
+    assert st == STATUS_NOCONV and m == 10 ** 12
+
+
+def test_worked_example_from_pages():
+    # [PI] App. F.1 worked example, pi as printed
+    ex = json.load(open(os.path.join(GOLDEN, "ccp_worked_example.json")))
+    pi = np.array(ex["pi"])
+    n = ex["n"]
+    comp = 1 - expected_distinct(pi, ex["m_example"]) / n
+    assert abs(comp - ex["compression_at_m_example"]) < ex["compression_tolerance"]
+    for t in ex["targets"]:
+        band = [m for m in range(0, 20000) if abs(expected_distinct(pi, m) - t["kept"]) <= 0.5]
+        assert band, t
+        lo, hi = min(band), max(band)
+        assert lo <= t["m_page"] <= hi, (t, lo, hi)
+        m, st = expected_samples_search(pi, float(t["kept"]))
+        assert lo <= m <= hi and st == 0
+
+
+# ---------------------------------------------------------------- Philox
+def test_philox_matches_numpy_library():
+    # numpy.random.Philox is Philox-4x64-10; it increments the counter before
+    # producing a block, so counter c-1 yields the block of counter c.
+    rng = np.random.default_rng(77)
+    for _ in range(50):
+        c = [int(x) for x in rng.integers(1, 2 ** 63, size=4, dtype=np.int64)]
+        key = [int(x) for x in rng.integers(0, 2 ** 63, size=2, dtype=np.int64)]
+        mine = philox4x64_10(*[np.uint64(x) for x in c], np.uint64(key[0]), np.uint64(key[1]))
+        ref = np.random.Philox(counter=[c[0] - 1] + c[1:], key=key).random_raw(4)
+        assert [int(a) for a in mine] == [int(b) for b in ref]
+    # vectorised evaluation equals per-element evaluation
+    js = np.arange(1000, dtype=np.uint64)
+    vec = philox4x64_10(js, np.uint64(3), np.uint64(2), np.uint64(0), np.uint64(99), np.uint64(0))[0]
+    one = [int(philox4x64_10(np.uint64(j), np.uint64(3), np.uint64(2), np.uint64(0),
+                             np.uint64(99), np.uint64(0))[0]) for j in (0, 1, 999)]
+    assert [int(vec[0]), int(vec[1]), int(vec[999])] == one
+
+
+def test_uniform_chi_square():
+    u = uniform53(12345, 0, 0, np.arange(1 << 20))
+    assert u.min() > 0 and u.max() < 1
+    counts = np.bincount((u * 65536).astype(np.int64), minlength=65536)
+    chi2 = ((counts - counts.mean()) ** 2 / counts.mean()).sum()
+    p = stats.chi2.sf(chi2, 65535)
+    assert 1e-4 < p < 1 - 1e-4
+
+
+# ---------------------------------------------------------------- Gumbel top-B
+def _exact_inclusion(pi, B):
+    """P(j among the first B draws of sequential sampling without
+    replacement), by enumerating ordered prefixes."""
+    n = len(pi)
+    inc = np.zeros(n)
+    for perm in itertools.permutations(range(n), B):
+        p, rem = 1.0, 1.0
+        for j in perm:
+            p *= pi[j] / rem
+            rem -= pi[j]
+        for j in perm:
+            inc[j] += p
+    return inc
+
+
+@pytest.mark.parametrize("n,B", [(4, 1), (5, 2), (6, 3)])
+def test_gumbel_topB_is_sampling_without_replacement(n, B):
+    rng = np.random.default_rng(n * 10 + B)
+    s = rng.uniform(0.05, 1.0, size=n)
+    tau = 0.5
+    pi = proposal(s, tau)
+    exact = _exact_inclusion(pi, B)
+    seeds = 200000
+    from oracle.select import proposal_log
+    lp = proposal_log(s, tau)
+    # draw u for every seed in one vectorised Philox call
+    j = np.tile(np.arange(n, dtype=np.uint64), seeds)
+    sd = np.repeat(np.arange(seeds, dtype=np.uint64), n)
+    x0 = philox4x64_10(j, np.uint64(0), np.uint64(0), np.uint64(0), sd, np.uint64(0))[0]
+    u = ((x0 >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+    kappa = (lp[None, :] - np.log(-np.log(u.reshape(seeds, n))))
+    top = np.argsort(-kappa, axis=1, kind="stable")[:, :B]
+    freq = np.zeros(n)
+    for b in range(B):
+        freq += np.bincount(top[:, b], minlength=n)
+    freq /= seeds
+    sigma = np.sqrt(exact * (1 - exact) / seeds)
+    assert np.all(np.abs(freq - exact) <= 4 * sigma + 1e-9), (freq, exact)
+    # the oracle's sample_select uses the same keys
+    idx, _, _, _ = sample_select(s, B, tau, 1.0, 7, 0, 0)
+    assert len(idx) == B and np.all(np.diff(idx) > 0)
+
+
+# ---------------------------------------------------------------- weights
+def test_inclusion_identity_and_full_budget():
+    rng = np.random.default_rng(5)
+    s = np.exp(rng.standard_normal(500) * 2).astype(np.float32)
+    pi = proposal(s, 0.5)
+    m, _ = expected_samples_search(pi, 50.0)
+    assert np.isclose(inclusion_prob(pi, m).sum(), expected_distinct(pi, m), rtol=1e-13)
+    idx, bias, m_all, st = sample_select(s, 500, 0.5, 1.0, 1, 0, 0)
+    assert list(idx) == list(range(500)) and np.all(bias == 0.0)
+    idx, bias, _, _ = sample_select(s, 50, 0.5, 1.0, 1, 0, 0)
+    q = inclusion_prob(pi[idx], m)
+    assert np.allclose(bias, -np.log(q))
+    assert np.all(bias >= 0)
+
+
+def test_select_workload_ragged_layout():
+    rng = np.random.default_rng(8)
+    lens = [30, 50]
+    off = np.array([0, 30, 80])
+    sc = rng.random((2, 80)).astype(np.float32)
+    idx, bias, m, st = select_workload(sc, off, [3, 5], "topk")
+    assert idx.shape == (2, 8)
+    for h in range(2):
+        assert list(idx[h, :3]) == list(topk_select(sc[h, :30], 3))
+        assert list(idx[h, 3:]) == list(topk_select(sc[h, 30:], 5))
