@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Eviction-time throughput of the HIP path on one MI355X.
+
+One step = kvevict_score + kvevict_select + kvevict_compact over one layer of
+the workload (inputs resident in HBM before timing starts).  The default
+workload is the Llama-3.1-8B-shaped layer at n = 131072 (32 q-heads, 8 KV
+heads, d = 128, w = 32, bf16, 5 % top-k budget, max-pool 7).
+
+Prints one JSON line with the throughput (scored tokens / s per layer), a
+roofline entry for the dominant kernel (per-launch HIP-event durations
+recorded on the launch stream over the timed steps) and the fp64 oracle timed
+on a bounded sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="KV heads the oracle baseline scores")
+    return ap.parse_args()
+
+
+def _stage_bytes(wl, esize):
+    """Algorithmic HBM bytes per launch of each stage (what the method has to
+    move, not implementation scratch)."""
+    T, Hkv, d = wl.T, wl.Hkv, wl.d
+    kv = 2 * Hkv * T * d * esize            # K and V read once
+    planes = ((wl.Hq // wl.Hkv) * wl.w + 127) // 128 if wl.dtype == "bf16" else 1
+    B = int(sum(wl.budgets()))
+    return {
+        "score_pass1": kv + 4 * Hkv * T,                       # + ||v||^2 written
+        "score_pass2": kv + 4 * Hkv * T + 4 * Hkv * T * planes,  # + ||v||^2 read, raw scores written
+        "score_pool": 4 * Hkv * T * planes + 4 * Hkv * T,
+        "select": 4 * Hkv * T + 8 * Hkv * B,
+        "compact": 2 * (2 * Hkv * B * d * esize) + 12 * Hkv * B,
+    }
+
+
+def _cpu_baseline(wl, data, heads):
+    """Oracle score + select + compact of `heads` KV heads, wall clock."""
+    import numpy as np
+    import oracle
+    from oracle.score import max_pool_fast
+    from long_context_attention_kvevict_amd import synth
+    cores = len(os.sched_getaffinity(0))
+    q = synth.to_f64(data["q_win"], wl.dtype)
+    off = wl.seq_off()
+    budgets = wl.budgets()
+    t0 = time.perf_counter()
+    for h in range(heads):
+        k = synth.to_f64(data["k"][h], wl.dtype)
+        v = synth.to_f64(data["v"][h], wl.dtype)
+        for s in range(wl.S):
+            a, b = off[s], off[s + 1]
+            sc = max_pool_fast(oracle.group_scores(q[s], k[a:b], v[a:b], h, wl.g, wl.sm_scale, True),
+                               wl.pool_kernel).astype(np.float32)
+            if wl.mode == "topk":
+                idx = oracle.topk_select(sc, budgets[s])
+            else:
+                idx, _, _, _ = oracle.sample_select(sc, budgets[s], wl.tau, wl.tau_w, wl.hash_seed, s, h)
+            _ = k[a:b][idx], v[a:b][idx]
+    dt = time.perf_counter() - t0
+    tokens_per_s = wl.T / (dt * wl.Hkv / heads)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {wl.Hkv} KV heads (all {wl.T} tokens, {wl.g * wl.w} window rows), "
+                      f"{dt:.1f} s, scaled by {wl.Hkv / heads:g}"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from long_context_attention_kvevict_amd import kvevict as K
+    from long_context_attention_kvevict_amd import synth, workloads
+
+    wl = workloads.ALL[args.workload]()
+    print(f"# generating {wl.name}", file=sys.stderr, flush=True)
+    data = synth.generate(wl)
+    dev = torch.device("cuda:0")
+    b = K.Batch(wl.lens, wl.Hq, wl.Hkv, wl.d, wl.w, wl.dtype, device=dev)
+    q = K.to_device(data["q_win"], wl.dtype, dev)
+    k = K.to_device(data["k"], wl.dtype, dev)
+    v = K.to_device(data["v"], wl.dtype, dev)
+    budgets = wl.budgets()
+    caps = wl.caps()
+    bud = b.offsets(budgets, dev)
+    cap = b.offsets(caps, dev)
+    mode = K.KVE_TOPK if wl.mode == "topk" else K.KVE_SAMPLE
+    total_B, total_C = int(budgets.sum()), int(caps.sum())
+    scores = torch.empty((wl.Hkv, wl.T), dtype=torch.float32, device=dev)
+    sel = (torch.empty((wl.Hkv, max(total_B, 1)), dtype=torch.int32, device=dev),
+           torch.empty((wl.Hkv, max(total_B, 1)), dtype=torch.float32, device=dev),
+           torch.empty((wl.S, wl.Hkv), dtype=torch.float64, device=dev),
+           torch.empty((wl.S, wl.Hkv), dtype=torch.int32, device=dev))
+    cmp = (torch.empty((wl.Hkv, total_C, wl.d), dtype=k.dtype, device=dev),
+           torch.empty((wl.Hkv, total_C, wl.d), dtype=v.dtype, device=dev),
+           torch.empty((wl.Hkv, total_C), dtype=torch.float32, device=dev))
+
+    def step():
+        b.score(q, k, v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel, out=scores)
+        idx, bias, _, _ = b.select(scores, budgets, mode=mode, tau=wl.tau, tau_w=wl.tau_w, seed=wl.hash_seed,
+                                   out=sel, bud_offsets=bud)
+        b.compact(k, v, budgets, idx, bias, caps, out=cmp, bud_offsets=bud, cap_offsets=cap)
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K.timing_enable(True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    stages = K.timing_summary()
+    K.timing_enable(False)
+    print(f"# {args.steps} steps: {ms:.3f} ms/step; stages {stages}", file=sys.stderr, flush=True)
+
+    esize = 2 if wl.dtype == "bf16" else 4
+    sbytes = _stage_bytes(wl, esize)
+    dominant = max((s for s in stages if s in sbytes), key=lambda s: stages[s][0])
+    dom_ms = stages[dominant][0]
+    achieved = sbytes[dominant] / (dom_ms * 1e-3) / 1e9
+    step_bytes = sum(sbytes[s] for s in ("score_pass1", "score_pass2", "score_pool", "select", "compact"))
+    tokens_per_s = wl.T / (ms * 1e-3)
+    result = {
+        "metric": "scored KV tokens/sec per layer (score+select+compact) at n=128K; % HBM peak",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "S": wl.S, "n": int(max(wl.lens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "d": wl.d, "w": wl.w, "budget_frac": wl.budget_frac, "mode": wl.mode,
+                   "pool_kernel": wl.pool_kernel, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stage_ms": {s: round(v[0], 5) for s, v in stages.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = _cpu_baseline(wl, data, max(1, min(args.cpu_heads, wl.Hkv)))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

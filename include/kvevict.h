@@ -1,0 +1,205 @@
+/*
+ * kvevict.h -- C ABI of the MI355X (gfx950) windowed KV-cache eviction library.
+ *
+ * Four calls make up the eviction-time path and the decode step:
+ *
+ *   kvevict_score        output-aware per-token eviction scores
+ *   kvevict_select       per-head budgeted selection (top-k or sampling)
+ *   kvevict_compact      gather of the kept K/V rows and their logit bias
+ *   kvevict_decode_snis  decode attention over the compacted cache with a
+ *                        per-entry logit bias (self-normalised importance
+ *                        sampling correction)
+ *
+ * Pages cited:
+ *   [PI] "A Probabilistic Interpretation of KV Cache Eviction"
+ *   [DK] "DropKV: Decoupling Residual-Output Perturbation for Near-Optimal
+ *        KV-Cache Eviction"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Notation: S sequences, Hq query heads, Hkv KV heads (g = Hq/Hkv query
+ *    heads share one KV head: q-head qh uses KV head qh / g), d head dim,
+ *    w observation-window rows, n_s tokens of sequence s, T = sum n_s.
+ *  - Memory: every tensor argument is a device pointer unless its name ends
+ *    in _host.  All tensors are dense, row-major, with the innermost
+ *    dimension contiguous.  bf16 data is raw IEEE bfloat16 bits (uint16).
+ *    K and V rows must be 16-byte aligned (d * element size is a multiple
+ *    of 16 for every supported d).
+ *  - Ownership: the caller owns every buffer, including the workspace.  The
+ *    library never allocates device memory and keeps no state between
+ *    calls except a thread-local error string.  Inputs are read-only.
+ *    Outputs must not alias inputs.
+ *  - Execution: each call validates its arguments on the host, then
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = default stream)
+ *    and returns without synchronising.  Faults during execution surface
+ *    at the caller's next synchronisation.
+ *  - Errors: argument errors return KVE_EINVAL / KVE_ENOTSUP /
+ *    KVE_EWORKSPACE before anything is launched or written; a failed launch
+ *    returns KVE_EHIP.  kvevict_last_error() describes the last failure of
+ *    the calling thread.
+ */
+#ifndef KVEVICT_H
+#define KVEVICT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVE_OK = 0,
+  KVE_EINVAL = 1,      /* bad argument (null pointer, inconsistent sizes) */
+  KVE_ENOTSUP = 2,     /* valid but unsupported shape (e.g. head dim)      */
+  KVE_EWORKSPACE = 3,  /* workspace smaller than the *_workspace() query   */
+  KVE_EHIP = 4,        /* a HIP runtime call failed                        */
+  KVE_ENOCONV = 5      /* per-head status only: expected-samples search did
+                          not reach its tolerance band (see kvevict_select) */
+} kve_status;
+
+typedef enum { KVE_BF16 = 0, KVE_F32 = 1 } kve_dtype;
+typedef enum { KVE_TOPK = 0, KVE_SAMPLE = 1 } kve_mode;
+
+/* Shape of a (possibly ragged) batch; shared by all calls. */
+typedef struct {
+  int32_t S, Hq, Hkv, d, w;
+  int32_t dtype;                /* kve_dtype of q/k/v                        */
+  const int32_t* seq_off;       /* device [S+1]: token offsets on axis T     */
+  const int32_t* seq_off_host;  /* host   [S+1]: the same values             */
+} kve_layout;
+
+/* Supported shapes: bf16 needs d = 128, fp32 d in {64, 128}; Hq % Hkv == 0;
+ * 1 <= w <= 64; w <= n_s for every sequence (score); T < 2^30. */
+
+/* ------------------------------------------------------------------ score
+ * Window scoring ([DK] §3.2 single-token perturbation, §3.3 windowed
+ * squared score, §3.4 two-pass fused computation; [PI] §5 GQA groups;
+ * SnapKV-style pooling as described in [PI] App. D).
+ *
+ * For every sequence s, KV head h and key j < n_s:
+ *   score[h][off_s + j] = maxpool_j( sum_{qh in group(h)} sum_{i<w}
+ *        (a_ij / (1 - a_ij))^2 * || o_i - v_j ||^2 )
+ * where row i of q-head qh is q_win[s][qh][i], logits are
+ * sm_scale * <q_i, k_j>, a_ij is the row softmax (keys j > n_s - w + i
+ * hidden when causal != 0; hidden pairs contribute 0), o_i = sum_j a_ij v_j,
+ * and maxpool takes the maximum over |j' - j| <= (pool_kernel-1)/2 within
+ * the sequence.  1 - a_ij is clamped below by about 2^-20 (only a key
+ * holding nearly all of a row's weight is affected).
+ *
+ *   q_win   [S][Hq][w][d]  dtype
+ *   k, v    [Hkv][T][d]    dtype
+ *   scores  [Hkv][T]       float32, written for every token
+ *   pool_kernel  odd, 1..31 (1 = no pooling)
+ *   ws      device workspace of at least kvevict_score_workspace() bytes,
+ *           no alignment beyond 256 bytes required, contents undefined
+ *           on entry and on return.
+ * Deterministic: no floating-point atomics; identical inputs give
+ * bit-identical scores. */
+size_t kvevict_score_workspace(const kve_layout* L);
+kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k,
+                         const void* v, float sm_scale, int32_t causal,
+                         int32_t pool_kernel, float* scores, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------- select
+ * Per (sequence, KV head) budgeted selection of B_s = bud_off[s+1] -
+ * bud_off[s] tokens (0 <= B_s <= n_s), written to
+ * idx[h][bud_off[s] .. bud_off[s+1]) as sequence-relative token indices in
+ * ascending order, with the logit bias of each kept token in bias[h][..].
+ *
+ * KVE_TOPK ([DK] §3.3: evict the smallest scores; [PI] §4 top-k
+ *   estimator): the B_s largest scores, ties -> lower index, NaN ranked
+ *   below every number.  bias = 0.
+ * KVE_SAMPLE ([PI] §4 probabilistic eviction with a proposal; App. D.1
+ *   tempering; App. F Problem 5 / Algorithm 2 expected-samples search;
+ *   §6 Eq. 10 weight temperature):
+ *   proposal log pi~_j = log(max(score_j, 2^-126)) / tau, pi = pi~/sum pi~;
+ *   m >= 0 integer with |sum_j 1 - (1-pi_j)^m - B_s| <= 0.5 (searched in
+ *   [0, 10^12]); the kept set is the B_s largest Gumbel keys
+ *   log pi~_j - log(-log u_j), u_j = ((x >> 11) + 0.5) 2^-53 with x the
+ *   first word of Philox-4x64-10(counter = (j, h, s, 0), key = (seed, 0));
+ *   bias_j = -log(q_j) / tau_w with q_j = 1 - (1 - pi_j)^m.  B_s = n_s keeps
+ *   all tokens with bias 0.  If no m <= 10^12 reaches the band, m = 10^12 and
+ *   status_out[s][h] = KVE_ENOCONV (outputs remain valid).
+ *
+ *   scores     [Hkv][T] float32 (e.g. from kvevict_score)
+ *   bud_off    device [S+1], bud_off_host host [S+1] (same values)
+ *   idx        [Hkv][bud_off[S]] int32 out
+ *   bias       [Hkv][bud_off[S]] float32 out
+ *   m_out      [S][Hkv] float64 out, or NULL (0 in top-k mode)
+ *   status_out [S][Hkv] int32 out, or NULL (KVE_OK or KVE_ENOCONV)
+ *   ws         at least kvevict_select_workspace() bytes. */
+size_t kvevict_select_workspace(const kve_layout* L, const int32_t* bud_off_host,
+                                int32_t mode);
+kve_status kvevict_select(const kve_layout* L, const float* scores,
+                          const int32_t* bud_off, const int32_t* bud_off_host,
+                          int32_t mode, float tau, float tau_w, uint64_t seed,
+                          int32_t* idx, float* bias, double* m_out,
+                          int32_t* status_out, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------- compact
+ * Gather of the kept entries ([PI] §2 Eq. 3: evicted attention uses the
+ * rows of K and V indexed by the kept set; [PI] §5: evicted entries are
+ * ignored).  For r < B_s:
+ *   k_c[h][cap_off[s] + r] = k[h][seq_off[s] + idx[h][bud_off[s] + r]]
+ *   v_c likewise, bias_c[h][cap_off[s] + r] = bias[h][bud_off[s] + r].
+ * Slots r >= B_s of each sequence are left untouched (decode headroom).
+ *   k, v      [Hkv][T][d] dtype;      idx, bias as produced by select
+ *   cap_off   device [S+1] with cap_s = cap_off[s+1]-cap_off[s] >= B_s
+ *   k_c, v_c  [Hkv][cap_off[S]][d] dtype out;  bias_c [Hkv][cap_off[S]] out
+ * An idx entry outside [0, n_s) is skipped on the device (its slot is left
+ * untouched). */
+kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v,
+                           const int32_t* bud_off, const int32_t* bud_off_host,
+                           const int32_t* idx, const float* bias,
+                           const int32_t* cap_off, const int32_t* cap_off_host,
+                           void* k_c, void* v_c, float* bias_c, void* stream);
+
+/* ------------------------------------------------------------ decode_snis
+ * Corrected decode attention ([PI] §5 Definition 3-4 and Algorithm 1; GQA
+ * paragraph of §5): for every sequence s and q-head qh (KV head h),
+ *   out[s][qh] = sum_{r < cache_len[s]} softmax_r(sm_scale <q[s][qh], k_c[h][c+r]>
+ *                                                 + bias_c[h][c+r]) v_c[h][c+r]
+ * with c = cap_off[s].  With bias = log(weight) this is Algorithm 1's
+ * (mu_hat + mu) / (z_hat + z): kept history entries carry bias -log q_j,
+ * entries appended after eviction carry bias 0 (weight 1).  The caller
+ * appends a new token by writing k_c, v_c and bias_c = 0 at slot
+ * cap_off[s] + cache_len[s] and incrementing cache_len[s].
+ *   q         [S][Hq][d] dtype
+ *   cache_len device [S], 1 <= cache_len[s] <= cap_s
+ *   max_cache_len  host upper bound of cache_len[s] (grid sizing)
+ *   out       [S][Hq][d] float32
+ *   ws        at least kvevict_decode_workspace() bytes. */
+size_t kvevict_decode_workspace(const kve_layout* L, int32_t max_cache_len);
+kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k_c,
+                               const void* v_c, const float* bias_c,
+                               const int32_t* cap_off, const int32_t* cap_off_host,
+                               const int32_t* cache_len, int32_t max_cache_len,
+                               float sm_scale, float* out, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- instrumentation
+ * Not part of the eviction path.  Opt-in per-kernel timing with HIP events
+ * recorded on the launch stream around every kernel the four calls enqueue.
+ * Stage ids: 0 score pass 1, 1 score merge, 2 score pass 2, 3 score pool,
+ * 4 select, 5 compact, 6 decode split, 7 decode merge.
+ * kvevict_timing_enable(1) creates an event pool on first use (no device
+ * memory) and clears previous records; 0 stops recording.
+ * kvevict_timing_summary() waits for the recorded events, writes the mean
+ * duration in ms and the number of launches per stage (n_stages entries),
+ * and clears the records.  Process-wide, not thread-safe. */
+int32_t kvevict_timing_enable(int32_t on);
+int32_t kvevict_timing_summary(double* avg_ms, int32_t* counts, int32_t n_stages);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* kvevict_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t kvevict_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVEVICT_H */

@@ -1,0 +1,146 @@
+// C ABI of libkvevict: host validation, workspace sizing, kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/kvevict.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kve_status set_err(kve_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+kve_status hip_err(hipError_t e, const char* where) {
+  return set_err(KVE_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvevict_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvevict_version(void) { return 100; }
+
+size_t kvevict_score_workspace(const kve_layout* L) {
+  kve::ScoreGeom G;
+  std::string msg;
+  if (kve::plan_score(L, &G, &msg) != KVE_OK) return 0;
+  return G.bytes;
+}
+
+kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k, const void* v,
+                         float sm_scale, int32_t causal, int32_t pool_kernel, float* scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  kve::ScoreGeom G;
+  std::string msg;
+  kve_status st = kve::plan_score(L, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_score: " + msg);
+  if (!q_win || !k || !v || !scores) return set_err(KVE_EINVAL, "kvevict_score: null tensor pointer");
+  if (!(sm_scale > 0.f) || sm_scale > 1e6f) return set_err(KVE_EINVAL, "kvevict_score: sm_scale must be in (0, 1e6]");
+  if (pool_kernel < 1 || pool_kernel > 31 || pool_kernel % 2 == 0)
+    return set_err(KVE_EINVAL, "kvevict_score: pool_kernel must be odd and in [1, 31]");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_score: workspace smaller than kvevict_score_workspace()");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(q_win)) & 15)
+    return set_err(KVE_EINVAL, "kvevict_score: q_win, k and v must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return set_err(KVE_EINVAL, "kvevict_score: workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = (L->dtype == KVE_BF16)
+                     ? kve::launch_score_bf16(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, ws, s)
+                     : kve::launch_score_f32(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, ws, s);
+  if (e != hipSuccess) return hip_err(e, "kvevict_score");
+  e = kve::launch_pool(G, L->seq_off, pool_kernel, ws, scores, s);
+  if (e != hipSuccess) return hip_err(e, "kvevict_score (pool)");
+  return KVE_OK;
+}
+
+size_t kvevict_select_workspace(const kve_layout* L, const int32_t* bud_off_host, int32_t mode) {
+  kve::SelectGeom G;
+  std::string msg;
+  if (kve::plan_select(L, bud_off_host, mode, &G, &msg) != KVE_OK) return 0;
+  return G.bytes;
+}
+
+kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_t* bud_off,
+                          const int32_t* bud_off_host, int32_t mode, float tau, float tau_w, uint64_t seed,
+                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  kve::SelectGeom G;
+  std::string msg;
+  kve_status st = kve::plan_select(L, bud_off_host, mode, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_select: " + msg);
+  if (!scores || !bud_off || !idx || !bias) return set_err(KVE_EINVAL, "kvevict_select: null tensor pointer");
+  if (mode == KVE_SAMPLE) {
+    if (!(tau > 0.f) || !(tau_w > 0.f)) return set_err(KVE_EINVAL, "kvevict_select: tau and tau_w must be > 0");
+    if (!ws || ws_bytes < G.bytes)
+      return set_err(KVE_EWORKSPACE, "kvevict_select: workspace smaller than kvevict_select_workspace()");
+    if (reinterpret_cast<uintptr_t>(ws) & 255)
+      return set_err(KVE_EINVAL, "kvevict_select: workspace must be 256-byte aligned");
+  }
+  hipError_t e = kve::launch_select(G, scores, L->seq_off, bud_off, tau, tau_w, seed, idx, bias, m_out,
+                                    status_out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "kvevict_select");
+  return KVE_OK;
+}
+
+kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v, const int32_t* bud_off,
+                           const int32_t* bud_off_host, const int32_t* idx, const float* bias,
+                           const int32_t* cap_off, const int32_t* cap_off_host, void* k_c, void* v_c,
+                           float* bias_c, void* stream) {
+  std::string msg;
+  kve_status st = kve::check_compact(L, bud_off_host, cap_off_host, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_compact: " + msg);
+  if (!k || !v || !bud_off || !idx || !bias || !cap_off || !k_c || !v_c || !bias_c)
+    return set_err(KVE_EINVAL, "kvevict_compact: null tensor pointer");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(k_c) |
+       reinterpret_cast<uintptr_t>(v_c)) & 15)
+    return set_err(KVE_EINVAL, "kvevict_compact: k, v, k_c, v_c must be 16-byte aligned");
+  if (k_c == k || v_c == v || k_c == v || v_c == k)
+    return set_err(KVE_EINVAL, "kvevict_compact: outputs must not alias inputs");
+  int maxB = 0;
+  for (int s = 0; s < L->S; ++s) maxB = std::max(maxB, bud_off_host[s + 1] - bud_off_host[s]);
+  const int esize = (L->dtype == KVE_BF16) ? 2 : 4;
+  hipError_t e = kve::launch_compact(L->S, L->Hkv, L->d, esize, L->seq_off_host[L->S], bud_off_host[L->S],
+                                     cap_off_host[L->S], maxB, k, v, L->seq_off, bud_off, idx, bias, cap_off,
+                                     k_c, v_c, bias_c, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "kvevict_compact");
+  return KVE_OK;
+}
+
+size_t kvevict_decode_workspace(const kve_layout* L, int32_t max_cache_len) {
+  kve::DecodeGeom G;
+  std::string msg;
+  // sizing depends on the shape and max_cache_len only (no capacity check)
+  if (kve::plan_decode(L, nullptr, max_cache_len, &G, &msg) != KVE_OK) return 0;
+  return G.bytes;
+}
+
+kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k_c, const void* v_c,
+                               const float* bias_c, const int32_t* cap_off, const int32_t* cap_off_host,
+                               const int32_t* cache_len, int32_t max_cache_len, float sm_scale, float* out,
+                               void* ws, size_t ws_bytes, void* stream) {
+  kve::DecodeGeom G;
+  std::string msg;
+  if (!cap_off_host) return set_err(KVE_EINVAL, "kvevict_decode_snis: cap_off_host is NULL");
+  kve_status st = kve::plan_decode(L, cap_off_host, max_cache_len, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_decode_snis: " + msg);
+  if (!q || !k_c || !v_c || !bias_c || !cap_off || !cache_len || !out)
+    return set_err(KVE_EINVAL, "kvevict_decode_snis: null tensor pointer");
+  if (!(sm_scale > 0.f)) return set_err(KVE_EINVAL, "kvevict_decode_snis: sm_scale must be > 0");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_decode_snis: workspace smaller than kvevict_decode_workspace()");
+  hipError_t e = kve::launch_decode(G, cap_off_host[L->S], q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale,
+                                    out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "kvevict_decode_snis");
+  return KVE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Kernel launchers (one per translation unit), called by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace kve {
+
+hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
+                             const int32_t* seq_off, float sm_scale, int causal, void* ws,
+                             hipStream_t st);
+hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
+                            const int32_t* seq_off, float sm_scale, int causal, void* ws,
+                            hipStream_t st);
+hipError_t launch_merge_f32(const ScoreGeom& G, const int32_t* seq_off, void* ws, hipStream_t st);
+hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, const void* ws,
+                       float* scores, hipStream_t st);
+
+hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
+                         const int32_t* bud_off, float tau, float tau_w, uint64_t seed, int32_t* idx,
+                         float* bias, double* m_out, int32_t* status_out, void* ws, hipStream_t st);
+
+hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t totalB, int64_t totalC,
+                          int maxB, const void* k, const void* v, const int32_t* seq_off,
+                          const int32_t* bud_off, const int32_t* idx, const float* bias,
+                          const int32_t* cap_off, void* k_c, void* v_c, float* bias_c,
+                          hipStream_t st);
+
+hipError_t launch_decode(const DecodeGeom& G, int64_t totalC, const void* q, const void* k_c,
+                         const void* v_c, const float* bias_c, const int32_t* cap_off,
+                         const int32_t* cache_len, float sm_scale, float* out, void* ws,
+                         hipStream_t st);
+
+}  // namespace kve

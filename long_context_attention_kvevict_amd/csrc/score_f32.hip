@@ -1,0 +1,230 @@
+// fp32 eviction scorer (vector ALU; used for fp32 inputs, d in {64, 128}).
+//
+// Same two passes as the bf16 MFMA path ("DropKV" page, §3.4), written for
+// plain fp32 arithmetic: pass 1 produces per-chunk softmax partials of every
+// window row (merged by score_merge into lse2 and o), pass 2 assigns one key
+// per thread and accumulates (p / (1 - p))^2 ||o - v||^2 over all rows of the
+// GQA group, forming o - v explicitly.
+#include "common.h"
+#include "launch.h"
+#include "timing.h"
+
+namespace kve {
+
+constexpr int ROWS32 = 128;
+
+struct F32Args {
+  const float* q_win;
+  const float* k;
+  const float* v;
+  const int32_t* seq_off;
+  int S, Hq, Hkv, w, T, RG, CH, P, causal;
+  float c2;
+  float* part_ml;
+  float* part_o;
+  float* lse2;
+  float* no2;
+  float* o32;
+  float* sraw;
+};
+
+template <int DD>
+__global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
+  const int c = blockIdx.x;
+  const int h = blockIdx.y / a.RG;
+  const int rg = blockIdx.y % a.RG;
+  const int s = blockIdx.z;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int c0 = c * a.CH;
+  if (c0 >= n) return;
+  const int c1 = min(c0 + a.CH, n);
+  const int g = a.Hq / a.Hkv;
+  const int R = g * a.w;
+  const int tid = threadIdx.x;
+  constexpr int NP = 256 / DD;          // key partitions of the o update
+
+  __shared__ float qs[DD];
+  __shared__ float ps[256];
+  __shared__ float red[256 / 64];
+  __shared__ float ored[256];
+
+  const float* kb = a.k + (static_cast<size_t>(h) * a.T + base) * DD;
+  const float* vb = a.v + (static_cast<size_t>(h) * a.T + base) * DD;
+  const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rg);
+
+  for (int rl = 0; rl < ROWS32; ++rl) {
+    const int row = rg * ROWS32 + rl;
+    if (row >= R) break;
+    const int qh = h * g + row / a.w;
+    const int wi = row % a.w;
+    const int pos = n - a.w + wi;
+    __syncthreads();
+    if (tid < DD) qs[tid] = a.q_win[((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * DD + tid];
+    __syncthreads();
+    float m_run = -INFINITY, l_run = 0.f, o_part = 0.f;
+    const int d = tid % DD, part = tid / DD;
+    for (int t0 = c0; t0 < c1; t0 += 256) {
+      const int key = t0 + tid;
+      float x = -INFINITY;
+      if (key < c1 && !(a.causal && key > pos)) {
+        const float* kr = kb + static_cast<size_t>(key) * DD;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < DD; ++e) acc = fmaf(qs[e], kr[e], acc);
+        x = acc * a.c2;
+      }
+      float tm = wave_max(x);
+      __syncthreads();
+      if ((tid & 63) == 0) red[tid >> 6] = tm;
+      __syncthreads();
+      tm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const float m_new = fmaxf(m_run, tm);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float scale = exp2f(m_run - m_use);
+      const float p = exp2f(x - m_use);
+      ps[tid] = p;
+      l_run = l_run * scale + p;       // per-thread partial, combined at the end
+      o_part *= scale;
+      m_run = m_new;
+      __syncthreads();
+      const int kn = min(256, c1 - t0);
+      for (int j = part; j < kn; j += NP) o_part = fmaf(ps[j], vb[static_cast<size_t>(t0 + j) * DD + d], o_part);
+    }
+    // combine l over all threads, o over partitions
+    float lt = wave_sum(l_run);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = lt;
+    ored[tid] = o_part;
+    __syncthreads();
+    const size_t pr = (grp * a.P + c) * ROWS32 + rl;
+    if (tid == 0) {
+      a.part_ml[pr * 2] = m_run;
+      a.part_ml[pr * 2 + 1] = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+    if (tid < DD) {
+      float o = 0.f;
+      for (int q = 0; q < NP; ++q) o += ored[q * DD + tid];
+      a.part_o[pr * DD + tid] = o;
+    }
+  }
+}
+
+// One thread per key; rows of the group staged in LDS 32 at a time.
+template <int DD>
+__global__ __launch_bounds__(256) void score_p2_f32(F32Args a) {
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int c0 = c * a.CH;
+  if (c0 >= n) return;
+  const int c1 = min(c0 + a.CH, n);
+  const int g = a.Hq / a.Hkv;
+  const int R = g * a.w;
+  const int tid = threadIdx.x;
+
+  __shared__ float qs[32 * DD];
+  __shared__ float os[32 * DD];
+  __shared__ float ls[32];
+  __shared__ int ps[32];
+
+  const float* kb = a.k + (static_cast<size_t>(h) * a.T + base) * DD;
+  const float* vb = a.v + (static_cast<size_t>(h) * a.T + base) * DD;
+
+  for (int t0 = c0; t0 < c1; t0 += 256) {
+    const int key = t0 + tid;
+    const bool kok = key < c1;
+    float kr[DD], vr[DD];
+#pragma unroll
+    for (int e = 0; e < DD; ++e) {
+      kr[e] = kok ? kb[static_cast<size_t>(key) * DD + e] : 0.f;
+      vr[e] = kok ? vb[static_cast<size_t>(key) * DD + e] : 0.f;
+    }
+    float sc = 0.f;
+    for (int r0 = 0; r0 < R; r0 += 32) {
+      __syncthreads();
+      for (int i = tid; i < 32 * DD; i += 256) {
+        const int rr = r0 + i / DD, e = i % DD;
+        float qv = 0.f, ov = 0.f;
+        if (rr < R) {
+          const int qh = h * g + rr / a.w, wi = rr % a.w;
+          qv = a.q_win[((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * DD + e];
+          const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rr / ROWS32);
+          ov = a.o32[(grp * ROWS32 + rr % ROWS32) * DD + e];
+        }
+        qs[i] = qv;
+        os[i] = ov;
+      }
+      if (tid < 32) {
+        const int rr = r0 + tid;
+        if (rr < R) {
+          const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rr / ROWS32);
+          ls[tid] = a.lse2[grp * ROWS32 + rr % ROWS32];
+          ps[tid] = n - a.w + rr % a.w;
+        } else {
+          ls[tid] = INFINITY;
+          ps[tid] = -1;
+        }
+      }
+      __syncthreads();
+      if (!kok) continue;
+      const int rn = min(32, R - r0);
+      for (int r = 0; r < rn; ++r) {
+        if (a.causal && key > ps[r]) continue;
+        float dot = 0.f, d2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < DD; ++e) {
+          dot = fmaf(qs[r * DD + e], kr[e], dot);
+          const float df = os[r * DD + e] - vr[e];
+          d2 = fmaf(df, df, d2);
+        }
+        const float x = fmaf(dot, a.c2, -ls[r]);
+        const float y = exp2f(-x) - 1.f;
+        const float y2 = fmaf(y, y, 9.094947e-13f);
+        sc = fmaf(d2, 1.f / y2, sc);
+      }
+    }
+    if (kok) a.sraw[static_cast<size_t>(h) * a.T + base + key] = sc;
+  }
+}
+
+hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
+                            const int32_t* seq_off, float sm_scale, int causal, void* ws,
+                            hipStream_t st) {
+  F32Args a;
+  a.q_win = static_cast<const float*>(q_win);
+  a.k = static_cast<const float*>(k);
+  a.v = static_cast<const float*>(v);
+  a.seq_off = seq_off;
+  a.S = G.S; a.Hq = G.Hq; a.Hkv = G.Hkv; a.w = G.w; a.T = G.T;
+  a.RG = G.RG; a.CH = G.CH; a.P = G.P; a.causal = causal;
+  a.c2 = sm_scale * kLog2e;
+  char* base = static_cast<char*>(ws);
+  a.part_ml = reinterpret_cast<float*>(base + G.off_part_ml);
+  a.part_o = reinterpret_cast<float*>(base + G.off_part_o);
+  a.lse2 = reinterpret_cast<float*>(base + G.off_lse2);
+  a.no2 = reinterpret_cast<float*>(base + G.off_no2);
+  a.o32 = reinterpret_cast<float*>(base + G.off_ohi);
+  a.sraw = reinterpret_cast<float*>(base + G.off_sraw);
+  dim3 grid(G.P, G.Hkv * G.RG, G.S);
+  stage_begin(ST_SCORE_P1, st);
+  if (G.d == 64) hipLaunchKernelGGL(score_p1_f32<64>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(score_p1_f32<128>, grid, dim3(256), 0, st, a);
+  stage_end(ST_SCORE_P1, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  stage_begin(ST_SCORE_MERGE, st);
+  e = launch_merge_f32(G, seq_off, ws, st);
+  stage_end(ST_SCORE_MERGE, st);
+  if (e != hipSuccess) return e;
+  dim3 grid2(G.P, G.Hkv, G.S);
+  stage_begin(ST_SCORE_P2, st);
+  if (G.d == 64) hipLaunchKernelGGL(score_p2_f32<64>, grid2, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(score_p2_f32<128>, grid2, dim3(256), 0, st, a);
+  stage_end(ST_SCORE_P2, st);
+  return hipGetLastError();
+}
+
+}  // namespace kve

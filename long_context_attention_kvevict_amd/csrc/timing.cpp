@@ -1,0 +1,89 @@
+// Event-based stage timing (see timing.h).  Process-wide, not thread-safe:
+// meant for a benchmark driving one stream.
+#include "timing.h"
+
+#include <vector>
+
+#include "../../include/kvevict.h"
+
+namespace kve {
+
+namespace {
+
+struct Rec {
+  int stage;
+  hipEvent_t begin, end;
+};
+
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> pool;   // reusable events
+  size_t next = 0;
+  std::vector<Rec> recs;
+  hipEvent_t open[ST_COUNT] = {};
+};
+
+Timing g;
+constexpr size_t kPool = 4096;
+
+hipEvent_t take_event() {
+  if (g.next >= g.pool.size()) return nullptr;
+  return g.pool[g.next++];
+}
+
+}  // namespace
+
+void stage_begin(int stage, hipStream_t st) {
+  if (!g.on) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, st) == hipSuccess) g.open[stage] = e;
+  else g.open[stage] = nullptr;
+}
+
+void stage_end(int stage, hipStream_t st) {
+  if (!g.on) return;
+  hipEvent_t b = g.open[stage];
+  hipEvent_t e = take_event();
+  if (!b || !e) return;
+  if (hipEventRecord(e, st) == hipSuccess) g.recs.push_back({stage, b, e});
+  g.open[stage] = nullptr;
+}
+
+}  // namespace kve
+
+extern "C" {
+
+int32_t kvevict_timing_enable(int32_t on) {
+  using namespace kve;
+  if (on && g.pool.empty()) {
+    g.pool.reserve(kPool);
+    for (size_t i = 0; i < kPool; ++i) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return KVE_EHIP;
+      g.pool.push_back(e);
+    }
+  }
+  g.on = on != 0;
+  g.next = 0;
+  g.recs.clear();
+  return KVE_OK;
+}
+
+int32_t kvevict_timing_summary(double* avg_ms, int32_t* counts, int32_t n_stages) {
+  using namespace kve;
+  if (!avg_ms || !counts) return KVE_EINVAL;
+  for (int i = 0; i < n_stages; ++i) { avg_ms[i] = 0.0; counts[i] = 0; }
+  for (const Rec& r : g.recs) {
+    if (hipEventSynchronize(r.end) != hipSuccess) return KVE_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.begin, r.end) != hipSuccess) return KVE_EHIP;
+    if (r.stage < n_stages) { avg_ms[r.stage] += ms; counts[r.stage] += 1; }
+  }
+  for (int i = 0; i < n_stages; ++i)
+    if (counts[i]) avg_ms[i] /= counts[i];
+  g.next = 0;
+  g.recs.clear();
+  return KVE_OK;
+}
+
+}  // extern "C"

@@ -95,6 +95,47 @@ def group_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, h: int, g: int
     return total
 
 
+def group_scores_at(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, h: int, g: int,
+                    sm_scale: float, causal: bool, keys: np.ndarray, row_chunk: int = 32) -> np.ndarray:
+    """The same group score as group_scores, evaluated only at `keys`
+    (sorted unique indices).  Every row's softmax still spans all n keys;
+    only the per-key perturbation terms are restricted.  For large n."""
+    w, d = q_win.shape[1], q_win.shape[2]
+    n = k.shape[0]
+    keys = np.asarray(keys, dtype=np.int64)
+    rows = q_win[h * g:(h + 1) * g].reshape(g * w, d)
+    pos_all = np.tile(row_positions(n, w), g)
+    total = np.zeros(len(keys))
+    vk = v[keys]
+    for r0 in range(0, rows.shape[0], row_chunk):
+        q = rows[r0:r0 + row_chunk]
+        pos = pos_all[r0:r0 + row_chunk] if causal else None
+        att = window_attention(q, k, v, pos, sm_scale)
+        alpha, e, z, o = att["alpha"], att["e"], att["z"], att["o"]
+        a = alpha[:, keys]
+        one_minus = 1.0 - a
+        dist2 = (o * o).sum(1)[:, None] + (vk * vk).sum(1)[None, :] - 2.0 * (o @ vk.T)
+        dist2 = np.maximum(dist2, 0.0)
+        jstar = np.argmax(alpha, axis=1)
+        for r in range(q.shape[0]):
+            hit = np.nonzero(keys == jstar[r])[0]
+            if len(hit):
+                c = hit[0]
+                others = e[r].copy()
+                others[jstar[r]] = 0.0
+                one_minus[r, c] = others.sum() / z[r]
+                wts = alpha[r].copy()
+                wts[jstar[r]] = 0.0
+                diff = wts @ (v - v[jstar[r]][None, :])
+                dist2[r, c] = diff @ diff
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(a > 0.0, a / one_minus, 0.0)
+            contrib = ratio * ratio * dist2
+        contrib = np.where(one_minus == 0.0, 0.0, contrib)
+        total += contrib.sum(axis=0)
+    return total
+
+
 def max_pool(s: np.ndarray, kernel: int) -> np.ndarray:
     """s'_j = max of s_k over |k - j| <= (kernel-1)/2, 0 <= k < n."""
     if kernel <= 1:

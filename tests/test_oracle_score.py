@@ -183,3 +183,18 @@ def test_value_norm_example_ordering():
     pa = a["alpha"] / (1 - a["alpha"]) * a["value_norm"]
     pb = b["alpha"] / (1 - b["alpha"]) * b["value_norm"]
     assert pa > pb
+
+
+def test_scores_at_keys_equals_full_scores():
+    # the sampled-key evaluation used at full sizes equals the full vector
+    from oracle.score import group_scores_at
+    rng = np.random.default_rng(31)
+    Hq, Hkv, w, n, d = 4, 2, 5, 300, 16
+    q_win = rng.standard_normal((Hq, w, d))
+    k = rng.standard_normal((n, d)) * 1.5
+    v = rng.standard_normal((n, d))
+    k[7] = 6 * q_win[2, 4] / np.linalg.norm(q_win[2, 4]) * np.sqrt(d)   # a dominant key
+    full = group_scores(q_win, k, v, 1, 2, 0.25, True)
+    keys = np.array([0, 7, 8, 150, 299])
+    got = group_scores_at(q_win, k, v, 1, 2, 0.25, True, keys, row_chunk=3)
+    assert np.allclose(got, full[keys], rtol=1e-10, atol=1e-14 * full.max())
