@@ -78,13 +78,12 @@ kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_
   kve_status st = kve::plan_select(L, bud_off_host, mode, &G, &msg);
   if (st != KVE_OK) return set_err(st, "kvevict_select: " + msg);
   if (!scores || !bud_off || !idx || !bias) return set_err(KVE_EINVAL, "kvevict_select: null tensor pointer");
-  if (mode == KVE_SAMPLE) {
-    if (!(tau > 0.f) || !(tau_w > 0.f)) return set_err(KVE_EINVAL, "kvevict_select: tau and tau_w must be > 0");
-    if (!ws || ws_bytes < G.bytes)
-      return set_err(KVE_EWORKSPACE, "kvevict_select: workspace smaller than kvevict_select_workspace()");
-    if (reinterpret_cast<uintptr_t>(ws) & 255)
-      return set_err(KVE_EINVAL, "kvevict_select: workspace must be 256-byte aligned");
-  }
+  if (mode == KVE_SAMPLE && (!(tau > 0.f) || !(tau_w > 0.f)))
+    return set_err(KVE_EINVAL, "kvevict_select: tau and tau_w must be > 0");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_select: workspace smaller than kvevict_select_workspace()");
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return set_err(KVE_EINVAL, "kvevict_select: workspace must be 256-byte aligned");
   hipError_t e = kve::launch_select(G, scores, L->seq_off, bud_off, tau, tau_w, seed, idx, bias, m_out,
                                     status_out, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_err(e, "kvevict_select");

@@ -106,11 +106,15 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   SelectGeom g{};
   g.S = L->S; g.Hkv = L->Hkv; g.T = static_cast<int>(T); g.max_len = max_len; g.mode = mode;
   g.total_B = bud_off_host[L->S];
-  const size_t plane = static_cast<size_t>(g.Hkv) * g.T * sizeof(double);
+  g.nchunk = (max_len + kSelChunk - 1) / kSelChunk;
+  const size_t SH = static_cast<size_t>(g.S) * g.Hkv;
+  const size_t plane = (mode == KVE_SAMPLE) ? static_cast<size_t>(g.Hkv) * g.T * sizeof(double) : 0;
   size_t off = 0;
   g.off_a = off; off = align256(off + plane);
   g.off_b = off; off = align256(off + plane);
-  g.off_hist = off; off = align256(off + static_cast<size_t>(g.S) * g.Hkv * 64 * sizeof(double));
+  g.off_hist = off; off = align256(off + kSelLevels32 * SH * kSelBins * sizeof(int32_t));
+  g.off_cnt = off; off = align256(off + SH * g.nchunk * 2 * sizeof(int32_t));
+  g.off_state = off; off = align256(off + SH * 2 * sizeof(uint32_t));
   g.bytes = off;
   *G = g;
   return KVE_OK;

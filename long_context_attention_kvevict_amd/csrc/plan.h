@@ -25,10 +25,20 @@ struct ScoreGeom {
   size_t bytes;
 };
 
+// Keys per workgroup of the multi-workgroup radix select and its histogram
+// width (2048 bins = 11-bit digits).
+constexpr int kSelChunk = 4096;
+constexpr int kSelBins = 2048;
+constexpr int kSelLevels32 = 3;
+
 struct SelectGeom {
   int S, Hkv, T, max_len, mode;
+  int nchunk;                      // chunks of kSelChunk keys per (sequence, head)
   int64_t total_B;
-  size_t off_a, off_b, off_hist;   // fp64 scratch planes [S*Hkv][max_len]
+  size_t off_a, off_b;             // sample mode: fp64 planes [Hkv][T]
+  size_t off_hist;                 // top-k: int [levels][S*Hkv][kSelBins]
+  size_t off_cnt;                  // top-k: int [S*Hkv][nchunk][2]
+  size_t off_state;                // top-k: uint32 [S*Hkv][2]
   size_t bytes;
 };
 

@@ -266,56 +266,87 @@ __global__ __launch_bounds__(256, 2) void score_p1_bf16(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup of DD threads per (s, h, rg) and 8 rows; thread = feature d.
+// One wave per window row.  Lanes l and l + 32 take alternate chunks (two
+// independent load streams); each lane holds DD/32 consecutive features.
+// Chunks wholly beyond a row's causal horizon carry max = -inf and weight 0.
 template <int DD, bool BF16OUT>
-__global__ __launch_bounds__(DD) void score_merge(ScoreArgs a, float* o32) {
-  const int grp = blockIdx.x;                  // (s*Hkv + h)*RG + rg
+__global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
+  constexpr int F = DD / 32;
+  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);   // grp * ROWS + rl
+  const int grp = gr / ROWS;
+  const int rl = gr % ROWS;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, ln = lane & 31;
   const int s = grp / (a.Hkv * a.RG);
   const int rg = grp % a.RG;
   const int n = a.seq_off[s + 1] - a.seq_off[s];
   const int nch = (n + a.CH - 1) / a.CH;
   const int R = (a.Hq / a.Hkv) * a.w;
-  const int d = threadIdx.x;
-  __shared__ float red[DD / 64];
-  for (int rr = 0; rr < 8; ++rr) {
-    const int rl = blockIdx.y * 8 + rr;
-    const int row = rg * ROWS + rl;
-    const size_t ro = static_cast<size_t>(grp) * ROWS + rl;
-    if (row >= R) {
-      if (d == 0) { a.lse2[ro] = INFINITY; a.no2[ro] = 0.f; }
-      if (BF16OUT) { a.ohi[ro * DD + d] = 0; a.olo[ro * DD + d] = 0; }
-      else o32[ro * DD + d] = 0.f;
-      continue;
+  const size_t ro = static_cast<size_t>(gr);
+  if (rg * ROWS + rl >= R) {   // padding row of the last row group
+    if (lane == 0) { a.lse2[ro] = INFINITY; a.no2[ro] = 0.f; }
+    if (half == 0) {
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        if (BF16OUT) { a.ohi[ro * DD + ln * F + f] = 0; a.olo[ro * DD + ln * F + f] = 0; }
+        else o32[ro * DD + ln * F + f] = 0.f;
+      }
     }
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c)
-      M = fmaxf(M, a.part_ml[((static_cast<size_t>(grp) * a.P + c) * ROWS + rl) * 2]);
-    float L = 0.f, o = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const size_t pr = (static_cast<size_t>(grp) * a.P + c) * ROWS + rl;
-      const float m = a.part_ml[pr * 2];
-      const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      L += a.part_ml[pr * 2 + 1] * f;
-      o += a.part_o[pr * DD + d] * f;
-    }
-    o /= L;
-    float sq = wave_sum(o * o);
-    if ((d & 63) == 0) red[d >> 6] = sq;
-    __syncthreads();
-    if (d == 0) {
-      float t = 0.f;
-      for (int i = 0; i < DD / 64; ++i) t += red[i];
-      a.no2[ro] = t;
-      a.lse2[ro] = M + log2f(L);
-    }
-    __syncthreads();
-    if (BF16OUT) {
-      const float x = -2.f * o;
-      const uint16_t hi = f32_to_bf16(x);
-      a.ohi[ro * DD + d] = hi;
-      a.olo[ro * DD + d] = f32_to_bf16(x - bf16_to_f32(hi));
+    return;
+  }
+  const size_t cstride_ml = static_cast<size_t>(ROWS) * 2;
+  const size_t cstride_o = static_cast<size_t>(ROWS) * DD;
+  const float* ml = a.part_ml + (static_cast<size_t>(grp) * a.P * ROWS + rl) * 2;
+  const float* po = a.part_o + (static_cast<size_t>(grp) * a.P * ROWS + rl) * DD + ln * F;
+  float M = -INFINITY;
+  for (int c = lane; c < nch; c += 64) M = fmaxf(M, ml[c * cstride_ml]);
+  M = wave_max(M);
+  float L = 0.f;
+  float acc[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = 0.f;
+#pragma unroll 8
+  for (int c = half; c < nch; c += 2) {
+    const float m = ml[c * cstride_ml];
+    const float l = ml[c * cstride_ml + 1];
+    const float wgt = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    L = fmaf(l, wgt, L);
+    if (F == 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(po + c * cstride_o);
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = fmaf(x[f], wgt, acc[f]);
     } else {
-      o32[ro * DD + d] = o;
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = fmaf(po[c * cstride_o + f], wgt, acc[f]);
+    }
+  }
+  L += xor32(L);
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] += xor32(acc[f]);
+  const float inv = 1.f / L;
+  float sq = 0.f;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    acc[f] *= inv;
+    sq = fmaf(acc[f], acc[f], sq);
+  }
+  // sum over the 32 lanes of one half (both halves hold identical values)
+  for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  if (lane == 0) {
+    a.no2[ro] = sq;
+    a.lse2[ro] = M + log2f(L);
+  }
+  if (half == 0) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      if (BF16OUT) {
+        const float x = -2.f * acc[f];
+        const uint16_t hi = f32_to_bf16(x);
+        a.ohi[ro * DD + ln * F + f] = hi;
+        a.olo[ro * DD + ln * F + f] = f32_to_bf16(x - bf16_to_f32(hi));
+      } else {
+        o32[ro * DD + ln * F + f] = acc[f];
+      }
     }
   }
 }
@@ -480,7 +511,7 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_SCORE_MERGE, st);
-  hipLaunchKernelGGL((score_merge<D, true>), dim3(G.S * G.Hkv * G.RG, ROWS / 8), dim3(D), 0, st, a,
+  hipLaunchKernelGGL((score_merge<D, true>), dim3(G.S * G.Hkv * G.RG * (ROWS / 4)), dim3(256), 0, st, a,
                      static_cast<float*>(nullptr));
   stage_end(ST_SCORE_MERGE, st);
   e = hipGetLastError();
@@ -502,9 +533,9 @@ hipError_t launch_merge_f32(const ScoreGeom& G, const int32_t* seq_off, void* ws
   a.lse2 = reinterpret_cast<float*>(base + G.off_lse2);
   a.no2 = reinterpret_cast<float*>(base + G.off_no2);
   float* o32 = reinterpret_cast<float*>(base + G.off_ohi);
-  dim3 grid(G.S * G.Hkv * G.RG, ROWS / 8);
-  if (G.d == 64) hipLaunchKernelGGL((score_merge<64, false>), grid, dim3(64), 0, st, a, o32);
-  else hipLaunchKernelGGL((score_merge<128, false>), grid, dim3(128), 0, st, a, o32);
+  dim3 grid(G.S * G.Hkv * G.RG * (ROWS / 4));
+  if (G.d == 64) hipLaunchKernelGGL((score_merge<64, false>), grid, dim3(256), 0, st, a, o32);
+  else hipLaunchKernelGGL((score_merge<128, false>), grid, dim3(256), 0, st, a, o32);
   return hipGetLastError();
 }
 

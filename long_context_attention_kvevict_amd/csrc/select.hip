@@ -73,72 +73,262 @@ __device__ __forceinline__ void pick_digit(const int* hist, int need, int* digit
   *above = cum;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_topk(const float* __restrict__ scores,
-                                                          const int32_t* __restrict__ seq_off,
-                                                          const int32_t* __restrict__ bud_off, int T,
-                                                          int64_t totalB, int Hkv, int32_t* __restrict__ idx,
-                                                          float* __restrict__ bias,
-                                                          double* __restrict__ m_out,
-                                                          int32_t* __restrict__ status_out) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  if (threadIdx.x == 0) {
-    if (m_out) m_out[s * Hkv + h] = 0.0;
-    if (status_out) status_out[s * Hkv + h] = KVE_OK;
+// ------------------------------------------------------------------ top-k
+// Multi-workgroup radix select.  Every (sequence, KV head) is cut into chunks
+// of TK_CHUNK keys, one workgroup each.  Three histogram launches resolve the
+// B-th largest key digit by digit (bits 31..21, 20..10, 9..0); a count launch
+// tallies keys above / equal to that threshold per chunk; the write launch
+// places each chunk's kept indices after those of all earlier chunks, so the
+// output is ascending.  Integer atomics only: the result is deterministic.
+constexpr int TK_THREADS = 256;
+constexpr int TK_PER = 16;
+constexpr int TK_CHUNK = TK_THREADS * TK_PER;
+constexpr int TK_BINS = 2048;
+constexpr int TK_LEVELS = 3;
+static_assert(TK_CHUNK == kSelChunk && TK_BINS == kSelBins && TK_LEVELS == kSelLevels32,
+              "host and device select geometry disagree");
+
+__device__ __forceinline__ int tk_shift(int lv) { return lv == 0 ? 21 : (lv == 1 ? 10 : 0); }
+
+// Inclusive prefix sum over a 256-thread block; *total gets the block sum.
+// lds: 4 ints.  Two barriers.
+__device__ __forceinline__ int block_incl_scan256(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
   }
+  if (lane == 63) lds[wave] = v;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int wv = 0; wv < 4; ++wv) {
+    const int c = lds[wv];
+    if (wv < wave) off += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return v + off;
+}
+
+// Scans a TK_BINS histogram from the top bin down; returns the bin at which
+// the running count first reaches `need` and the count strictly above it.
+// Thread t owns bins 2047-8t .. 2040-8t.  lds: 6 ints.
+__device__ void tk_pick(const int* __restrict__ gh, int need, int* lds, int* digit, int* above) {
+  const int t = threadIdx.x;
+  int c[8];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    c[i] = gh[TK_BINS - 1 - 8 * t - i];
+    sum += c[i];
+  }
+  if (t == 0) { lds[4] = 0; lds[5] = 0; }
+  int total;
+  const int incl = block_incl_scan256(sum, lds, &total);   // barriers order the init above
+  const int excl = incl - sum;
+  if (excl < need && need <= incl) {
+    int cum = excl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (cum + c[i] >= need) {
+        lds[4] = TK_BINS - 1 - 8 * t - i;
+        lds[5] = cum;
+        break;
+      }
+      cum += c[i];
+    }
+  }
+  __syncthreads();
+  *digit = lds[4];
+  *above = lds[5];
+  __syncthreads();
+}
+
+// Resolves levels 0 .. nlv-1: key prefix, its mask and the count still
+// needed among keys carrying that prefix.
+__device__ void tk_resolve(const int* __restrict__ hist, int SH, int sh, int nlv, int B, int* lds,
+                           uint32_t* prefix, uint32_t* mask, int* need) {
+  uint32_t p = 0, m = 0;
+  int nd = B;
+  for (int lv = 0; lv < nlv; ++lv) {
+    int dg, ab;
+    tk_pick(hist + (static_cast<size_t>(lv) * SH + sh) * TK_BINS, nd, lds, &dg, &ab);
+    const int sft = tk_shift(lv);
+    const uint32_t width_mask = (lv == 2) ? 0x3ffu : 0x7ffu;
+    p |= static_cast<uint32_t>(dg) << sft;
+    m |= width_mask << sft;
+    nd -= ab;
+  }
+  *prefix = p;
+  *mask = m;
+  *need = nd;
+}
+
+__global__ __launch_bounds__(256) void topk_zero(int* __restrict__ hist, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) hist[i] = 0;
+}
+
+template <int LV>
+__global__ __launch_bounds__(TK_THREADS) void topk_hist(const float* __restrict__ scores,
+                                                        const int32_t* __restrict__ seq_off,
+                                                        const int32_t* __restrict__ bud_off, int T, int Hkv,
+                                                        int SH, int* __restrict__ hist) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = seq_off[s];
   const int n = seq_off[s + 1] - base;
   const int B = bud_off[s + 1] - bud_off[s];
-  int32_t* out = idx + h * totalB + bud_off[s];
-  float* bout = bias + h * totalB + bud_off[s];
-  const float* sc = scores + static_cast<size_t>(h) * T + base;
-  const int tid = threadIdx.x;
-  if (B <= 0) return;
-  if (B >= n) {
-    for (int j = tid; j < n; j += SEL_THREADS) { out[j] = j; bout[j] = 0.f; }
-    return;
-  }
-  __shared__ int hist[256];
-  __shared__ int scan_lds[2 * SEL_WAVES];
-  __shared__ int sh_digit, sh_above;
-
+  const int j0 = ch * TK_CHUNK;
+  if (B <= 0 || B >= n || j0 >= n) return;
+  const int sh = s * Hkv + h;
+  __shared__ int lh[TK_BINS];
+  __shared__ int lds[8];
+  for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) lh[i] = 0;
   uint32_t prefix = 0, mask = 0;
   int need = B;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += SEL_THREADS) {
+  if (LV > 0) tk_resolve(hist, SH, sh, LV, B, lds, &prefix, &mask, &need);
+  __syncthreads();
+  const float* sc = scores + static_cast<size_t>(h) * T + base;
+  const int sft = tk_shift(LV);
+  const uint32_t dmask = (LV == 2) ? 0x3ffu : 0x7ffu;
+#pragma unroll 4
+  for (int i = 0; i < TK_PER; ++i) {
+    const int j = j0 + i * TK_THREADS + threadIdx.x;
+    if (j < n) {
       const uint32_t u = f32_order_key(sc[j]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+      if ((u & mask) == prefix) atomicAdd(&lh[(u >> sft) & dmask], 1);
     }
-    __syncthreads();
-    if (tid == 0) pick_digit(hist, need, &sh_digit, &sh_above);
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(sh_digit) << shift;
-    mask |= 255u << shift;
-    need -= sh_above;
-    __syncthreads();
   }
-  const uint32_t thr = prefix;   // key of the B-th largest; `need` equal keys are taken
-  int run_eq = 0, run_sel = 0;
-  for (int j0 = 0; j0 < n; j0 += SEL_THREADS) {
-    const int j = j0 + tid;
-    uint32_t u = 0;
-    if (j < n) u = f32_order_key(sc[j]);
-    const bool gt = j < n && u > thr;
-    const bool eq = j < n && u == thr;
-    int pe, dummy, te, td;
-    block_scan2(eq, false, &pe, &dummy, &te, &td, scan_lds);
-    const bool take = gt || (eq && run_eq + pe < need);
-    int ps, tsel;
-    block_scan2(take, false, &ps, &dummy, &tsel, &td, scan_lds);
-    if (take && run_sel + ps < B) {   // bounded even if the threshold logic were off
-      out[run_sel + ps] = j;
-      bout[run_sel + ps] = 0.f;
+  __syncthreads();
+  int* gh = hist + (static_cast<size_t>(LV) * SH + sh) * TK_BINS;
+  for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) {
+    const int c = lh[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// Per chunk: keys above the threshold and keys equal to it.  Chunk 0 also
+// stores the threshold and the number of equal keys to keep.
+__global__ __launch_bounds__(TK_THREADS) void topk_count(const float* __restrict__ scores,
+                                                         const int32_t* __restrict__ seq_off,
+                                                         const int32_t* __restrict__ bud_off, int T, int Hkv,
+                                                         int SH, int nchunk, const int* __restrict__ hist,
+                                                         int* __restrict__ cnt, uint32_t* __restrict__ state) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = seq_off[s];
+  const int n = seq_off[s + 1] - base;
+  const int B = bud_off[s + 1] - bud_off[s];
+  const int j0 = ch * TK_CHUNK;
+  if (B <= 0 || B >= n || j0 >= n) return;
+  const int sh = s * Hkv + h;
+  __shared__ int lds[8];
+  uint32_t thr, mask;
+  int need;
+  tk_resolve(hist, SH, sh, TK_LEVELS, B, lds, &thr, &mask, &need);
+  const float* sc = scores + static_cast<size_t>(h) * T + base;
+  int gt = 0, eq = 0;
+#pragma unroll 4
+  for (int i = 0; i < TK_PER; ++i) {
+    const int j = j0 + i * TK_THREADS + threadIdx.x;
+    if (j < n) {
+      const uint32_t u = f32_order_key(sc[j]);
+      gt += (u > thr);
+      eq += (u == thr);
     }
-    run_eq += te;
-    run_sel += tsel;
+  }
+  const int packed = (gt << 16) | eq;   // each count <= TK_CHUNK < 2^16
+  int tot;
+  block_incl_scan256(packed, lds, &tot);
+  if (threadIdx.x == 0) {
+    cnt[(static_cast<size_t>(sh) * nchunk + ch) * 2 + 0] = tot >> 16;
+    cnt[(static_cast<size_t>(sh) * nchunk + ch) * 2 + 1] = tot & 0xffff;
+    if (ch == 0) {
+      state[sh * 2 + 0] = thr;
+      state[sh * 2 + 1] = static_cast<uint32_t>(need);
+    }
+  }
+}
+
+// Ordered write: thread t owns keys j0 + 16t .. j0 + 16t + 15.
+__global__ __launch_bounds__(TK_THREADS) void topk_write(const float* __restrict__ scores,
+                                                         const int32_t* __restrict__ seq_off,
+                                                         const int32_t* __restrict__ bud_off, int T, int Hkv,
+                                                         int64_t totalB, int nchunk, const int* __restrict__ cnt,
+                                                         const uint32_t* __restrict__ state,
+                                                         int32_t* __restrict__ idx, float* __restrict__ bias,
+                                                         double* __restrict__ m_out,
+                                                         int32_t* __restrict__ status_out) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = seq_off[s];
+  const int n = seq_off[s + 1] - base;
+  const int B = bud_off[s + 1] - bud_off[s];
+  const int j0 = ch * TK_CHUNK;
+  const int sh = s * Hkv + h;
+  if (ch == 0 && threadIdx.x == 0) {
+    if (m_out) m_out[sh] = 0.0;
+    if (status_out) status_out[sh] = KVE_OK;
+  }
+  if (B <= 0 || j0 >= n) return;
+  int32_t* out = idx + h * totalB + bud_off[s];
+  float* bout = bias + h * totalB + bud_off[s];
+  if (B >= n) {
+    for (int i = threadIdx.x; i < TK_CHUNK; i += TK_THREADS) {
+      const int j = j0 + i;
+      if (j < n) { out[j] = j; bout[j] = 0.f; }
+    }
+    return;
+  }
+  __shared__ int lds[8];
+  const uint32_t thr = state[sh * 2 + 0];
+  const int need = static_cast<int>(state[sh * 2 + 1]);
+  // keys above / equal to the threshold in earlier chunks
+  int gt_b = 0, eq_b = 0;
+  for (int c = threadIdx.x; c < ch; c += TK_THREADS) {
+    gt_b += cnt[(static_cast<size_t>(sh) * nchunk + c) * 2 + 0];
+    eq_b += cnt[(static_cast<size_t>(sh) * nchunk + c) * 2 + 1];
+  }
+  int tot;
+  block_incl_scan256(gt_b, lds, &tot);
+  gt_b = tot;
+  block_incl_scan256(eq_b, lds, &tot);
+  eq_b = tot;
+  const float* sc = scores + static_cast<size_t>(h) * T + base;
+  const int jt = j0 + TK_PER * threadIdx.x;
+  uint32_t u[TK_PER];
+  int neq = 0;
+#pragma unroll
+  for (int i = 0; i < TK_PER; ++i) {
+    u[i] = (jt + i < n) ? f32_order_key(sc[jt + i]) : 0u;
+    neq += (jt + i < n) && (u[i] == thr);
+  }
+  int eq_tot;
+  int eq_rank = eq_b + block_incl_scan256(neq, lds, &eq_tot) - neq;
+  int ntake = 0;
+  uint32_t take_bits = 0;
+#pragma unroll
+  for (int i = 0; i < TK_PER; ++i) {
+    const bool in = jt + i < n;
+    const bool gt = in && u[i] > thr;
+    const bool eq = in && u[i] == thr;
+    const bool take = gt || (eq && eq_rank < need);
+    eq_rank += eq;
+    take_bits |= static_cast<uint32_t>(take) << i;
+    ntake += take;
+  }
+  int take_tot;
+  int pos = gt_b + min(eq_b, need) + block_incl_scan256(ntake, lds, &take_tot) - ntake;
+#pragma unroll
+  for (int i = 0; i < TK_PER; ++i) {
+    if ((take_bits >> i) & 1u) {
+      if (pos < B) {   // bounded even if the counts were inconsistent
+        out[pos] = jt + i;
+        bout[pos] = 0.f;
+      }
+      ++pos;
+    }
   }
 }
 
@@ -362,13 +552,24 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
                          float* bias, double* m_out, int32_t* status_out, void* ws, hipStream_t st) {
   dim3 grid(G.Hkv, G.S);
   if (G.mode == KVE_TOPK) {
+    char* wsb = static_cast<char*>(ws);
+    int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
+    int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
+    uint32_t* state = reinterpret_cast<uint32_t*>(wsb + G.off_state);
+    const int SH = G.S * G.Hkv;
+    const int nhist = TK_LEVELS * SH * TK_BINS;
+    dim3 cgrid(G.nchunk, G.Hkv, G.S);
     stage_begin(ST_SELECT, st);
-    hipLaunchKernelGGL(select_topk, grid, dim3(SEL_THREADS), 0, st, scores, seq_off, bud_off, G.T,
-                       G.total_B, G.Hkv, idx, bias, m_out, status_out);
+    hipLaunchKernelGGL(topk_zero, dim3((nhist + 255) / 256), dim3(256), 0, st, hist, nhist);
+    hipLaunchKernelGGL(topk_hist<0>, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH, hist);
+    hipLaunchKernelGGL(topk_hist<1>, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH, hist);
+    hipLaunchKernelGGL(topk_hist<2>, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH, hist);
+    hipLaunchKernelGGL(topk_count, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH,
+                       G.nchunk, hist, cnt, state);
+    hipLaunchKernelGGL(topk_write, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv,
+                       G.total_B, G.nchunk, cnt, state, idx, bias, m_out, status_out);
     stage_end(ST_SELECT, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return hipSuccess;
+    return hipGetLastError();
   }
   char* base = static_cast<char*>(ws);
   stage_begin(ST_SELECT, st);
