@@ -64,11 +64,21 @@ kve_status plan_score(const kve_layout* L, ScoreGeom* G, std::string* msg) {
   g.T = static_cast<int>(T); g.dtype = L->dtype; g.max_len = max_len;
   g.R = (L->Hq / L->Hkv) * L->w;
   g.RG = (g.R + 127) / 128;
-  // chunk length: about 512 workgroups over the batch, multiple of 256 keys
   const int64_t work = static_cast<int64_t>(T) * g.Hkv * g.RG;
-  int64_t ch = (work + 511) / 512;
-  ch = std::max<int64_t>(256, ((ch + 255) / 256) * 256);
-  g.CH = static_cast<int>(std::min<int64_t>(ch, ((max_len + 255) / 256) * 256));
+  const int64_t len_cap = ((max_len + 255) / 256) * 256;
+  int64_t ch;
+  if (L->dtype == KVE_BF16) {
+    // about one 8-wave workgroup per CU (256), multiple of 256 keys, at most
+    // kScoreChunkMax
+    ch = (work + 255) / 256;
+    ch = std::max<int64_t>(256, ((ch + 255) / 256) * 256);
+    ch = std::min<int64_t>(ch, kScoreChunkMax);
+  } else {
+    // about 512 workgroups over the batch, multiple of 256 keys
+    ch = (work + 511) / 512;
+    ch = std::max<int64_t>(256, ((ch + 255) / 256) * 256);
+  }
+  g.CH = static_cast<int>(std::min<int64_t>(ch, len_cap));
   g.P = (max_len + g.CH - 1) / g.CH;
   g.pool_rg = (L->dtype == KVE_BF16) ? g.RG : 1;
   const size_t groups = static_cast<size_t>(g.S) * g.Hkv * g.RG;
@@ -78,6 +88,7 @@ kve_status plan_score(const kve_layout* L, ScoreGeom* G, std::string* msg) {
   g.off_vnorm = off;   off = align256(off + static_cast<size_t>(g.Hkv) * g.T * sizeof(float));
   g.off_lse2 = off;    off = align256(off + groups * 128 * sizeof(float));
   g.off_no2 = off;     off = align256(off + groups * 128 * sizeof(float));
+  g.off_no2d = off;    off = align256(off + groups * 128 * sizeof(float));
   // bf16: hi/lo planes of -2o; fp32: o itself (stored in the "hi" region)
   const size_t oel = (L->dtype == KVE_BF16) ? 2 : 4;
   g.off_ohi = off;     off = align256(off + groups * 128 * static_cast<size_t>(g.d) * oel);

@@ -11,6 +11,10 @@
 
 namespace kve {
 
+// Largest key chunk one scorer workgroup handles (its per-key LDS buffers
+// are sized for it).
+constexpr int kScoreChunkMax = 4096;
+
 // Geometry of one kvevict_score call; the workspace is carved into the
 // regions below (byte offsets, each 256-byte aligned).
 struct ScoreGeom {
@@ -21,7 +25,7 @@ struct ScoreGeom {
   int CH;       // keys per chunk (multiple of 256)
   int P;        // chunks per sequence (grid x), ceil(max_len / CH)
   int pool_rg;  // partial score planes summed by the pool kernel
-  size_t off_part_ml, off_part_o, off_vnorm, off_lse2, off_no2, off_ohi, off_olo, off_sraw;
+  size_t off_part_ml, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw;
   size_t bytes;
 };
 

@@ -6,16 +6,23 @@
 //   FlashAttention-2 style forward pass yields each row's log-sum-exp and
 //   output; split-K partials are merged afterwards.)
 // Merge (score_merge): combines the chunk partials of each row into its
-//   log2-sum-exp, o (fp32), ||o||^2 and a bf16 hi/lo split of -2 o.
+//   log2-sum-exp, ||o||^2 and a bf16 hi/lo split of -2 o.
 // Pass 2 (score_p2_bf16): recomputes the logits, forms the softmax weight
 //   p = 2^(x - lse2), the distance ||o - v||^2 = ||o||^2 + ||v||^2 - 2 <o, v>
 //   with <o, v> from an MFMA contraction, and accumulates
 //   (p / (1 - p))^2 ||o - v||^2 over all rows of the group for each key
 //   ("DropKV" page, §3.3 window score and §3.4 scoring kernel).
 //
-// Work decomposition: a workgroup of 4 waves owns one (sequence, KV head,
-// row group of 128 rows, key chunk).  Each wave owns 32 rows; the K/V tile of
-// 64 keys is staged once in LDS and read by all 4 waves.
+// Work decomposition of both passes: one workgroup of 8 waves per
+// (sequence, KV head, group of 128 window rows, chunk of keys), sized so the
+// launch is about one workgroup per CU.  K and V stream through a 4-stage LDS
+// ring of 64-key tiles filled by direct global->LDS loads (no register
+// staging), so three tiles stay in flight while one is consumed.  Wave w
+// owns rows 32(w%4)..+32 and keys 32(w/4)..+32 of each tile.  Rows of a tile
+// are stored unpadded with a 16-byte-chunk XOR swizzle (see swz), which keeps
+// the MFMA operand reads and the transposing reads free of bank conflicts.
+// Pass 1 reads V^T operands with the transposing LDS read, so V keeps its
+// natural [key][d] layout in LDS as well.
 #include "common.h"
 #include "launch.h"
 #include "timing.h"
@@ -23,14 +30,18 @@
 namespace kve {
 
 constexpr int D = 128;          // head dim of the bf16 path
-constexpr int KT = 64;          // keys per tile
-constexpr int KS = D + 8;       // LDS row stride (bf16 elements) of K/V [key][d] tiles
-constexpr int VTS = KT + 8;     // LDS row stride of the transposed V tile [d][key]
-constexpr int ROWS = 128;       // rows per workgroup (4 waves x 32)
+constexpr int KT = 64;          // keys per tile (one ring stage)
+constexpr int NSTAGE = 4;       // ring stages
+constexpr int ROWS = 128;       // window rows per workgroup
+constexpr int WG = 512;         // threads per workgroup (8 waves)
+constexpr int ROWB = D * 2;     // bytes per K/V row
+constexpr int TILE_BYTES = KT * ROWB;          // one K (or V) tile
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // K tile then V tile
+static_assert(kScoreChunkMax % KT == 0, "chunk bound must be a multiple of the tile");
 
 // Slot s of a 32-key block holds key keymap(s): bits 2 and 3 swapped.  With
 // this order the P values a lane holds after the K.Q^T MFMA are 8
-// consecutive keys, so the V^T operand of P.V is one 16-byte LDS read.
+// consecutive keys, matching the k-slices of the P.V contraction.
 __device__ __forceinline__ int keymap(int s) {
   return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1);
 }
@@ -40,6 +51,17 @@ __device__ __forceinline__ int keymap(int s) {
 __device__ __forceinline__ int p1_key_of(int r, int hl) {
   return (r & 3) + 4 * ((r >> 2) & 1) + 8 * hl + 16 * (r >> 3);
 }
+
+// Chunk swizzle of a tile row: chunk c of key k is stored at chunk c ^ swz(k).
+// swz permutes the 16 residues of k (16 consecutive keys hit 16 distinct
+// chunks: the MFMA operand reads), gives the four keys 4a..4a+3 distinct
+// swz >> 1 (the transposing reads touch chunk pairs 2m, 2m+1 of four keys)
+// and flips bit 0 between keys 2a and 2a+1 (the ||v||^2 reads).
+__device__ __forceinline__ int swz(int key) {
+  return (key & 8) | ((key & 3) << 1) | (((key >> 2) ^ key) & 1);
+}
+// Byte offset of 16-byte chunk c of row `key` inside a swizzled tile.
+__device__ __forceinline__ int tile_off(int key, int c) { return key * ROWB + ((c ^ swz(key)) << 4); }
 
 struct ScoreArgs {
   const uint16_t* q_win;   // [S][Hq][w][D]
@@ -52,14 +74,94 @@ struct ScoreArgs {
   float* part_o;           // [S*Hkv*RG][P][ROWS][D]
   float* vnorm;            // [Hkv][T]
   float* lse2;             // [S*Hkv*RG][ROWS]
-  float* no2;              // [S*Hkv*RG][ROWS]
+  float* no2;              // [S*Hkv*RG][ROWS]  ||o_h||^2 of the bf16-rounded output o_h = -ohi / 2
+  float* no2d;             // [S*Hkv*RG][ROWS]  ||o||^2 - ||o_h||^2 (used with the residual plane)
   uint16_t* ohi;           // [S*Hkv*RG][ROWS][D]  bf16 of -2 o
   uint16_t* olo;           // residual
   float* sraw;             // [RG][Hkv][T]
 };
 
+// ------------------------------------------------------------ LDS pipeline
+// Workgroup barrier that orders LDS traffic only: global->LDS loads stay in
+// flight across it (a full __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding.  They complete in issue order, so every earlier one is done.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// 16 bytes per lane from `gptr` into LDS at lds_base + 16 * lane (one 1 KiB
+// block per wave).  Issued from inline assembly so that the compiler's own
+// wait insertion, which cannot tell the ring stages apart, does not drain
+// the whole pipeline before every LDS read; the kernels wait explicitly.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// Per-lane constants of the ring fill.  Wave w loads tile rows 8w .. 8w+7:
+// two 1 KiB LDS blocks of K and two of V (rows 4j .. 4j+3 for j = 2w, 2w+1),
+// four 16-byte loads per lane per tile.
+struct RingFill {
+  int key[2];        // tile row loaded by this lane in block i
+  int goff[2];       // byte offset of that row's chunk from the tile's first row
+  uint32_t lds[2];   // LDS byte address of block i in stage 0 (wave-uniform)
+
+  __device__ void init(uint32_t ring0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = 2 * wave + i;
+      key[i] = 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ swz(key[i]);   // logical chunk stored at this lane's slot
+      goff[i] = key[i] * ROWB + 16 * c;
+      lds[i] = __builtin_amdgcn_readfirstlane(ring0 + j * 1024);
+    }
+  }
+  // Keys kt0 .. kt0+63 into stage `stage`; rows past the chunk end c1 repeat
+  // its last key (callers mask them).
+  __device__ __forceinline__ void issue(const char* kb, const char* vb, int kt0, int c1, int stage) const {
+    const size_t tbase = static_cast<size_t>(kt0) * ROWB;
+    const uint32_t sb = static_cast<uint32_t>(stage) * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int off = goff[i];
+      if (kt0 + KT > c1 && kt0 + key[i] >= c1) off += (c1 - 1 - kt0 - key[i]) * ROWB;
+      dma16(kb + tbase + off, lds[i] + sb);
+      dma16(vb + tbase + off, lds[i] + sb + TILE_BYTES);
+    }
+  }
+};
+
+// Waits for the stage of tile t given how many later tiles are in flight.
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if (ahead >= 2) wait_vm<8>();
+  else if (ahead == 1) wait_vm<4>();
+  else wait_vm<0>();
+}
+
+// Sum of squares of 16 bf16 values (two 16-byte chunks).
+__device__ __forceinline__ float sumsq16(u32x4 x, u32x4 y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = __uint_as_float(x[e] << 16), a1 = __uint_as_float(x[e] & 0xffff0000u);
+    const float b0 = __uint_as_float(y[e] << 16), b1 = __uint_as_float(y[e] & 0xffff0000u);
+    acc = fmaf(a0, a0, acc);
+    acc = fmaf(a1, a1, acc);
+    acc = fmaf(b0, b0, acc);
+    acc = fmaf(b1, b1, acc);
+  }
+  return acc;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------- pass 1
-__global__ __launch_bounds__(256, 2) void score_p1_bf16(ScoreArgs a) {
+__global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y / a.RG;
   const int rg = blockIdx.y % a.RG;
@@ -70,20 +172,21 @@ __global__ __launch_bounds__(256, 2) void score_p1_bf16(ScoreArgs a) {
   if (c0 >= n) return;
   const int c1 = min(c0 + a.CH, n);
 
-  __shared__ __align__(16) uint16_t Ks[KT * KS];
-  __shared__ __align__(16) uint16_t Vt[D * VTS];
-  __shared__ __align__(16) float vred[16 * KT];
+  __shared__ __align__(1024) char ring[NSTAGE * STAGE_BYTES];
+  __shared__ __align__(16) float vn[kScoreChunkMax];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int hl = lane >> 5;
   const int col = lane & 31;
+  const int rb = wave & 3;        // row block
+  const int kh = wave >> 2;       // key half of each tile
   const int g = a.Hq / a.Hkv;
   const int R = g * a.w;
 
   // this lane's query row (N index of the K.Q^T MFMA)
-  const int row = rg * ROWS + wave * 32 + col;
+  const int row = rg * ROWS + rb * 32 + col;
   const bool row_ok = row < R;
   const int qh = h * g + (row_ok ? row / a.w : 0);
   const int wi = row_ok ? row % a.w : 0;
@@ -99,159 +202,183 @@ __global__ __launch_bounds__(256, 2) void score_p1_bf16(ScoreArgs a) {
       qreg[kk] = as_bf16x8(t);
     }
   }
+  __syncthreads();   // operand loads complete before the ring starts counting
 
-  const uint16_t* kbase = a.k + (static_cast<size_t>(h) * a.T + base) * D;
-  const uint16_t* vbase = a.v + (static_cast<size_t>(h) * a.T + base) * D;
-
-  // tile loaders: K as [key][d] (thread -> key tid/16 + 16u, d chunk tid%16);
-  // V transposed (thread -> key group kg = tid%16 of 4 keys, d chunk tid/16)
-  const int kkey = tid >> 4, kdc = tid & 15;
-  const int vkg = tid & 15, vdc = tid >> 4;
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = kt0 + kkey + 16 * u;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (key < c1) t = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(key) * D + 8 * kdc);
-      kreg[u] = t;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt0 + 4 * vkg + i;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (key < c1) t = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(key) * D + 8 * vdc);
-      vreg[i] = t;
-    }
-  };
+  const char* kb8 = reinterpret_cast<const char*>(a.k + (static_cast<size_t>(h) * a.T + base) * D);
+  const char* vb8 = reinterpret_cast<const char*>(a.v + (static_cast<size_t>(h) * a.T + base) * D);
+  RingFill fill;
+  fill.init(lds_addr(ring), wave, lane);
+  const int ntile = (c1 - c0 + KT - 1) / KT;
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  // Online softmax with a lazily raised reference: p = 2^(x - m_run) with
+  // m_run within 8 of the running max, so p <= 256 and the accumulators are
+  // rescaled only when the max climbs by more than 8 (log2 units).
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  load_tile(c0);
-  for (int kt0 = c0; kt0 < c1; kt0 += KT) {
-    __syncthreads();   // previous tile fully consumed
+  // loop-invariant LDS offsets: K operand rows, ||v||^2 reads, and the
+  // transposing V^T reads (feature block db adds db << 6 by XOR)
+  int koff[D / 16];
+  {
+    const int krow = kh * 32 + keymap(col);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<u32x4*>(&Ks[(kkey + 16 * u) * KS + 8 * kdc]) = kreg[u];
-    {
-      // transpose 4 keys x 8 d into Vt[d][key]; also ||v||^2 partials
-      float vsq[4];
+    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(krow, 2 * kk + hl);
+  }
+  const int vkey = tid >> 3, vpart = tid & 7;   // 8 lanes per key, two chunks each
+  const int voff0 = tile_off(vkey, 2 * vpart), voff1 = tile_off(vkey, 2 * vpart + 1);
+  // A operand of O^T += V^T P^T: lane (d = db*32 + l%32, k-slice l/32) holds 8
+  // consecutive keys of feature d, from two transposing reads; in each
+  // 16-lane group lane j names row key0 + j/4 at features dbase + 4(j%4)..+4
+  // and receives feature dbase + j of rows key0 .. key0+3.
+  int toff[2][2];
+  {
+    const int grpl = lane >> 4, j = lane & 15;
+    const int dl = 16 * (grpl & 1) + 4 * (j & 3);   // feature within a 32-block
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float acc = 0.f;
+    for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t wv = vreg[i][e];
-          const float lo = __uint_as_float(wv << 16), hi = __uint_as_float(wv & 0xffff0000u);
-          acc = fmaf(lo, lo, acc);
-          acc = fmaf(hi, hi, acc);
-        }
-        vsq[i] = acc;
-      }
-      *reinterpret_cast<f32x4*>(&vred[vdc * KT + 4 * vkg]) = f32x4{vsq[0], vsq[1], vsq[2], vsq[3]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // d = 8*vdc + 2e (low halves) and 2e+1 (high halves)
-        const uint32_t k0 = vreg[0][e], k1 = vreg[1][e], k2 = vreg[2][e], k3 = vreg[3][e];
-        const uint32_t lo01 = (k0 & 0xffffu) | (k1 << 16);
-        const uint32_t lo23 = (k2 & 0xffffu) | (k3 << 16);
-        const uint32_t hi01 = (k0 >> 16) | (k1 & 0xffff0000u);
-        const uint32_t hi23 = (k2 >> 16) | (k3 & 0xffff0000u);
-        const int d0 = 8 * vdc + 2 * e;
-        *reinterpret_cast<uint2*>(&Vt[d0 * VTS + 4 * vkg]) = make_uint2(lo01, lo23);
-        *reinterpret_cast<uint2*>(&Vt[(d0 + 1) * VTS + 4 * vkg]) = make_uint2(hi01, hi23);
-      }
-    }
-    __syncthreads();
-    if (tid < KT) {
-      float sum = 0.f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sum += vred[q * KT + tid];
-      if (kt0 + tid < c1) a.vnorm[static_cast<size_t>(h) * a.T + base + kt0 + tid] = sum;
-    }
-    if (kt0 + KT < c1) load_tile(kt0 + KT);   // prefetch next tile into registers
-
-    // S^T = K . Q^T for the two 32-key blocks
-    f32x16 sacc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sacc[b] = f32x16{};
-      const uint16_t* kr = &Ks[(b * 32 + keymap(col)) * KS + 8 * hl];
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * kk));
-        sacc[b] = mfma32(av, qreg[kk], sacc[b]);
-      }
-    }
-    // scale to log2 units; mask keys past the chunk or the causal horizon
-    const bool edge = (kt0 + KT > c1) || (a.causal && kt0 + KT - 1 > n - a.w);
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[b][r] * a.c2;
-        if (edge) {
-          const int key = kt0 + b * 32 + p1_key_of(r, hl);
-          if (key >= c1 || (a.causal && key > pos)) x = -INFINITY;
-        }
-        sacc[b][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    }
-    tmax = fmaxf(tmax, xor32(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float scale = exp2f(m_run - m_use);
-    if (__any(scale != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) oacc[i] *= scale;
-    }
-    l_run *= scale;
-    m_run = m_new;
-
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2f(sacc[b][8 * t + 2 * e] - m_use);
-          const float p1 = exp2f(sacc[b][8 * t + 2 * e + 1] - m_use);
-          l_run += p0 + p1;
-          pk[e] = pack_bf16x2(p0, p1);
-        }
-        pb[b][t] = as_bf16x8(pk);
-      }
-    }
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const uint16_t* vr = &Vt[(db * 32 + col) * VTS + 8 * hl];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(vr + b * 32 + 16 * t));
-          oacc[db] = mfma32(av, pb[b][t], oacc[db]);
-        }
+      for (int hf = 0; hf < 2; ++hf) {
+        const int key0 = kh * 32 + 16 * k2 + 8 * (grpl >> 1) + 4 * hf + (j >> 2);
+        toff[k2][hf] = tile_off(key0, dl >> 3) + ((dl >> 2) & 1) * 8;
       }
     }
   }
 
-  const float l_tot = l_run + xor32(l_run);
+  for (int t = 0; t < NSTAGE - 1 && t < ntile; ++t) fill.issue(kb8, vb8, c0 + t * KT, c1, t);
+
+  for (int t = 0; t < ntile; ++t) {
+    wait_stage(min(NSTAGE - 2, ntile - 1 - t));
+    lds_barrier();   // tile t visible to all waves; stage of tile t-1 free
+    if (t + NSTAGE - 1 < ntile) fill.issue(kb8, vb8, c0 + (t + NSTAGE - 1) * KT, c1, (t + NSTAGE - 1) % NSTAGE);
+    const int kt0 = c0 + t * KT;
+    const char* Kt = ring + (t % NSTAGE) * STAGE_BYTES;
+    const char* Vt = Kt + TILE_BYTES;
+    {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + voff0);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(Vt + voff1);
+      float q = sumsq16(x, y);
+      q += __shfl_xor(q, 1, 64);
+      q += __shfl_xor(q, 2, 64);
+      q += __shfl_xor(q, 4, 64);
+      if (vpart == 0) vn[t * KT + vkey] = q;
+    }
+    // S^T = K . Q^T for this wave's 32 keys (slot order through keymap)
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + koff[kk]));
+      sacc = mfma32(av, qreg[kk], sacc);
+    }
+    // mask keys past the chunk or the causal horizon (uniform branch)
+    if ((kt0 + KT > c1) || (a.causal && kt0 + KT - 1 > n - a.w)) {
+      const bool causal = a.causal != 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt0 + kh * 32 + p1_key_of(r, hl);
+        const bool hidden = (key >= c1) | (causal & (key > pos));
+        sacc[r] = hidden ? -INFINITY : sacc[r];
+      }
+    }
+    float tmax = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+    tmax = fmaxf(tmax, xor32(tmax)) * a.c2;
+    const bool raise = tmax > m_run + 8.f;
+    if (__any(raise)) {
+      const float m_new = raise ? tmax : m_run;
+      const float scale = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= scale;
+      l_run *= scale;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    f32x8 pf[2];
+    bf16x8 pb[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf[k2][e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * k2 + e], a.c2, -m_use));
+        l_run += pf[k2][e];
+      }
+      pb[k2] = __builtin_convertvector(pf[k2], bf16x8);   // round to nearest even
+    }
+    // O^T += V^T . P^T
+    auto pv = [&](const bf16x8 (&pm)[2]) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(Vt + (toff[k2][0] ^ (db << 6))));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(Vt + (toff[k2][1] ^ (db << 6))));
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pm[k2], oacc[db]);
+        }
+      }
+    };
+    pv(pb);
+    // A weight that is a sizeable share of its row's running sum (at least
+    // 1/16 of this lane's half) can dominate o, and then the bf16 rounding
+    // of that weight moves o by a relative 2^-9 -- large against ||o - v_j||
+    // for the dominant key j.  Such tiles also contract the rounding residual
+    // of P, which makes the weights exact to about 2^-17.
+    const float pmax = __builtin_amdgcn_exp2f(tmax - m_use);
+    if (__any(16.f * pmax > l_run)) {
+      bf16x8 pr[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        f32x8 rem;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rem[e] = pf[k2][e] - static_cast<float>(pb[k2][e]);
+        pr[k2] = __builtin_convertvector(rem, bf16x8);
+      }
+      pv(pr);
+    }
+  }
+  lds_barrier();   // ring reads done: reuse the ring for the half merge
+
+  // ||v||^2 of the chunk
+  for (int i = tid; i < c1 - c0; i += WG) a.vnorm[static_cast<size_t>(h) * a.T + base + c0 + i] = vn[i];
+
+  // combine the two key halves: waves kh=1 hand (m, l, o) to waves kh=0
+  float* xo = reinterpret_cast<float*>(ring);                 // [4][32 rows][D]
+  float* xml = xo + 4 * 32 * D;                               // [4][32 rows][2]
+  const float l_half = l_run + xor32(l_run);
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * hl;
+        *reinterpret_cast<f32x4*>(&xo[(rb * 32 + col) * D + d]) =
+            f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+      }
+    }
+    if (hl == 0) {
+      xml[(rb * 32 + col) * 2] = m_run;
+      xml[(rb * 32 + col) * 2 + 1] = l_half;
+    }
+  }
+  lds_barrier();
+  if (kh == 1) return;
+  const float mo = xml[(rb * 32 + col) * 2], lo_ = xml[(rb * 32 + col) * 2 + 1];
+  const float M = fmaxf(m_run, mo);
+  const float fa = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
+  const float fb = (mo == -INFINITY) ? 0.f : exp2f(mo - M);
   if (!row_ok) return;
   const size_t part = (static_cast<size_t>((s * a.Hkv + h) * a.RG + rg)) * a.P + c;
-  const int rl = wave * 32 + col;
+  const int rl = rb * 32 + col;
   if (hl == 0) {
-    a.part_ml[(part * ROWS + rl) * 2 + 0] = m_run;
-    a.part_ml[(part * ROWS + rl) * 2 + 1] = l_tot;
+    a.part_ml[(part * ROWS + rl) * 2 + 0] = M;
+    a.part_ml[(part * ROWS + rl) * 2 + 1] = l_half * fa + lo_ * fb;
   }
   float* op = a.part_o + (part * ROWS + rl) * D;
 #pragma unroll
@@ -259,8 +386,11 @@ __global__ __launch_bounds__(256, 2) void score_p1_bf16(ScoreArgs a) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = db * 32 + 8 * q4 + 4 * hl;
-      *reinterpret_cast<f32x4*>(op + d) =
-          f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+      const f32x4 other = *reinterpret_cast<const f32x4*>(&xo[rl * D + d]);
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = oacc[db][4 * q4 + e] * fa + other[e] * fb;
+      *reinterpret_cast<f32x4*>(op + d) = r;
     }
   }
 }
@@ -284,7 +414,11 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   const int R = (a.Hq / a.Hkv) * a.w;
   const size_t ro = static_cast<size_t>(gr);
   if (rg * ROWS + rl >= R) {   // padding row of the last row group
-    if (lane == 0) { a.lse2[ro] = INFINITY; a.no2[ro] = 0.f; }
+    if (lane == 0) {
+      a.lse2[ro] = INFINITY;
+      a.no2[ro] = 0.f;
+      if (BF16OUT) a.no2d[ro] = 0.f;
+    }
     if (half == 0) {
 #pragma unroll
       for (int f = 0; f < F; ++f) {
@@ -324,26 +458,40 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] += xor32(acc[f]);
   const float inv = 1.f / L;
-  float sq = 0.f;
+  float sq = 0.f, sqh = 0.f;
+  uint16_t hi[F], lo[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) {
     acc[f] *= inv;
     sq = fmaf(acc[f], acc[f], sq);
+    if (BF16OUT) {
+      const float x = -2.f * acc[f];
+      hi[f] = f32_to_bf16(x);
+      const float xh = bf16_to_f32(hi[f]);
+      lo[f] = f32_to_bf16(x - xh);
+      sqh = fmaf(0.5f * xh, 0.5f * xh, sqh);
+    }
   }
   // sum over the 32 lanes of one half (both halves hold identical values)
-  for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  for (int o = 16; o > 0; o >>= 1) {
+    sq += __shfl_xor(sq, o, 64);
+    if (BF16OUT) sqh += __shfl_xor(sqh, o, 64);
+  }
   if (lane == 0) {
-    a.no2[ro] = sq;
     a.lse2[ro] = M + log2f(L);
+    if (BF16OUT) {
+      a.no2[ro] = sqh;
+      a.no2d[ro] = sq - sqh;
+    } else {
+      a.no2[ro] = sq;
+    }
   }
   if (half == 0) {
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       if (BF16OUT) {
-        const float x = -2.f * acc[f];
-        const uint16_t hi = f32_to_bf16(x);
-        a.ohi[ro * DD + ln * F + f] = hi;
-        a.olo[ro * DD + ln * F + f] = f32_to_bf16(x - bf16_to_f32(hi));
+        a.ohi[ro * DD + ln * F + f] = hi[f];
+        a.olo[ro * DD + ln * F + f] = lo[f];
       } else {
         o32[ro * DD + ln * F + f] = acc[f];
       }
@@ -352,7 +500,15 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
 }
 
 // ---------------------------------------------------------------- pass 2
-__global__ __launch_bounds__(256, 2) void score_p2_bf16(ScoreArgs a) {
+// A 32x32 block of (row, key) pairs whose softmax weights all stay at or
+// below 2^-6 measures distances from the bf16-rounded output o_h
+// alone: ||o_h - v||^2 is then exact for o_h and differs from ||o - v||^2 by
+// at most about 2^-8 ||o|| / ||o - v|| relative.  With a larger weight (where
+// o can approach v_j and that bound degrades) the block also contracts the
+// residual plane o - o_h, restoring an fp32-accurate distance.
+constexpr float kResidY = 63.f;   // (1 - p) / p below this <=> p > 2^-6
+
+__global__ __launch_bounds__(WG, 1) void score_p2_bf16(ScoreArgs a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y / a.RG;
   const int rg = blockIdx.y % a.RG;
@@ -363,123 +519,148 @@ __global__ __launch_bounds__(256, 2) void score_p2_bf16(ScoreArgs a) {
   if (c0 >= n) return;
   const int c1 = min(c0 + a.CH, n);
 
-  __shared__ __align__(16) uint16_t Ks[KT * KS];
-  __shared__ __align__(16) uint16_t Vs[KT * KS];
-  __shared__ float red[4 * KT];
+  __shared__ __align__(1024) char ring[NSTAGE * STAGE_BYTES];
+  __shared__ __align__(16) float sbuf[kScoreChunkMax];   // ||v||^2 in, scores out
+  __shared__ __align__(16) float red[2][4][KT];
+  __shared__ __align__(16) float rowc[2 * ROWS];
+  __shared__ int rowhz[ROWS];   // causal horizon (last visible key) of each row
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int hl = lane >> 5;
   const int col = lane & 31;
+  const int rb = wave & 3;
+  const int kh = wave >> 2;
   const int g = a.Hq / a.Hkv;
   const int R = g * a.w;
   const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rg);
 
-  // A operands: rows wave*32 + col (M index)
-  const int arow = rg * ROWS + wave * 32 + col;
+  // A operands: rows rb*32 + col (M index)
+  const int arow = rg * ROWS + rb * 32 + col;
   const bool arow_ok = arow < R;
-  bf16x8 qa[D / 16], oha[D / 16], ola[D / 16];
+  bf16x8 qa[D / 16], oha[D / 16];
   {
     const int qh = h * g + (arow_ok ? arow / a.w : 0);
     const int wi = arow_ok ? arow % a.w : 0;
     const uint16_t* qp = a.q_win + ((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * D;
-    const uint16_t* hp = a.ohi + (grp * ROWS + wave * 32 + col) * D;
-    const uint16_t* lp = a.olo + (grp * ROWS + wave * 32 + col) * D;
+    const uint16_t* hp = a.ohi + (grp * ROWS + rb * 32 + col) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 t = {0u, 0u, 0u, 0u};
       if (arow_ok) t = *reinterpret_cast<const u32x4*>(qp + 16 * kk + 8 * hl);
       qa[kk] = as_bf16x8(t);
       oha[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(hp + 16 * kk + 8 * hl));
-      ola[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(lp + 16 * kk + 8 * hl));
     }
   }
-  // per-row constants of the output layout: rows 8(r/4) + 4hl + r%4
-  float lse2c[16], no2c[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rl = wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-    lse2c[r] = a.lse2[grp * ROWS + rl];
-    no2c[r] = a.no2[grp * ROWS + rl];
+  // per-row constants (log2-sum-exp, ||o_h||^2); register r of the output
+  // layout is row 8(r/4) + 4hl + r%4 of the wave's 32
+  for (int i = tid; i < ROWS; i += WG) {
+    rowc[i] = a.lse2[grp * ROWS + i];
+    rowc[ROWS + i] = a.no2[grp * ROWS + i];
+    const int rrow = rg * ROWS + i;
+    rowhz[i] = (rrow < R) ? n - a.w + rrow % a.w : -1;
   }
-
-  const uint16_t* kbase = a.k + (static_cast<size_t>(h) * a.T + base) * D;
-  const uint16_t* vbase = a.v + (static_cast<size_t>(h) * a.T + base) * D;
   const float* vnb = a.vnorm + static_cast<size_t>(h) * a.T + base;
-  float* sout = a.sraw + (static_cast<size_t>(rg) * a.Hkv + h) * a.T + base;
+  for (int i = tid; i < c1 - c0; i += WG) sbuf[i] = vnb[c0 + i];
+  __syncthreads();   // operand loads complete before the ring starts counting
 
-  const int lkey = tid >> 4, ldc = tid & 15;
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = kt0 + lkey + 16 * u;
-      u32x4 tk = {0u, 0u, 0u, 0u}, tv = {0u, 0u, 0u, 0u};
-      if (key < c1) {
-        tk = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(key) * D + 8 * ldc);
-        tv = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(key) * D + 8 * ldc);
-      }
-      kreg[u] = tk;
-      vreg[u] = tv;
+  const char* kb8 = reinterpret_cast<const char*>(a.k + (static_cast<size_t>(h) * a.T + base) * D);
+  const char* vb8 = reinterpret_cast<const char*>(a.v + (static_cast<size_t>(h) * a.T + base) * D);
+  RingFill fill;
+  fill.init(lds_addr(ring), wave, lane);
+  const int ntile = (c1 - c0 + KT - 1) / KT;
+
+  auto reduce_tile = [&](int t) {   // 4 row-block partials -> sbuf
+    if (tid < KT) {
+      const float* rr = &red[t & 1][0][0];
+      sbuf[t * KT + tid] = (rr[tid] + rr[KT + tid]) + (rr[2 * KT + tid] + rr[3 * KT + tid]);
     }
   };
-
-  load_tile(c0);
-  for (int kt0 = c0; kt0 < c1; kt0 += KT) {
-    __syncthreads();
+  const int krow = kh * 32 + col;   // tile row of this lane's key (N index)
+  int koff[D / 16];                 // loop-invariant operand offsets (K and V share them)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<u32x4*>(&Ks[(lkey + 16 * u) * KS + 8 * ldc]) = kreg[u];
-      *reinterpret_cast<u32x4*>(&Vs[(lkey + 16 * u) * KS + 8 * ldc]) = vreg[u];
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(krow, 2 * kk + hl);
+
+  for (int t = 0; t < NSTAGE - 1 && t < ntile; ++t) fill.issue(kb8, vb8, c0 + t * KT, c1, t);
+
+  for (int t = 0; t < ntile; ++t) {
+    wait_stage(min(NSTAGE - 2, ntile - 1 - t));
+    lds_barrier();
+    if (t > 0) reduce_tile(t - 1);
+    if (t + NSTAGE - 1 < ntile) fill.issue(kb8, vb8, c0 + (t + NSTAGE - 1) * KT, c1, (t + NSTAGE - 1) % NSTAGE);
+    const int kt0 = c0 + t * KT;
+    const char* Kt = ring + (t % NSTAGE) * STAGE_BYTES;
+    const char* Vt = Kt + TILE_BYTES;
+    const float vn2 = sbuf[t * KT + krow];
+    f32x16 sacc = f32x16{};
+    f32x16 gacc;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 nv = *reinterpret_cast<const f32x4*>(&rowc[ROWS + rb * 32 + 8 * q4 + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gacc[4 * q4 + e] = nv[e] + vn2;
     }
-    __syncthreads();
-    if (kt0 + KT < c1) load_tile(kt0 + KT);
-    const bool edge = (kt0 + KT > c1) || (a.causal && kt0 + KT - 1 > n - a.w);
-
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int key = kt0 + b * 32 + col;
-      const float vn2 = (key < c1) ? vnb[key] : 0.f;
-      f32x16 sacc = f32x16{};
-      f32x16 gacc;
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + koff[kk]));
+      sacc = mfma32(qa[kk], kb, sacc);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) gacc[r] = no2c[r];
-      const uint16_t* kr = &Ks[(b * 32 + col) * KS + 8 * hl];
-      const uint16_t* vr = &Vs[(b * 32 + col) * KS + 8 * hl];
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + koff[kk]));
+      gacc = mfma32(oha[kk], vb, gacc);
+    }
+    // y = (1 - p) / p = 2^-x - 1 with x = log2 p; hidden pairs get y = inf
+    float y[16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * kk));
-        const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(vr + 16 * kk));
-        sacc = mfma32(qa[kk], kb, sacc);
-        gacc = mfma32(oha[kk], vb, gacc);
-        gacc = mfma32(ola[kk], vb, gacc);
-      }
-      float sc = 0.f;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowc[rb * 32 + 8 * q4 + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[4 * q4 + e] = fmaf(sacc[4 * q4 + e], a.c2, -lv[e]);
+    }
+    if ((kt0 + KT > c1) || (a.causal && kt0 + KT - 1 > n - a.w)) {   // uniform: edge tile
+      const int key = kt0 + krow;
+      const bool causal = a.causal != 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = fmaf(sacc[r], a.c2, -lse2c[r]);
-        if (edge) {
-          bool ok = key < c1;
-          if (a.causal) {
-            const int rrow = rg * ROWS + wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const int wi = (rrow < R) ? rrow % a.w : 0;
-            ok = ok && (key <= n - a.w + wi);
-          }
-          if (!ok) x = -INFINITY;
-        }
-        const float y = exp2f(-x) - 1.f;                 // (1 - p) / p
-        const float y2 = fmaf(y, y, 9.094947e-13f);       // + 2^-40 keeps 1/y2 finite
-        const float d2 = gacc[r] + vn2;                   // ||o - v||^2
-        sc = fmaf(d2, __builtin_amdgcn_rcpf(y2), sc);
+        const int hz = rowhz[rb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
+        const bool hidden = (key >= c1) | (causal & (key > hz));
+        y[r] = hidden ? -INFINITY : y[r];
       }
-      sc += xor32(sc);
-      if (hl == 0) red[wave * KT + b * 32 + col] = sc;
     }
-    __syncthreads();
-    if (tid < KT && kt0 + tid < c1)
-      sout[kt0 + tid] = (red[tid] + red[KT + tid]) + (red[2 * KT + tid] + red[3 * KT + tid]);
+    float ymin = INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      y[r] = __builtin_amdgcn_exp2f(-y[r]) - 1.f;
+      ymin = fminf(ymin, y[r]);
+    }
+    if (__any(ymin < kResidY)) {   // wave-uniform: add the residual plane of o
+      const uint16_t* lp = a.olo + (grp * ROWS + rb * 32 + col) * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 ola = as_bf16x8(*reinterpret_cast<const u32x4*>(lp + 16 * kk + 8 * hl));
+        const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + koff[kk]));
+        gacc = mfma32(ola, vb, gacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        gacc[r] += a.no2d[grp * ROWS + rb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float y2 = fmaf(y[r], y[r], 9.094947e-13f);   // + 2^-40 keeps 1/y2 finite
+      sc = fmaf(gacc[r], __builtin_amdgcn_rcpf(y2), sc);  // gacc = ||o - v||^2
+    }
+    sc += xor32(sc);
+    if (hl == 0) red[t & 1][rb][krow] = sc;
   }
+  lds_barrier();
+  if (ntile > 0) reduce_tile(ntile - 1);
+  lds_barrier();
+  float* sout = a.sraw + (static_cast<size_t>(rg) * a.Hkv + h) * a.T + base;
+  for (int i = tid; i < c1 - c0; i += WG) sout[c0 + i] = sbuf[i];
 }
 
 // ---------------------------------------------------------------- launchers
@@ -500,13 +681,14 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   a.vnorm = reinterpret_cast<float*>(base + G.off_vnorm);
   a.lse2 = reinterpret_cast<float*>(base + G.off_lse2);
   a.no2 = reinterpret_cast<float*>(base + G.off_no2);
+  a.no2d = reinterpret_cast<float*>(base + G.off_no2d);
   a.ohi = reinterpret_cast<uint16_t*>(base + G.off_ohi);
   a.olo = reinterpret_cast<uint16_t*>(base + G.off_olo);
   a.sraw = reinterpret_cast<float*>(base + G.off_sraw);
 
   dim3 grid(G.P, G.Hkv * G.RG, G.S);
   stage_begin(ST_SCORE_P1, st);
-  hipLaunchKernelGGL(score_p1_bf16, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(score_p1_bf16, grid, dim3(WG), 0, st, a);
   stage_end(ST_SCORE_P1, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -517,7 +699,7 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_SCORE_P2, st);
-  hipLaunchKernelGGL(score_p2_bf16, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(score_p2_bf16, grid, dim3(WG), 0, st, a);
   stage_end(ST_SCORE_P2, st);
   return hipGetLastError();
 }
