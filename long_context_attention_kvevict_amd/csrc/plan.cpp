@@ -68,9 +68,9 @@ kve_status plan_score(const kve_layout* L, ScoreGeom* G, std::string* msg) {
   const int64_t len_cap = ((max_len + 255) / 256) * 256;
   int64_t ch;
   if (L->dtype == KVE_BF16) {
-    // about one 8-wave workgroup per CU (256), multiple of 256 keys, at most
+    // about two 4-wave workgroups per CU (512), multiple of 256 keys, at most
     // kScoreChunkMax
-    ch = (work + 255) / 256;
+    ch = (work + 511) / 512;
     ch = std::max<int64_t>(256, ((ch + 255) / 256) * 256);
     ch = std::min<int64_t>(ch, kScoreChunkMax);
   } else {

@@ -13,7 +13,7 @@ namespace kve {
 
 // Largest key chunk one scorer workgroup handles (its per-key LDS buffers
 // are sized for it).
-constexpr int kScoreChunkMax = 4096;
+constexpr int kScoreChunkMax = 2048;
 
 // Geometry of one kvevict_score call; the workspace is carved into the
 // regions below (byte offsets, each 256-byte aligned).

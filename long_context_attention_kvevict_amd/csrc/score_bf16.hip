@@ -13,12 +13,13 @@
 //   (p / (1 - p))^2 ||o - v||^2 over all rows of the group for each key
 //   ("DropKV" page, §3.3 window score and §3.4 scoring kernel).
 //
-// Work decomposition of both passes: one workgroup of 8 waves per
+// Work decomposition of both passes: one workgroup of 4 waves per
 // (sequence, KV head, group of 128 window rows, chunk of keys), sized so the
-// launch is about one workgroup per CU.  K and V stream through a 4-stage LDS
-// ring of 64-key tiles filled by direct global->LDS loads (no register
-// staging), so three tiles stay in flight while one is consumed.  Wave w
-// owns rows 32(w%4)..+32 and keys 32(w/4)..+32 of each tile.  Rows of a tile
+// launch is about two workgroups per CU; the two run independently, so one's
+// MFMA phase overlaps the other's vector-ALU phase.  K and V stream through a
+// 2-stage LDS ring of 64-key tiles filled by direct global->LDS loads (no
+// register staging): the next tile is in flight while one is consumed.  Wave
+// w owns rows 32w..32w+31 and both 32-key halves of each tile.  Rows of a tile
 // are stored unpadded with a 16-byte-chunk XOR swizzle (see swz), which keeps
 // the MFMA operand reads and the transposing reads free of bank conflicts.
 // Pass 1 reads V^T operands with the transposing LDS read, so V keeps its
@@ -31,9 +32,9 @@ namespace kve {
 
 constexpr int D = 128;          // head dim of the bf16 path
 constexpr int KT = 64;          // keys per tile (one ring stage)
-constexpr int NSTAGE = 4;       // ring stages
+constexpr int NSTAGE = 2;       // ring stages
 constexpr int ROWS = 128;       // window rows per workgroup
-constexpr int WG = 512;         // threads per workgroup (8 waves)
+constexpr int WG = 256;         // threads per workgroup (4 waves)
 constexpr int ROWB = D * 2;     // bytes per K/V row
 constexpr int TILE_BYTES = KT * ROWB;          // one K (or V) tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // K tile then V tile
@@ -99,6 +100,12 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "s"(lds_base) : "memory");
 }
 
+// Makes the register operand `x` ready here: the compiler places its wait for
+// the load that produced it before this point (outside the tile loop), so it
+// never emits a drain of the whole vector-memory counter inside the loop.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) { asm volatile("" :: "v"(x)); }
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
@@ -107,14 +114,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // two 1 KiB LDS blocks of K and two of V (rows 4j .. 4j+3 for j = 2w, 2w+1),
 // four 16-byte loads per lane per tile.
 struct RingFill {
-  int key[2];        // tile row loaded by this lane in block i
-  int goff[2];       // byte offset of that row's chunk from the tile's first row
-  uint32_t lds[2];   // LDS byte address of block i in stage 0 (wave-uniform)
+  static constexpr int NB = TILE_BYTES / 1024 / (WG / 64);   // 1 KiB blocks per wave and tile
+  int key[NB];        // tile row loaded by this lane in block i
+  int goff[NB];       // byte offset of that row's chunk from the tile's first row
+  uint32_t lds[NB];   // LDS byte address of block i in stage 0 (wave-uniform)
 
   __device__ void init(uint32_t ring0, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = 2 * wave + i;
+    for (int i = 0; i < NB; ++i) {
+      const int j = NB * wave + i;               // block j holds rows 4j .. 4j+3
       key[i] = 4 * j + (lane >> 4);
       const int c = (lane & 15) ^ swz(key[i]);   // logical chunk stored at this lane's slot
       goff[i] = key[i] * ROWB + 16 * c;
@@ -127,7 +135,7 @@ struct RingFill {
     const size_t tbase = static_cast<size_t>(kt0) * ROWB;
     const uint32_t sb = static_cast<uint32_t>(stage) * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NB; ++i) {
       int off = goff[i];
       if (kt0 + KT > c1 && kt0 + key[i] >= c1) off += (c1 - 1 - kt0 - key[i]) * ROWB;
       dma16(kb + tbase + off, lds[i] + sb);
@@ -135,13 +143,6 @@ struct RingFill {
     }
   }
 };
-
-// Waits for the stage of tile t given how many later tiles are in flight.
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if (ahead >= 2) wait_vm<8>();
-  else if (ahead == 1) wait_vm<4>();
-  else wait_vm<0>();
-}
 
 // Sum of squares of 16 bf16 values (two 16-byte chunks).
 __device__ __forceinline__ float sumsq16(u32x4 x, u32x4 y) {
@@ -161,7 +162,7 @@ __device__ __forceinline__ float sumsq16(u32x4 x, u32x4 y) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- pass 1
-__global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
+__global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y / a.RG;
   const int rg = blockIdx.y % a.RG;
@@ -180,13 +181,11 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
   const int lane = tid & 63;
   const int hl = lane >> 5;
   const int col = lane & 31;
-  const int rb = wave & 3;        // row block
-  const int kh = wave >> 2;       // key half of each tile
   const int g = a.Hq / a.Hkv;
   const int R = g * a.w;
 
   // this lane's query row (N index of the K.Q^T MFMA)
-  const int row = rg * ROWS + rb * 32 + col;
+  const int row = rg * ROWS + wave * 32 + col;
   const bool row_ok = row < R;
   const int qh = h * g + (row_ok ? row / a.w : 0);
   const int wi = row_ok ? row % a.w : 0;
@@ -202,7 +201,8 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
       qreg[kk] = as_bf16x8(t);
     }
   }
-  __syncthreads();   // operand loads complete before the ring starts counting
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) settle(qreg[kk]);
 
   const char* kb8 = reinterpret_cast<const char*>(a.k + (static_cast<size_t>(h) * a.T + base) * D);
   const char* vb8 = reinterpret_cast<const char*>(a.v + (static_cast<size_t>(h) * a.T + base) * D);
@@ -219,20 +219,23 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // loop-invariant LDS offsets: K operand rows, ||v||^2 reads, and the
-  // transposing V^T reads (feature block db adds db << 6 by XOR)
+  // loop-invariant LDS offsets (the second 32-key half adds 32 rows = 8 KiB;
+  // the swizzle depends on the row mod 16 only)
   int koff[D / 16];
   {
-    const int krow = kh * 32 + keymap(col);
+    const int krow = keymap(col);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(krow, 2 * kk + hl);
   }
-  const int vkey = tid >> 3, vpart = tid & 7;   // 8 lanes per key, two chunks each
-  const int voff0 = tile_off(vkey, 2 * vpart), voff1 = tile_off(vkey, 2 * vpart + 1);
+  const int vkey = tid >> 2, vpart = tid & 3;   // 4 lanes per key, chunks vpart + 4i
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = tile_off(vkey, vpart + 4 * i);
   // A operand of O^T += V^T P^T: lane (d = db*32 + l%32, k-slice l/32) holds 8
   // consecutive keys of feature d, from two transposing reads; in each
   // 16-lane group lane j names row key0 + j/4 at features dbase + 4(j%4)..+4
-  // and receives feature dbase + j of rows key0 .. key0+3.
+  // and receives feature dbase + j of rows key0 .. key0+3.  Feature block db
+  // toggles offset bits 6-7 (XOR db << 6).
   int toff[2][2];
   {
     const int grpl = lane >> 4, j = lane & 15;
@@ -241,50 +244,60 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
     for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int key0 = kh * 32 + 16 * k2 + 8 * (grpl >> 1) + 4 * hf + (j >> 2);
+        const int key0 = 16 * k2 + 8 * (grpl >> 1) + 4 * hf + (j >> 2);
         toff[k2][hf] = tile_off(key0, dl >> 3) + ((dl >> 2) & 1) * 8;
       }
     }
   }
+  const bool causal = a.causal != 0;
 
-  for (int t = 0; t < NSTAGE - 1 && t < ntile; ++t) fill.issue(kb8, vb8, c0 + t * KT, c1, t);
+  if (ntile > 0) fill.issue(kb8, vb8, c0, c1, 0);
 
   for (int t = 0; t < ntile; ++t) {
-    wait_stage(min(NSTAGE - 2, ntile - 1 - t));
-    lds_barrier();   // tile t visible to all waves; stage of tile t-1 free
-    if (t + NSTAGE - 1 < ntile) fill.issue(kb8, vb8, c0 + (t + NSTAGE - 1) * KT, c1, (t + NSTAGE - 1) % NSTAGE);
+    wait_vm<0>();    // this lane's loads of tile t
+    lds_barrier();   // everyone's loads of tile t; the other stage is free
+    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
     const int kt0 = c0 + t * KT;
-    const char* Kt = ring + (t % NSTAGE) * STAGE_BYTES;
+    const char* Kt = ring + (t & 1) * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
     {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + voff0);
-      const u32x4 y = *reinterpret_cast<const u32x4*>(Vt + voff1);
-      float q = sumsq16(x, y);
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + voff[i]);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(Vt + voff[i + 1]);
+        q += sumsq16(x, y);
+      }
       q += __shfl_xor(q, 1, 64);
       q += __shfl_xor(q, 2, 64);
-      q += __shfl_xor(q, 4, 64);
       if (vpart == 0) vn[t * KT + vkey] = q;
     }
-    // S^T = K . Q^T for this wave's 32 keys (slot order through keymap)
-    f32x16 sacc = f32x16{};
+    // S^T = K . Q^T for both 32-key halves (slot order through keymap)
+    f32x16 sacc[2];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + koff[kk]));
-      sacc = mfma32(av, qreg[kk], sacc);
-    }
-    // mask keys past the chunk or the causal horizon (uniform branch)
-    if ((kt0 + KT > c1) || (a.causal && kt0 + KT - 1 > n - a.w)) {
-      const bool causal = a.causal != 0;
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt0 + kh * 32 + p1_key_of(r, hl);
-        const bool hidden = (key >= c1) | (causal & (key > pos));
-        sacc[r] = hidden ? -INFINITY : sacc[r];
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * ROWB + koff[kk]));
+        sacc[kb] = mfma32(av, qreg[kk], sacc[kb]);
       }
     }
-    float tmax = sacc[0];
+    // mask keys past the chunk or the causal horizon (uniform branch)
+    if ((kt0 + KT > c1) || (causal && kt0 + KT - 1 > n - a.w)) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + kb * 32 + p1_key_of(r, hl);
+          const bool hidden = (key >= c1) | (causal & (key > pos));
+          sacc[kb][r] = hidden ? -INFINITY : sacc[kb][r];
+        }
+      }
+    }
+    float tmax = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(sacc[0][r], sacc[1][r]));
     tmax = fmaxf(tmax, xor32(tmax)) * a.c2;
     const bool raise = tmax > m_run + 8.f;
     if (__any(raise)) {
@@ -297,30 +310,37 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    f32x8 pf[2];
-    bf16x8 pb[2];
+    f32x8 pf[2][2];
+    bf16x8 pb[2][2];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf[k2][e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * k2 + e], a.c2, -m_use));
-        l_run += pf[k2][e];
+      for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pf[kb][k2][e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k2 + e], a.c2, -m_use));
+          l_run += pf[kb][k2][e];
+        }
+        pb[kb][k2] = __builtin_convertvector(pf[kb][k2], bf16x8);   // round to nearest even
       }
-      pb[k2] = __builtin_convertvector(pf[k2], bf16x8);   // round to nearest even
     }
     // O^T += V^T . P^T
-    auto pv = [&](const bf16x8 (&pm)[2]) {
+    auto pv = [&](const bf16x8 (&pm)[2][2]) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(Vt + (toff[k2][0] ^ (db << 6))));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(Vt + (toff[k2][1] ^ (db << 6))));
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pm[k2], oacc[db]);
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const char* vbase = Vt + kb * 32 * ROWB;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vbase + (toff[k2][0] ^ (db << 6))));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vbase + (toff[k2][1] ^ (db << 6))));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pm[kb][k2], oacc[db]);
+          }
         }
       }
     };
@@ -332,53 +352,32 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
     // of P, which makes the weights exact to about 2^-17.
     const float pmax = __builtin_amdgcn_exp2f(tmax - m_use);
     if (__any(16.f * pmax > l_run)) {
-      bf16x8 pr[2];
+      bf16x8 pr[2][2];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        f32x8 rem;
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rem[e] = pf[k2][e] - static_cast<float>(pb[k2][e]);
-        pr[k2] = __builtin_convertvector(rem, bf16x8);
+        for (int k2 = 0; k2 < 2; ++k2) {
+          f32x8 rem;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rem[e] = pf[kb][k2][e] - static_cast<float>(pb[kb][k2][e]);
+          pr[kb][k2] = __builtin_convertvector(rem, bf16x8);
+        }
       }
       pv(pr);
     }
   }
-  lds_barrier();   // ring reads done: reuse the ring for the half merge
+  lds_barrier();   // vn complete
 
   // ||v||^2 of the chunk
   for (int i = tid; i < c1 - c0; i += WG) a.vnorm[static_cast<size_t>(h) * a.T + base + c0 + i] = vn[i];
 
-  // combine the two key halves: waves kh=1 hand (m, l, o) to waves kh=0
-  float* xo = reinterpret_cast<float*>(ring);                 // [4][32 rows][D]
-  float* xml = xo + 4 * 32 * D;                               // [4][32 rows][2]
-  const float l_half = l_run + xor32(l_run);
-  if (kh == 1) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * hl;
-        *reinterpret_cast<f32x4*>(&xo[(rb * 32 + col) * D + d]) =
-            f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
-      }
-    }
-    if (hl == 0) {
-      xml[(rb * 32 + col) * 2] = m_run;
-      xml[(rb * 32 + col) * 2 + 1] = l_half;
-    }
-  }
-  lds_barrier();
-  if (kh == 1) return;
-  const float mo = xml[(rb * 32 + col) * 2], lo_ = xml[(rb * 32 + col) * 2 + 1];
-  const float M = fmaxf(m_run, mo);
-  const float fa = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
-  const float fb = (mo == -INFINITY) ? 0.f : exp2f(mo - M);
+  const float l_tot = l_run + xor32(l_run);
   if (!row_ok) return;
   const size_t part = (static_cast<size_t>((s * a.Hkv + h) * a.RG + rg)) * a.P + c;
-  const int rl = rb * 32 + col;
+  const int rl = wave * 32 + col;
   if (hl == 0) {
-    a.part_ml[(part * ROWS + rl) * 2 + 0] = M;
-    a.part_ml[(part * ROWS + rl) * 2 + 1] = l_half * fa + lo_ * fb;
+    a.part_ml[(part * ROWS + rl) * 2 + 0] = m_run;
+    a.part_ml[(part * ROWS + rl) * 2 + 1] = l_tot;
   }
   float* op = a.part_o + (part * ROWS + rl) * D;
 #pragma unroll
@@ -386,11 +385,8 @@ __global__ __launch_bounds__(WG, 1) void score_p1_bf16(ScoreArgs a) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = db * 32 + 8 * q4 + 4 * hl;
-      const f32x4 other = *reinterpret_cast<const f32x4*>(&xo[rl * D + d]);
-      f32x4 r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = oacc[db][4 * q4 + e] * fa + other[e] * fb;
-      *reinterpret_cast<f32x4*>(op + d) = r;
+      *reinterpret_cast<f32x4*>(op + d) =
+          f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
     }
   }
 }
@@ -508,7 +504,7 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
 // residual plane o - o_h, restoring an fp32-accurate distance.
 constexpr float kResidY = 63.f;   // (1 - p) / p below this <=> p > 2^-6
 
-__global__ __launch_bounds__(WG, 1) void score_p2_bf16(ScoreArgs a) {
+__global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y / a.RG;
   const int rg = blockIdx.y % a.RG;
@@ -530,21 +526,19 @@ __global__ __launch_bounds__(WG, 1) void score_p2_bf16(ScoreArgs a) {
   const int lane = tid & 63;
   const int hl = lane >> 5;
   const int col = lane & 31;
-  const int rb = wave & 3;
-  const int kh = wave >> 2;
   const int g = a.Hq / a.Hkv;
   const int R = g * a.w;
   const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rg);
 
-  // A operands: rows rb*32 + col (M index)
-  const int arow = rg * ROWS + rb * 32 + col;
+  // A operands: rows wave*32 + col (M index)
+  const int arow = rg * ROWS + wave * 32 + col;
   const bool arow_ok = arow < R;
   bf16x8 qa[D / 16], oha[D / 16];
   {
     const int qh = h * g + (arow_ok ? arow / a.w : 0);
     const int wi = arow_ok ? arow % a.w : 0;
     const uint16_t* qp = a.q_win + ((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * D;
-    const uint16_t* hp = a.ohi + (grp * ROWS + rb * 32 + col) * D;
+    const uint16_t* hp = a.ohi + (grp * ROWS + wave * 32 + col) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 t = {0u, 0u, 0u, 0u};
@@ -563,7 +557,12 @@ __global__ __launch_bounds__(WG, 1) void score_p2_bf16(ScoreArgs a) {
   }
   const float* vnb = a.vnorm + static_cast<size_t>(h) * a.T + base;
   for (int i = tid; i < c1 - c0; i += WG) sbuf[i] = vnb[c0 + i];
-  __syncthreads();   // operand loads complete before the ring starts counting
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    settle(qa[kk]);
+    settle(oha[kk]);
+  }
+  __syncthreads();
 
   const char* kb8 = reinterpret_cast<const char*>(a.k + (static_cast<size_t>(h) * a.T + base) * D);
   const char* vb8 = reinterpret_cast<const char*>(a.v + (static_cast<size_t>(h) * a.T + base) * D);
@@ -577,84 +576,91 @@ __global__ __launch_bounds__(WG, 1) void score_p2_bf16(ScoreArgs a) {
       sbuf[t * KT + tid] = (rr[tid] + rr[KT + tid]) + (rr[2 * KT + tid] + rr[3 * KT + tid]);
     }
   };
-  const int krow = kh * 32 + col;   // tile row of this lane's key (N index)
-  int koff[D / 16];                 // loop-invariant operand offsets (K and V share them)
+  int koff[D / 16];   // loop-invariant operand offsets (K and V share them; +8 KiB per half)
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(krow, 2 * kk + hl);
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(col, 2 * kk + hl);
+  const bool causal = a.causal != 0;
 
-  for (int t = 0; t < NSTAGE - 1 && t < ntile; ++t) fill.issue(kb8, vb8, c0 + t * KT, c1, t);
+  if (ntile > 0) fill.issue(kb8, vb8, c0, c1, 0);
 
   for (int t = 0; t < ntile; ++t) {
-    wait_stage(min(NSTAGE - 2, ntile - 1 - t));
+    wait_vm<0>();
     lds_barrier();
     if (t > 0) reduce_tile(t - 1);
-    if (t + NSTAGE - 1 < ntile) fill.issue(kb8, vb8, c0 + (t + NSTAGE - 1) * KT, c1, (t + NSTAGE - 1) % NSTAGE);
+    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
     const int kt0 = c0 + t * KT;
-    const char* Kt = ring + (t % NSTAGE) * STAGE_BYTES;
+    const char* Kt = ring + (t & 1) * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
-    const float vn2 = sbuf[t * KT + krow];
-    f32x16 sacc = f32x16{};
-    f32x16 gacc;
+    const bool edge = (kt0 + KT > c1) || (causal && kt0 + KT - 1 > n - a.w);
+    f32x16 sacc[2], gacc[2];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 nv = *reinterpret_cast<const f32x4*>(&rowc[ROWS + rb * 32 + 8 * q4 + 4 * hl]);
+    for (int kb = 0; kb < 2; ++kb) {
+      const float vn2 = sbuf[t * KT + kb * 32 + col];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gacc[4 * q4 + e] = nv[e] + vn2;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 nv = *reinterpret_cast<const f32x4*>(&rowc[ROWS + wave * 32 + 8 * q4 + 4 * hl]);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + koff[kk]));
-      sacc = mfma32(qa[kk], kb, sacc);
-    }
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + koff[kk]));
-      gacc = mfma32(oha[kk], vb, gacc);
-    }
-    // y = (1 - p) / p = 2^-x - 1 with x = log2 p; hidden pairs get y = inf
-    float y[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowc[rb * 32 + 8 * q4 + 4 * hl]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[4 * q4 + e] = fmaf(sacc[4 * q4 + e], a.c2, -lv[e]);
-    }
-    if ((kt0 + KT > c1) || (a.causal && kt0 + KT - 1 > n - a.w)) {   // uniform: edge tile
-      const int key = kt0 + krow;
-      const bool causal = a.causal != 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hz = rowhz[rb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
-        const bool hidden = (key >= c1) | (causal & (key > hz));
-        y[r] = hidden ? -INFINITY : y[r];
+        for (int e = 0; e < 4; ++e) gacc[kb][4 * q4 + e] = nv[e] + vn2;
       }
-    }
-    float ymin = INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      y[r] = __builtin_amdgcn_exp2f(-y[r]) - 1.f;
-      ymin = fminf(ymin, y[r]);
-    }
-    if (__any(ymin < kResidY)) {   // wave-uniform: add the residual plane of o
-      const uint16_t* lp = a.olo + (grp * ROWS + rb * 32 + col) * D;
+      sacc[kb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 ola = as_bf16x8(*reinterpret_cast<const u32x4*>(lp + 16 * kk + 8 * hl));
-        const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + koff[kk]));
-        gacc = mfma32(ola, vb, gacc);
+        const bf16x8 kv = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * ROWB + koff[kk]));
+        sacc[kb] = mfma32(qa[kk], kv, sacc[kb]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        gacc[r] += a.no2d[grp * ROWS + rb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 vv = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + kb * 32 * ROWB + koff[kk]));
+        gacc[kb] = mfma32(oha[kk], vv, gacc[kb]);
+      }
     }
-    float sc = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float y2 = fmaf(y[r], y[r], 9.094947e-13f);   // + 2^-40 keeps 1/y2 finite
-      sc = fmaf(gacc[r], __builtin_amdgcn_rcpf(y2), sc);  // gacc = ||o - v||^2
+    for (int kb = 0; kb < 2; ++kb) {
+      const int krow = kb * 32 + col;
+      // y = (1 - p) / p = 2^-x - 1 with x = log2 p; hidden pairs get y = inf
+      float y[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowc[wave * 32 + 8 * q4 + 4 * hl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * q4 + e] = fmaf(sacc[kb][4 * q4 + e], a.c2, -lv[e]);
+      }
+      if (edge) {   // uniform
+        const int key = kt0 + krow;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int hz = rowhz[wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
+          const bool hidden = (key >= c1) | (causal & (key > hz));
+          y[r] = hidden ? -INFINITY : y[r];
+        }
+      }
+      float ymin = INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        y[r] = __builtin_amdgcn_exp2f(-y[r]) - 1.f;
+        ymin = fminf(ymin, y[r]);
+      }
+      if (__any(ymin < kResidY)) {   // wave-uniform: add the residual plane of o
+        const uint16_t* lp = a.olo + (grp * ROWS + wave * 32 + col) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 ola = as_bf16x8(*reinterpret_cast<const u32x4*>(lp + 16 * kk + 8 * hl));
+          const bf16x8 vv = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + kb * 32 * ROWB + koff[kk]));
+          gacc[kb] = mfma32(ola, vv, gacc[kb]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          gacc[kb][r] += a.no2d[grp * ROWS + wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float y2 = fmaf(y[r], y[r], 9.094947e-13f);       // + 2^-40 keeps 1/y2 finite
+        sc = fmaf(gacc[kb][r], __builtin_amdgcn_rcpf(y2), sc);  // gacc = ||o - v||^2
+      }
+      sc += xor32(sc);
+      if (hl == 0) red[t & 1][wave][krow] = sc;
     }
-    sc += xor32(sc);
-    if (hl == 0) red[t & 1][rb][krow] = sc;
   }
   lds_barrier();
   if (ntile > 0) reduce_tile(ntile - 1);
