@@ -118,14 +118,22 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.S = L->S; g.Hkv = L->Hkv; g.T = static_cast<int>(T); g.max_len = max_len; g.mode = mode;
   g.total_B = bud_off_host[L->S];
   g.nchunk = (max_len + kSelChunk - 1) / kSelChunk;
+  const bool smp = mode == KVE_SAMPLE;
   const size_t SH = static_cast<size_t>(g.S) * g.Hkv;
-  const size_t plane = (mode == KVE_SAMPLE) ? static_cast<size_t>(g.Hkv) * g.T * sizeof(double) : 0;
+  const size_t plane = smp ? static_cast<size_t>(g.Hkv) * g.T * sizeof(double) : 0;
+  const int levels = smp ? kSelLevels64 : kSelLevels32;
   size_t off = 0;
   g.off_a = off; off = align256(off + plane);
   g.off_b = off; off = align256(off + plane);
-  g.off_hist = off; off = align256(off + kSelLevels32 * SH * kSelBins * sizeof(int32_t));
+  g.off_hist = off; off = align256(off + levels * SH * kSelBins * sizeof(int32_t));
+  g.zero_end = off;
   g.off_cnt = off; off = align256(off + SH * g.nchunk * 2 * sizeof(int32_t));
-  g.off_state = off; off = align256(off + SH * 2 * sizeof(uint32_t));
+  g.off_thr = off; off = align256(off + SH * sizeof(uint64_t));
+  g.off_need = off; off = align256(off + SH * sizeof(int32_t));
+  g.off_part = off; off = align256(off + (smp ? SH * g.nchunk * 4 * sizeof(double) : 0));
+  g.off_state = off; off = align256(off + (smp ? SH * kSelStateSlots * sizeof(double) : 0));
+  g.off_arrive = off; off = align256(off + (smp ? SH * sizeof(uint32_t) : 0));
+  if (smp) g.zero_end = off;
   g.bytes = off;
   *G = g;
   return KVE_OK;

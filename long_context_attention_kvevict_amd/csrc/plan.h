@@ -29,20 +29,31 @@ struct ScoreGeom {
   size_t bytes;
 };
 
-// Keys per workgroup of the multi-workgroup radix select and its histogram
-// width (2048 bins = 11-bit digits).
+// Keys per workgroup of the multi-workgroup selection, histogram width
+// (2048 bins = 11-bit digits), digit levels for fp32 scores and fp64 Gumbel
+// keys, per-head state slots and the step budget of the expected-samples
+// search (a safeguarded Newton iteration in log m that converges in well
+// under ten steps on the score distributions tried).
 constexpr int kSelChunk = 4096;
 constexpr int kSelBins = 2048;
 constexpr int kSelLevels32 = 3;
+constexpr int kSelLevels64 = 6;
+constexpr int kSelStateSlots = 8;
+constexpr int kSelSearchSteps = 12;
 
 struct SelectGeom {
   int S, Hkv, T, max_len, mode;
   int nchunk;                      // chunks of kSelChunk keys per (sequence, head)
   int64_t total_B;
-  size_t off_a, off_b;             // sample mode: fp64 planes [Hkv][T]
-  size_t off_hist;                 // top-k: int [levels][S*Hkv][kSelBins]
-  size_t off_cnt;                  // top-k: int [S*Hkv][nchunk][2]
-  size_t off_state;                // top-k: uint32 [S*Hkv][2]
+  size_t off_a, off_b;             // sampling: fp64 planes [Hkv][T]
+  size_t off_hist;                 // int [levels][S*Hkv][kSelBins]
+  size_t off_cnt;                  // int [S*Hkv][nchunk][2]
+  size_t off_thr;                  // uint64 [S*Hkv]
+  size_t off_need;                 // int [S*Hkv]
+  size_t off_part;                 // sampling: double [S*Hkv][nchunk][4]
+  size_t off_state;                // sampling: double [S*Hkv][kSelStateSlots]
+  size_t off_arrive;               // sampling: uint32 [S*Hkv]
+  size_t zero_end;                 // [off_hist, zero_end) is cleared on entry
   size_t bytes;
 };
 

@@ -1,95 +1,40 @@
 // Budgeted per-head selection.
 //
-// Top-k ("DropKV" page, §3.3: evict the smallest scores, keep the B largest;
-// "A Probabilistic Interpretation of KV Cache Eviction", §4: top-k as a
-// zero-variance estimator).  Radix select over the order-preserving uint32
-// image of the fp32 scores (four 8-bit digit passes, most significant first)
-// finds the B-th largest key; an ordered stream compaction (wave ballot +
-// mbcnt prefix + per-wave totals in LDS) then writes the kept indices in
-// ascending order: every key above the threshold plus the lowest-indexed
-// keys equal to it.
+// Top-k ("DropKV" page, §3.3: evict the smallest scores, i.e. keep the B
+// largest; "A Probabilistic Interpretation of KV Cache Eviction", §4: top-k
+// as a zero-variance estimator): the B largest scores of each (sequence, KV
+// head), ties to the lower index, NaN below every number.
 //
-// Sampling ("A Probabilistic Interpretation ...", §4 proposals, App. D.1
-// temperature, App. F Problem 5 / Algorithm 2, §6 Eq. 10): fp64 proposal,
-// expected-samples search for m (Newton iterations on the concave
-// E[J(m)] = sum 1 - (1-pi)^m, then an integer check of the +-0.5 band),
-// Gumbel keys from Philox-4x64-10, radix select on the fp64 keys, bias
-// -log(q_j)/tau_w with q_j = 1 - (1-pi_j)^m.
+// Sampling ("A Probabilistic Interpretation ...", §4 proposals with full
+// support, App. D.1 tempering, App. F Problem 5 / Algorithm 2 and Eq. 24-25,
+// §6 Eq. 10): fp64 proposal log pi~ = log(max(s, 2^-126)) / tau, a number of
+// with-replacement draws m whose expected distinct count
+// E(m) = sum_j 1 - (1 - pi_j)^m lies within 0.5 of B, Gumbel keys from
+// Philox-4x64-10 (the B largest are kept), bias -log(q_j) / tau_w with
+// q_j = 1 - (1 - pi_j)^m.
 //
-// One workgroup of 1024 threads per (sequence, KV head).
+// Work is spread over workgroups of SEL_CHUNK keys of one (sequence, head),
+// one launch per pass.  Selection is a radix select over the order-preserving
+// integer image of the keys (11-bit digits, most significant first):
+// histogram launches resolve the B-th largest key, a count launch tallies the
+// keys above / equal to it per chunk, and the write launch places each
+// chunk's kept indices after those of earlier chunks, so the output is
+// ascending.  Sums across workgroups (the proposal's normaliser and E(m)) are
+// finished by the last workgroup of each head to arrive, in chunk order, and
+// histograms use integer atomics: results are bit-reproducible.
 #include "common.h"
 #include "launch.h"
 #include "timing.h"
 
 namespace kve {
 
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_PER = 16;
+constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER;
+constexpr int SEL_BINS = 2048;
+static_assert(SEL_CHUNK == kSelChunk && SEL_BINS == kSelBins, "host and device select geometry disagree");
 
-// Block-wide exclusive prefix of two predicates at once.  Returns the prefix
-// of each and writes the block totals.  Contains two barriers.
-__device__ __forceinline__ void block_scan2(bool p0, bool p1, int* pre0, int* pre1, int* tot0, int* tot1,
-                                            int* lds /* [2][SEL_WAVES] */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t b0 = __ballot(p0), b1 = __ballot(p1);
-  const int in0 = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b0 >> 32),
-                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b0), 0));
-  const int in1 = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b1 >> 32),
-                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b1), 0));
-  if (lane == 0) {
-    lds[wave] = __popcll(b0);
-    lds[SEL_WAVES + wave] = __popcll(b1);
-  }
-  __syncthreads();
-  int o0 = 0, o1 = 0, t0 = 0, t1 = 0;
-  for (int wv = 0; wv < SEL_WAVES; ++wv) {
-    const int c0 = lds[wv], c1 = lds[SEL_WAVES + wv];
-    if (wv < wave) { o0 += c0; o1 += c1; }
-    t0 += c0;
-    t1 += c1;
-  }
-  __syncthreads();
-  *pre0 = o0 + in0;
-  *pre1 = o1 + in1;
-  *tot0 = t0;
-  *tot1 = t1;
-}
-
-// Finds the digit d (scanning from 255 down) where the running count of
-// candidates with a larger digit first reaches `need`; returns d and the
-// count strictly above it.  hist has 256 entries; executed by thread 0.
-__device__ __forceinline__ void pick_digit(const int* hist, int need, int* digit, int* above) {
-  int cum = 0;
-  for (int dg = 255; dg >= 0; --dg) {
-    const int c = hist[dg];
-    if (cum + c >= need) {
-      *digit = dg;
-      *above = cum;
-      return;
-    }
-    cum += c;
-  }
-  *digit = 0;
-  *above = cum;
-}
-
-// ------------------------------------------------------------------ top-k
-// Multi-workgroup radix select.  Every (sequence, KV head) is cut into chunks
-// of TK_CHUNK keys, one workgroup each.  Three histogram launches resolve the
-// B-th largest key digit by digit (bits 31..21, 20..10, 9..0); a count launch
-// tallies keys above / equal to that threshold per chunk; the write launch
-// places each chunk's kept indices after those of all earlier chunks, so the
-// output is ascending.  Integer atomics only: the result is deterministic.
-constexpr int TK_THREADS = 256;
-constexpr int TK_PER = 16;
-constexpr int TK_CHUNK = TK_THREADS * TK_PER;
-constexpr int TK_BINS = 2048;
-constexpr int TK_LEVELS = 3;
-static_assert(TK_CHUNK == kSelChunk && TK_BINS == kSelBins && TK_LEVELS == kSelLevels32,
-              "host and device select geometry disagree");
-
-__device__ __forceinline__ int tk_shift(int lv) { return lv == 0 ? 21 : (lv == 1 ? 10 : 0); }
-
+// ------------------------------------------------------------ block helpers
 // Inclusive prefix sum over a 256-thread block; *total gets the block sum.
 // lds: 4 ints.  Two barriers.
 __device__ __forceinline__ int block_incl_scan256(int v, int* lds, int* total) {
@@ -113,28 +58,86 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* lds, int* total) {
   return v + off;
 }
 
-// Scans a TK_BINS histogram from the top bin down; returns the bin at which
+// Block sum / max of fp64 in a fixed order (lanes, then waves 0..3).
+__device__ __forceinline__ double block_sum_d(double v, double* lds) {
+  v = wave_sum_d(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  const double t = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+  __syncthreads();
+  return t;
+}
+__device__ __forceinline__ double block_max_d(double v, double* lds) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  const double t = fmax(fmax(lds[0], lds[1]), fmax(lds[2], lds[3]));
+  __syncthreads();
+  return t;
+}
+
+// --------------------------------------------------------------- key types
+template <typename K>
+struct Radix;
+template <>
+struct Radix<uint32_t> {   // digits of 11 + 11 + 10 bits
+  static constexpr int LEVELS = 3;
+  __device__ static int shift(int lv) { return lv == 0 ? 21 : (lv == 1 ? 10 : 0); }
+  __device__ static uint32_t wmask(int lv) { return lv == 2 ? 0x3ffu : 0x7ffu; }
+};
+template <>
+struct Radix<uint64_t> {   // digits of 5 x 11 + 9 bits
+  static constexpr int LEVELS = 6;
+  __device__ static int shift(int lv) { return lv < 5 ? 53 - 11 * lv : 0; }
+  __device__ static uint64_t wmask(int lv) { return lv < 5 ? 0x7ffull : 0x1ffull; }
+};
+static_assert(Radix<uint32_t>::LEVELS == kSelLevels32 && Radix<uint64_t>::LEVELS == kSelLevels64,
+              "host and device digit counts disagree");
+
+// Keys of a [Hkv][T] plane: fp32 scores (top-k) or fp64 Gumbel keys.
+struct ScoreKeys {
+  typedef uint32_t K;
+  const float* p;
+  __device__ K key(size_t i) const { return f32_order_key(p[i]); }
+};
+struct GumbelKeys {
+  typedef uint64_t K;
+  const double* p;
+  __device__ K key(size_t i) const { return f64_order_key(p[i]); }
+};
+
+// Geometry shared by the selection kernels.
+struct SelArgs {
+  const int32_t* seq_off;
+  const int32_t* bud_off;
+  int S, Hkv, T, nchunk;
+  int64_t totalB;
+};
+
+// Scans a SEL_BINS histogram from the top bin down; returns the bin at which
 // the running count first reaches `need` and the count strictly above it.
 // Thread t owns bins 2047-8t .. 2040-8t.  lds: 6 ints.
-__device__ void tk_pick(const int* __restrict__ gh, int need, int* lds, int* digit, int* above) {
+__device__ void pick_bin(const int* __restrict__ gh, int need, int* lds, int* digit, int* above) {
   const int t = threadIdx.x;
   int c[8];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    c[i] = gh[TK_BINS - 1 - 8 * t - i];
+    c[i] = gh[SEL_BINS - 1 - 8 * t - i];
     sum += c[i];
   }
   if (t == 0) { lds[4] = 0; lds[5] = 0; }
   int total;
-  const int incl = block_incl_scan256(sum, lds, &total);   // barriers order the init above
+  const int incl = block_incl_scan256(sum, lds, &total);   // its barriers order the init above
   const int excl = incl - sum;
   if (excl < need && need <= incl) {
     int cum = excl;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (cum + c[i] >= need) {
-        lds[4] = TK_BINS - 1 - 8 * t - i;
+        lds[4] = SEL_BINS - 1 - 8 * t - i;
         lds[5] = cum;
         break;
       }
@@ -147,19 +150,18 @@ __device__ void tk_pick(const int* __restrict__ gh, int need, int* lds, int* dig
   __syncthreads();
 }
 
-// Resolves levels 0 .. nlv-1: key prefix, its mask and the count still
-// needed among keys carrying that prefix.
-__device__ void tk_resolve(const int* __restrict__ hist, int SH, int sh, int nlv, int B, int* lds,
-                           uint32_t* prefix, uint32_t* mask, int* need) {
-  uint32_t p = 0, m = 0;
+// Resolves digit levels 0 .. nlv-1: key prefix, its mask and the count still
+// needed among the keys carrying that prefix.
+template <typename K>
+__device__ void resolve(const int* __restrict__ hist, int SH, int sh, int nlv, int B, int* lds, K* prefix, K* mask,
+                        int* need) {
+  K p = 0, m = 0;
   int nd = B;
   for (int lv = 0; lv < nlv; ++lv) {
     int dg, ab;
-    tk_pick(hist + (static_cast<size_t>(lv) * SH + sh) * TK_BINS, nd, lds, &dg, &ab);
-    const int sft = tk_shift(lv);
-    const uint32_t width_mask = (lv == 2) ? 0x3ffu : 0x7ffu;
-    p |= static_cast<uint32_t>(dg) << sft;
-    m |= width_mask << sft;
+    pick_bin(hist + (static_cast<size_t>(lv) * SH + sh) * SEL_BINS, nd, lds, &dg, &ab);
+    p |= static_cast<K>(dg) << Radix<K>::shift(lv);
+    m |= Radix<K>::wmask(lv) << Radix<K>::shift(lv);
     nd -= ab;
   }
   *prefix = p;
@@ -167,44 +169,44 @@ __device__ void tk_resolve(const int* __restrict__ hist, int SH, int sh, int nlv
   *need = nd;
 }
 
-__global__ __launch_bounds__(256) void topk_zero(int* __restrict__ hist, int n) {
+__global__ __launch_bounds__(256) void sel_zero(int* __restrict__ p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) hist[i] = 0;
+  if (i < n) p[i] = 0;
 }
 
-template <int LV>
-__global__ __launch_bounds__(TK_THREADS) void topk_hist(const float* __restrict__ scores,
-                                                        const int32_t* __restrict__ seq_off,
-                                                        const int32_t* __restrict__ bud_off, int T, int Hkv,
-                                                        int SH, int* __restrict__ hist) {
+// One histogram level over the keys matching the prefix of earlier levels.
+template <class Src, int LV>
+__global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int* __restrict__ hist) {
+  typedef typename Src::K K;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int base = seq_off[s];
-  const int n = seq_off[s + 1] - base;
-  const int B = bud_off[s + 1] - bud_off[s];
-  const int j0 = ch * TK_CHUNK;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int B = a.bud_off[s + 1] - a.bud_off[s];
+  const int j0 = ch * SEL_CHUNK;
   if (B <= 0 || B >= n || j0 >= n) return;
-  const int sh = s * Hkv + h;
-  __shared__ int lh[TK_BINS];
+  const int SH = a.S * a.Hkv;
+  const int sh = s * a.Hkv + h;
+  __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
-  for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) lh[i] = 0;
-  uint32_t prefix = 0, mask = 0;
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+  K prefix = 0, mask = 0;
   int need = B;
-  if (LV > 0) tk_resolve(hist, SH, sh, LV, B, lds, &prefix, &mask, &need);
+  if (LV > 0) resolve<K>(hist, SH, sh, LV, B, lds, &prefix, &mask, &need);
   __syncthreads();
-  const float* sc = scores + static_cast<size_t>(h) * T + base;
-  const int sft = tk_shift(LV);
-  const uint32_t dmask = (LV == 2) ? 0x3ffu : 0x7ffu;
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  const int sft = Radix<K>::shift(LV);
+  const K dm = Radix<K>::wmask(LV);
 #pragma unroll 4
-  for (int i = 0; i < TK_PER; ++i) {
-    const int j = j0 + i * TK_THREADS + threadIdx.x;
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = j0 + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
-      const uint32_t u = f32_order_key(sc[j]);
-      if ((u & mask) == prefix) atomicAdd(&lh[(u >> sft) & dmask], 1);
+      const K u = src.key(row + j);
+      if ((u & mask) == prefix) atomicAdd(&lh[static_cast<int>((u >> sft) & dm)], 1);
     }
   }
   __syncthreads();
-  int* gh = hist + (static_cast<size_t>(LV) * SH + sh) * TK_BINS;
-  for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) {
+  int* gh = hist + (static_cast<size_t>(LV) * SH + sh) * SEL_BINS;
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) {
     const int c = lh[i];
     if (c) atomicAdd(&gh[i], c);
   }
@@ -212,96 +214,102 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist(const float* __restrict_
 
 // Per chunk: keys above the threshold and keys equal to it.  Chunk 0 also
 // stores the threshold and the number of equal keys to keep.
-__global__ __launch_bounds__(TK_THREADS) void topk_count(const float* __restrict__ scores,
-                                                         const int32_t* __restrict__ seq_off,
-                                                         const int32_t* __restrict__ bud_off, int T, int Hkv,
-                                                         int SH, int nchunk, const int* __restrict__ hist,
-                                                         int* __restrict__ cnt, uint32_t* __restrict__ state) {
+template <class Src>
+__global__ __launch_bounds__(SEL_THREADS) void sel_count(Src src, SelArgs a, const int* __restrict__ hist,
+                                                         int* __restrict__ cnt, uint64_t* __restrict__ thr_out,
+                                                         int* __restrict__ need_out) {
+  typedef typename Src::K K;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int base = seq_off[s];
-  const int n = seq_off[s + 1] - base;
-  const int B = bud_off[s + 1] - bud_off[s];
-  const int j0 = ch * TK_CHUNK;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int B = a.bud_off[s + 1] - a.bud_off[s];
+  const int j0 = ch * SEL_CHUNK;
   if (B <= 0 || B >= n || j0 >= n) return;
-  const int sh = s * Hkv + h;
+  const int SH = a.S * a.Hkv;
+  const int sh = s * a.Hkv + h;
   __shared__ int lds[8];
-  uint32_t thr, mask;
+  K thr, mask;
   int need;
-  tk_resolve(hist, SH, sh, TK_LEVELS, B, lds, &thr, &mask, &need);
-  const float* sc = scores + static_cast<size_t>(h) * T + base;
+  resolve<K>(hist, SH, sh, Radix<K>::LEVELS, B, lds, &thr, &mask, &need);
+  const size_t row = static_cast<size_t>(h) * a.T + base;
   int gt = 0, eq = 0;
 #pragma unroll 4
-  for (int i = 0; i < TK_PER; ++i) {
-    const int j = j0 + i * TK_THREADS + threadIdx.x;
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = j0 + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
-      const uint32_t u = f32_order_key(sc[j]);
+      const K u = src.key(row + j);
       gt += (u > thr);
       eq += (u == thr);
     }
   }
-  const int packed = (gt << 16) | eq;   // each count <= TK_CHUNK < 2^16
+  const int packed = (gt << 16) | eq;   // each count <= SEL_CHUNK < 2^16
   int tot;
   block_incl_scan256(packed, lds, &tot);
   if (threadIdx.x == 0) {
-    cnt[(static_cast<size_t>(sh) * nchunk + ch) * 2 + 0] = tot >> 16;
-    cnt[(static_cast<size_t>(sh) * nchunk + ch) * 2 + 1] = tot & 0xffff;
+    cnt[(static_cast<size_t>(sh) * a.nchunk + ch) * 2 + 0] = tot >> 16;
+    cnt[(static_cast<size_t>(sh) * a.nchunk + ch) * 2 + 1] = tot & 0xffff;
     if (ch == 0) {
-      state[sh * 2 + 0] = thr;
-      state[sh * 2 + 1] = static_cast<uint32_t>(need);
+      thr_out[sh] = static_cast<uint64_t>(thr);
+      need_out[sh] = need;
     }
   }
 }
 
+// Bias of a kept entry: 0 (top-k) or -log(q_j) / tau_w (sampling).
+struct ZeroBias {
+  __device__ float operator()(int, size_t) const { return 0.f; }
+};
+struct SnisBias {
+  const double* L;        // log1p(-pi), [Hkv][T]
+  const double* state;    // per (sequence, head) search state, m at kStM
+  double inv_tau_w;
+  __device__ float operator()(int sh, size_t i) const;
+};
+
 // Ordered write: thread t owns keys j0 + 16t .. j0 + 16t + 15.
-__global__ __launch_bounds__(TK_THREADS) void topk_write(const float* __restrict__ scores,
-                                                         const int32_t* __restrict__ seq_off,
-                                                         const int32_t* __restrict__ bud_off, int T, int Hkv,
-                                                         int64_t totalB, int nchunk, const int* __restrict__ cnt,
-                                                         const uint32_t* __restrict__ state,
-                                                         int32_t* __restrict__ idx, float* __restrict__ bias,
-                                                         double* __restrict__ m_out,
-                                                         int32_t* __restrict__ status_out) {
+template <class Src, class Bias>
+__global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, SelArgs a, const int* __restrict__ cnt,
+                                                         const uint64_t* __restrict__ thr_in,
+                                                         const int* __restrict__ need_in, int32_t* __restrict__ idx,
+                                                         float* __restrict__ bias) {
+  typedef typename Src::K K;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int base = seq_off[s];
-  const int n = seq_off[s + 1] - base;
-  const int B = bud_off[s + 1] - bud_off[s];
-  const int j0 = ch * TK_CHUNK;
-  const int sh = s * Hkv + h;
-  if (ch == 0 && threadIdx.x == 0) {
-    if (m_out) m_out[sh] = 0.0;
-    if (status_out) status_out[sh] = KVE_OK;
-  }
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int B = a.bud_off[s + 1] - a.bud_off[s];
+  const int j0 = ch * SEL_CHUNK;
+  const int sh = s * a.Hkv + h;
   if (B <= 0 || j0 >= n) return;
-  int32_t* out = idx + h * totalB + bud_off[s];
-  float* bout = bias + h * totalB + bud_off[s];
-  if (B >= n) {
-    for (int i = threadIdx.x; i < TK_CHUNK; i += TK_THREADS) {
+  int32_t* out = idx + h * a.totalB + a.bud_off[s];
+  float* bout = bias + h * a.totalB + a.bud_off[s];
+  if (B >= n) {   // everything kept, weight 1
+    for (int i = threadIdx.x; i < SEL_CHUNK; i += SEL_THREADS) {
       const int j = j0 + i;
       if (j < n) { out[j] = j; bout[j] = 0.f; }
     }
     return;
   }
   __shared__ int lds[8];
-  const uint32_t thr = state[sh * 2 + 0];
-  const int need = static_cast<int>(state[sh * 2 + 1]);
+  const K thr = static_cast<K>(thr_in[sh]);
+  const int need = need_in[sh];
   // keys above / equal to the threshold in earlier chunks
   int gt_b = 0, eq_b = 0;
-  for (int c = threadIdx.x; c < ch; c += TK_THREADS) {
-    gt_b += cnt[(static_cast<size_t>(sh) * nchunk + c) * 2 + 0];
-    eq_b += cnt[(static_cast<size_t>(sh) * nchunk + c) * 2 + 1];
+  for (int c = threadIdx.x; c < ch; c += SEL_THREADS) {
+    gt_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2 + 0];
+    eq_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2 + 1];
   }
   int tot;
   block_incl_scan256(gt_b, lds, &tot);
   gt_b = tot;
   block_incl_scan256(eq_b, lds, &tot);
   eq_b = tot;
-  const float* sc = scores + static_cast<size_t>(h) * T + base;
-  const int jt = j0 + TK_PER * threadIdx.x;
-  uint32_t u[TK_PER];
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  const int jt = j0 + SEL_PER * threadIdx.x;
+  K u[SEL_PER];
   int neq = 0;
 #pragma unroll
-  for (int i = 0; i < TK_PER; ++i) {
-    u[i] = (jt + i < n) ? f32_order_key(sc[jt + i]) : 0u;
+  for (int i = 0; i < SEL_PER; ++i) {
+    u[i] = (jt + i < n) ? src.key(row + jt + i) : K(0);
     neq += (jt + i < n) && (u[i] == thr);
   }
   int eq_tot;
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write(const float* __restrict
   int ntake = 0;
   uint32_t take_bits = 0;
 #pragma unroll
-  for (int i = 0; i < TK_PER; ++i) {
+  for (int i = 0; i < SEL_PER; ++i) {
     const bool in = jt + i < n;
     const bool gt = in && u[i] > thr;
     const bool eq = in && u[i] == thr;
@@ -321,18 +329,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write(const float* __restrict
   int take_tot;
   int pos = gt_b + min(eq_b, need) + block_incl_scan256(ntake, lds, &take_tot) - ntake;
 #pragma unroll
-  for (int i = 0; i < TK_PER; ++i) {
+  for (int i = 0; i < SEL_PER; ++i) {
     if ((take_bits >> i) & 1u) {
       if (pos < B) {   // bounded even if the counts were inconsistent
         out[pos] = jt + i;
-        bout[pos] = 0.f;
+        bout[pos] = bias_of(sh, row + jt + i);
       }
       ++pos;
     }
   }
 }
 
-// ------------------------------------------------------------------ sampling
+// ----------------------------------------------------------------- sampling
 __device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
   *lo = a * b;
   *hi = __umul64hi(a, b);
@@ -355,228 +363,352 @@ __device__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint
   return c0;
 }
 
-__device__ double block_sum_d(double v, double* lds /* [SEL_WAVES] */) {
-  v = wave_sum_d(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) lds[wave] = v;
-  __syncthreads();
-  double t = 0.0;
-  for (int i = 0; i < SEL_WAVES; ++i) t += lds[i];
-  __syncthreads();
-  return t;
+// Per (sequence, head) state of the sampling pipeline (fp64 slots).
+constexpr int kStMax = 0;     // max of log pi~
+constexpr int kStLse = 1;     // log-sum-exp of log pi~
+constexpr int kStU = 2;       // current log m of the search
+constexpr int kStLo = 3;      // search bracket in log m
+constexpr int kStHi = 4;
+constexpr int kStDone = 5;    // 0 searching, 1 converged, 2 target out of reach
+constexpr int kStM = 6;       // final integer m
+constexpr int kStStatus = 7;  // KVE_OK or KVE_ENOCONV
+static_assert(kSelStateSlots == 8, "host and device state size disagree");
+
+constexpr double kAlphaMax = 1e12;   // upper end of the search range for m
+
+__device__ float SnisBias::operator()(int sh, size_t i) const {
+  const double q = -expm1(state[sh * kSelStateSlots + kStM] * L[i]);
+  return static_cast<float>(-log(q) * inv_tau_w);
 }
 
-__device__ double block_max_d(double v, double* lds) {
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) lds[wave] = v;
-  __syncthreads();
-  double t = -INFINITY;
-  for (int i = 0; i < SEL_WAVES; ++i) t = fmax(t, lds[i]);
-  __syncthreads();
-  return t;
-}
+struct SmpArgs {
+  SelArgs g;
+  const float* scores;
+  double* lp;         // [Hkv][T]: log pi~, then the Gumbel keys
+  double* L;          // [Hkv][T]: log1p(-pi)
+  double* part;       // [S*Hkv][nchunk][4] per-chunk partials
+  double* state;      // [S*Hkv][kSelStateSlots]
+  unsigned* arrive;   // [S*Hkv] arrival counters, 0 between launches
+  double inv_tau;
+  uint64_t seed;
+};
 
-// E[J(m)] - target and its derivative over the head's log1p(-pi) plane.
-__device__ void eval_E(const double* L, int n, double m, double target, double* f, double* fp,
-                       double* lds) {
-  double e = 0.0, de = 0.0;
-  for (int j = threadIdx.x; j < n; j += SEL_THREADS) {
-    const double x = m * L[j];
-    const double ex = exp(x);
-    e += -expm1(x);
-    de += -L[j] * ex;
+// Stores the chunk's partials and counts its arrival.  True (in every
+// thread) for the head's last workgroup to arrive, which then sees all the
+// partials of the launch.
+__device__ bool publish(const SmpArgs& A, int sh, int ch, int nch, double v0, double v1, double v2) {
+  __shared__ int last;
+  if (threadIdx.x == 0) {
+    double* p = A.part + (static_cast<size_t>(sh) * A.g.nchunk + ch) * 4;
+    p[0] = v0;
+    p[1] = v1;
+    p[2] = v2;
+    __threadfence();
+    const unsigned prev = atomicAdd(&A.arrive[sh], 1u);
+    last = (prev == static_cast<unsigned>(nch - 1));
   }
-  const double se = block_sum_d(e, lds);
-  const double sde = block_sum_d(de, lds);
-  *f = se - target;
-  *fp = sde;
+  __syncthreads();
+  if (last) __threadfence();
+  return last != 0;
 }
 
-__device__ double eval_E_only(const double* L, int n, double m, double* lds) {
-  double e = 0.0;
-  for (int j = threadIdx.x; j < n; j += SEL_THREADS) e += -expm1(m * L[j]);
-  return block_sum_d(e, lds);
+// Fixed-order block reduction of component c over the head's nch partials.
+__device__ double sum_partials(const SmpArgs& A, int sh, int nch, int c, double* dl) {
+  double v = 0.0;
+  for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v += A.part[(static_cast<size_t>(sh) * A.g.nchunk + i) * 4 + c];
+  return block_sum_d(v, dl);
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_sample(const float* __restrict__ scores,
-                                                            const int32_t* __restrict__ seq_off,
-                                                            const int32_t* __restrict__ bud_off, int Hkv,
-                                                            int T, int64_t totalB, double inv_tau,
-                                                            double inv_tau_w, uint64_t seed,
-                                                            double* __restrict__ planeA,
-                                                            double* __restrict__ planeB,
-                                                            int32_t* __restrict__ idx,
-                                                            float* __restrict__ bias,
-                                                            double* __restrict__ m_out,
-                                                            int32_t* __restrict__ status_out) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int base = seq_off[s];
-  const int n = seq_off[s + 1] - base;
-  const int B = bud_off[s + 1] - bud_off[s];
-  int32_t* out = idx + h * totalB + bud_off[s];
-  float* bout = bias + h * totalB + bud_off[s];
-  const float* sc = scores + static_cast<size_t>(h) * T + base;
-  double* lp = planeA + static_cast<size_t>(h) * T + base;   // log proposal, then Gumbel keys
-  double* L = planeB + static_cast<size_t>(h) * T + base;    // log1p(-pi)
-  const int tid = threadIdx.x;
-  __shared__ double dl[SEL_WAVES];
-  __shared__ int hist[256];
-  __shared__ int scan_lds[2 * SEL_WAVES];
-  __shared__ int sh_digit, sh_above;
+// Whether (sequence s, chunk ch) takes part in the sampling search.
+__device__ __forceinline__ bool smp_active(const SmpArgs& A, int s, int ch, int* n_out, int* B_out, int* base_out) {
+  const int base = A.g.seq_off[s];
+  const int n = A.g.seq_off[s + 1] - base;
+  const int B = A.g.bud_off[s + 1] - A.g.bud_off[s];
+  *n_out = n;
+  *B_out = B;
+  *base_out = base;
+  return B > 0 && B < n && ch * SEL_CHUNK < n;
+}
 
-  if (B <= 0 || B >= n) {
-    if (B >= n)
-      for (int j = tid; j < n; j += SEL_THREADS) { out[j] = j; bout[j] = 0.f; }
-    if (tid == 0) {
-      if (m_out) m_out[s * Hkv + h] = 0.0;
-      if (status_out) status_out[s * Hkv + h] = KVE_OK;
+// Pass A: log pi~ and its maximum.
+__global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  int n, B, base;
+  if (!smp_active(A, s, ch, &n, &B, &base)) return;
+  const int sh = s * A.g.Hkv + h;
+  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  __shared__ double dl[4];
+  double mx = -INFINITY;
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+    if (j < n) {
+      const double x = log(static_cast<double>(fmaxf(A.scores[row + j], 1.17549435e-38f))) * A.inv_tau;
+      A.lp[row + j] = x;
+      mx = fmax(mx, x);
+    }
+  }
+  mx = block_max_d(mx, dl);
+  if (publish(A, sh, ch, nch, mx, 0.0, 0.0)) {
+    double v = -INFINITY;
+    for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v = fmax(v, A.part[(static_cast<size_t>(sh) * A.g.nchunk + i) * 4]);
+    v = block_max_d(v, dl);
+    if (threadIdx.x == 0) {
+      A.state[sh * kSelStateSlots + kStMax] = v;
+      A.arrive[sh] = 0;
+    }
+  }
+}
+
+// Pass B: normaliser sum_j exp(log pi~_j - max); initialises the search.
+__global__ __launch_bounds__(SEL_THREADS) void smp_norm(SmpArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  int n, B, base;
+  if (!smp_active(A, s, ch, &n, &B, &base)) return;
+  const int sh = s * A.g.Hkv + h;
+  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  const double mx = A.state[sh * kSelStateSlots + kStMax];
+  __shared__ double dl[4];
+  double z = 0.0;
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+    if (j < n) z += exp(A.lp[row + j] - mx);
+  }
+  z = block_sum_d(z, dl);
+  if (publish(A, sh, ch, nch, z, 0.0, 0.0)) {
+    const double t = sum_partials(A, sh, nch, 0, dl);
+    if (threadIdx.x == 0) {
+      double* st = A.state + sh * kSelStateSlots;
+      st[kStLse] = mx + log(t);
+      // E(m) <= m, so the root lies at or above m = B
+      st[kStU] = log(static_cast<double>(B));
+      st[kStLo] = log(static_cast<double>(B));
+      st[kStHi] = log(kAlphaMax);
+      st[kStDone] = 0.0;
+      st[kStM] = 0.0;
+      st[kStStatus] = KVE_OK;
+      A.arrive[sh] = 0;
+    }
+  }
+}
+
+// Pass C: log1p(-pi_j) and the Gumbel keys kappa_j = log pi~_j - log(-log u_j),
+// u_j = ((x >> 11) + 0.5) 2^-53 with x the Philox word 0 of counter (j, h, s, 0).
+__global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  int n, B, base;
+  if (!smp_active(A, s, ch, &n, &B, &base)) return;
+  const int sh = s * A.g.Hkv + h;
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  const double lse = A.state[sh * kSelStateSlots + kStLse];
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+    if (j < n) {
+      const double x = A.lp[row + j];
+      A.L[row + j] = log1p(-exp(x - lse));
+      const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h),
+                                          static_cast<uint64_t>(s), 0ull, A.seed, 0ull);
+      const double u = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
+      A.lp[row + j] = x - log(-log(u));
+    }
+  }
+}
+
+// One step of the expected-samples search: E(m) and dE/dm at m = e^u (the
+// first step also E(10^12), to detect a target out of reach).  The head's
+// last workgroup then takes a safeguarded Newton step in log m -- Newton on
+// E(e^u) - B, bisection of the bracket [lo, hi] when the step leaves it --
+// or marks the search converged once |E - B| <= 0.5.
+__global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int first) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  int n, B, base;
+  if (!smp_active(A, s, ch, &n, &B, &base)) return;
+  const int sh = s * A.g.Hkv + h;
+  double* st = A.state + sh * kSelStateSlots;
+  if (st[kStDone] != 0.0) return;   // the same for all of the head's workgroups
+  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  const double m = exp(st[kStU]);
+  __shared__ double dl[4];
+  double e = 0.0, de = 0.0, eh = 0.0;
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+    if (j < n) {
+      const double l = A.L[row + j];
+      const double x = expm1(m * l);
+      e -= x;
+      de -= l * (x + 1.0);
+      if (first) eh -= expm1(kAlphaMax * l);
+    }
+  }
+  e = block_sum_d(e, dl);
+  de = block_sum_d(de, dl);
+  if (first) eh = block_sum_d(eh, dl);
+  if (publish(A, sh, ch, nch, e, de, eh)) {
+    const double E = sum_partials(A, sh, nch, 0, dl);
+    const double dE = sum_partials(A, sh, nch, 1, dl);
+    const double Eh = first ? sum_partials(A, sh, nch, 2, dl) : 0.0;
+    if (threadIdx.x == 0) {
+      const double target = static_cast<double>(B);
+      const double g = E - target;
+      if (first && Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
+        st[kStDone] = 2.0;
+        st[kStM] = kAlphaMax;
+        st[kStStatus] = KVE_ENOCONV;
+      } else if (fabs(g) <= 0.5) {
+        st[kStDone] = 1.0;
+      } else {
+        double u = st[kStU], lo = st[kStLo], hi = st[kStHi];
+        if (g < 0.0) lo = u; else hi = u;
+        const double dg = m * dE;   // dE / dlog m
+        double un = (dg > 0.0) ? u - g / dg : 0.5 * (lo + hi);
+        if (!(un > lo && un < hi)) un = 0.5 * (lo + hi);
+        st[kStU] = un;
+        st[kStLo] = lo;
+        st[kStHi] = hi;
+      }
+      A.arrive[sh] = 0;
+    }
+  }
+}
+
+// Integer m: with E(e^u) within 0.5 of B and E rising by at most 1 per unit
+// step, floor(e^u) or floor(e^u) + 1 lies in the band; the head's last
+// workgroup keeps the first that does and writes m and the status.
+__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, double* m_out, int32_t* status_out) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int sh = s * A.g.Hkv + h;
+  int n, B, base;
+  if (!smp_active(A, s, ch, &n, &B, &base)) {
+    if (ch == 0 && threadIdx.x == 0 && (B <= 0 || B >= n)) {   // nothing searched
+      if (m_out) m_out[sh] = 0.0;
+      if (status_out) status_out[sh] = KVE_OK;
     }
     return;
   }
-  // proposal: log pi~ = log(max(s, 2^-126)) / tau ; pi = softmax(log pi~)
-  double mx = -INFINITY;
-  for (int j = tid; j < n; j += SEL_THREADS) {
-    const double x = log(static_cast<double>(fmaxf(sc[j], 1.17549435e-38f))) * inv_tau;
-    lp[j] = x;
-    mx = fmax(mx, x);
+  double* st = A.state + sh * kSelStateSlots;
+  if (st[kStDone] == 2.0) {   // out of reach: m = 10^12 already set
+    if (ch == 0 && threadIdx.x == 0) {
+      if (m_out) m_out[sh] = st[kStM];
+      if (status_out) status_out[sh] = static_cast<int32_t>(st[kStStatus]);
+    }
+    return;
   }
-  mx = block_max_d(mx, dl);
-  double z = 0.0;
-  for (int j = tid; j < n; j += SEL_THREADS) z += exp(lp[j] - mx);
-  z = block_sum_d(z, dl);
-  const double lse = mx + log(z);
-  for (int j = tid; j < n; j += SEL_THREADS) L[j] = log1p(-exp(lp[j] - lse));
-  __syncthreads();
+  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const double m0 = fmin(floor(exp(st[kStU])), kAlphaMax - 1.0);
+  const double m1 = m0 + 1.0;
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  __shared__ double dl[4];
+  double e0 = 0.0, e1 = 0.0;
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+    if (j < n) {
+      const double l = A.L[row + j];
+      e0 -= expm1(m0 * l);
+      e1 -= expm1(m1 * l);
+    }
+  }
+  e0 = block_sum_d(e0, dl);
+  e1 = block_sum_d(e1, dl);
+  if (publish(A, sh, ch, nch, e0, e1, 0.0)) {
+    const double E0 = sum_partials(A, sh, nch, 0, dl);
+    const double E1 = sum_partials(A, sh, nch, 1, dl);
+    if (threadIdx.x == 0) {
+      const double target = static_cast<double>(B);
+      double m = m0;
+      int status = KVE_OK;
+      if (fabs(E0 - target) <= 0.5) {
+        m = m0;
+      } else if (fabs(E1 - target) <= 0.5) {
+        m = m1;
+      } else {   // the search used up its steps without converging
+        m = (fabs(E1 - target) < fabs(E0 - target)) ? m1 : m0;
+        status = KVE_ENOCONV;
+      }
+      st[kStM] = m;
+      st[kStStatus] = status;
+      if (m_out) m_out[sh] = m;
+      if (status_out) status_out[sh] = status;
+      A.arrive[sh] = 0;
+    }
+  }
+}
 
-  // expected-samples search
-  const double target = static_cast<double>(B);
-  const double ALPHA = 1e12;
-  double m;
-  int status = KVE_OK;
-  double f, fp;
-  eval_E(L, n, ALPHA, target, &f, &fp, dl);
-  if (f < -0.5) {
-    m = ALPHA;
-    status = KVE_ENOCONV;
-  } else {
-    // Newton from the left on the concave increasing f: iterates increase
-    // monotonically towards the root (E[J(m)] <= m, so m = B is left of it)
-    m = target;
-    for (int it = 0; it < 200; ++it) {
-      eval_E(L, n, m, target, &f, &fp, dl);
-      if (f >= -1e-3 || !(fp > 0.0)) break;
-      const double step = -f / fp;
-      m = fmin(m + step, ALPHA);
-      if (step < 1e-9 * m) break;
-    }
-    // integer in the band |E - B| <= 0.5: bracket search around round(m)
-    double lo = fmax(0.0, floor(m) - 2.0), hi = fmin(ALPHA, ceil(m) + 2.0);
-    for (int grow = 0; grow < 64; ++grow) {
-      const double elo = eval_E_only(L, n, lo, dl) - target;
-      const double ehi = eval_E_only(L, n, hi, dl) - target;
-      if (elo <= 0.5 && ehi >= -0.5) break;
-      const double wdt = hi - lo + 1.0;
-      if (elo > 0.5) lo = fmax(0.0, lo - wdt);
-      if (ehi < -0.5) hi = fmin(ALPHA, hi + wdt);
-    }
-    // integer binary search (the steps of Algorithm 2) inside [lo, hi]
-    m = -1.0;
-    for (int it = 0; it < 128 && lo <= hi; ++it) {
-      const double mid = floor((lo + hi) * 0.5);
-      const double e = eval_E_only(L, n, mid, dl) - target;
-      if (fabs(e) <= 0.5) { m = mid; break; }
-      if (e < 0.0) lo = mid + 1.0; else hi = mid - 1.0;
-    }
-    if (m < 0.0) { m = ALPHA; status = KVE_ENOCONV; }
+// ----------------------------------------------------------------- launch
+template <class Src, class Bias>
+static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,
+                         uint64_t* thr, int* need, int32_t* idx, float* bias, hipStream_t st) {
+  typedef typename Src::K K;
+  const dim3 grid(G.nchunk, G.Hkv, G.S);
+  hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+  hipLaunchKernelGGL((sel_hist<Src, 1>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+  hipLaunchKernelGGL((sel_hist<Src, 2>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+  if (Radix<K>::LEVELS > 3) {
+    hipLaunchKernelGGL((sel_hist<Src, 3>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    hipLaunchKernelGGL((sel_hist<Src, 4>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    hipLaunchKernelGGL((sel_hist<Src, 5>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
   }
-  if (tid == 0) {
-    if (m_out) m_out[s * Hkv + h] = m;
-    if (status_out) status_out[s * Hkv + h] = status;
-  }
+  hipLaunchKernelGGL((sel_count<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, cnt, thr, need);
+  hipLaunchKernelGGL((sel_write<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, cnt, thr, need, idx,
+                     bias);
+}
 
-  // Gumbel keys kappa = log pi~ - log(-log u), stored over the log-proposal
-  for (int j = tid; j < n; j += SEL_THREADS) {
-    const uint64_t x = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h),
-                                        static_cast<uint64_t>(s), 0ull, seed, 0ull);
-    const double u = (static_cast<double>(x >> 11) + 0.5) * 0x1.0p-53;
-    lp[j] = lp[j] - log(-log(u));
-  }
-  __syncthreads();
-
-  // radix select of the B-th largest 64-bit key
-  uint64_t prefix = 0, mask = 0;
-  int need = B;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += SEL_THREADS) {
-      const uint64_t u = f64_order_key(lp[j]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255ull], 1);
-    }
-    __syncthreads();
-    if (tid == 0) pick_digit(hist, need, &sh_digit, &sh_above);
-    __syncthreads();
-    prefix |= static_cast<uint64_t>(sh_digit) << shift;
-    mask |= 255ull << shift;
-    need -= sh_above;
-    __syncthreads();
-  }
-  const uint64_t thr = prefix;
-  int run_eq = 0, run_sel = 0;
-  for (int j0 = 0; j0 < n; j0 += SEL_THREADS) {
-    const int j = j0 + tid;
-    uint64_t u = 0;
-    if (j < n) u = f64_order_key(lp[j]);
-    const bool gt = j < n && u > thr;
-    const bool eq = j < n && u == thr;
-    int pe, dummy, te, td;
-    block_scan2(eq, false, &pe, &dummy, &te, &td, scan_lds);
-    const bool take = gt || (eq && run_eq + pe < need);
-    int ps, tsel;
-    block_scan2(take, false, &ps, &dummy, &tsel, &td, scan_lds);
-    if (take && run_sel + ps < B) {   // bounded even if the threshold logic were off
-      const double q = -expm1(m * L[j]);
-      out[run_sel + ps] = j;
-      bout[run_sel + ps] = static_cast<float>(-log(q) * inv_tau_w);
-    }
-    run_eq += te;
-    run_sel += tsel;
+// Top-k: m = 0 and status OK for every (sequence, head).
+__global__ __launch_bounds__(256) void topk_meta(double* m_out, int32_t* status_out, int SH) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < SH) {
+    if (m_out) m_out[i] = 0.0;
+    if (status_out) status_out[i] = KVE_OK;
   }
 }
 
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, uint64_t seed, int32_t* idx,
                          float* bias, double* m_out, int32_t* status_out, void* ws, hipStream_t st) {
-  dim3 grid(G.Hkv, G.S);
-  if (G.mode == KVE_TOPK) {
-    char* wsb = static_cast<char*>(ws);
-    int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
-    int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
-    uint32_t* state = reinterpret_cast<uint32_t*>(wsb + G.off_state);
-    const int SH = G.S * G.Hkv;
-    const int nhist = TK_LEVELS * SH * TK_BINS;
-    dim3 cgrid(G.nchunk, G.Hkv, G.S);
-    stage_begin(ST_SELECT, st);
-    hipLaunchKernelGGL(topk_zero, dim3((nhist + 255) / 256), dim3(256), 0, st, hist, nhist);
-    hipLaunchKernelGGL(topk_hist<0>, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH, hist);
-    hipLaunchKernelGGL(topk_hist<1>, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH, hist);
-    hipLaunchKernelGGL(topk_hist<2>, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH, hist);
-    hipLaunchKernelGGL(topk_count, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv, SH,
-                       G.nchunk, hist, cnt, state);
-    hipLaunchKernelGGL(topk_write, cgrid, dim3(TK_THREADS), 0, st, scores, seq_off, bud_off, G.T, G.Hkv,
-                       G.total_B, G.nchunk, cnt, state, idx, bias, m_out, status_out);
-    stage_end(ST_SELECT, st);
-    return hipGetLastError();
-  }
-  char* base = static_cast<char*>(ws);
+  char* wsb = static_cast<char*>(ws);
+  int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
+  int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
+  uint64_t* thr = reinterpret_cast<uint64_t*>(wsb + G.off_thr);
+  int* need = reinterpret_cast<int*>(wsb + G.off_need);
+  const int SH = G.S * G.Hkv;
+  SelArgs a;
+  a.seq_off = seq_off;
+  a.bud_off = bud_off;
+  a.S = G.S;
+  a.Hkv = G.Hkv;
+  a.T = G.T;
+  a.nchunk = G.nchunk;
+  a.totalB = G.total_B;
+  const dim3 grid(G.nchunk, G.Hkv, G.S);
+  // histograms (and, in sampling mode, everything up to the arrival
+  // counters, which must start at zero) are cleared by a kernel
+  const int nzero = static_cast<int>((G.zero_end - G.off_hist) / sizeof(int));
   stage_begin(ST_SELECT, st);
-  hipLaunchKernelGGL(select_sample, grid, dim3(SEL_THREADS), 0, st, scores, seq_off, bud_off, G.Hkv, G.T,
-                     G.total_B, 1.0 / static_cast<double>(tau), 1.0 / static_cast<double>(tau_w), seed,
-                     reinterpret_cast<double*>(base + G.off_a), reinterpret_cast<double*>(base + G.off_b),
-                     idx, bias, m_out, status_out);
+  hipLaunchKernelGGL(sel_zero, dim3((nzero + 255) / 256), dim3(256), 0, st, hist, nzero);
+  if (G.mode == KVE_TOPK) {
+    hipLaunchKernelGGL(topk_meta, dim3((SH + 255) / 256), dim3(256), 0, st, m_out, status_out, SH);
+    launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, thr, need, idx, bias, st);
+  } else {
+    SmpArgs A;
+    A.g = a;
+    A.scores = scores;
+    A.lp = reinterpret_cast<double*>(wsb + G.off_a);
+    A.L = reinterpret_cast<double*>(wsb + G.off_b);
+    A.part = reinterpret_cast<double*>(wsb + G.off_part);
+    A.state = reinterpret_cast<double*>(wsb + G.off_state);
+    A.arrive = reinterpret_cast<unsigned*>(wsb + G.off_arrive);
+    A.inv_tau = 1.0 / static_cast<double>(tau);
+    A.seed = seed;
+    hipLaunchKernelGGL(smp_logp, grid, dim3(SEL_THREADS), 0, st, A);
+    hipLaunchKernelGGL(smp_norm, grid, dim3(SEL_THREADS), 0, st, A);
+    hipLaunchKernelGGL(smp_keys, grid, dim3(SEL_THREADS), 0, st, A);
+    for (int it = 0; it < kSelSearchSteps; ++it)
+      hipLaunchKernelGGL(smp_search, grid, dim3(SEL_THREADS), 0, st, A, it == 0 ? 1 : 0);
+    hipLaunchKernelGGL(smp_finish, grid, dim3(SEL_THREADS), 0, st, A, m_out, status_out);
+    const SnisBias bias_of{A.L, A.state, 1.0 / static_cast<double>(tau_w)};
+    launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, thr, need, idx, bias, st);
+  }
   stage_end(ST_SELECT, st);
   return hipGetLastError();
 }
