@@ -12,14 +12,33 @@ recorded on the launch stream over the timed steps) and the fp64 oracle timed
 on a bounded sample of the same workload on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-probe MIB     # plain device copy of known size (counter calibration)
+
+roofline.traffic is the HBM traffic per launch of the dominant kernel from
+hardware counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
+counter reads for a plain copy of known size), taken from the committed
+counter summary under profiles/; it is null when no summary exists for the
+kernel and workload or when the kernel's source has changed since.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "long_context_attention_kvevict_amd", "csrc")
+# dominant-kernel stage -> (kernel symbol, source file)
+STAGE_KERNEL = {
+    "score_pass1": ("score_p1_bf16", "score_bf16.hip"),
+    "score_pass2": ("score_p2_bf16", "score_bf16.hip"),
+    "score_merge": ("score_merge", "score_bf16.hip"),
+    "select": ("sel_", "select.hip"),
+    "compact": ("compact_rows", "compact.hip"),
+}
 
 HBM_PEAK_GBS = 8000.0
 
@@ -31,8 +50,50 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1, help="KV heads the oracle baseline scores")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="KV heads the oracle baseline scores")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (5 times) and exit")
     return ap.parse_args()
+
+
+def _source_sha(fname):
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(stage, workload):
+    """HBM bytes per launch of `stage` from the committed counter summary, or
+    None if there is none for this workload or the kernel source changed."""
+    if stage not in STAGE_KERNEL:
+        return None
+    kernel, src = STAGE_KERNEL[stage]
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != _source_sha(src):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _copy_probe(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)   # one elementwise kernel: reads and writes n*4 bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
 
 
 def _stage_bytes(wl, esize):
@@ -83,6 +144,9 @@ def _cpu_baseline(wl, data, heads):
 
 def main():
     args = _parse()
+    if args.copy_probe:
+        _copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -163,7 +227,8 @@ def main():
                    "d": wl.d, "w": wl.w, "budget_frac": wl.budget_frac, "mode": wl.mode,
                    "pool_kernel": wl.pool_kernel, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dominant, wl.name),
+                     "algorithmic_bytes": sbytes[dominant], "launch_ms": dom_ms},
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stage_ms": {s: round(v[0], 5) for s, v in stages.items()},
     }
