@@ -51,6 +51,8 @@ def _parse():
     ap.add_argument("--workload", default="llama128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="KV heads the oracle baseline scores")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph instead of eager launches")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (5 times) and exit")
     return ap.parse_args()
@@ -189,19 +191,35 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The timed step is the library's eager launches, or with --graph one
+    # HIP-graph replay of them (every kernel of the step still runs).
+    run = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    K.timing_enable(True)
-    torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # per-kernel durations: eager steps with HIP events around every launch
+    K.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     stages = K.timing_summary()
     K.timing_enable(False)
-    print(f"# {args.steps} steps: {ms:.3f} ms/step; stages {stages}", file=sys.stderr, flush=True)
+    print(f"# {args.steps} steps: {ms:.3f} ms/step ({'graph replay' if args.graph else 'eager'}); "
+          f"stages {stages}", file=sys.stderr, flush=True)
 
     esize = 2 if wl.dtype == "bf16" else 4
     sbytes = _stage_bytes(wl, esize)
@@ -225,7 +243,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "S": wl.S, "n": int(max(wl.lens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "d": wl.d, "w": wl.w, "budget_frac": wl.budget_frac, "mode": wl.mode,
-                   "pool_kernel": wl.pool_kernel, "parallelism": "none (1 GPU)"},
+                   "pool_kernel": wl.pool_kernel, "parallelism": "none (1 GPU)",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dominant, wl.name),
                      "algorithmic_bytes": sbytes[dominant], "launch_ms": dom_ms},

@@ -128,12 +128,10 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.off_hist = off; off = align256(off + levels * SH * kSelBins * sizeof(int32_t));
   g.zero_end = off;
   g.off_cnt = off; off = align256(off + SH * g.nchunk * 2 * sizeof(int32_t));
-  g.off_thr = off; off = align256(off + SH * sizeof(uint64_t));
-  g.off_need = off; off = align256(off + SH * sizeof(int32_t));
-  g.off_part = off; off = align256(off + (smp ? SH * g.nchunk * 4 * sizeof(double) : 0));
-  g.off_state = off; off = align256(off + (smp ? SH * kSelStateSlots * sizeof(double) : 0));
-  g.off_arrive = off; off = align256(off + (smp ? SH * sizeof(uint32_t) : 0));
-  if (smp) g.zero_end = off;
+  g.off_rstate = off; off = align256(off + SH * kSelRStateBytes);
+  g.off_part = off; off = align256(off + (smp ? 2 * SH * g.nchunk * 3 * sizeof(double) : 0));
+  g.off_state = off; off = align256(off + (smp ? 2 * SH * kSelSearchBytes : 0));
+  g.off_mvals = off; off = align256(off + (smp ? SH * sizeof(double) : 0));
   g.bytes = off;
   *G = g;
   return KVE_OK;

@@ -38,8 +38,9 @@ constexpr int kSelChunk = 4096;
 constexpr int kSelBins = 2048;
 constexpr int kSelLevels32 = 3;
 constexpr int kSelLevels64 = 6;
-constexpr int kSelStateSlots = 8;
 constexpr int kSelSearchSteps = 12;
+constexpr int kSelRStateBytes = 16;   // per-head radix threshold and count of equal keys kept
+constexpr int kSelSearchBytes = 32;   // per-head search state
 
 struct SelectGeom {
   int S, Hkv, T, max_len, mode;
@@ -47,13 +48,12 @@ struct SelectGeom {
   int64_t total_B;
   size_t off_a, off_b;             // sampling: fp64 planes [Hkv][T]
   size_t off_hist;                 // int [levels][S*Hkv][kSelBins]
-  size_t off_cnt;                  // int [S*Hkv][nchunk][2]
-  size_t off_thr;                  // uint64 [S*Hkv]
-  size_t off_need;                 // int [S*Hkv]
-  size_t off_part;                 // sampling: double [S*Hkv][nchunk][4]
-  size_t off_state;                // sampling: double [S*Hkv][kSelStateSlots]
-  size_t off_arrive;               // sampling: uint32 [S*Hkv]
   size_t zero_end;                 // [off_hist, zero_end) is cleared on entry
+  size_t off_cnt;                  // int [S*Hkv][nchunk][2]
+  size_t off_rstate;               // [S*Hkv] radix threshold state (kSelRStateBytes each)
+  size_t off_part;                 // sampling: double [2][S*Hkv][nchunk][3]
+  size_t off_state;                // sampling: [2][S*Hkv] search state (kSelSearchBytes each)
+  size_t off_mvals;                // sampling: double [S*Hkv] final m
   size_t bytes;
 };
 

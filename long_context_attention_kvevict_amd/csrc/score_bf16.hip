@@ -392,17 +392,19 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------- merge
-// One wave per window row.  Lanes l and l + 32 take alternate chunks (two
-// independent load streams); each lane holds DD/32 consecutive features.
-// Chunks wholly beyond a row's causal horizon carry max = -inf and weight 0.
+// One workgroup per window row: 8 streams of 32 lanes take every 8th chunk
+// (lane = DD/32 consecutive features), then combine through LDS in a fixed
+// order.  Chunks wholly beyond a row's causal horizon carry max = -inf and
+// weight 0.
 template <int DD, bool BF16OUT>
 __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   constexpr int F = DD / 32;
-  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);   // grp * ROWS + rl
+  constexpr int NSTR = 8;
+  const int gr = blockIdx.x;   // grp * ROWS + rl
   const int grp = gr / ROWS;
   const int rl = gr % ROWS;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, ln = lane & 31;
+  const int tid = threadIdx.x;
+  const int st = tid >> 5, ln = tid & 31;
   const int s = grp / (a.Hkv * a.RG);
   const int rg = grp % a.RG;
   const int n = a.seq_off[s + 1] - a.seq_off[s];
@@ -410,12 +412,12 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   const int R = (a.Hq / a.Hkv) * a.w;
   const size_t ro = static_cast<size_t>(gr);
   if (rg * ROWS + rl >= R) {   // padding row of the last row group
-    if (lane == 0) {
+    if (tid == 0) {
       a.lse2[ro] = INFINITY;
       a.no2[ro] = 0.f;
       if (BF16OUT) a.no2d[ro] = 0.f;
     }
-    if (half == 0) {
+    if (tid < 32) {
 #pragma unroll
       for (int f = 0; f < F; ++f) {
         if (BF16OUT) { a.ohi[ro * DD + ln * F + f] = 0; a.olo[ro * DD + ln * F + f] = 0; }
@@ -424,19 +426,25 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
     }
     return;
   }
+  __shared__ float red_o[NSTR][DD];
+  __shared__ float red_l[NSTR];
+  __shared__ float red_m[4];
   const size_t cstride_ml = static_cast<size_t>(ROWS) * 2;
   const size_t cstride_o = static_cast<size_t>(ROWS) * DD;
   const float* ml = a.part_ml + (static_cast<size_t>(grp) * a.P * ROWS + rl) * 2;
   const float* po = a.part_o + (static_cast<size_t>(grp) * a.P * ROWS + rl) * DD + ln * F;
   float M = -INFINITY;
-  for (int c = lane; c < nch; c += 64) M = fmaxf(M, ml[c * cstride_ml]);
+  for (int c = tid; c < nch; c += 256) M = fmaxf(M, ml[c * cstride_ml]);
   M = wave_max(M);
+  if ((tid & 63) == 0) red_m[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   float L = 0.f;
   float acc[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
-#pragma unroll 8
-  for (int c = half; c < nch; c += 2) {
+#pragma unroll 4
+  for (int c = st; c < nch; c += NSTR) {
     const float m = ml[c * cstride_ml];
     const float l = ml[c * cstride_ml + 1];
     const float wgt = (m == -INFINITY) ? 0.f : exp2f(m - M);
@@ -450,9 +458,20 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
       for (int f = 0; f < F; ++f) acc[f] = fmaf(po[c * cstride_o + f], wgt, acc[f]);
     }
   }
-  L += xor32(L);
 #pragma unroll
-  for (int f = 0; f < F; ++f) acc[f] += xor32(acc[f]);
+  for (int f = 0; f < F; ++f) red_o[st][ln * F + f] = acc[f];
+  if (ln == 0) red_l[st] = L;
+  __syncthreads();
+  if (tid >= 32) return;
+  L = 0.f;
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NSTR; ++k) {
+    L += red_l[k];
+#pragma unroll
+    for (int f = 0; f < F; ++f) acc[f] += red_o[k][ln * F + f];
+  }
   const float inv = 1.f / L;
   float sq = 0.f, sqh = 0.f;
   uint16_t hi[F], lo[F];
@@ -468,12 +487,11 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
       sqh = fmaf(0.5f * xh, 0.5f * xh, sqh);
     }
   }
-  // sum over the 32 lanes of one half (both halves hold identical values)
   for (int o = 16; o > 0; o >>= 1) {
-    sq += __shfl_xor(sq, o, 64);
-    if (BF16OUT) sqh += __shfl_xor(sqh, o, 64);
+    sq += __shfl_xor(sq, o, 32);
+    if (BF16OUT) sqh += __shfl_xor(sqh, o, 32);
   }
-  if (lane == 0) {
+  if (ln == 0) {
     a.lse2[ro] = M + log2f(L);
     if (BF16OUT) {
       a.no2[ro] = sqh;
@@ -482,15 +500,13 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
       a.no2[ro] = sq;
     }
   }
-  if (half == 0) {
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      if (BF16OUT) {
-        a.ohi[ro * DD + ln * F + f] = hi[f];
-        a.olo[ro * DD + ln * F + f] = lo[f];
-      } else {
-        o32[ro * DD + ln * F + f] = acc[f];
-      }
+  for (int f = 0; f < F; ++f) {
+    if (BF16OUT) {
+      a.ohi[ro * DD + ln * F + f] = hi[f];
+      a.olo[ro * DD + ln * F + f] = lo[f];
+    } else {
+      o32[ro * DD + ln * F + f] = acc[f];
     }
   }
 }
@@ -699,7 +715,7 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_SCORE_MERGE, st);
-  hipLaunchKernelGGL((score_merge<D, true>), dim3(G.S * G.Hkv * G.RG * (ROWS / 4)), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((score_merge<D, true>), dim3(G.S * G.Hkv * G.RG * ROWS), dim3(256), 0, st, a,
                      static_cast<float*>(nullptr));
   stage_end(ST_SCORE_MERGE, st);
   e = hipGetLastError();
@@ -721,7 +737,7 @@ hipError_t launch_merge_f32(const ScoreGeom& G, const int32_t* seq_off, void* ws
   a.lse2 = reinterpret_cast<float*>(base + G.off_lse2);
   a.no2 = reinterpret_cast<float*>(base + G.off_no2);
   float* o32 = reinterpret_cast<float*>(base + G.off_ohi);
-  dim3 grid(G.S * G.Hkv * G.RG * (ROWS / 4));
+  dim3 grid(G.S * G.Hkv * G.RG * ROWS);
   if (G.d == 64) hipLaunchKernelGGL((score_merge<64, false>), grid, dim3(256), 0, st, a, o32);
   else hipLaunchKernelGGL((score_merge<128, false>), grid, dim3(256), 0, st, a, o32);
   return hipGetLastError();

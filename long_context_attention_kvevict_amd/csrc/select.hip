@@ -14,14 +14,16 @@
 // q_j = 1 - (1 - pi_j)^m.
 //
 // Work is spread over workgroups of SEL_CHUNK keys of one (sequence, head),
-// one launch per pass.  Selection is a radix select over the order-preserving
-// integer image of the keys (11-bit digits, most significant first):
-// histogram launches resolve the B-th largest key, a count launch tallies the
-// keys above / equal to it per chunk, and the write launch places each
-// chunk's kept indices after those of earlier chunks, so the output is
-// ascending.  Sums across workgroups (the proposal's normaliser and E(m)) are
-// finished by the last workgroup of each head to arrive, in chunk order, and
-// histograms use integer atomics: results are bit-reproducible.
+// one launch per pass; no launch waits on another workgroup of the same
+// launch.  Selection is a radix select over the order-preserving integer
+// image of the keys (11-bit digits, most significant first): histogram
+// launches count one digit each (integer atomics), the next launch reads the
+// finished histograms and fixes the digits of the B-th largest key, a count
+// launch tallies the keys above / equal to it per chunk, and the write launch
+// places each chunk's kept indices after those of earlier chunks, so the
+// output is ascending.  Cross-chunk sums of the sampling pass (the proposal's
+// normaliser, E(m) and its derivative) are per-chunk partials that the next
+// launch adds up in chunk order: results are bit-reproducible.
 #include "common.h"
 #include "launch.h"
 #include "timing.h"
@@ -116,18 +118,15 @@ struct SelArgs {
   int64_t totalB;
 };
 
-// Scans a SEL_BINS histogram from the top bin down; returns the bin at which
-// the running count first reaches `need` and the count strictly above it.
-// Thread t owns bins 2047-8t .. 2040-8t.  lds: 6 ints.
-__device__ void pick_bin(const int* __restrict__ gh, int need, int* lds, int* digit, int* above) {
+// Scans the 8 bins a thread holds (thread t owns bins 2047-8t .. 2040-8t, in
+// that order) across the block from the top bin down; returns the bin at
+// which the running count first reaches `need` and the count strictly above
+// it.  lds: 6 ints.
+__device__ void pick_bin(const int (&c)[8], int need, int* lds, int* digit, int* above) {
   const int t = threadIdx.x;
-  int c[8];
   int sum = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    c[i] = gh[SEL_BINS - 1 - 8 * t - i];
-    sum += c[i];
-  }
+  for (int i = 0; i < 8; ++i) sum += c[i];
   if (t == 0) { lds[4] = 0; lds[5] = 0; }
   int total;
   const int incl = block_incl_scan256(sum, lds, &total);   // its barriers order the init above
@@ -150,31 +149,36 @@ __device__ void pick_bin(const int* __restrict__ gh, int need, int* lds, int* di
   __syncthreads();
 }
 
-// Resolves digit levels 0 .. nlv-1: key prefix, its mask and the count still
-// needed among the keys carrying that prefix.
-template <typename K>
-__device__ void resolve(const int* __restrict__ hist, int SH, int sh, int nlv, int B, int* lds, K* prefix, K* mask,
-                        int* need) {
+// Resolves digit levels 0 .. NLV-1 from the finished histograms: key prefix,
+// its mask and the count still needed among the keys carrying that prefix.
+// The histograms of all levels are loaded at once.
+template <typename K, int NLV>
+__device__ void resolve(const int* __restrict__ hist, int SH, int sh, int B, int* lds, K* prefix, K* mask, int* need) {
   K p = 0, m = 0;
   int nd = B;
-  for (int lv = 0; lv < nlv; ++lv) {
-    int dg, ab;
-    pick_bin(hist + (static_cast<size_t>(lv) * SH + sh) * SEL_BINS, nd, lds, &dg, &ab);
-    p |= static_cast<K>(dg) << Radix<K>::shift(lv);
-    m |= Radix<K>::wmask(lv) << Radix<K>::shift(lv);
-    nd -= ab;
+  if (NLV > 0) {
+    int c[NLV > 0 ? NLV : 1][8];
+#pragma unroll
+    for (int lv = 0; lv < NLV; ++lv) {
+      const int* gh = hist + (static_cast<size_t>(lv) * SH + sh) * SEL_BINS;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[lv][i] = gh[SEL_BINS - 1 - 8 * threadIdx.x - i];
+    }
+#pragma unroll
+    for (int lv = 0; lv < NLV; ++lv) {
+      int dg, ab;
+      pick_bin(c[lv], nd, lds, &dg, &ab);
+      p |= static_cast<K>(dg) << Radix<K>::shift(lv);
+      m |= Radix<K>::wmask(lv) << Radix<K>::shift(lv);
+      nd -= ab;
+    }
   }
   *prefix = p;
   *mask = m;
   *need = nd;
 }
 
-__global__ __launch_bounds__(256) void sel_zero(int* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
-// One histogram level over the keys matching the prefix of earlier levels.
+// One digit level: histogram of the keys matching the prefix resolved so far.
 template <class Src, int LV>
 __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int* __restrict__ hist) {
   typedef typename Src::K K;
@@ -188,21 +192,24 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   const int sh = s * a.Hkv + h;
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
-  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
-  K prefix = 0, mask = 0;
-  int need = B;
-  if (LV > 0) resolve<K>(hist, SH, sh, LV, B, lds, &prefix, &mask, &need);
-  __syncthreads();
   const size_t row = static_cast<size_t>(h) * a.T + base;
+  K u[SEL_PER];
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {   // all key loads in flight at once
+    const int j = j0 + i * SEL_THREADS + threadIdx.x;
+    u[i] = (j < n) ? src.key(row + j) : K(0);
+  }
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+  K prefix, mask;
+  int need;
+  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need);
+  __syncthreads();   // lh cleared (level 0 resolves nothing and has no barrier of its own)
   const int sft = Radix<K>::shift(LV);
   const K dm = Radix<K>::wmask(LV);
-#pragma unroll 4
+#pragma unroll
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = j0 + i * SEL_THREADS + threadIdx.x;
-    if (j < n) {
-      const K u = src.key(row + j);
-      if ((u & mask) == prefix) atomicAdd(&lh[static_cast<int>((u >> sft) & dm)], 1);
-    }
+    if (j < n && (u[i] & mask) == prefix) atomicAdd(&lh[static_cast<int>((u[i] >> sft) & dm)], 1);
   }
   __syncthreads();
   int* gh = hist + (static_cast<size_t>(LV) * SH + sh) * SEL_BINS;
@@ -212,13 +219,20 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   }
 }
 
+// Threshold (the B-th largest key) and the number of keys equal to it that
+// are kept, per (sequence, head).
+struct RState {
+  uint64_t thr;
+  int32_t need, pad;
+};
+
 // Per chunk: keys above the threshold and keys equal to it.  Chunk 0 also
 // stores the threshold and the number of equal keys to keep.
 template <class Src>
 __global__ __launch_bounds__(SEL_THREADS) void sel_count(Src src, SelArgs a, const int* __restrict__ hist,
-                                                         int* __restrict__ cnt, uint64_t* __restrict__ thr_out,
-                                                         int* __restrict__ need_out) {
+                                                         int* __restrict__ cnt, RState* __restrict__ rs) {
   typedef typename Src::K K;
+  constexpr int NLV = Radix<K>::LEVELS;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
@@ -228,19 +242,22 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_count(Src src, SelArgs a, con
   const int SH = a.S * a.Hkv;
   const int sh = s * a.Hkv + h;
   __shared__ int lds[8];
-  K thr, mask;
-  int need;
-  resolve<K>(hist, SH, sh, Radix<K>::LEVELS, B, lds, &thr, &mask, &need);
   const size_t row = static_cast<size_t>(h) * a.T + base;
-  int gt = 0, eq = 0;
-#pragma unroll 4
+  K u[SEL_PER];
+#pragma unroll
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = j0 + i * SEL_THREADS + threadIdx.x;
-    if (j < n) {
-      const K u = src.key(row + j);
-      gt += (u > thr);
-      eq += (u == thr);
-    }
+    u[i] = (j < n) ? src.key(row + j) : K(0);
+  }
+  K thr, mask;
+  int need;
+  resolve<K, NLV>(hist, SH, sh, B, lds, &thr, &mask, &need);
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = j0 + i * SEL_THREADS + threadIdx.x;
+    gt += (j < n) && (u[i] > thr);
+    eq += (j < n) && (u[i] == thr);
   }
   const int packed = (gt << 16) | eq;   // each count <= SEL_CHUNK < 2^16
   int tot;
@@ -249,8 +266,11 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_count(Src src, SelArgs a, con
     cnt[(static_cast<size_t>(sh) * a.nchunk + ch) * 2 + 0] = tot >> 16;
     cnt[(static_cast<size_t>(sh) * a.nchunk + ch) * 2 + 1] = tot & 0xffff;
     if (ch == 0) {
-      thr_out[sh] = static_cast<uint64_t>(thr);
-      need_out[sh] = need;
+      RState r;
+      r.thr = static_cast<uint64_t>(thr);
+      r.need = need;
+      r.pad = 0;
+      rs[sh] = r;
     }
   }
 }
@@ -261,16 +281,18 @@ struct ZeroBias {
 };
 struct SnisBias {
   const double* L;        // log1p(-pi), [Hkv][T]
-  const double* state;    // per (sequence, head) search state, m at kStM
+  const double* mvals;    // final m per (sequence, head)
   double inv_tau_w;
-  __device__ float operator()(int sh, size_t i) const;
+  __device__ float operator()(int sh, size_t i) const {
+    const double q = -expm1(mvals[sh] * L[i]);
+    return static_cast<float>(-log(q) * inv_tau_w);
+  }
 };
 
 // Ordered write: thread t owns keys j0 + 16t .. j0 + 16t + 15.
 template <class Src, class Bias>
 __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, SelArgs a, const int* __restrict__ cnt,
-                                                         const uint64_t* __restrict__ thr_in,
-                                                         const int* __restrict__ need_in, int32_t* __restrict__ idx,
+                                                         const RState* __restrict__ rs, int32_t* __restrict__ idx,
                                                          float* __restrict__ bias) {
   typedef typename Src::K K;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -290,8 +312,13 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
     return;
   }
   __shared__ int lds[8];
-  const K thr = static_cast<K>(thr_in[sh]);
-  const int need = need_in[sh];
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  const int jt = j0 + SEL_PER * threadIdx.x;
+  K u[SEL_PER];
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) u[i] = (jt + i < n) ? src.key(row + jt + i) : K(0);
+  const K thr = static_cast<K>(rs[sh].thr);
+  const int need = rs[sh].need;
   // keys above / equal to the threshold in earlier chunks
   int gt_b = 0, eq_b = 0;
   for (int c = threadIdx.x; c < ch; c += SEL_THREADS) {
@@ -303,15 +330,9 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
   gt_b = tot;
   block_incl_scan256(eq_b, lds, &tot);
   eq_b = tot;
-  const size_t row = static_cast<size_t>(h) * a.T + base;
-  const int jt = j0 + SEL_PER * threadIdx.x;
-  K u[SEL_PER];
   int neq = 0;
 #pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) {
-    u[i] = (jt + i < n) ? src.key(row + jt + i) : K(0);
-    neq += (jt + i < n) && (u[i] == thr);
-  }
+  for (int i = 0; i < SEL_PER; ++i) neq += (jt + i < n) && (u[i] == thr);
   int eq_tot;
   int eq_rank = eq_b + block_incl_scan256(neq, lds, &eq_tot) - neq;
   int ntake = 0;
@@ -363,60 +384,43 @@ __device__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint
   return c0;
 }
 
-// Per (sequence, head) state of the sampling pipeline (fp64 slots).
-constexpr int kStMax = 0;     // max of log pi~
-constexpr int kStLse = 1;     // log-sum-exp of log pi~
-constexpr int kStU = 2;       // current log m of the search
-constexpr int kStLo = 3;      // search bracket in log m
-constexpr int kStHi = 4;
-constexpr int kStDone = 5;    // 0 searching, 1 converged, 2 target out of reach
-constexpr int kStM = 6;       // final integer m
-constexpr int kStStatus = 7;  // KVE_OK or KVE_ENOCONV
-static_assert(kSelStateSlots == 8, "host and device state size disagree");
-
 constexpr double kAlphaMax = 1e12;   // upper end of the search range for m
 
-__device__ float SnisBias::operator()(int sh, size_t i) const {
-  const double q = -expm1(state[sh * kSelStateSlots + kStM] * L[i]);
-  return static_cast<float>(-log(q) * inv_tau_w);
-}
+// Search state of one (sequence, head): current log m, bracket in log m,
+// and whether the search has stopped (1: converged, 2: target out of reach).
+struct Search {
+  double u, lo, hi, done;
+};
+static_assert(sizeof(Search) == kSelSearchBytes, "host and device state size disagree");
 
 struct SmpArgs {
   SelArgs g;
   const float* scores;
   double* lp;         // [Hkv][T]: log pi~, then the Gumbel keys
   double* L;          // [Hkv][T]: log1p(-pi)
-  double* part;       // [S*Hkv][nchunk][4] per-chunk partials
-  double* state;      // [S*Hkv][kSelStateSlots]
-  unsigned* arrive;   // [S*Hkv] arrival counters, 0 between launches
+  double* part;       // [2][S*Hkv][nchunk][3] per-chunk partials (ping-pong)
+  Search* state;      // [2][S*Hkv] search state (ping-pong)
+  double* mvals;      // [S*Hkv] final m
   double inv_tau;
   uint64_t seed;
 };
 
-// Stores the chunk's partials and counts its arrival.  True (in every
-// thread) for the head's last workgroup to arrive, which then sees all the
-// partials of the launch.
-__device__ bool publish(const SmpArgs& A, int sh, int ch, int nch, double v0, double v1, double v2) {
-  __shared__ int last;
-  if (threadIdx.x == 0) {
-    double* p = A.part + (static_cast<size_t>(sh) * A.g.nchunk + ch) * 4;
-    p[0] = v0;
-    p[1] = v1;
-    p[2] = v2;
-    __threadfence();
-    const unsigned prev = atomicAdd(&A.arrive[sh], 1u);
-    last = (prev == static_cast<unsigned>(nch - 1));
-  }
-  __syncthreads();
-  if (last) __threadfence();
-  return last != 0;
+__device__ __forceinline__ double* part_of(const SmpArgs& A, int buf, int sh, int ch) {
+  const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
+  return A.part + ((buf * SH + sh) * A.g.nchunk + ch) * 3;
 }
 
-// Fixed-order block reduction of component c over the head's nch partials.
-__device__ double sum_partials(const SmpArgs& A, int sh, int nch, int c, double* dl) {
+// Fixed-order sums of components c of the head's nch partials in buffer buf
+// (every workgroup of the head gets the same value).
+__device__ double sum_part(const SmpArgs& A, int buf, int sh, int nch, int c, double* dl) {
   double v = 0.0;
-  for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v += A.part[(static_cast<size_t>(sh) * A.g.nchunk + i) * 4 + c];
+  for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v += part_of(A, buf, sh, i)[c];
   return block_sum_d(v, dl);
+}
+__device__ double max_part(const SmpArgs& A, int buf, int sh, int nch, int c, double* dl) {
+  double v = -INFINITY;
+  for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v = fmax(v, part_of(A, buf, sh, i)[c]);
+  return block_max_d(v, dl);
 }
 
 // Whether (sequence s, chunk ch) takes part in the sampling search.
@@ -430,16 +434,16 @@ __device__ __forceinline__ bool smp_active(const SmpArgs& A, int s, int ch, int*
   return B > 0 && B < n && ch * SEL_CHUNK < n;
 }
 
-// Pass A: log pi~ and its maximum.
+// Pass A: log pi~ = log(max(s, 2^-126)) / tau and its per-chunk maximum.
 __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
-  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   __shared__ double dl[4];
   double mx = -INFINITY;
+#pragma unroll 4
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
@@ -449,18 +453,10 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
     }
   }
   mx = block_max_d(mx, dl);
-  if (publish(A, sh, ch, nch, mx, 0.0, 0.0)) {
-    double v = -INFINITY;
-    for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v = fmax(v, A.part[(static_cast<size_t>(sh) * A.g.nchunk + i) * 4]);
-    v = block_max_d(v, dl);
-    if (threadIdx.x == 0) {
-      A.state[sh * kSelStateSlots + kStMax] = v;
-      A.arrive[sh] = 0;
-    }
-  }
+  if (threadIdx.x == 0) part_of(A, 0, sh, ch)[0] = mx;
 }
 
-// Pass B: normaliser sum_j exp(log pi~_j - max); initialises the search.
+// Pass B: per-chunk sum of exp(log pi~ - max).
 __global__ __launch_bounds__(SEL_THREADS) void smp_norm(SmpArgs A) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
@@ -468,40 +464,36 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_norm(SmpArgs A) {
   const int sh = s * A.g.Hkv + h;
   const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
-  const double mx = A.state[sh * kSelStateSlots + kStMax];
   __shared__ double dl[4];
+  const double mx = max_part(A, 0, sh, nch, 0, dl);
   double z = 0.0;
+#pragma unroll 4
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) z += exp(A.lp[row + j] - mx);
   }
   z = block_sum_d(z, dl);
-  if (publish(A, sh, ch, nch, z, 0.0, 0.0)) {
-    const double t = sum_partials(A, sh, nch, 0, dl);
-    if (threadIdx.x == 0) {
-      double* st = A.state + sh * kSelStateSlots;
-      st[kStLse] = mx + log(t);
-      // E(m) <= m, so the root lies at or above m = B
-      st[kStU] = log(static_cast<double>(B));
-      st[kStLo] = log(static_cast<double>(B));
-      st[kStHi] = log(kAlphaMax);
-      st[kStDone] = 0.0;
-      st[kStM] = 0.0;
-      st[kStStatus] = KVE_OK;
-      A.arrive[sh] = 0;
-    }
-  }
+  if (threadIdx.x == 0) part_of(A, 1, sh, ch)[0] = z;
 }
 
 // Pass C: log1p(-pi_j) and the Gumbel keys kappa_j = log pi~_j - log(-log u_j),
 // u_j = ((x >> 11) + 0.5) 2^-53 with x the Philox word 0 of counter (j, h, s, 0).
+// Chunk 0 initialises the search: E(m) <= m, so the root lies at or above B.
 __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
+  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
-  const double lse = A.state[sh * kSelStateSlots + kStLse];
+  __shared__ double dl[4];
+  const double mx = max_part(A, 0, sh, nch, 0, dl);
+  const double lse = mx + log(sum_part(A, 1, sh, nch, 0, dl));
+  if (ch == 0 && threadIdx.x == 0) {
+    const double u0 = log(static_cast<double>(B));
+    A.state[sh] = Search{u0, u0, log(kAlphaMax), 0.0};
+  }
+#pragma unroll 2
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
@@ -509,29 +501,64 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
       A.L[row + j] = log1p(-exp(x - lse));
       const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h),
                                           static_cast<uint64_t>(s), 0ull, A.seed, 0ull);
-      const double u = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
-      A.lp[row + j] = x - log(-log(u));
+      const double uu = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
+      A.lp[row + j] = x - log(-log(uu));
     }
   }
 }
 
-// One step of the expected-samples search: E(m) and dE/dm at m = e^u (the
-// first step also E(10^12), to detect a target out of reach).  The head's
-// last workgroup then takes a safeguarded Newton step in log m -- Newton on
-// E(e^u) - B, bisection of the bracket [lo, hi] when the step leaves it --
-// or marks the search converged once |E - B| <= 0.5.
-__global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int first) {
+// The search state after step `step`: step 0 starts from the state smp_keys
+// wrote; later steps apply the update of the previous step's partials (every
+// workgroup computes the same update, in the same order).  The update is a
+// safeguarded Newton step in log m on E(e^u) - B (bisection of the bracket
+// when the step leaves it), or stop once |E - B| <= 0.5, or -- on step 1,
+// from E(10^12) -- stop with the target out of reach.
+__device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int B, double* dl) {
+  const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
+  Search st = A.state[(step & 1) * SH + sh];
+  if (step == 0 || st.done != 0.0) return st;
+  const int pb = (step - 1) & 1;
+  const double E = sum_part(A, pb, sh, nch, 0, dl);
+  const double dE = sum_part(A, pb, sh, nch, 1, dl);
+  const double target = static_cast<double>(B);
+  if (step == 1) {
+    const double Eh = sum_part(A, pb, sh, nch, 2, dl);
+    if (Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
+      st.done = 2.0;
+      return st;
+    }
+  }
+  const double g = E - target;
+  if (fabs(g) <= 0.5) {
+    st.done = 1.0;
+    return st;
+  }
+  if (g < 0.0) st.lo = st.u; else st.hi = st.u;
+  const double dg = exp(st.u) * dE;   // dE / dlog m
+  double un = (dg > 0.0) ? st.u - g / dg : 0.5 * (st.lo + st.hi);
+  if (!(un > st.lo && un < st.hi)) un = 0.5 * (st.lo + st.hi);
+  st.u = un;
+  return st;
+}
+
+// One step of the expected-samples search: brings the state up to date,
+// then (if still searching) writes the chunk's E(m), dE/dm at m = e^u, and
+// on the first step also E(10^12).
+__global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
-  double* st = A.state + sh * kSelStateSlots;
-  if (st[kStDone] != 0.0) return;   // the same for all of the head's workgroups
   const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
-  const size_t row = static_cast<size_t>(h) * A.g.T + base;
-  const double m = exp(st[kStU]);
+  const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[4];
+  const Search st = search_state(A, step, sh, nch, B, dl);
+  if (ch == 0 && threadIdx.x == 0) A.state[((step + 1) & 1) * SH + sh] = st;
+  if (st.done != 0.0) return;
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  const double m = exp(st.u);
   double e = 0.0, de = 0.0, eh = 0.0;
+#pragma unroll 4
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
@@ -539,106 +566,100 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int first) 
       const double x = expm1(m * l);
       e -= x;
       de -= l * (x + 1.0);
-      if (first) eh -= expm1(kAlphaMax * l);
+      if (step == 0) eh -= expm1(kAlphaMax * l);
     }
   }
   e = block_sum_d(e, dl);
   de = block_sum_d(de, dl);
-  if (first) eh = block_sum_d(eh, dl);
-  if (publish(A, sh, ch, nch, e, de, eh)) {
-    const double E = sum_partials(A, sh, nch, 0, dl);
-    const double dE = sum_partials(A, sh, nch, 1, dl);
-    const double Eh = first ? sum_partials(A, sh, nch, 2, dl) : 0.0;
-    if (threadIdx.x == 0) {
-      const double target = static_cast<double>(B);
-      const double g = E - target;
-      if (first && Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
-        st[kStDone] = 2.0;
-        st[kStM] = kAlphaMax;
-        st[kStStatus] = KVE_ENOCONV;
-      } else if (fabs(g) <= 0.5) {
-        st[kStDone] = 1.0;
-      } else {
-        double u = st[kStU], lo = st[kStLo], hi = st[kStHi];
-        if (g < 0.0) lo = u; else hi = u;
-        const double dg = m * dE;   // dE / dlog m
-        double un = (dg > 0.0) ? u - g / dg : 0.5 * (lo + hi);
-        if (!(un > lo && un < hi)) un = 0.5 * (lo + hi);
-        st[kStU] = un;
-        st[kStLo] = lo;
-        st[kStHi] = hi;
-      }
-      A.arrive[sh] = 0;
-    }
+  if (step == 0) eh = block_sum_d(eh, dl);
+  if (threadIdx.x == 0) {
+    double* p = part_of(A, step & 1, sh, ch);
+    p[0] = e;
+    p[1] = de;
+    p[2] = eh;
   }
 }
 
-// Integer m: with E(e^u) within 0.5 of B and E rising by at most 1 per unit
-// step, floor(e^u) or floor(e^u) + 1 lies in the band; the head's last
-// workgroup keeps the first that does and writes m and the status.
-__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, double* m_out, int32_t* status_out) {
+// Brings the state up to date after the last step, then writes the chunk's
+// E at m0 = floor(e^u) and m0 + 1 (one of them lies in the band when the
+// search converged: E rises by at most 1 per unit step).
+__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int sh = s * A.g.Hkv + h;
   int n, B, base;
-  if (!smp_active(A, s, ch, &n, &B, &base)) {
-    if (ch == 0 && threadIdx.x == 0 && (B <= 0 || B >= n)) {   // nothing searched
-      if (m_out) m_out[sh] = 0.0;
-      if (status_out) status_out[sh] = KVE_OK;
-    }
-    return;
-  }
-  double* st = A.state + sh * kSelStateSlots;
-  if (st[kStDone] == 2.0) {   // out of reach: m = 10^12 already set
-    if (ch == 0 && threadIdx.x == 0) {
-      if (m_out) m_out[sh] = st[kStM];
-      if (status_out) status_out[sh] = static_cast<int32_t>(st[kStStatus]);
-    }
-    return;
-  }
+  if (!smp_active(A, s, ch, &n, &B, &base)) return;
+  const int sh = s * A.g.Hkv + h;
   const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
-  const double m0 = fmin(floor(exp(st[kStU])), kAlphaMax - 1.0);
-  const double m1 = m0 + 1.0;
-  const size_t row = static_cast<size_t>(h) * A.g.T + base;
+  const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[4];
+  const Search st = search_state(A, steps, sh, nch, B, dl);
+  if (ch == 0 && threadIdx.x == 0) A.state[((steps + 1) & 1) * SH + sh] = st;
+  if (st.done == 2.0) return;
+  const double m0 = fmin(floor(exp(st.u)), kAlphaMax - 1.0);
+  const size_t row = static_cast<size_t>(h) * A.g.T + base;
   double e0 = 0.0, e1 = 0.0;
+#pragma unroll 4
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
       const double l = A.L[row + j];
       e0 -= expm1(m0 * l);
-      e1 -= expm1(m1 * l);
+      e1 -= expm1((m0 + 1.0) * l);
     }
   }
   e0 = block_sum_d(e0, dl);
   e1 = block_sum_d(e1, dl);
-  if (publish(A, sh, ch, nch, e0, e1, 0.0)) {
-    const double E0 = sum_partials(A, sh, nch, 0, dl);
-    const double E1 = sum_partials(A, sh, nch, 1, dl);
-    if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) {
+    double* p = part_of(A, steps & 1, sh, ch);
+    p[0] = e0;
+    p[1] = e1;
+    p[2] = 0.0;
+  }
+}
+
+// Final m and status per (sequence, head): the first of m0, m0 + 1 in the
+// band; 10^12 and KVE_ENOCONV if the target is out of reach; the closer one
+// and KVE_ENOCONV if the search ran out of steps.  One workgroup per head.
+__global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, double* m_out, int32_t* status_out) {
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int sh = s * A.g.Hkv + h;
+  int n, B, base;
+  const bool active = smp_active(A, s, 0, &n, &B, &base);
+  double m = 0.0;
+  int status = KVE_OK;
+  if (active) {
+    const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
+    const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+    __shared__ double dl[4];
+    const Search st = A.state[((steps + 1) & 1) * SH + sh];
+    if (st.done == 2.0) {
+      m = kAlphaMax;
+      status = KVE_ENOCONV;
+    } else {
       const double target = static_cast<double>(B);
-      double m = m0;
-      int status = KVE_OK;
+      const double m0 = fmin(floor(exp(st.u)), kAlphaMax - 1.0);
+      const double E0 = sum_part(A, steps & 1, sh, nch, 0, dl);
+      const double E1 = sum_part(A, steps & 1, sh, nch, 1, dl);
       if (fabs(E0 - target) <= 0.5) {
         m = m0;
       } else if (fabs(E1 - target) <= 0.5) {
-        m = m1;
-      } else {   // the search used up its steps without converging
-        m = (fabs(E1 - target) < fabs(E0 - target)) ? m1 : m0;
+        m = m0 + 1.0;
+      } else {
+        m = (fabs(E1 - target) < fabs(E0 - target)) ? m0 + 1.0 : m0;
         status = KVE_ENOCONV;
       }
-      st[kStM] = m;
-      st[kStStatus] = status;
-      if (m_out) m_out[sh] = m;
-      if (status_out) status_out[sh] = status;
-      A.arrive[sh] = 0;
     }
+  }
+  if (threadIdx.x == 0) {
+    A.mvals[sh] = m;
+    if (m_out) m_out[sh] = m;
+    if (status_out) status_out[sh] = status;
   }
 }
 
 // ----------------------------------------------------------------- launch
 template <class Src, class Bias>
 static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,
-                         uint64_t* thr, int* need, int32_t* idx, float* bias, hipStream_t st) {
+                         RState* rs, int32_t* idx, float* bias, hipStream_t st) {
   typedef typename Src::K K;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
   hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
@@ -649,14 +670,15 @@ static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bi
     hipLaunchKernelGGL((sel_hist<Src, 4>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     hipLaunchKernelGGL((sel_hist<Src, 5>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
   }
-  hipLaunchKernelGGL((sel_count<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, cnt, thr, need);
-  hipLaunchKernelGGL((sel_write<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, cnt, thr, need, idx,
-                     bias);
+  hipLaunchKernelGGL((sel_count<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, cnt, rs);
+  hipLaunchKernelGGL((sel_write<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, cnt, rs, idx, bias);
 }
 
-// Top-k: m = 0 and status OK for every (sequence, head).
-__global__ __launch_bounds__(256) void topk_meta(double* m_out, int32_t* status_out, int SH) {
+// Clears the histograms and, in top-k mode, writes m = 0 and status OK.
+__global__ __launch_bounds__(256) void sel_init(int* __restrict__ p, int n, double* m_out, int32_t* status_out,
+                                                int SH) {
   const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
   if (i < SH) {
     if (m_out) m_out[i] = 0.0;
     if (status_out) status_out[i] = KVE_OK;
@@ -669,8 +691,8 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   char* wsb = static_cast<char*>(ws);
   int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
   int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
-  uint64_t* thr = reinterpret_cast<uint64_t*>(wsb + G.off_thr);
-  int* need = reinterpret_cast<int*>(wsb + G.off_need);
+  RState* rs = reinterpret_cast<RState*>(wsb + G.off_rstate);
+  static_assert(sizeof(RState) == kSelRStateBytes, "host and device state size disagree");
   const int SH = G.S * G.Hkv;
   SelArgs a;
   a.seq_off = seq_off;
@@ -681,14 +703,15 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   a.nchunk = G.nchunk;
   a.totalB = G.total_B;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
-  // histograms (and, in sampling mode, everything up to the arrival
-  // counters, which must start at zero) are cleared by a kernel
+  // histograms start at zero; cleared by a kernel, so that a captured graph
+  // holds no memset node
   const int nzero = static_cast<int>((G.zero_end - G.off_hist) / sizeof(int));
+  const bool topk = G.mode == KVE_TOPK;
   stage_begin(ST_SELECT, st);
-  hipLaunchKernelGGL(sel_zero, dim3((nzero + 255) / 256), dim3(256), 0, st, hist, nzero);
-  if (G.mode == KVE_TOPK) {
-    hipLaunchKernelGGL(topk_meta, dim3((SH + 255) / 256), dim3(256), 0, st, m_out, status_out, SH);
-    launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, thr, need, idx, bias, st);
+  hipLaunchKernelGGL(sel_init, dim3((max(nzero, SH) + 255) / 256), dim3(256), 0, st, hist, nzero,
+                     topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
+  if (topk) {
+    launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st);
   } else {
     SmpArgs A;
     A.g = a;
@@ -696,18 +719,20 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.lp = reinterpret_cast<double*>(wsb + G.off_a);
     A.L = reinterpret_cast<double*>(wsb + G.off_b);
     A.part = reinterpret_cast<double*>(wsb + G.off_part);
-    A.state = reinterpret_cast<double*>(wsb + G.off_state);
-    A.arrive = reinterpret_cast<unsigned*>(wsb + G.off_arrive);
+    A.state = reinterpret_cast<Search*>(wsb + G.off_state);
+    A.mvals = reinterpret_cast<double*>(wsb + G.off_mvals);
     A.inv_tau = 1.0 / static_cast<double>(tau);
     A.seed = seed;
     hipLaunchKernelGGL(smp_logp, grid, dim3(SEL_THREADS), 0, st, A);
     hipLaunchKernelGGL(smp_norm, grid, dim3(SEL_THREADS), 0, st, A);
     hipLaunchKernelGGL(smp_keys, grid, dim3(SEL_THREADS), 0, st, A);
     for (int it = 0; it < kSelSearchSteps; ++it)
-      hipLaunchKernelGGL(smp_search, grid, dim3(SEL_THREADS), 0, st, A, it == 0 ? 1 : 0);
-    hipLaunchKernelGGL(smp_finish, grid, dim3(SEL_THREADS), 0, st, A, m_out, status_out);
-    const SnisBias bias_of{A.L, A.state, 1.0 / static_cast<double>(tau_w)};
-    launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, thr, need, idx, bias, st);
+      hipLaunchKernelGGL(smp_search, grid, dim3(SEL_THREADS), 0, st, A, it);
+    hipLaunchKernelGGL(smp_finish, grid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps);
+    hipLaunchKernelGGL(smp_decide, dim3(G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
+                       status_out);
+    const SnisBias bias_of{A.L, A.mvals, 1.0 / static_cast<double>(tau_w)};
+    launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st);
   }
   stage_end(ST_SELECT, st);
   return hipGetLastError();
