@@ -53,6 +53,8 @@ def _parse():
     ap.add_argument("--cpu-heads", type=int, default=4, help="KV heads the oracle baseline scores")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph instead of eager launches")
+    ap.add_argument("--no-decode", action="store_true", help="skip the SNIS decode measurement")
+    ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (5 times) and exit")
     return ap.parse_args()
@@ -142,6 +144,90 @@ def _cpu_baseline(wl, data, heads):
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} of {wl.Hkv} KV heads (all {wl.T} tokens, {wl.g * wl.w} window rows), "
                       f"{dt:.1f} s, scaled by {wl.Hkv / heads:g}"}
+
+
+def _decode_leg(steps_max, want_cpu):
+    """SNIS decode over a compacted cache of the Mistral-7B-shaped ragged
+    batch: every step appends one token per (sequence, KV head) with bias 0
+    and runs kvevict_decode_snis for all 32 q-heads of the 8 sequences."""
+    import numpy as np
+    import torch
+    from long_context_attention_kvevict_amd import kvevict as K
+    from long_context_attention_kvevict_amd import synth, workloads
+
+    wl = workloads.mistral7b_ragged()
+    steps = min(wl.decode_steps, steps_max)
+    dev = torch.device("cuda:0")
+    cache = synth.generate_cache(wl)
+    dec = synth.generate_decode(wl, steps)
+    b = K.Batch(wl.lens, wl.Hq, wl.Hkv, wl.d, wl.w, wl.dtype, device=dev)
+    caps, budgets = wl.caps(), wl.budgets()
+    cap = b.offsets(caps, dev)
+    k0, v0 = K.to_device(cache["k"], wl.dtype, dev), K.to_device(cache["v"], wl.dtype, dev)
+    b0 = torch.from_numpy(cache["bias"]).to(dev)
+    qd = K.to_device(dec["q"], wl.dtype, dev)
+    kd = K.to_device(dec["k"], wl.dtype, dev).transpose(1, 2).contiguous()   # [t][Hkv][S][d]
+    vd = K.to_device(dec["v"], wl.dtype, dev).transpose(1, 2).contiguous()
+    coff = torch.from_numpy(wl.cap_off()[:-1].astype(np.int64)).to(dev)
+    max_len = int(caps.max())
+    out = torch.empty((wl.S, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+
+    def run():
+        k_c, v_c, b_c = k0.clone(), v0.clone(), b0.clone()
+        cache_len = torch.from_numpy(budgets.copy()).to(dev)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for t in range(steps):
+            rows = coff + cache_len
+            k_c.index_copy_(1, rows, kd[t])
+            v_c.index_copy_(1, rows, vd[t])
+            b_c.index_fill_(1, rows, 0.0)
+            cache_len += 1
+            b.decode(qd[t], k_c, v_c, b_c, caps, cache_len, max_len, wl.sm_scale, out=out, cap_offsets=cap)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    run()                                    # warmup
+    ms = run()
+    K.timing_enable(True)
+    run()
+    stages = K.timing_summary()
+    K.timing_enable(False)
+    esize = 2 if wl.dtype == "bf16" else 4
+    # entries read per step, averaged over the steps: sum_s (B_s + t + 1)
+    entries = float(budgets.sum()) * wl.Hkv + wl.S * wl.Hkv * (steps + 1) / 2.0
+    kv_bytes = entries * (2 * wl.d * esize + 4) + wl.S * wl.Hq * wl.d * esize
+    split_ms, merge_ms = stages["decode_split"][0], stages["decode_merge"][0]
+    achieved = kv_bytes / (split_ms * 1e-3) / 1e9
+    res = {
+        "workload": wl.name, "S": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
+        "cache_len": [int(x) for x in budgets], "steps": steps,
+        "cache": "synthetic compacted cache of the batch's capacities (N(0,1) rows, sample-mode biases)",
+        "ms_per_step": ms, "tokens_per_s": wl.S / (ms * 1e-3),
+        "kernel_ms": {"decode_split": split_ms, "decode_merge": merge_ms},
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": kv_bytes, "launch_ms": split_ms},
+    }
+    if want_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        kc = synth.to_f64(cache["k"], wl.dtype)
+        vc = synth.to_f64(cache["v"], wl.dtype)
+        bc = cache["bias"].astype(np.float64)
+        lens = budgets.astype(np.int64)
+        q0 = synth.to_f64(dec["q"][0], wl.dtype)
+        t1 = time.perf_counter()
+        reps = 3
+        for _ in range(reps):
+            oracle.decode_attention(q0, kc, vc, bc, wl.cap_off().astype(np.int64), lens, wl.Hq, wl.sm_scale)
+        dt = (time.perf_counter() - t1) / reps
+        res["cpu_baseline"] = {"value": wl.S / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"{reps} decode steps over the step-0 cache "
+                               f"(widening {t1 - t0:.1f} s not counted)"}
+    return res
 
 
 def main():
@@ -251,9 +337,20 @@ def main():
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stage_ms": {s: round(v[0], 5) for s, v in stages.items()},
     }
+    rows = {}
+    for st, v in stages.items():
+        if st in sbytes:
+            gbs = sbytes[st] / (v[0] * 1e-3) / 1e9
+            rows[st] = {"ms": round(v[0], 5), "algorithmic_bytes": sbytes[st], "GB/s": round(gbs, 1),
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    result["rows"] = rows
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = _cpu_baseline(wl, data, max(1, min(args.cpu_heads, wl.Hkv)))
+    del data
+    if not args.no_decode:
+        print("# decode leg", file=sys.stderr, flush=True)
+        result["decode"] = _decode_leg(args.decode_steps, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
 
 

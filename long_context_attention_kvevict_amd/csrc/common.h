@@ -41,6 +41,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lane layout (wave64):
+//   A: lane l holds A[m = l%16][k = 8*(l/16) .. +8]
+//   B: lane l holds B[k = 8*(l/16) .. +8][n = l%16]
+//   C: lane l, register r holds C[m = 4*(l/16) + r][n = l%16]
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Value held by lane (l ^ 32).

@@ -14,6 +14,8 @@
 #include "launch.h"
 #include "timing.h"
 
+#include <type_traits>
+
 namespace kve {
 
 template <typename T>
@@ -139,25 +141,256 @@ __global__ __launch_bounds__(256) void decode_split(const T* __restrict__ q, con
   }
 }
 
+// bf16 caches: both contractions on the matrix cores.  Workgroup = 256
+// consecutive entries of one (sequence, KV head), 4 waves of two 32-entry
+// blocks each.  Per block a wave forms the logits S = K . Q^T with
+// 16x16x32 MFMAs (entries as M, the group's q-heads as N, padded to 16),
+// updates an online softmax per q-head and accumulates O += P . V with P
+// split into bf16 hi + lo parts (so the weights keep ~16 mantissa bits) and
+// V read back transposed from LDS.  K and bias go straight to registers;
+// all loads of the wave's two blocks are issued before any compute.
+//
+// Lane roles (l = lane, ln = l % 16, lq = l / 16):
+//   K operand   entry 16*mb + ln of the block, 16-byte chunk 4*j + lq
+//   Q operand   q-head ln of the group (zero past g), same chunk
+//   logits      entries 16*mb + 4*lq + r (r < 4) of q-head ln
+//   P operand   the same 8 values, k-slot 8*lq + i <-> entry 4*lq + i (i < 4)
+//               or 16 + 4*lq + i - 4 (i >= 4)
+//   V operand   two transposing LDS reads: entries 4*lq..+3 and
+//               16 + 4*lq..+3 at feature 16*dt + ln
+//   O           q-head 4*lq + r, feature 16*dt + ln
+constexpr int kDecBlk = 32;
+constexpr int kDecWaveBlocks = 2;
+static_assert(4 * kDecWaveBlocks * kDecBlk == kDecodeChunkBf16, "decode chunk geometry");
+
+template <int DD>
+__device__ __forceinline__ int dec_swz(int row) {
+  return (row & (DD / 16 - 1)) << 1;   // keeps 16-byte chunk pairs together
+}
+
+template <int DD>
+__global__ __launch_bounds__(256, 2) void decode_split_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_c, const uint16_t* __restrict__ v_c,
+    const float* __restrict__ bias_c, const int32_t* __restrict__ cap_off,
+    const int32_t* __restrict__ cache_len, int Hq, int Hkv, int64_t totalC, int splits, float c2,
+    float* __restrict__ part_ml, float* __restrict__ part_o) {
+  constexpr int KS = DD / 32;             // k-steps of S = K . Q^T
+  constexpr int DT = DD / 16;             // 16-feature tiles of O
+  constexpr int ROWB = DD * 2;            // bytes per cache row
+  constexpr int CPR = DD / 8;             // 16-byte chunks per row
+  constexpr int VPL = kDecBlk * CPR / 64; // 16-byte V pieces per lane per block
+  constexpr int WAVE_LDS = kDecBlk * ROWB;
+  __shared__ __align__(16) char lds[4 * WAVE_LDS + 512];
+
+  const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int g = Hq / Hkv;
+  // never read past this sequence's capacity, whatever cache_len holds
+  const int len = min(cache_len[s], cap_off[s + 1] - cap_off[s]);
+  const int e0 = sp * kDecodeChunkBf16;
+  if (e0 >= len) return;                  // uniform over the workgroup
+  const int e1 = min(e0 + kDecodeChunkBf16, len);
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, ln = l & 15, lq = l >> 4;
+  const size_t rowbase = static_cast<size_t>(h) * totalC + cap_off[s];
+  const char* kbase = reinterpret_cast<const char*>(k_c + rowbase * DD);
+  const char* vbase = reinterpret_cast<const char*>(v_c + rowbase * DD);
+  const float* bbase = bias_c + rowbase;
+  const int we0 = e0 + wave * kDecWaveBlocks * kDecBlk;
+  const int last = e1 - 1;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (we0 < e1) {                         // uniform over the wave
+    bf16x8 qop[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (ln < g)
+        z = *reinterpret_cast<const u32x4*>(q + (static_cast<size_t>(s) * Hq + h * g + ln) * DD + (4 * j + lq) * 8);
+      qop[j] = as_bf16x8(z);
+    }
+    u32x4 kr[kDecWaveBlocks][2][KS], vr[kDecWaveBlocks][VPL];
+    float bi[kDecWaveBlocks][2][4];
+#pragma unroll
+    for (int b = 0; b < kDecWaveBlocks; ++b) {
+      const int eb = we0 + b * kDecBlk;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int er = min(eb + 16 * mb + ln, last);
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          kr[b][mb][j] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(er) * ROWB + (4 * j + lq) * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bi[b][mb][r] = bbase[min(eb + 16 * mb + 4 * lq + r, last)];
+      }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int pc = i * 64 + l, ent = pc / CPR, ch = pc % CPR;
+        const int er = min(eb + ent, last);
+        vr[b][i] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(er) * ROWB + ch * 16);
+      }
+    }
+    // keep every load of both blocks ahead of the compute
+    __builtin_amdgcn_sched_barrier(0);
+    char* vl = lds + wave * WAVE_LDS;
+#pragma unroll
+    for (int b = 0; b < kDecWaveBlocks; ++b) {
+      const int eb = we0 + b * kDecBlk;
+      f32x4 sacc[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) sacc[mb] = mfma16(as_bf16x8(kr[b][mb][j]), qop[j], sacc[mb]);
+      }
+      // this block's V into the wave's LDS rows (the previous block's
+      // transposing reads were issued earlier by this wave, LDS keeps order)
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int pc = i * 64 + l, ent = pc / CPR, ch = pc % CPR;
+        *reinterpret_cast<u32x4*>(vl + ent * ROWB + ((ch ^ dec_swz<DD>(ent)) << 4)) = vr[b][i];
+      }
+      float x[2][4];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float xv = fmaf(sacc[mb][r], c2, bi[b][mb][r] * kLog2e);
+          x[mb][r] = (eb + 16 * mb + 4 * lq + r < e1) ? xv : -INFINITY;
+          mloc = fmaxf(mloc, x[mb][r]);
+        }
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      // Raise the reference only when the block max exceeds it by 2^8, so
+      // weights stay below 256 and O is rarely rescaled.
+      if (__ballot(mloc > m_run + 8.f)) {
+        const float mn = fmaxf(m_run, mloc);
+        const float a = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= a;
+        m_run = mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(a, 4 * lq + r, 64);   // lane 4*lq + r holds q-head 4*lq + r
+#pragma unroll
+          for (int t = 0; t < DT; ++t) oacc[t][r] *= ar;
+        }
+      }
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+      bf16x8 phi, plo;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pf = __builtin_amdgcn_exp2f(x[mb][r] - mu);
+          l_run += pf;
+          const __bf16 hb = static_cast<__bf16>(pf);
+          phi[4 * mb + r] = hb;
+          plo[4 * mb + r] = static_cast<__bf16>(pf - static_cast<float>(hb));
+        }
+      }
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int chp = 2 * t + ((ln >> 1) & 1);
+        const int r0 = 4 * lq + (ln >> 2), r1 = 16 + 4 * lq + (ln >> 2);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vl + r0 * ROWB + ((chp ^ dec_swz<DD>(r0)) << 4) + 8 * (ln & 1)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vl + r1 * ROWB + ((chp ^ dec_swz<DD>(r1)) << 4) + 8 * (ln & 1)));
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[t] = mfma16(phi, vop, oacc[t]);
+        oacc[t] = mfma16(plo, vop, oacc[t]);
+      }
+    }
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  // merge the 4 waves through LDS
+  __syncthreads();
+  float* sm = reinterpret_cast<float*>(lds);          // [4][16]
+  float* sl = sm + 64;                                // [4][16]
+  float* so = sl + 64;                                // [4][g][DD]
+  if (lq == 0 && ln < g) {
+    sm[wave * 16 + ln] = m_run;
+    sl[wave * 16 + ln] = l_run;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * lq + r;
+    if (row < g) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) so[(wave * g + row) * DD + 16 * t + ln] = oacc[t][r];
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < g * DD; t += 256) {
+    const int i = t / DD, dcol = t % DD;
+    float M = -INFINITY;
+    for (int u = 0; u < 4; ++u) M = fmaxf(M, sm[u * 16 + i]);
+    float L = 0.f, O = 0.f;
+    for (int u = 0; u < 4; ++u) {
+      const float f = (sm[u * 16 + i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[u * 16 + i] - M);
+      L += sl[u * 16 + i] * f;
+      O += so[(u * g + i) * DD + dcol] * f;
+    }
+    const size_t row = (static_cast<size_t>(s) * Hq + h * g + i) * splits + sp;
+    part_o[row * DD + dcol] = O;
+    if (dcol == 0) {
+      part_ml[row * 2] = M;
+      part_ml[row * 2 + 1] = L;
+    }
+  }
+}
+
+// Merge of the split partials of one (sequence, q-head) row.  Each thread
+// owns one feature; the partial outputs of up to PR splits per round are
+// loaded together with the split maxima and sums (staged in LDS), so a
+// round costs one memory round trip.
 template <int DD>
 __global__ __launch_bounds__(DD) void decode_merge(const float* __restrict__ part_ml, const float* __restrict__ part_o,
                                                    const int32_t* __restrict__ cache_len,
                                                    const int32_t* __restrict__ cap_off, int Hq, int splits,
                                                    int split_len, float* __restrict__ out) {
+  constexpr int PR = 32;             // splits per round
+  __shared__ float sml[PR][2];
   const int r = blockIdx.x;          // s * Hq + qh
   const int s = r / Hq;
   const int d = threadIdx.x;
   const int len = min(cache_len[s], cap_off[s + 1] - cap_off[s]);
   const int ns = max(0, min(splits, (len + split_len - 1) / split_len));
-  float M = -INFINITY;
-  for (int p = 0; p < ns; ++p) M = fmaxf(M, part_ml[(static_cast<size_t>(r) * splits + p) * 2]);
-  float L = 0.f, O = 0.f;
-  for (int p = 0; p < ns; ++p) {
-    const size_t row = static_cast<size_t>(r) * splits + p;
-    const float mm = part_ml[row * 2];
-    const float f = (mm == -INFINITY) ? 0.f : exp2f(mm - M);
-    L += part_ml[row * 2 + 1] * f;
-    O += part_o[row * DD + d] * f;
+  const float* ml = part_ml + static_cast<size_t>(r) * splits * 2;
+  const float* po = part_o + static_cast<size_t>(r) * splits * DD;
+  // running merge over rounds (the reference M only grows)
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int p0 = 0; p0 < ns; p0 += PR) {
+    const int cnt = min(PR, ns - p0);
+    if (d < 2 * cnt) sml[d >> 1][d & 1] = ml[2 * p0 + d];
+    float v[PR];
+#pragma unroll
+    for (int u = 0; u < PR; ++u) v[u] = (u < cnt) ? po[static_cast<size_t>(p0 + u) * DD + d] : 0.f;
+    __syncthreads();
+    float Mr = M;
+    for (int u = 0; u < cnt; ++u) Mr = fmaxf(Mr, sml[u][0]);
+    if (Mr != -INFINITY) {
+      const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mr);
+      L *= a;
+      O *= a;
+#pragma unroll
+      for (int u = 0; u < PR; ++u) {
+        if (u < cnt) {
+          const float mm = sml[u][0];
+          const float f = (mm == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm - Mr);
+          L = fmaf(sml[u][1], f, L);
+          O = fmaf(v[u], f, O);
+        }
+      }
+      M = Mr;
+    }
+    __syncthreads();
   }
   out[static_cast<size_t>(r) * DD + d] = (L > 0.f) ? O / L : 0.f;   // empty cache -> 0
 }
@@ -174,6 +407,12 @@ static hipError_t launch_decode_t(const DecodeGeom& G, int64_t totalC, const voi
   const int g = G.Hq / G.Hkv;
   const float c2 = sm_scale * kLog2e;
   stage_begin(ST_DECODE_SPLIT, st);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    (void)g;
+    hipLaunchKernelGGL((decode_split_mfma<DD>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k_c), static_cast<const uint16_t*>(v_c), bias_c, cap_off,
+                       cache_len, G.Hq, G.Hkv, totalC, G.splits, c2, pml, po);
+  } else {
   if (g <= 4)
     hipLaunchKernelGGL((decode_split<T, DD, 4>), grid, dim3(256), 0, st, static_cast<const T*>(q),
                        static_cast<const T*>(k_c), static_cast<const T*>(v_c), bias_c, cap_off, cache_len,
@@ -186,6 +425,7 @@ static hipError_t launch_decode_t(const DecodeGeom& G, int64_t totalC, const voi
     hipLaunchKernelGGL((decode_split<T, DD, 16>), grid, dim3(256), 0, st, static_cast<const T*>(q),
                        static_cast<const T*>(k_c), static_cast<const T*>(v_c), bias_c, cap_off, cache_len,
                        G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po);
+  }
   stage_end(ST_DECODE_SPLIT, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -176,11 +176,17 @@ kve_status plan_decode(const kve_layout* L, const int32_t* cap_off_host, int max
   }
   DecodeGeom g{};
   g.S = L->S; g.Hq = L->Hq; g.Hkv = L->Hkv; g.d = L->d; g.dtype = L->dtype;
-  // split-K over the cache: about 256 workgroups, >= 64 entries each
-  const int64_t heads = static_cast<int64_t>(g.S) * g.Hkv;
-  int64_t splits = std::max<int64_t>(1, (256 + heads - 1) / heads);
-  int64_t len = (max_cache_len + splits - 1) / splits;
-  len = std::max<int64_t>(64, ((len + 63) / 64) * 64);
+  int64_t len;
+  if (g.dtype == KVE_BF16) {
+    // fixed chunks: workgroups scale with the cache, short sequences take few
+    len = kDecodeChunkBf16;
+  } else {
+    // split-K over the cache: about 256 workgroups, >= 64 entries each
+    const int64_t heads = static_cast<int64_t>(g.S) * g.Hkv;
+    const int64_t splits = std::max<int64_t>(1, (256 + heads - 1) / heads);
+    len = (max_cache_len + splits - 1) / splits;
+    len = std::max<int64_t>(64, ((len + 63) / 64) * 64);
+  }
   g.split_len = static_cast<int>(len);
   g.splits = static_cast<int>((max_cache_len + len - 1) / len);
   const size_t rows = static_cast<size_t>(g.S) * g.Hq * g.splits;

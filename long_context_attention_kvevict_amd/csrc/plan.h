@@ -57,6 +57,10 @@ struct SelectGeom {
   size_t bytes;
 };
 
+// Cache entries per decode workgroup for bf16 caches: 4 waves, each two
+// blocks of 32 entries.
+constexpr int kDecodeChunkBf16 = 256;
+
 struct DecodeGeom {
   int S, Hq, Hkv, d, dtype, splits, split_len;
   size_t off_ml, off_o;

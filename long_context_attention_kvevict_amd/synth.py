@@ -190,6 +190,34 @@ def generate_decode(wl: Workload, steps: int | None = None) -> dict:
     return {"q": _store(q, wl.dtype), "k": _store(k, wl.dtype), "v": _store(v, wl.dtype)}
 
 
+def generate_cache(wl: Workload) -> dict:
+    """A compacted cache of the workload's shape, for decode-only runs.
+
+    Sequence s owns rows [cap_off[s], cap_off[s+1]) of every KV head; the
+    first B_s rows hold N(0, 1) keys and values, the rest (decode headroom)
+    are zero.  Biases of the kept rows are -log(q)/tau_w with q log-uniform
+    on [1e-3, 1] in sample mode (the range inclusion probabilities of a
+    10 % budget span), 0 in top-k mode.  Decode cost depends only on these
+    shapes, not on which tokens a selection kept.
+    """
+    rng = np.random.Generator(np.random.PCG64(wl.data_seed + 104729))
+    Hkv, d = wl.Hkv, wl.d
+    budgets, coff = wl.budgets(), wl.cap_off()
+    C = int(coff[-1])
+    k = np.zeros((Hkv, C, d), dtype=np.float32)
+    v = np.zeros((Hkv, C, d), dtype=np.float32)
+    bias = np.zeros((Hkv, C), dtype=np.float32)
+    for s, B in enumerate(budgets):
+        a = int(coff[s])
+        k[:, a:a + B] = rng.standard_normal((Hkv, B, d), dtype=np.float32)
+        v[:, a:a + B] = rng.standard_normal((Hkv, B, d), dtype=np.float32)
+        if wl.mode == "sample":
+            q = np.exp(rng.uniform(np.log(1e-3), 0.0, size=(Hkv, B)))
+            bias[:, a:a + B] = (-np.log(q) / wl.tau_w).astype(np.float32)
+    return {"k": _store(k, wl.dtype), "v": _store(v, wl.dtype), "bias": bias,
+            "cache_len": budgets.copy(), "cap_off": coff}
+
+
 def random_scores(Hkv: int, lens, seed: int, ties: bool = True) -> np.ndarray:
     """Positive fp32 score arrays [Hkv][T] with a heavy tail and (optionally)
     runs of exactly equal values, like max-pooled eviction scores."""

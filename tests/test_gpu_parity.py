@@ -272,3 +272,33 @@ def test_decode_full_budget_is_exact_attention():
             p = torch.softmax(kf[h] @ qf[qh] / np.sqrt(d), 0)
             ref = p @ vf[h]
             assert (out[s, qh] - ref).abs().max().item() < 1e-3
+
+
+@pytest.mark.parametrize("g,d", [(1, 128), (4, 64), (7, 128), (16, 128)])
+def test_decode_shapes_and_ragged_caches(g, d):
+    # caches of 0, 1, 31, 33, 257 and 700 entries inside larger capacities,
+    # nonzero biases; every q-head group width the ABI accepts up to 16
+    rng = np.random.default_rng(100 + g * d)
+    lens = [0, 1, 31, 33, 257, 700]
+    caps = [x + 40 for x in lens]
+    S, Hkv = len(lens), 2
+    Hq = g * Hkv
+    C = sum(caps)
+    kk = synth.f32_to_bf16_bits(rng.standard_normal((Hkv, C, d)).astype(np.float32))
+    vv = synth.f32_to_bf16_bits(rng.standard_normal((Hkv, C, d)).astype(np.float32))
+    qq = synth.f32_to_bf16_bits((2.0 * rng.standard_normal((S, Hq, d))).astype(np.float32))
+    bias = rng.uniform(0.0, 7.0, size=(Hkv, C)).astype(np.float32)
+    b = K.Batch([max(x, 1) for x in lens], Hq, Hkv, d, 8, "bf16")
+    k_c, v_c, q = (K.to_device(x, "bf16") for x in (kk, vv, qq))
+    b_c = torch.from_numpy(bias).cuda()
+    cache_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = b.decode(q, k_c, v_c, b_c, caps, cache_len, max(caps), 1 / np.sqrt(d)).cpu().numpy()
+    coff = np.concatenate([[0], np.cumsum(caps)]).astype(np.int64)
+    # the oracle covers the non-empty caches (sequences 1..S-1)
+    ref = oracle.decode_attention(synth.to_f64(qq[1:], "bf16"), synth.to_f64(kk, "bf16"),
+                                  synth.to_f64(vv, "bf16"), bias.astype(np.float64), coff[1:],
+                                  np.array(lens[1:], dtype=np.int64), Hq, 1 / np.sqrt(d))
+    err = np.abs(out[1:] - ref).max()
+    say(f"[gpu] decode g={g} d={d}: max abs err {err:.2e}")
+    assert np.all(out[0] == 0.0)          # empty cache -> zeros
+    assert err <= 1e-3, err
