@@ -31,11 +31,16 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-ffp-contract=fast", "-munsafe-fp-atomics"]
 
 
+# The bf16 scorer never sees NaN (finite inputs; masking uses -inf): without
+# IEEE mode its max/min reductions need no NaN-quieting instructions.
+PER_FILE = {"score_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *PER_FILE.get(src, []), "-c", path, "-o", obj]
     else:
         cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

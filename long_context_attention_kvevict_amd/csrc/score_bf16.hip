@@ -28,6 +28,8 @@
 #include "launch.h"
 #include "timing.h"
 
+#include <type_traits>
+
 namespace kve {
 
 constexpr int D = 128;          // head dim of the bf16 path
@@ -227,10 +229,16 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(krow, 2 * kk + hl);
   }
-  const int vkey = tid >> 2, vpart = tid & 3;   // 4 lanes per key, chunks vpart + 4i
-  int voff[4];
+  // ||v||^2 of tile keys 16*wave .. +15 as the diagonal of the Gram block
+  // V V^T (16x16x32 MFMA, one operand register serving as A and B): lane l
+  // reads key 16*wave + l%16, chunk 4j + l/16 for k-step j.  The diagonal
+  // element of key l%16 sits in register l%4 of the lanes with
+  // (l%16)/4 == l/16.
+  const int gkey = 16 * wave + (lane & 15);
+  int goffv[D / 32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = tile_off(vkey, vpart + 4 * i);
+  for (int j = 0; j < D / 32; ++j) goffv[j] = tile_off(gkey, 4 * j + (lane >> 4));
+  const bool gdiag = ((lane & 15) >> 2) == (lane >> 4);
   // A operand of O^T += V^T P^T: lane (d = db*32 + l%32, k-slice l/32) holds 8
   // consecutive keys of feature d, from two transposing reads; in each
   // 16-lane group lane j names row key0 + j/4 at features dbase + 4(j%4)..+4
@@ -253,24 +261,21 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 
   if (ntile > 0) fill.issue(kb8, vb8, c0, c1, 0);
 
-  for (int t = 0; t < ntile; ++t) {
-    wait_vm<0>();    // this lane's loads of tile t
-    lds_barrier();   // everyone's loads of tile t; the other stage is free
-    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+  // One tile; EDGE tiles reach past the chunk end or the earliest causal
+  // horizon and mask keys, interior tiles carry no masking code.
+  auto tile = [&](const int t, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int kt0 = c0 + t * KT;
     const char* Kt = ring + (t & 1) * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
     {
-      float q = 0.f;
+      f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(Vt + voff[i]);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(Vt + voff[i + 1]);
-        q += sumsq16(x, y);
+      for (int j = 0; j < D / 32; ++j) {
+        const bf16x8 x = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + goffv[j]));
+        gram = mfma16(x, x, gram);
       }
-      q += __shfl_xor(q, 1, 64);
-      q += __shfl_xor(q, 2, 64);
-      if (vpart == 0) vn[t * KT + vkey] = q;
+      if (gdiag) vn[t * KT + gkey] = gram[lane & 3];
     }
     // S^T = K . Q^T for both 32-key halves (slot order through keymap)
     f32x16 sacc[2];
@@ -283,8 +288,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
         sacc[kb] = mfma32(av, qreg[kk], sacc[kb]);
       }
     }
-    // mask keys past the chunk or the causal horizon (uniform branch)
-    if ((kt0 + KT > c1) || (causal && kt0 + KT - 1 > n - a.w)) {
+    if constexpr (EDGE) {   // keys past the chunk or the causal horizon
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -357,14 +361,25 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          f32x8 rem;
+          f32x8 rem = pf[kb][k2];
+          // keeps the residual arithmetic inside this rarely taken branch
+          asm volatile("" : "+v"(rem));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rem[e] = pf[kb][k2][e] - static_cast<float>(pb[kb][k2][e]);
+          for (int e = 0; e < 8; ++e) rem[e] -= static_cast<float>(pb[kb][k2][e]);
           pr[kb][k2] = __builtin_convertvector(rem, bf16x8);
         }
       }
       pv(pr);
     }
+  };
+
+  const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;   // first key of an edge tile
+  for (int t = 0; t < ntile; ++t) {
+    wait_vm<0>();    // this lane's loads of tile t
+    lds_barrier();   // everyone's loads of tile t; the other stage is free
+    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+    if (c0 + t * KT > edge_from) tile(t, std::true_type{});
+    else tile(t, std::false_type{});
   }
   lds_barrier();   // vn complete
 
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
 // at most about 2^-8 ||o|| / ||o - v|| relative.  With a larger weight (where
 // o can approach v_j and that bound degrades) the block also contracts the
 // residual plane o - o_h, restoring an fp32-accurate distance.
-constexpr float kResidY = 63.f;   // (1 - p) / p below this <=> p > 2^-6
+constexpr float kResidX = -6.f;   // log2 p above this <=> p > 2^-6
 
 __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   const int c = blockIdx.x;
@@ -599,15 +614,13 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
 
   if (ntile > 0) fill.issue(kb8, vb8, c0, c1, 0);
 
-  for (int t = 0; t < ntile; ++t) {
-    wait_vm<0>();
-    lds_barrier();
-    if (t > 0) reduce_tile(t - 1);
-    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+  // One tile; EDGE tiles mask keys past the chunk end or a row's causal
+  // horizon, interior tiles carry no masking code.
+  auto tile = [&](const int t, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int kt0 = c0 + t * KT;
     const char* Kt = ring + (t & 1) * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
-    const bool edge = (kt0 + KT > c1) || (causal && kt0 + KT - 1 > n - a.w);
     f32x16 sacc[2], gacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -633,31 +646,32 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int krow = kb * 32 + col;
-      // y = (1 - p) / p = 2^-x - 1 with x = log2 p; hidden pairs get y = inf
-      float y[16];
+      // x = log2 p; hidden pairs get x = -inf (p = 0)
+      float x[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowc[wave * 32 + 8 * q4 + 4 * hl]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[4 * q4 + e] = fmaf(sacc[kb][4 * q4 + e], a.c2, -lv[e]);
+        for (int e = 0; e < 4; ++e) x[4 * q4 + e] = fmaf(sacc[kb][4 * q4 + e], a.c2, -lv[e]);
       }
-      if (edge) {   // uniform
+      if constexpr (EDGE) {
         const int key = kt0 + krow;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int hz = rowhz[wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
           const bool hidden = (key >= c1) | (causal & (key > hz));
-          y[r] = hidden ? -INFINITY : y[r];
+          x[r] = hidden ? -INFINITY : x[r];
         }
       }
-      float ymin = INFINITY;
+      float xmax = x[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        y[r] = __builtin_amdgcn_exp2f(-y[r]) - 1.f;
-        ymin = fminf(ymin, y[r]);
-      }
-      if (__any(ymin < kResidY)) {   // wave-uniform: add the residual plane of o
+      for (int r = 1; r < 16; ++r) xmax = fmaxf(xmax, x[r]);
+      float sc = 0.f;
+      if (__any(xmax > kResidX)) {
+        // some weight above 2^-6 (uniform): add the residual plane of o and
+        // use the exact weight factor 1 / y^2, y = (1 - p) / p = 2^-x - 1
         const uint16_t* lp = a.olo + (grp * ROWS + wave * 32 + col) * D;
+        asm volatile("" : "+v"(gacc[kb]));   // keeps this work inside the branch
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           const bf16x8 ola = as_bf16x8(*reinterpret_cast<const u32x4*>(lp + 16 * kk + 8 * hl));
@@ -665,18 +679,34 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
           gacc[kb] = mfma32(ola, vv, gacc[kb]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r) {
           gacc[kb][r] += a.no2d[grp * ROWS + wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
-      }
-      float sc = 0.f;
+          const float y = __builtin_amdgcn_exp2f(-x[r]) - 1.f;
+          const float y2 = fmaf(y, y, 9.094947e-13f);                 // + 2^-40 keeps 1/y2 finite
+          sc = fmaf(gacc[kb][r], __builtin_amdgcn_rcpf(y2), sc);       // gacc = ||o - v||^2
+        }
+      } else {
+        // every p <= 2^-6: p / (1 - p) = p + p^2 + p^3 to a relative 2^-18
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float y2 = fmaf(y[r], y[r], 9.094947e-13f);       // + 2^-40 keeps 1/y2 finite
-        sc = fmaf(gacc[kb][r], __builtin_amdgcn_rcpf(y2), sc);  // gacc = ||o - v||^2
+        for (int r = 0; r < 16; ++r) {
+          const float pw = __builtin_amdgcn_exp2f(x[r]);
+          const float q = fmaf(pw, fmaf(pw, pw, pw), pw);
+          sc = fmaf(gacc[kb][r] * q, q, sc);
+        }
       }
       sc += xor32(sc);
       if (hl == 0) red[t & 1][wave][krow] = sc;
     }
+  };
+
+  const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;   // first key of an edge tile
+  for (int t = 0; t < ntile; ++t) {
+    wait_vm<0>();
+    lds_barrier();
+    if (t > 0) reduce_tile(t - 1);
+    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+    if (c0 + t * KT > edge_from) tile(t, std::true_type{});
+    else tile(t, std::false_type{});
   }
   lds_barrier();
   if (ntile > 0) reduce_tile(ntile - 1);
