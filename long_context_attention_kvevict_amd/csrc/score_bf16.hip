@@ -108,6 +108,17 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 template <typename T>
 __device__ __forceinline__ void settle(const T& x) { asm volatile("" :: "v"(x)); }
 
+// v + (the value lane l ^ 32 holds), through the cross-half lane swap
+// (no LDS round trip).
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
     float tmax = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(sacc[0][r], sacc[1][r]));
-    tmax = fmaxf(tmax, xor32(tmax)) * a.c2;
+    tmax = max_xor32(tmax) * a.c2;
     const bool raise = tmax > m_run + 8.f;
     if (__any(raise)) {
       const float m_new = raise ? tmax : m_run;
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   // ||v||^2 of the chunk
   for (int i = tid; i < c1 - c0; i += WG) a.vnorm[static_cast<size_t>(h) * a.T + base + c0 + i] = vn[i];
 
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_xor32(l_run);
   if (!row_ok) return;
   const size_t part = (static_cast<size_t>((s * a.Hkv + h) * a.RG + rg)) * a.P + c;
   const int rl = wave * 32 + col;
@@ -621,9 +632,19 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
     const int kt0 = c0 + t * KT;
     const char* Kt = ring + (t & 1) * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
+    // S = Q K^T and G = ||o_h||^2 + ||v||^2 - 2 O_h V^T for both 32-key
+    // halves; each half's operands are read in one batch so the LDS
+    // latency is paid once per chain rather than once per MFMA
     f32x16 sacc[2], gacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kop[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        kop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * ROWB + koff[kk]));
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) sacc[kb] = mfma32(qa[kk], kop[kk], sacc[kb]);
       const float vn2 = sbuf[t * KT + kb * 32 + col];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -631,47 +652,52 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) gacc[kb][4 * q4 + e] = nv[e] + vn2;
       }
-      sacc[kb] = f32x16{};
+      bf16x8 vop[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kv = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * ROWB + koff[kk]));
-        sacc[kb] = mfma32(qa[kk], kv, sacc[kb]);
-      }
+      for (int kk = 0; kk < D / 16; ++kk)
+        vop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + kb * 32 * ROWB + koff[kk]));
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 vv = as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + kb * 32 * ROWB + koff[kk]));
-        gacc[kb] = mfma32(oha[kk], vv, gacc[kb]);
+      for (int kk = 0; kk < D / 16; ++kk) gacc[kb] = mfma32(oha[kk], vop[kk], gacc[kb]);
+      // issue order: four operand reads ahead of the MFMA that consumes
+      // them, the K chain then the V chain
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 16) - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+    // x = log2 p in place of the logits; hidden pairs get x = -inf (p = 0)
+    float xmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int krow = kb * 32 + col;
-      // x = log2 p; hidden pairs get x = -inf (p = 0)
-      float x[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowc[wave * 32 + 8 * q4 + 4 * hl]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * q4 + e] = fmaf(sacc[kb][4 * q4 + e], a.c2, -lv[e]);
+        for (int e = 0; e < 4; ++e) sacc[kb][4 * q4 + e] = fmaf(sacc[kb][4 * q4 + e], a.c2, -lv[e]);
       }
       if constexpr (EDGE) {
-        const int key = kt0 + krow;
+        const int key = kt0 + kb * 32 + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int hz = rowhz[wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
           const bool hidden = (key >= c1) | (causal & (key > hz));
-          x[r] = hidden ? -INFINITY : x[r];
+          sacc[kb][r] = hidden ? -INFINITY : sacc[kb][r];
         }
       }
-      float xmax = x[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) xmax = fmaxf(xmax, x[r]);
-      float sc = 0.f;
-      if (__any(xmax > kResidX)) {
-        // some weight above 2^-6 (uniform): add the residual plane of o and
-        // use the exact weight factor 1 / y^2, y = (1 - p) / p = 2^-x - 1
-        const uint16_t* lp = a.olo + (grp * ROWS + wave * 32 + col) * D;
-        asm volatile("" : "+v"(gacc[kb]));   // keeps this work inside the branch
+      for (int r = 0; r < 16; ++r) xmax = fmaxf(xmax, sacc[kb][r]);
+    }
+    float sc[2] = {0.f, 0.f};
+    if (__any(xmax > kResidX)) {
+      // some weight above 2^-6 (uniform): add the residual plane of o and
+      // use the exact weight factor 1 / y^2, y = (1 - p) / p = 2^-x - 1
+      const uint16_t* lp = a.olo + (grp * ROWS + wave * 32 + col) * D;
+      asm volatile("" : "+v"(gacc[0]), "+v"(gacc[1]));   // keeps this work inside the branch
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           const bf16x8 ola = as_bf16x8(*reinterpret_cast<const u32x4*>(lp + 16 * kk + 8 * hl));
@@ -681,21 +707,27 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           gacc[kb][r] += a.no2d[grp * ROWS + wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
-          const float y = __builtin_amdgcn_exp2f(-x[r]) - 1.f;
-          const float y2 = fmaf(y, y, 9.094947e-13f);                 // + 2^-40 keeps 1/y2 finite
-          sc = fmaf(gacc[kb][r], __builtin_amdgcn_rcpf(y2), sc);       // gacc = ||o - v||^2
-        }
-      } else {
-        // every p <= 2^-6: p / (1 - p) = p + p^2 + p^3 to a relative 2^-18
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pw = __builtin_amdgcn_exp2f(x[r]);
-          const float q = fmaf(pw, fmaf(pw, pw, pw), pw);
-          sc = fmaf(gacc[kb][r] * q, q, sc);
+          const float y = __builtin_amdgcn_exp2f(-sacc[kb][r]) - 1.f;
+          const float y2 = fmaf(y, y, 9.094947e-13f);                    // + 2^-40 keeps 1/y2 finite
+          sc[kb] = fmaf(gacc[kb][r], __builtin_amdgcn_rcpf(y2), sc[kb]);  // gacc = ||o - v||^2
         }
       }
-      sc += xor32(sc);
-      if (hl == 0) red[t & 1][wave][krow] = sc;
+    } else {
+      // every p <= 2^-6: p / (1 - p) = p + p^2 + p^3 to a relative 2^-18
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pw = __builtin_amdgcn_exp2f(sacc[kb][r]);
+          const float q = fmaf(pw, fmaf(pw, pw, pw), pw);
+          sc[kb] = fmaf(gacc[kb][r] * q, q, sc[kb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float tot = sum_xor32(sc[kb]);
+      if (hl == 0) red[t & 1][wave][kb * 32 + col] = tot;
     }
   };
 
