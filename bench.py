@@ -38,6 +38,7 @@ STAGE_KERNEL = {
     "score_merge": ("score_merge", "score_bf16.hip"),
     "select": ("sel_", "select.hip"),
     "compact": ("compact_rows", "compact.hip"),
+    "decode_split": ("decode_split_mfma", "decode.hip"),
 }
 
 HBM_PEAK_GBS = 8000.0
@@ -208,7 +209,7 @@ def _decode_leg(steps_max, want_cpu):
         "ms_per_step": ms, "tokens_per_s": wl.S / (ms * 1e-3),
         "kernel_ms": {"decode_split": split_ms, "decode_merge": merge_ms},
         "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic("decode_split", wl.name),
                      "algorithmic_bytes": kv_bytes, "launch_ms": split_ms},
     }
     if want_cpu:
