@@ -185,12 +185,13 @@ kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k
  * recorded on the launch stream around every kernel the four calls enqueue.
  * Stage ids: 0 score pass 1, 1 score merge, 2 score pass 2, 3 score pool,
  * 4 select, 5 compact, 6 decode split, 7 decode merge.
- * kvevict_timing_enable(1) creates an event pool on first use (no device
- * memory) and clears previous records; 0 stops recording.
+ * kvevict_timing_enable(mask) times the stages whose bit is set in mask
+ * (bit i = stage i; 0xff = all), creates an event pool on first use (no
+ * device memory) and clears previous records; 0 stops recording.
  * kvevict_timing_summary() waits for the recorded events, writes the mean
  * duration in ms and the number of launches per stage (n_stages entries),
  * and clears the records.  Process-wide, not thread-safe. */
-int32_t kvevict_timing_enable(int32_t on);
+int32_t kvevict_timing_enable(int32_t stage_mask);
 int32_t kvevict_timing_summary(double* avg_ms, int32_t* counts, int32_t n_stages);
 
 /* Message describing the last failed call on this thread ("" if none). */

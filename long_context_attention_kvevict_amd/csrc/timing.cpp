@@ -16,7 +16,7 @@ struct Rec {
 };
 
 struct Timing {
-  bool on = false;
+  uint32_t mask = 0;   // stages being timed
   std::vector<hipEvent_t> pool;   // reusable events
   size_t next = 0;
   std::vector<Rec> recs;
@@ -34,14 +34,14 @@ hipEvent_t take_event() {
 }  // namespace
 
 void stage_begin(int stage, hipStream_t st) {
-  if (!g.on) return;
+  if (!((g.mask >> stage) & 1u)) return;
   hipEvent_t e = take_event();
   if (e && hipEventRecord(e, st) == hipSuccess) g.open[stage] = e;
   else g.open[stage] = nullptr;
 }
 
 void stage_end(int stage, hipStream_t st) {
-  if (!g.on) return;
+  if (!((g.mask >> stage) & 1u)) return;
   hipEvent_t b = g.open[stage];
   hipEvent_t e = take_event();
   if (!b || !e) return;
@@ -53,9 +53,9 @@ void stage_end(int stage, hipStream_t st) {
 
 extern "C" {
 
-int32_t kvevict_timing_enable(int32_t on) {
+int32_t kvevict_timing_enable(int32_t stage_mask) {
   using namespace kve;
-  if (on && g.pool.empty()) {
+  if (stage_mask && g.pool.empty()) {
     g.pool.reserve(kPool);
     for (size_t i = 0; i < kPool; ++i) {
       hipEvent_t e;
@@ -63,7 +63,7 @@ int32_t kvevict_timing_enable(int32_t on) {
       g.pool.push_back(e);
     }
   }
-  g.on = on != 0;
+  g.mask = static_cast<uint32_t>(stage_mask) & ((1u << ST_COUNT) - 1u);
   g.next = 0;
   g.recs.clear();
   return KVE_OK;

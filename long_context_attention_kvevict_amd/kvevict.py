@@ -83,8 +83,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     return lib
 
 
-def timing_enable(on: bool = True):
-    _check(load_library().kvevict_timing_enable(int(bool(on))))
+def timing_enable(on=True):
+    """on: True (every stage), False (off), or a list of stage names."""
+    if on is True:
+        mask = (1 << len(STAGES)) - 1
+    elif not on:
+        mask = 0
+    else:
+        mask = sum(1 << STAGES.index(name) for name in on)
+    _check(load_library().kvevict_timing_enable(mask))
 
 
 def timing_summary() -> dict:
