@@ -31,14 +31,16 @@ struct ScoreGeom {
 
 // Keys per workgroup of the multi-workgroup selection, histogram width
 // (2048 bins = 11-bit digits), digit levels for fp32 scores and fp64 Gumbel
-// keys, per-head state slots and the step budget of the expected-samples
-// search (a safeguarded Newton iteration in log m that converges in well
-// under ten steps on the score distributions tried).
+// keys, per-head state slots, the points of the coarse expected-samples
+// grid that brackets the search, and the step budget of the search that
+// follows (a safeguarded Newton iteration in log m; started from the grid
+// it needs at most 3 evaluations on the score distributions tried).
 constexpr int kSelChunk = 4096;
 constexpr int kSelBins = 2048;
 constexpr int kSelLevels32 = 3;
 constexpr int kSelLevels64 = 6;
-constexpr int kSelSearchSteps = 12;
+constexpr int kSelGrid = 32;
+constexpr int kSelSearchSteps = 5;
 constexpr int kSelRStateBytes = 16;   // per-head radix threshold and count of equal keys kept
 constexpr int kSelSearchBytes = 32;   // per-head search state
 
@@ -52,6 +54,7 @@ struct SelectGeom {
   size_t off_cnt;                  // int [S*Hkv][nchunk][2]
   size_t off_rstate;               // [S*Hkv] radix threshold state (kSelRStateBytes each)
   size_t off_part;                 // sampling: double [2][S*Hkv][nchunk][3]
+  size_t off_grid;                 // sampling: float [S*Hkv][nchunk][kSelGrid]
   size_t off_state;                // sampling: [2][S*Hkv] search state (kSelSearchBytes each)
   size_t off_mvals;                // sampling: double [S*Hkv] final m
   size_t bytes;

@@ -84,6 +84,24 @@ struct ScoreArgs {
   float* sraw;             // [RG][Hkv][T]
 };
 
+// Work item of a workgroup of either pass.  The RG row groups of one
+// (sequence, KV head, key chunk) read the same K/V tiles, so their
+// workgroups get consecutive dispatch slots on one XCD (workgroups are dealt
+// to the 8 XCDs round-robin by linear id): tiles that one of them brings into
+// that XCD's L2 serve the others.  Grid: 8 * ceil(S*Hkv*P / 8) * RG.
+struct ScoreWork {
+  int s, h, rg, c;
+};
+__device__ __forceinline__ bool score_work(const ScoreArgs& a, int lin, ScoreWork* w) {
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int item = (slot / a.RG) * 8 + xcd;   // (s, h, c), chunk fastest
+  w->rg = slot % a.RG;
+  w->c = item % a.P;
+  w->h = (item / a.P) % a.Hkv;
+  w->s = item / (a.P * a.Hkv);
+  return w->s < a.S;
+}
+
 // ------------------------------------------------------------ LDS pipeline
 // Workgroup barrier that orders LDS traffic only: global->LDS loads stay in
 // flight across it (a full __syncthreads would drain them).
@@ -176,10 +194,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- pass 1
 __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
-  const int c = blockIdx.x;
-  const int h = blockIdx.y / a.RG;
-  const int rg = blockIdx.y % a.RG;
-  const int s = blockIdx.z;
+  ScoreWork wk;
+  if (!score_work(a, blockIdx.x, &wk)) return;
+  const int c = wk.c, h = wk.h, rg = wk.rg, s = wk.s;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
   const int c0 = c * a.CH;
@@ -547,10 +564,9 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
 constexpr float kResidX = -6.f;   // log2 p above this <=> p > 2^-6
 
 __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
-  const int c = blockIdx.x;
-  const int h = blockIdx.y / a.RG;
-  const int rg = blockIdx.y % a.RG;
-  const int s = blockIdx.z;
+  ScoreWork wk;
+  if (!score_work(a, blockIdx.x, &wk)) return;
+  const int c = wk.c, h = wk.h, rg = wk.rg, s = wk.s;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
   const int c0 = c * a.CH;
@@ -770,7 +786,8 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   a.olo = reinterpret_cast<uint16_t*>(base + G.off_olo);
   a.sraw = reinterpret_cast<float*>(base + G.off_sraw);
 
-  dim3 grid(G.P, G.Hkv * G.RG, G.S);
+  const int items = G.S * G.Hkv * G.P;
+  dim3 grid(8 * ((items + 7) / 8) * G.RG);
   stage_begin(ST_SCORE_P1, st);
   hipLaunchKernelGGL(score_p1_bf16, grid, dim3(WG), 0, st, a);
   stage_end(ST_SCORE_P1, st);

@@ -399,6 +399,7 @@ struct SmpArgs {
   double* lp;         // [Hkv][T]: log pi~, then the Gumbel keys
   double* L;          // [Hkv][T]: log1p(-pi)
   double* part;       // [2][S*Hkv][nchunk][3] per-chunk partials (ping-pong)
+  float* grid;        // [S*Hkv][nchunk][kSelGrid] per-chunk E(m) on the start grid
   Search* state;      // [2][S*Hkv] search state (ping-pong)
   double* mvals;      // [S*Hkv] final m
   double inv_tau;
@@ -434,7 +435,8 @@ __device__ __forceinline__ bool smp_active(const SmpArgs& A, int s, int ch, int*
   return B > 0 && B < n && ch * SEL_CHUNK < n;
 }
 
-// Pass A: log pi~ = log(max(s, 2^-126)) / tau and its per-chunk maximum.
+// Pass A: log pi~ = log(max(s, 2^-126)) / tau, its per-chunk maximum and
+// the chunk's sum of exp(log pi~ - maximum) (the normaliser in parts).
 __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
@@ -442,43 +444,41 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
   const int sh = s * A.g.Hkv + h;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   __shared__ double dl[4];
+  double x[SEL_PER];
   double mx = -INFINITY;
-#pragma unroll 4
+#pragma unroll
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+    x[i] = -INFINITY;
     if (j < n) {
-      const double x = log(static_cast<double>(fmaxf(A.scores[row + j], 1.17549435e-38f))) * A.inv_tau;
-      A.lp[row + j] = x;
-      mx = fmax(mx, x);
+      x[i] = log(static_cast<double>(fmaxf(A.scores[row + j], 1.17549435e-38f))) * A.inv_tau;
+      A.lp[row + j] = x[i];
+      mx = fmax(mx, x[i]);
     }
   }
   mx = block_max_d(mx, dl);
-  if (threadIdx.x == 0) part_of(A, 0, sh, ch)[0] = mx;
-}
-
-// Pass B: per-chunk sum of exp(log pi~ - max).
-__global__ __launch_bounds__(SEL_THREADS) void smp_norm(SmpArgs A) {
-  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  int n, B, base;
-  if (!smp_active(A, s, ch, &n, &B, &base)) return;
-  const int sh = s * A.g.Hkv + h;
-  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
-  const size_t row = static_cast<size_t>(h) * A.g.T + base;
-  __shared__ double dl[4];
-  const double mx = max_part(A, 0, sh, nch, 0, dl);
   double z = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < SEL_PER; ++i) {
-    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
-    if (j < n) z += exp(A.lp[row + j] - mx);
-  }
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) z += exp(x[i] - mx);   // exp(-inf) = 0 past the end
   z = block_sum_d(z, dl);
-  if (threadIdx.x == 0) part_of(A, 1, sh, ch)[0] = z;
+  if (threadIdx.x == 0) {
+    double* p = part_of(A, 0, sh, ch);
+    p[0] = mx;
+    p[1] = z;
+  }
 }
 
-// Pass C: log1p(-pi_j) and the Gumbel keys kappa_j = log pi~_j - log(-log u_j),
+// Grid of the expected-samples start: u_k = log B + k (log 10^12 - log B) /
+// (kSelGrid - 1), k = 0 .. kSelGrid - 1, in log m.
+__device__ __forceinline__ double grid_u(int k, int B) {
+  const double lo = log(static_cast<double>(B));
+  return lo + k * ((log(kAlphaMax) - lo) / (kSelGrid - 1));
+}
+
+// Pass B: log1p(-pi_j) and the Gumbel keys kappa_j = log pi~_j - log(-log u_j),
 // u_j = ((x >> 11) + 0.5) 2^-53 with x the Philox word 0 of counter (j, h, s, 0).
-// Chunk 0 initialises the search: E(m) <= m, so the root lies at or above B.
+// Also the chunk's E(m) = sum 1 - (1 - pi_j)^m on the start grid, in fp32
+// (it only brackets the search; every value the search accepts is fp64).
 __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
@@ -487,23 +487,45 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   __shared__ double dl[4];
-  const double mx = max_part(A, 0, sh, nch, 0, dl);
-  const double lse = mx + log(sum_part(A, 1, sh, nch, 0, dl));
-  if (ch == 0 && threadIdx.x == 0) {
-    const double u0 = log(static_cast<double>(B));
-    A.state[sh] = Search{u0, u0, log(kAlphaMax), 0.0};
+  __shared__ float eg[kSelGrid][SEL_THREADS + 1];
+  // log-sum-exp of the whole row from the chunk parts, in chunk order
+  const double M = max_part(A, 0, sh, nch, 0, dl);
+  double zp = 0.0;
+  for (int i = threadIdx.x; i < nch; i += SEL_THREADS) {
+    const double* p = part_of(A, 0, sh, i);
+    zp += p[1] * exp(p[0] - M);
   }
+  const double lse = M + log(block_sum_d(zp, dl));
+  float mk[kSelGrid];
+#pragma unroll
+  for (int k = 0; k < kSelGrid; ++k) mk[k] = static_cast<float>(exp(grid_u(k, B)) * 1.4426950408889634);
+  float e[kSelGrid];
+#pragma unroll
+  for (int k = 0; k < kSelGrid; ++k) e[k] = 0.f;
 #pragma unroll 2
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
       const double x = A.lp[row + j];
-      A.L[row + j] = log1p(-exp(x - lse));
+      const double l = log1p(-exp(x - lse));
+      A.L[row + j] = l;
       const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h),
                                           static_cast<uint64_t>(s), 0ull, A.seed, 0ull);
       const double uu = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
       A.lp[row + j] = x - log(-log(uu));
+      const float lf = static_cast<float>(l);
+#pragma unroll
+      for (int k = 0; k < kSelGrid; ++k) e[k] += 1.f - exp2f(mk[k] * lf);
     }
+  }
+  // per grid point, the chunk sum in a fixed order (column of threads)
+#pragma unroll
+  for (int k = 0; k < kSelGrid; ++k) eg[k][threadIdx.x] = e[k];
+  __syncthreads();
+  if (threadIdx.x < kSelGrid) {
+    float t = 0.f;
+    for (int i = 0; i < SEL_THREADS; ++i) t += eg[threadIdx.x][i];
+    A.grid[(static_cast<size_t>(sh) * A.g.nchunk + ch) * kSelGrid + threadIdx.x] = t;
   }
 }
 
@@ -515,8 +537,37 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
 // from E(10^12) -- stop with the target out of reach.
 __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int B, double* dl) {
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
+  if (step == 0) {
+    // start from the grid: the first point whose E reaches B, and a bracket
+    // one grid cell wider on each side than the crossing (the grid sums are
+    // fp32); log B is a true lower bound since E(m) <= m
+    const double target = static_cast<double>(B);
+    int kx = kSelGrid;   // first grid point with E >= B
+    double Ek = 0.0, Ep = 0.0;
+    for (int k = 0; k < kSelGrid; ++k) {
+      double v = 0.0;
+      for (int i = threadIdx.x; i < nch; i += SEL_THREADS)
+        v += static_cast<double>(A.grid[(static_cast<size_t>(sh) * A.g.nchunk + i) * kSelGrid + k]);
+      v = block_sum_d(v, dl);
+      if (v >= target) { kx = k; Ek = v; break; }
+      Ep = v;
+    }
+    Search st;
+    st.done = 0.0;
+    if (kx == 0) {
+      st.u = grid_u(0, B);
+    } else if (kx == kSelGrid) {
+      st.u = log(kAlphaMax);
+    } else {
+      const double u0 = grid_u(kx - 1, B), u1 = grid_u(kx, B);
+      st.u = (Ek > Ep) ? u0 + (target - Ep) / (Ek - Ep) * (u1 - u0) : u1;
+    }
+    st.lo = grid_u(max(kx - 2, 0), B);
+    st.hi = (kx + 1 < kSelGrid) ? grid_u(kx + 1, B) : log(kAlphaMax);
+    return st;
+  }
   Search st = A.state[(step & 1) * SH + sh];
-  if (step == 0 || st.done != 0.0) return st;
+  if (st.done != 0.0) return st;
   const int pb = (step - 1) & 1;
   const double E = sum_part(A, pb, sh, nch, 0, dl);
   const double dE = sum_part(A, pb, sh, nch, 1, dl);
@@ -719,12 +770,12 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.lp = reinterpret_cast<double*>(wsb + G.off_a);
     A.L = reinterpret_cast<double*>(wsb + G.off_b);
     A.part = reinterpret_cast<double*>(wsb + G.off_part);
+    A.grid = reinterpret_cast<float*>(wsb + G.off_grid);
     A.state = reinterpret_cast<Search*>(wsb + G.off_state);
     A.mvals = reinterpret_cast<double*>(wsb + G.off_mvals);
     A.inv_tau = 1.0 / static_cast<double>(tau);
     A.seed = seed;
     hipLaunchKernelGGL(smp_logp, grid, dim3(SEL_THREADS), 0, st, A);
-    hipLaunchKernelGGL(smp_norm, grid, dim3(SEL_THREADS), 0, st, A);
     hipLaunchKernelGGL(smp_keys, grid, dim3(SEL_THREADS), 0, st, A);
     for (int it = 0; it < kSelSearchSteps; ++it)
       hipLaunchKernelGGL(smp_search, grid, dim3(SEL_THREADS), 0, st, A, it);
