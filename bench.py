@@ -142,9 +142,27 @@ def _cpu_baseline(wl, data, heads):
             _ = k[a:b][idx], v[a:b][idx]
     dt = time.perf_counter() - t0
     tokens_per_s = wl.T / (dt * wl.Hkv / heads)
+    # the same work on one head with the BLAS pool limited to one thread
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        k = synth.to_f64(data["k"][0], wl.dtype)
+        v = synth.to_f64(data["v"][0], wl.dtype)
+        for s in range(wl.S):
+            a, b = off[s], off[s + 1]
+            sc = max_pool_fast(oracle.group_scores(q[s], k[a:b], v[a:b], 0, wl.g, wl.sm_scale, True),
+                               wl.pool_kernel).astype(np.float32)
+            if wl.mode == "topk":
+                idx = oracle.topk_select(sc, budgets[s])
+            else:
+                idx, _, _, _ = oracle.sample_select(sc, budgets[s], wl.tau, wl.tau_w, wl.hash_seed, s, 0)
+            _ = k[a:b][idx], v[a:b][idx]
+        dt1 = time.perf_counter() - t1
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} of {wl.Hkv} KV heads (all {wl.T} tokens, {wl.g * wl.w} window rows), "
-                      f"{dt:.1f} s, scaled by {wl.Hkv / heads:g}"}
+                      f"{dt:.1f} s, scaled by {wl.Hkv / heads:g}",
+            "value_1thread": wl.T / (dt1 * wl.Hkv),
+            "sample_1thread": f"1 of {wl.Hkv} KV heads, BLAS limited to 1 thread, {dt1:.1f} s, scaled by {wl.Hkv}"}
 
 
 def _decode_leg(steps_max, want_cpu):
@@ -356,15 +374,52 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dominant, wl.name),
                      "algorithmic_bytes": sbytes[dominant], "launch_ms": dom_ms},
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stage_ms": {s: round(v[0], 5) for s, v in stages.items()},
+        "stage_ms": {name: round(rec[0], 5) for name, rec in stages.items()},
     }
     rows = {}
-    for st, v in stages.items():
+    for st, rec in stages.items():
         if st in sbytes:
-            gbs = sbytes[st] / (v[0] * 1e-3) / 1e9
-            rows[st] = {"ms": round(v[0], 5), "algorithmic_bytes": sbytes[st], "GB/s": round(gbs, 1),
+            gbs = sbytes[st] / (rec[0] * 1e-3) / 1e9
+            rows[st] = {"ms": round(rec[0], 5), "algorithmic_bytes": sbytes[st], "GB/s": round(gbs, 1),
                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     result["rows"] = rows
+    # Per-step times with the L2 / Infinity Cache flushed before every step
+    # (a 512 MiB device write between steps), median over K steps.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flushed = []
+    for i in range(args.steps):
+        scratch.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        flushed.append(e0.elapsed_time(e1))
+    result["ms_per_step_flushed_median"] = float(np.median(flushed))
+    # device copy bandwidth on this GPU (1 GiB read + 1 GiB written)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del scratch, src, dst
+    result["copy_GBs"] = copy_gbs
+    result["step_frac_of_copy"] = step_bytes / (ms * 1e-3) / 1e9 / copy_gbs
+    # needles planted by the generator that the selection kept (context only)
+    if data.get("needle_pos"):
+        idx_h = sel[0].cpu().numpy()
+        boff = wl.bud_off()
+        kept = tot = 0
+        for (s_, h_), pos in data["needle_pos"].items():
+            chosen = set(idx_h[h_, boff[s_]:boff[s_ + 1]].tolist())
+            kept += sum(int(p_) in chosen for p_ in pos)
+            tot += len(pos)
+        result["needle_recall"] = kept / max(tot, 1)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = _cpu_baseline(wl, data, max(1, min(args.cpu_heads, wl.Hkv)))
