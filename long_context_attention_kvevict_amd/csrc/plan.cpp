@@ -118,6 +118,7 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.S = L->S; g.Hkv = L->Hkv; g.T = static_cast<int>(T); g.max_len = max_len; g.mode = mode;
   g.total_B = bud_off_host[L->S];
   g.nchunk = (max_len + kSelChunk - 1) / kSelChunk;
+  g.nsmp = (max_len + kSmpChunk - 1) / kSmpChunk;
   const bool smp = mode == KVE_SAMPLE;
   const size_t SH = static_cast<size_t>(g.S) * g.Hkv;
   const size_t plane = smp ? static_cast<size_t>(g.Hkv) * g.T * sizeof(double) : 0;
@@ -129,8 +130,8 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.zero_end = off;
   g.off_cnt = off; off = align256(off + SH * g.nchunk * 2 * sizeof(int32_t));
   g.off_rstate = off; off = align256(off + SH * kSelRStateBytes);
-  g.off_part = off; off = align256(off + (smp ? 2 * SH * g.nchunk * 3 * sizeof(double) : 0));
-  g.off_grid = off; off = align256(off + (smp ? SH * g.nchunk * kSelGrid * sizeof(float) : 0));
+  g.off_part = off; off = align256(off + (smp ? 2 * SH * g.nsmp * 3 * sizeof(double) : 0));
+  g.off_grid = off; off = align256(off + (smp ? SH * g.nsmp * kSelGrid * sizeof(float) : 0));
   g.off_state = off; off = align256(off + (smp ? 2 * SH * kSelSearchBytes : 0));
   g.off_mvals = off; off = align256(off + (smp ? SH * sizeof(double) : 0));
   g.bytes = off;

@@ -36,6 +36,7 @@ struct ScoreGeom {
 // follows (a safeguarded Newton iteration in log m; started from the grid
 // it needs at most 3 evaluations on the score distributions tried).
 constexpr int kSelChunk = 4096;
+constexpr int kSmpChunk = 1024;       // keys per workgroup of the sampling passes
 constexpr int kSelBins = 2048;
 constexpr int kSelLevels32 = 3;
 constexpr int kSelLevels64 = 6;
@@ -47,6 +48,7 @@ constexpr int kSelSearchBytes = 32;   // per-head search state
 struct SelectGeom {
   int S, Hkv, T, max_len, mode;
   int nchunk;                      // chunks of kSelChunk keys per (sequence, head)
+  int nsmp;                        // chunks of kSmpChunk keys (sampling passes)
   int64_t total_B;
   size_t off_a, off_b;             // sampling: fp64 planes [Hkv][T]
   size_t off_hist;                 // int [levels][S*Hkv][kSelBins]

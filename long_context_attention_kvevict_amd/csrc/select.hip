@@ -362,6 +362,12 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
 }
 
 // ----------------------------------------------------------------- sampling
+// The sampling passes are arithmetic-heavy (fp64 transcendentals, Philox, the
+// fp32 grid) and use smaller chunks than the radix passes, so that a head's
+// keys spread over four times as many workgroups.
+constexpr int SMP_PER = 4;
+constexpr int SMP_CHUNK = SEL_THREADS * SMP_PER;
+static_assert(SMP_CHUNK == kSmpChunk, "host and device sampling chunk disagree");
 __device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
   *lo = a * b;
   *hi = __umul64hi(a, b);
@@ -398,8 +404,9 @@ struct SmpArgs {
   const float* scores;
   double* lp;         // [Hkv][T]: log pi~, then the Gumbel keys
   double* L;          // [Hkv][T]: log1p(-pi)
-  double* part;       // [2][S*Hkv][nchunk][3] per-chunk partials (ping-pong)
-  float* grid;        // [S*Hkv][nchunk][kSelGrid] per-chunk E(m) on the start grid
+  int nsmp;           // chunks of SMP_CHUNK keys per (sequence, head)
+  double* part;       // [2][S*Hkv][nsmp][3] per-chunk partials (ping-pong)
+  float* grid;        // [S*Hkv][nsmp][kSelGrid] per-chunk E(m) on the start grid
   Search* state;      // [2][S*Hkv] search state (ping-pong)
   double* mvals;      // [S*Hkv] final m
   double inv_tau;
@@ -408,7 +415,7 @@ struct SmpArgs {
 
 __device__ __forceinline__ double* part_of(const SmpArgs& A, int buf, int sh, int ch) {
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
-  return A.part + ((buf * SH + sh) * A.g.nchunk + ch) * 3;
+  return A.part + ((buf * SH + sh) * A.nsmp + ch) * 3;
 }
 
 // Fixed-order sums of components c of the head's nch partials in buffer buf
@@ -432,7 +439,7 @@ __device__ __forceinline__ bool smp_active(const SmpArgs& A, int s, int ch, int*
   *n_out = n;
   *B_out = B;
   *base_out = base;
-  return B > 0 && B < n && ch * SEL_CHUNK < n;
+  return B > 0 && B < n && ch * SMP_CHUNK < n;
 }
 
 // Pass A: log pi~ = log(max(s, 2^-126)) / tau, its per-chunk maximum and
@@ -444,11 +451,11 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
   const int sh = s * A.g.Hkv + h;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   __shared__ double dl[4];
-  double x[SEL_PER];
+  double x[SMP_PER];
   double mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) {
-    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     x[i] = -INFINITY;
     if (j < n) {
       x[i] = log(static_cast<double>(fmaxf(A.scores[row + j], 1.17549435e-38f))) * A.inv_tau;
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
   mx = block_max_d(mx, dl);
   double z = 0.0;
 #pragma unroll
-  for (int i = 0; i < SEL_PER; ++i) z += exp(x[i] - mx);   // exp(-inf) = 0 past the end
+  for (int i = 0; i < SMP_PER; ++i) z += exp(x[i] - mx);   // exp(-inf) = 0 past the end
   z = block_sum_d(z, dl);
   if (threadIdx.x == 0) {
     double* p = part_of(A, 0, sh, ch);
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
-  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   __shared__ double dl[4];
   __shared__ float eg[kSelGrid][SEL_THREADS + 1];
@@ -503,8 +510,8 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
 #pragma unroll
   for (int k = 0; k < kSelGrid; ++k) e[k] = 0.f;
 #pragma unroll 2
-  for (int i = 0; i < SEL_PER; ++i) {
-    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
       const double x = A.lp[row + j];
       const double l = log1p(-exp(x - lse));
@@ -525,7 +532,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   if (threadIdx.x < kSelGrid) {
     float t = 0.f;
     for (int i = 0; i < SEL_THREADS; ++i) t += eg[threadIdx.x][i];
-    A.grid[(static_cast<size_t>(sh) * A.g.nchunk + ch) * kSelGrid + threadIdx.x] = t;
+    A.grid[(static_cast<size_t>(sh) * A.nsmp + ch) * kSelGrid + threadIdx.x] = t;
   }
 }
 
@@ -547,7 +554,7 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
     for (int k = 0; k < kSelGrid; ++k) {
       double v = 0.0;
       for (int i = threadIdx.x; i < nch; i += SEL_THREADS)
-        v += static_cast<double>(A.grid[(static_cast<size_t>(sh) * A.g.nchunk + i) * kSelGrid + k]);
+        v += static_cast<double>(A.grid[(static_cast<size_t>(sh) * A.nsmp + i) * kSelGrid + k]);
       v = block_sum_d(v, dl);
       if (v >= target) { kx = k; Ek = v; break; }
       Ep = v;
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
-  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[4];
   const Search st = search_state(A, step, sh, nch, B, dl);
@@ -610,8 +617,8 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
   const double m = exp(st.u);
   double e = 0.0, de = 0.0, eh = 0.0;
 #pragma unroll 4
-  for (int i = 0; i < SEL_PER; ++i) {
-    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
       const double l = A.L[row + j];
       const double x = expm1(m * l);
@@ -639,7 +646,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) 
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
-  const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+  const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[4];
   const Search st = search_state(A, steps, sh, nch, B, dl);
@@ -649,8 +656,8 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) 
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   double e0 = 0.0, e1 = 0.0;
 #pragma unroll 4
-  for (int i = 0; i < SEL_PER; ++i) {
-    const int j = ch * SEL_CHUNK + i * SEL_THREADS + threadIdx.x;
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
       const double l = A.L[row + j];
       e0 -= expm1(m0 * l);
@@ -679,7 +686,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
   int status = KVE_OK;
   if (active) {
     const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
-    const int nch = (n + SEL_CHUNK - 1) / SEL_CHUNK;
+    const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
     __shared__ double dl[4];
     const Search st = A.state[((steps + 1) & 1) * SH + sh];
     if (st.done == 2.0) {
@@ -769,17 +776,19 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.scores = scores;
     A.lp = reinterpret_cast<double*>(wsb + G.off_a);
     A.L = reinterpret_cast<double*>(wsb + G.off_b);
+    A.nsmp = G.nsmp;
     A.part = reinterpret_cast<double*>(wsb + G.off_part);
     A.grid = reinterpret_cast<float*>(wsb + G.off_grid);
     A.state = reinterpret_cast<Search*>(wsb + G.off_state);
     A.mvals = reinterpret_cast<double*>(wsb + G.off_mvals);
     A.inv_tau = 1.0 / static_cast<double>(tau);
     A.seed = seed;
-    hipLaunchKernelGGL(smp_logp, grid, dim3(SEL_THREADS), 0, st, A);
-    hipLaunchKernelGGL(smp_keys, grid, dim3(SEL_THREADS), 0, st, A);
+    const dim3 sgrid(G.nsmp, G.Hkv, G.S);
+    hipLaunchKernelGGL(smp_logp, sgrid, dim3(SEL_THREADS), 0, st, A);
+    hipLaunchKernelGGL(smp_keys, sgrid, dim3(SEL_THREADS), 0, st, A);
     for (int it = 0; it < kSelSearchSteps; ++it)
-      hipLaunchKernelGGL(smp_search, grid, dim3(SEL_THREADS), 0, st, A, it);
-    hipLaunchKernelGGL(smp_finish, grid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps);
+      hipLaunchKernelGGL(smp_search, sgrid, dim3(SEL_THREADS), 0, st, A, it);
+    hipLaunchKernelGGL(smp_finish, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps);
     hipLaunchKernelGGL(smp_decide, dim3(G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
                        status_out);
     const SnisBias bias_of{A.L, A.mvals, 1.0 / static_cast<double>(tau_w)};
