@@ -4,6 +4,7 @@
  * Four calls make up the eviction-time path and the decode step:
  *
  *   kvevict_score        output-aware per-token eviction scores
+ *   kvevict_score_ex     the same, or attention-weight scores, max/avg pool
  *   kvevict_select       per-head budgeted selection (top-k or sampling)
  *   kvevict_compact      gather of the kept K/V rows and their logit bias
  *   kvevict_decode_snis  decode attention over the compacted cache with a
@@ -101,6 +102,37 @@ kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k,
                          const void* v, float sm_scale, int32_t causal,
                          int32_t pool_kernel, float* scores, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* Other scores on the same two passes ([PI] App. D, Eq. 16-20, and App. H):
+ * sum over the group's q-heads and window rows i of c_i * a_ij, times
+ * ||v_j|| for the value-weighted kinds, then pooled:
+ *   KVE_SCORE_H2O     c_i = 1                (H2O column sums, Eq. 16)
+ *   KVE_SCORE_H2O_H   c_i = h_i              (pi_H2O-h)
+ *   KVE_SCORE_TOVA    c_i = [i == w - 1]     (TOVA, Eq. 19)
+ *   KVE_SCORE_MIN     c_i = [i == w - 1], times ||v_j||   (pi_min)
+ *   KVE_SCORE_MIN_H   c_i = h_i, times ||v_j||            (pi_min-h)
+ * with the harmonic prior h_i = 1 / ((w - i) H_w), H_w = sum_{k<=w} 1/k.
+ * KVE_SCORE_PERTURB is the output-aware score of kvevict_score.  The group
+ * sum stands for the layer or group mean of the pages (same ranking and
+ * same normalised proposal).  pool_mode KVE_POOL_AVG takes the mean over
+ * the in-sequence keys of the window instead of the maximum (SnapKV-style
+ * smoothing, App. D).  The attention-weight kinds need the bf16 path
+ * (KVE_ENOTSUP for fp32); both pool modes work for both.  Same workspace,
+ * layouts and determinism as kvevict_score. */
+typedef enum {
+  KVE_SCORE_PERTURB = 0,
+  KVE_SCORE_H2O = 1,
+  KVE_SCORE_H2O_H = 2,
+  KVE_SCORE_TOVA = 3,
+  KVE_SCORE_MIN = 4,
+  KVE_SCORE_MIN_H = 5
+} kve_score_kind;
+typedef enum { KVE_POOL_MAX = 0, KVE_POOL_AVG = 1 } kve_pool_mode;
+kve_status kvevict_score_ex(const kve_layout* L, const void* q_win, const void* k,
+                            const void* v, float sm_scale, int32_t causal,
+                            int32_t pool_kernel, int32_t score_kind,
+                            int32_t pool_mode, float* scores, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------- select
  * Per (sequence, KV head) budgeted selection of B_s = bud_off[s+1] -

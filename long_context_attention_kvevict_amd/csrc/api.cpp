@@ -35,9 +35,9 @@ size_t kvevict_score_workspace(const kve_layout* L) {
   return G.bytes;
 }
 
-kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k, const void* v,
-                         float sm_scale, int32_t causal, int32_t pool_kernel, float* scores, void* ws,
-                         size_t ws_bytes, void* stream) {
+kve_status kvevict_score_ex(const kve_layout* L, const void* q_win, const void* k, const void* v,
+                            float sm_scale, int32_t causal, int32_t pool_kernel, int32_t score_kind,
+                            int32_t pool_mode, float* scores, void* ws, size_t ws_bytes, void* stream) {
   kve::ScoreGeom G;
   std::string msg;
   kve_status st = kve::plan_score(L, &G, &msg);
@@ -46,6 +46,12 @@ kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k, 
   if (!(sm_scale > 0.f) || sm_scale > 1e6f) return set_err(KVE_EINVAL, "kvevict_score: sm_scale must be in (0, 1e6]");
   if (pool_kernel < 1 || pool_kernel > 31 || pool_kernel % 2 == 0)
     return set_err(KVE_EINVAL, "kvevict_score: pool_kernel must be odd and in [1, 31]");
+  if (score_kind < KVE_SCORE_PERTURB || score_kind > KVE_SCORE_MIN_H)
+    return set_err(KVE_EINVAL, "kvevict_score: unknown score kind");
+  if (pool_mode != KVE_POOL_MAX && pool_mode != KVE_POOL_AVG)
+    return set_err(KVE_EINVAL, "kvevict_score: unknown pool mode");
+  if (score_kind != KVE_SCORE_PERTURB && L->dtype != KVE_BF16)
+    return set_err(KVE_ENOTSUP, "kvevict_score: attention-weight score kinds need bf16 inputs");
   if (!ws || ws_bytes < G.bytes)
     return set_err(KVE_EWORKSPACE, "kvevict_score: workspace smaller than kvevict_score_workspace()");
   if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(q_win)) & 15)
@@ -54,12 +60,19 @@ kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k, 
     return set_err(KVE_EINVAL, "kvevict_score: workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = (L->dtype == KVE_BF16)
-                     ? kve::launch_score_bf16(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, ws, s)
+                     ? kve::launch_score_bf16(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, score_kind, ws, s)
                      : kve::launch_score_f32(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, ws, s);
   if (e != hipSuccess) return hip_err(e, "kvevict_score");
-  e = kve::launch_pool(G, L->seq_off, pool_kernel, ws, scores, s);
+  e = kve::launch_pool(G, L->seq_off, pool_kernel, pool_mode, ws, scores, s);
   if (e != hipSuccess) return hip_err(e, "kvevict_score (pool)");
   return KVE_OK;
+}
+
+kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k, const void* v,
+                         float sm_scale, int32_t causal, int32_t pool_kernel, float* scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return kvevict_score_ex(L, q_win, k, v, sm_scale, causal, pool_kernel, KVE_SCORE_PERTURB, KVE_POOL_MAX, scores,
+                          ws, ws_bytes, stream);
 }
 
 size_t kvevict_select_workspace(const kve_layout* L, const int32_t* bud_off_host, int32_t mode) {

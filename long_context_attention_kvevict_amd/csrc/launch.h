@@ -9,14 +9,14 @@
 namespace kve {
 
 hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
-                             const int32_t* seq_off, float sm_scale, int causal, void* ws,
+                             const int32_t* seq_off, float sm_scale, int causal, int score_kind, void* ws,
                              hipStream_t st);
 hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
                             const int32_t* seq_off, float sm_scale, int causal, void* ws,
                             hipStream_t st);
 hipError_t launch_merge_f32(const ScoreGeom& G, const int32_t* seq_off, void* ws, hipStream_t st);
-hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, const void* ws,
-                       float* scores, hipStream_t st);
+hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode,
+                       const void* ws, float* scores, hipStream_t st);
 
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, uint64_t seed, int32_t* idx,

@@ -1,7 +1,8 @@
-// Key-axis max pooling of the raw window scores ("A Probabilistic
+// Key-axis pooling of the raw window scores ("A Probabilistic
 // Interpretation of KV Cache Eviction", App. D, SnapKV: pooling along the
-// key axis).  Width-k window centred on each key, clipped to the sequence.
-// Also sums the per-row-group partial score planes in a fixed order.
+// key axis): maximum or mean over a width-k window centred on each key,
+// clipped to the sequence.  Also sums the per-row-group partial score planes
+// in a fixed order.
 #include "common.h"
 #include "launch.h"
 #include "timing.h"
@@ -14,7 +15,8 @@ namespace kve {
 constexpr int POOL_TILE = 256;
 constexpr int POOL_MAX_RADIUS = 15;
 
-__global__ __launch_bounds__(POOL_TILE) void pool_max(const float* __restrict__ sraw,
+template <bool AVG>
+__global__ __launch_bounds__(POOL_TILE) void pool_window(const float* __restrict__ sraw,
                                                       const int32_t* __restrict__ seq_off, int S, int Hkv, int T,
                                                       int planes, int radius, float* __restrict__ out) {
   __shared__ float v[POOL_TILE + 2 * POOL_MAX_RADIUS];
@@ -38,19 +40,30 @@ __global__ __launch_bounds__(POOL_TILE) void pool_max(const float* __restrict__ 
     if (seq_off[mid] <= t) lo = mid; else hi = mid;
   }
   const int j0 = max(seq_off[lo], t - radius), j1 = min(seq_off[lo + 1] - 1, t + radius);
-  float m = -INFINITY;
-  for (int j = j0; j <= j1; ++j) m = fmaxf(m, v[j - t0 + radius]);
+  float m;
+  if (AVG) {
+    m = 0.f;
+    for (int j = j0; j <= j1; ++j) m += v[j - t0 + radius];
+    m /= static_cast<float>(j1 - j0 + 1);
+  } else {
+    m = -INFINITY;
+    for (int j = j0; j <= j1; ++j) m = fmaxf(m, v[j - t0 + radius]);
+  }
   out[static_cast<size_t>(h) * T + t] = m;
 }
 
-hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, const void* ws,
-                       float* scores, hipStream_t st) {
+hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode,
+                       const void* ws, float* scores, hipStream_t st) {
   const float* sraw = reinterpret_cast<const float*>(static_cast<const char*>(ws) + G.off_sraw);
   if ((pool_kernel - 1) / 2 > POOL_MAX_RADIUS) return hipErrorInvalidValue;
   dim3 grid((G.T + POOL_TILE - 1) / POOL_TILE, G.Hkv);
   stage_begin(ST_SCORE_POOL, st);
-  hipLaunchKernelGGL(pool_max, grid, dim3(POOL_TILE), 0, st, sraw, seq_off, G.S, G.Hkv, G.T, G.pool_rg,
-                     (pool_kernel - 1) / 2, scores);
+  if (pool_mode == KVE_POOL_AVG)
+    hipLaunchKernelGGL((pool_window<true>), grid, dim3(POOL_TILE), 0, st, sraw, seq_off, G.S, G.Hkv, G.T, G.pool_rg,
+                       (pool_kernel - 1) / 2, scores);
+  else
+    hipLaunchKernelGGL((pool_window<false>), grid, dim3(POOL_TILE), 0, st, sraw, seq_off, G.S, G.Hkv, G.T,
+                       G.pool_rg, (pool_kernel - 1) / 2, scores);
   stage_end(ST_SCORE_POOL, st);
   return hipGetLastError();
 }

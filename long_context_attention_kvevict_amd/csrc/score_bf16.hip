@@ -173,6 +173,17 @@ struct RingFill {
       dma16(vb + tbase + off, lds[i] + sb + TILE_BYTES);
     }
   }
+  // K rows only, into stages of TILE_BYTES (the attention-weight scores).
+  __device__ __forceinline__ void issue_k(const char* kb, int kt0, int c1, int stage) const {
+    const size_t tbase = static_cast<size_t>(kt0) * ROWB;
+    const uint32_t sb = static_cast<uint32_t>(stage) * TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      int off = goff[i];
+      if (kt0 + KT > c1 && kt0 + key[i] >= c1) off += (c1 - 1 - kt0 - key[i]) * ROWB;
+      dma16(kb + tbase + off, lds[i] + sb);
+    }
+  }
 };
 
 // Sum of squares of 16 bf16 values (two 16-byte chunks).
@@ -763,10 +774,150 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   for (int i = tid; i < c1 - c0; i += WG) sout[c0 + i] = sbuf[i];
 }
 
+// ------------------------------------------------- pass 2, attention weights
+// The attention-weight scores of the proposals compared on "A Probabilistic
+// Interpretation of KV Cache Eviction" (App. D, Eq. 16 and 19; App. H): per
+// key, the sum over the group's window rows of c_i * p_ij, p_ij = 2^(x -
+// lse2) as in pass 2, times ||v_j|| for the value-weighted kinds.  The row
+// weight c_i is 1 (H2O), the harmonic prior 1 / ((w - i) H_w) of window row
+// i = 0 .. w-1 (H2O-h, min-h) or the last-row indicator (TOVA, min).  Only K
+// streams through the ring; ||v||^2 comes from pass 1.
+__device__ float score_row_weight(int kind, int wi, int w) {
+  if (kind == KVE_SCORE_H2O) return 1.f;
+  if (kind == KVE_SCORE_TOVA || kind == KVE_SCORE_MIN) return (wi == w - 1) ? 1.f : 0.f;
+  double hw = 0.0;   // harmonic number H_w
+  for (int k = 1; k <= w; ++k) hw += 1.0 / k;
+  return static_cast<float>(1.0 / ((w - wi) * hw));
+}
+
+template <bool VNORM>
+__global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
+  ScoreWork wk;
+  if (!score_work(a, blockIdx.x, &wk)) return;
+  const int c = wk.c, h = wk.h, rg = wk.rg, s = wk.s;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int c0 = c * a.CH;
+  if (c0 >= n) return;
+  const int c1 = min(c0 + a.CH, n);
+
+  __shared__ __align__(1024) char ring[NSTAGE * TILE_BYTES];
+  __shared__ __align__(16) float sbuf[kScoreChunkMax];   // ||v||^2 in (value-weighted kinds), scores out
+  __shared__ __align__(16) float red[2][4][KT];
+  __shared__ __align__(16) float rowc[2 * ROWS];        // lse2 and weight of each row
+  __shared__ int rowhz[ROWS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int col = lane & 31;
+  const int g = a.Hq / a.Hkv;
+  const int R = g * a.w;
+  const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rg);
+
+  const int arow = rg * ROWS + wave * 32 + col;
+  const bool arow_ok = arow < R;
+  bf16x8 qa[D / 16];
+  {
+    const int qh = h * g + (arow_ok ? arow / a.w : 0);
+    const int wi = arow_ok ? arow % a.w : 0;
+    const uint16_t* qp = a.q_win + ((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (arow_ok) t = *reinterpret_cast<const u32x4*>(qp + 16 * kk + 8 * hl);
+      qa[kk] = as_bf16x8(t);
+    }
+  }
+  for (int i = tid; i < ROWS; i += WG) {
+    const int rrow = rg * ROWS + i;
+    rowc[i] = a.lse2[grp * ROWS + i];
+    rowc[ROWS + i] = (rrow < R) ? score_row_weight(kind, rrow % a.w, a.w) : 0.f;
+    rowhz[i] = (rrow < R) ? n - a.w + rrow % a.w : -1;
+  }
+  if (VNORM) {
+    const float* vnb = a.vnorm + static_cast<size_t>(h) * a.T + base;
+    for (int i = tid; i < c1 - c0; i += WG) sbuf[i] = vnb[c0 + i];
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) settle(qa[kk]);
+  __syncthreads();
+
+  const char* kb8 = reinterpret_cast<const char*>(a.k + (static_cast<size_t>(h) * a.T + base) * D);
+  RingFill fill;
+  fill.init(lds_addr(ring), wave, lane);
+  const int ntile = (c1 - c0 + KT - 1) / KT;
+
+  auto reduce_tile = [&](int t) {   // 4 row-block partials -> sbuf
+    if (tid < KT) {
+      const float* rr = &red[t & 1][0][0];
+      float tot = (rr[tid] + rr[KT + tid]) + (rr[2 * KT + tid] + rr[3 * KT + tid]);
+      if (VNORM) tot *= sqrtf(sbuf[t * KT + tid]);
+      sbuf[t * KT + tid] = tot;
+    }
+  };
+  int koff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(col, 2 * kk + hl);
+  const bool causal = a.causal != 0;
+
+  auto tile = [&](const int t, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int kt0 = c0 + t * KT;
+    const char* Kt = ring + (t & 1) * TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kop[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        kop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * ROWB + koff[kk]));
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) sacc = mfma32(qa[kk], kop[kk], sacc);
+      float sc = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowc[wave * 32 + 8 * q4 + 4 * hl]);
+        const f32x4 cw = *reinterpret_cast<const f32x4*>(&rowc[ROWS + wave * 32 + 8 * q4 + 4 * hl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = fmaf(sacc[4 * q4 + e], a.c2, -lv[e]);
+          if constexpr (EDGE) {
+            const int key = kt0 + kb * 32 + col;
+            const int hz = rowhz[wave * 32 + 8 * q4 + 4 * hl + e];
+            const bool hidden = (key >= c1) | (causal & (key > hz));
+            x = hidden ? -INFINITY : x;
+          }
+          sc = fmaf(cw[e], __builtin_amdgcn_exp2f(x), sc);
+        }
+      }
+      sc = sum_xor32(sc);
+      if (hl == 0) red[t & 1][wave][kb * 32 + col] = sc;
+    }
+  };
+
+  if (ntile > 0) fill.issue_k(kb8, c0, c1, 0);
+  const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;
+  for (int t = 0; t < ntile; ++t) {
+    wait_vm<0>();
+    lds_barrier();
+    if (t > 0) reduce_tile(t - 1);
+    if (t + 1 < ntile) fill.issue_k(kb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+    if (c0 + t * KT > edge_from) tile(t, std::true_type{});
+    else tile(t, std::false_type{});
+  }
+  lds_barrier();
+  if (ntile > 0) reduce_tile(ntile - 1);
+  lds_barrier();
+  float* sout = a.sraw + (static_cast<size_t>(rg) * a.Hkv + h) * a.T + base;
+  for (int i = tid; i < c1 - c0; i += WG) sout[c0 + i] = sbuf[i];
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
-                             const int32_t* seq_off, float sm_scale, int causal, void* ws,
-                             hipStream_t st) {
+                             const int32_t* seq_off, float sm_scale, int causal, int score_kind,
+                             void* ws, hipStream_t st) {
   ScoreArgs a;
   a.q_win = static_cast<const uint16_t*>(q_win);
   a.k = static_cast<const uint16_t*>(k);
@@ -800,7 +951,12 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_SCORE_P2, st);
-  hipLaunchKernelGGL(score_p2_bf16, grid, dim3(WG), 0, st, a);
+  if (score_kind == KVE_SCORE_PERTURB)
+    hipLaunchKernelGGL(score_p2_bf16, grid, dim3(WG), 0, st, a);
+  else if (score_kind == KVE_SCORE_MIN || score_kind == KVE_SCORE_MIN_H)
+    hipLaunchKernelGGL((score_p2w_bf16<true>), grid, dim3(WG), 0, st, a, score_kind);
+  else
+    hipLaunchKernelGGL((score_p2w_bf16<false>), grid, dim3(WG), 0, st, a, score_kind);
   stage_end(ST_SCORE_P2, st);
   return hipGetLastError();
 }

@@ -17,9 +17,11 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 KVE_OK, KVE_EINVAL, KVE_ENOTSUP, KVE_EWORKSPACE, KVE_EHIP, KVE_ENOCONV = range(6)
 KVE_BF16, KVE_F32 = 0, 1
 KVE_TOPK, KVE_SAMPLE = 0, 1
+SCORE_KINDS = {"perturb": 0, "h2o": 1, "h2o_h": 2, "tova": 3, "min": 4, "min_h": 5}
+POOL_MODES = {"max": 0, "avg": 1}
 
 EXPORTS = [
-    "kvevict_score_workspace", "kvevict_score", "kvevict_select_workspace", "kvevict_select",
+    "kvevict_score_workspace", "kvevict_score", "kvevict_score_ex", "kvevict_select_workspace", "kvevict_select",
     "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
@@ -61,6 +63,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_score_workspace.restype = SZ
     lib.kvevict_score.argtypes = [LP, P, P, P, F32, I32, I32, P, P, SZ, P]
     lib.kvevict_score.restype = I32
+    lib.kvevict_score_ex.argtypes = [LP, P, P, P, F32, I32, I32, I32, I32, P, P, SZ, P]
+    lib.kvevict_score_ex.restype = I32
     lib.kvevict_select_workspace.argtypes = [LP, P, I32]
     lib.kvevict_select_workspace.restype = SZ
     lib.kvevict_select.argtypes = [LP, P, P, P, I32, F32, F32, U64, P, P, P, P, P, SZ, P]
@@ -167,7 +171,10 @@ class Batch:
 
     # ------------------------------------------------------------ calls
     def score(self, q_win, k, v, sm_scale: float, causal: bool = True, pool_kernel: int = 7,
-              out=None, stream=None):
+              out=None, stream=None, score_kind="perturb", pool_mode="max"):
+        """score_kind: a name of SCORE_KINDS or its code; pool_mode: "max" or "avg"."""
+        kind = SCORE_KINDS[score_kind] if isinstance(score_kind, str) else int(score_kind)
+        pmode = POOL_MODES[pool_mode] if isinstance(pool_mode, str) else int(pool_mode)
         lay = ctypes.byref(self.layout)
         nbytes = self._lib.kvevict_score_workspace(lay)
         if nbytes == 0:
@@ -176,9 +183,15 @@ class Batch:
         ws = self._workspace("score", nbytes)
         if out is None:
             out = torch.empty((self.Hkv, self.T), dtype=torch.float32, device=self.device)
-        _check(self._lib.kvevict_score(lay, _ptr(q_win), _ptr(k), _ptr(v), float(sm_scale),
-                                       int(bool(causal)), int(pool_kernel), _ptr(out), _ptr(ws),
-                                       ws.numel(), _stream(stream)))
+        if kind == 0 and pmode == 0:
+            st = self._lib.kvevict_score(lay, _ptr(q_win), _ptr(k), _ptr(v), float(sm_scale),
+                                         int(bool(causal)), int(pool_kernel), _ptr(out), _ptr(ws),
+                                         ws.numel(), _stream(stream))
+        else:
+            st = self._lib.kvevict_score_ex(lay, _ptr(q_win), _ptr(k), _ptr(v), float(sm_scale),
+                                            int(bool(causal)), int(pool_kernel), kind, pmode, _ptr(out),
+                                            _ptr(ws), ws.numel(), _stream(stream))
+        _check(st)
         return out
 
     def select(self, scores, budgets, mode: int = KVE_TOPK, tau: float = 1.0, tau_w: float = 1.0,

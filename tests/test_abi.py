@@ -78,6 +78,28 @@ def test_score_rejects_bad_arguments():
     assert _score(lay3) == K.KVE_EINVAL
 
 
+def _score_ex(lay, kind, pool_mode, ws_bytes=1 << 40):
+    lib = K.load_library()
+    return lib.kvevict_score_ex(ctypes.byref(lay), DUMMY, DUMMY, DUMMY, 0.1, 1, 7, kind, pool_mode, DUMMY, DUMMY,
+                                ws_bytes, None)
+
+
+def test_score_ex_rejects_bad_kind_and_pool_mode():
+    lay, keep = _layout()
+    assert _score_ex(lay, 6, 0) == K.KVE_EINVAL
+    assert _score_ex(lay, -1, 0) == K.KVE_EINVAL
+    assert _score_ex(lay, 1, 2) == K.KVE_EINVAL
+    assert K.load_library().kvevict_last_error().startswith(b"kvevict_score")
+    # attention-weight kinds are bf16-only; fp32 reports "not supported"
+    lay32, keep32 = _layout(dtype=K.KVE_F32)
+    for kind in range(1, 6):
+        assert _score_ex(lay32, kind, 0) == K.KVE_ENOTSUP
+    # every valid kind/mode pair reaches the workspace check
+    for kind in range(6):
+        for mode in range(2):
+            assert _score_ex(lay, kind, mode, ws_bytes=16) == K.KVE_EWORKSPACE
+
+
 def test_select_rejects_bad_budgets():
     lib = K.load_library()
     lay, keep = _layout(S=2, lens=(50, 60))

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from oracle.score import score_workload
+from oracle.score import score_workload, max_pool_fast
+from oracle.proposals import group_proposal_scores, avg_pool
 from oracle.select import select_workload, expected_distinct, proposal, inclusion_prob
 from long_context_attention_kvevict_amd import kvevict as K
 from long_context_attention_kvevict_amd import synth, workloads
@@ -115,6 +116,59 @@ def test_score_dominant_key_is_finite():
     mask = np.ones(1024, bool)
     mask[100 - 3:100 + 4] = False
     check_scores(got[0][mask], ref[0][mask], "dominant, other keys")
+
+
+# ------------------------------------------ attention-weight score kinds
+def _oracle_proposal_scores(r, kind, pool_mode, causal=True):
+    wl = r.wl
+    q, k, v = r.f64("q_win"), r.f64("k"), r.f64("v")
+    off = wl.seq_off()
+    g = wl.Hq // wl.Hkv
+    out = np.zeros((wl.Hkv, off[-1]))
+    for h in range(wl.Hkv):
+        for s in range(wl.S):
+            a, b = off[s], off[s + 1]
+            sc = group_proposal_scores(kind, q[s], k[h, a:b], v[h, a:b], h, g, wl.sm_scale, causal)
+            out[h, a:b] = avg_pool(sc, wl.pool_kernel) if pool_mode == "avg" else max_pool_fast(sc, wl.pool_kernel)
+    return out
+
+
+@pytest.mark.parametrize("kind,pool_mode,name", [
+    ("h2o", "max", "llama_n4099"), ("h2o_h", "avg", "llama_n4099"), ("tova", "max", "ragged3"),
+    ("min", "avg", "ragged3"), ("min_h", "max", "qwen_n3001"), ("h2o", "avg", "qwen_n3001"),
+    ("tova", "avg", "llama_n4099"),
+])
+def test_score_kinds_parity(runs, kind, pool_mode, name):
+    r = _run(runs, name)
+    say(f"[gpu] score kind {kind} pool {pool_mode} {name}")
+    got = r.b.score(r.q, r.k, r.v, r.wl.sm_scale, pool_kernel=r.wl.pool_kernel, score_kind=kind,
+                    pool_mode=pool_mode)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ref = _oracle_proposal_scores(r, kind, pool_mode)
+    off = r.wl.seq_off()
+    for h in range(r.wl.Hkv):
+        for s in range(r.wl.S):
+            a, b = off[s], off[s + 1]
+            check_scores(got[h, a:b], ref[h, a:b], f"{kind}/{pool_mode} {name} h{h} s{s}")
+
+
+def test_score_kinds_noncausal_and_perturb_avg(runs):
+    r = _run(runs, "llama_n4099")
+    got = r.b.score(r.q, r.k, r.v, r.wl.sm_scale, causal=False, pool_kernel=7, score_kind="h2o")
+    torch.cuda.synchronize()
+    ref = _oracle_proposal_scores(r, "h2o", "max", causal=False)
+    for h in range(r.wl.Hkv):
+        check_scores(got[h].cpu().numpy(), ref[h], f"h2o noncausal h{h}")
+    # the perturbation score with average pooling
+    got = r.b.score(r.q, r.k, r.v, r.wl.sm_scale, pool_kernel=7, pool_mode="avg")
+    torch.cuda.synchronize()
+    raw = _oracle_scores(r, pooled=False)
+    off = r.wl.seq_off()
+    for h in range(r.wl.Hkv):
+        for s in range(r.wl.S):
+            a, b = off[s], off[s + 1]
+            check_scores(got[h, a:b].cpu().numpy(), avg_pool(raw[h, a:b], 7), f"perturb/avg h{h} s{s}")
 
 
 # ---------------------------------------------------------------- select
