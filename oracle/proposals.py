@@ -12,6 +12,9 @@ attention of every observed query row, row j of t weighted by the harmonic
 prior h_j = 1 / ((t - j + 1) H_t), H_t the t-th harmonic number.
 [PI] App. D (SnapKV): the column sums are smoothed by 1-D average pooling
 along the key axis.
+[PI] App. D, Eq. 18 (K-norm): a score from an L2 norm per entry and a
+softmax proposal; the related-work page describes the method as keeping the
+entries whose KEYS have the smaller norms.
 
 Readings (also in the design notes):
  * the observed query rows are the w observation-window rows; t = w and row
@@ -21,7 +24,14 @@ Readings (also in the design notes):
    group mean differ by a constant factor, which leaves both the ranking and
    the normalised proposal unchanged);
  * average pooling divides by the number of in-range keys in the window
-   (out-of-range neighbours are ignored, as in the max pool).
+   (out-of-range neighbours are ignored, as in the max pool);
+ * K-norm (the two pages disagree on V versus K and on the sign): the
+   negative norm of the key row, written as the positive score
+   exp(KNORM_SHIFT - ||k_j||) so that the largest scores are the smallest
+   norms and the tempered proposal s^(1/tau) is the softmax of -||k|| / tau
+   (Eq. 18 with the prose's sign); the constant shift changes neither the
+   ranking nor the normalised proposal and keeps norms up to about 167
+   inside the fp32 normal range.
 
 Pinned by closed forms: column sums of attention weights add up to the
 number of rows (H2O), to the number of q-heads (TOVA, H2O-h), the harmonic
@@ -74,6 +84,14 @@ def group_proposal_scores(kind: str, q_win: np.ndarray, k: np.ndarray, v: np.nda
     if kind in ("min", "min_h"):
         total *= np.sqrt((v * v).sum(axis=1))
     return total
+
+
+KNORM_SHIFT = 80.0
+
+
+def knorm_scores(k: np.ndarray) -> np.ndarray:
+    """exp(KNORM_SHIFT - ||k_j||) for every key row of k [n][d] (float64)."""
+    return np.exp(KNORM_SHIFT - np.sqrt((k * k).sum(axis=1)))
 
 
 def avg_pool(s: np.ndarray, kernel: int) -> np.ndarray:

@@ -14,6 +14,9 @@ exp(log(w) / tau).
 Readings:
  * proposal log pi~_j = log(max(s_j, 2^-126)) / tau (pi ~ s^(1/tau)); NaN
    scores are treated as 2^-126;
+ * [PI] App. D.1 mixing with the uniform, pi' = alpha pi + (1 - alpha) / n,
+   is applied to the tempered, normalised proposal (mix = alpha; 1 = none);
+   with mixing the Gumbel keys use log pi'_j;
  * the target is the kept count, j* = B;
  * the kept set is B draws without replacement via Gumbel keys
    kappa_j = log pi~_j - log(-log u_j), u_j from Philox (see philox.py);
@@ -63,11 +66,15 @@ def proposal_log(s: np.ndarray, tau: float) -> np.ndarray:
     return np.log(np.fmax(s, FLT_MIN)) / tau
 
 
-def proposal(s: np.ndarray, tau: float) -> np.ndarray:
+def proposal(s: np.ndarray, tau: float, mix: float = 1.0) -> np.ndarray:
+    """Normalised tempered proposal, mixed with the uniform when mix < 1."""
     lp = proposal_log(s, tau)
     mx = lp.max()
     lse = mx + np.log(np.exp(lp - mx).sum())
-    return np.exp(lp - lse)
+    pi = np.exp(lp - lse)
+    if mix < 1.0:
+        pi = mix * pi + (1.0 - mix) / pi.shape[0]
+    return pi
 
 
 def expected_distinct(pi: np.ndarray, m) -> float:
@@ -102,7 +109,8 @@ def gumbel_keys(logp: np.ndarray, seed: int, s: int, h: int) -> np.ndarray:
     return logp - np.log(-np.log(u))
 
 
-def sample_select(s: np.ndarray, B: int, tau: float, tau_w: float, seed: int, seq: int, head: int):
+def sample_select(s: np.ndarray, B: int, tau: float, tau_w: float, seed: int, seq: int, head: int,
+                  mix: float = 1.0):
     """Sampling-mode selection for one (sequence, KV head).
     Returns (idx ascending, bias fp64, m, status)."""
     s = np.asarray(s, dtype=np.float64)
@@ -111,8 +119,8 @@ def sample_select(s: np.ndarray, B: int, tau: float, tau_w: float, seed: int, se
         return np.arange(n), np.zeros(n), 0, STATUS_OK
     if B <= 0:
         return np.zeros(0, dtype=np.int64), np.zeros(0), 0, STATUS_OK
-    lp = proposal_log(s, tau)
-    pi = proposal(s, tau)
+    pi = proposal(s, tau, mix)
+    lp = proposal_log(s, tau) if mix >= 1.0 else np.log(pi)
     m, status = expected_samples_search(pi, float(B))
     kappa = gumbel_keys(lp, seed, seq, head)
     order = np.lexsort((np.arange(n), -kappa))
@@ -123,7 +131,7 @@ def sample_select(s: np.ndarray, B: int, tau: float, tau_w: float, seed: int, se
 
 
 def select_workload(scores: np.ndarray, seq_off, budgets, mode: str, tau: float = 1.0,
-                    tau_w: float = 1.0, seed: int = 0, heads=None):
+                    tau_w: float = 1.0, seed: int = 0, heads=None, mix: float = 1.0):
     """Selection for a ragged batch: scores [Hkv][T] -> idx/bias [Hkv][sum B]
     (sequence-relative indices), m [S][Hkv], status [S][Hkv]."""
     Hkv = scores.shape[0]
@@ -143,7 +151,7 @@ def select_workload(scores: np.ndarray, seq_off, budgets, mode: str, tau: float 
                 bb = np.zeros(len(ii))
                 m, status = 0, STATUS_OK
             else:
-                ii, bb, m, status = sample_select(scores[h, a:b], Bs, tau, tau_w, seed, s, h)
+                ii, bb, m, status = sample_select(scores[h, a:b], Bs, tau, tau_w, seed, s, h, mix)
             idx[h, bud_off[s]:bud_off[s] + len(ii)] = ii
             bias[h, bud_off[s]:bud_off[s] + len(ii)] = bb
             m_out[s, h] = m

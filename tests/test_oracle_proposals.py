@@ -71,3 +71,24 @@ def test_avg_pool():
         assert np.allclose(got[r:-r], uniform_filter1d(s, kern, mode="constant")[r:-r], rtol=1e-13)
         assert abs(got[0] - s[:r + 1].mean()) < 1e-15 and abs(got[-1] - s[-r - 1:].mean()) < 1e-15
     assert np.array_equal(P.avg_pool(s, 1), s)
+
+
+def test_knorm_closed_form_and_softmax_proposal():
+    # keys r * e_1 have norm |r|: score exp(80 - |r|); rotation-invariant
+    r = np.array([0.0, 1.0, -3.5, 10.0, 150.0])
+    k = np.zeros((5, 8))
+    k[:, 0] = r
+    s = P.knorm_scores(k)
+    assert np.allclose(s, np.exp(80.0 - np.abs(r)), rtol=1e-15, atol=0)
+    rng = np.random.default_rng(7)
+    kk = rng.standard_normal((40, 16))
+    qmat, _ = np.linalg.qr(rng.standard_normal((16, 16)))
+    assert np.allclose(P.knorm_scores(kk @ qmat), P.knorm_scores(kk), rtol=1e-12, atol=0)
+    # the largest scores are the smallest norms; s^(1/tau), normalised, is
+    # the softmax of -||k|| / tau (Eq. 18 with the negative norm)
+    from scipy.special import softmax
+    from oracle.select import proposal, topk_select
+    norms = np.linalg.norm(kk, axis=1)
+    assert set(topk_select(P.knorm_scores(kk), 5)) == set(np.argsort(norms)[:5])
+    for tau in (1.0, 0.5, 3.0):
+        assert np.allclose(proposal(P.knorm_scores(kk), tau), softmax(-norms / tau), rtol=1e-12, atol=0)

@@ -202,3 +202,37 @@ def test_select_workload_ragged_layout():
     for h in range(2):
         assert list(idx[h, :3]) == list(topk_select(sc[h, :30], 3))
         assert list(idx[h, 3:]) == list(topk_select(sc[h, 30:], 5))
+
+
+def test_uniform_mixing_of_the_proposal():
+    from oracle import select as S
+    # [PI] App. D.1: pi' = alpha pi + (1 - alpha) / n sums to one and has
+    # full support; alpha = 0 is the uniform, where E[J(m)] = n (1 - (1 -
+    # 1/n)^m) and every kept entry carries the same bias
+    rng = np.random.default_rng(3)
+    s = rng.exponential(size=300) ** 4
+    n = s.shape[0]
+    pi = S.proposal(s, 0.7)
+    for a in (0.0, 0.3, 0.9):
+        pm = S.proposal(s, 0.7, mix=a)
+        assert abs(pm.sum() - 1.0) < 1e-12
+        assert pm.min() >= (1 - a) / n * (1 - 1e-12)
+        assert np.allclose(pm, a * pi + (1 - a) / n, rtol=1e-14, atol=0)
+    u = S.proposal(s, 0.7, mix=0.0)
+    for m in (10, 250, 4000):
+        assert abs(S.expected_distinct(u, m) - n * (1 - (1 - 1 / n) ** m)) < 1e-9
+    idx, bias, m, st = S.sample_select(s, 60, 0.7, 1.0, 11, 0, 0, mix=0.0)
+    assert st == S.STATUS_OK and len(idx) == 60 and np.ptp(bias) < 1e-12
+    # ... and the kept set ignores the scores: the B largest Gumbel noises
+    g = S.gumbel_keys(np.zeros(n), 11, 0, 0)
+    assert np.array_equal(idx, np.sort(np.argsort(-g, kind="stable")[:60]))
+    # mix = 1 is the unmixed selection, bit for bit
+    a = S.sample_select(s, 60, 0.7, 1.0, 11, 0, 0)
+    b = S.sample_select(s, 60, 0.7, 1.0, 11, 0, 0, mix=1.0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+    # mixing raises the inclusion of the least likely entries
+    idx1, bias1, m1, _ = S.sample_select(s, 60, 0.7, 1.0, 11, 0, 0, mix=0.5)
+    q0 = S.inclusion_prob(pi, S.expected_samples_search(pi, 60)[0])
+    q1 = S.inclusion_prob(S.proposal(s, 0.7, 0.5), m1)
+    lo = np.argsort(pi)[:50]
+    assert np.all(q1[lo] > q0[lo])
