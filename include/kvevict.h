@@ -116,16 +116,25 @@ kve_status kvevict_score(const kve_layout* L, const void* q_win, const void* k,
  * sum stands for the layer or group mean of the pages (same ranking and
  * same normalised proposal).  pool_mode KVE_POOL_AVG takes the mean over
  * the in-sequence keys of the window instead of the maximum (SnapKV-style
- * smoothing, App. D).  The attention-weight kinds need the bf16 path
- * (KVE_ENOTSUP for fp32); both pool modes work for both.  Same workspace,
- * layouts and determinism as kvevict_score. */
+ * smoothing, App. D).
+ *   KVE_SCORE_KNORM   exp(80 - ||k_j||) (K-norm, App. D Eq. 18, with the
+ *                     key norms of [DK]'s related work and the negative
+ *                     sign of [PI]'s prose): the largest scores are the
+ *                     smallest key norms, and the tempered proposal of
+ *                     kvevict_select is the softmax of -||k|| / tau.  Reads K
+ *                     only (q_win and v are checked but not read); the
+ *                     constant 80 keeps norms up to about 167 in range.
+ * The attention-weight kinds need the bf16 path (KVE_ENOTSUP for fp32);
+ * PERTURB and KNORM take both dtypes; both pool modes work for all.  Same
+ * workspace, layouts and determinism as kvevict_score. */
 typedef enum {
   KVE_SCORE_PERTURB = 0,
   KVE_SCORE_H2O = 1,
   KVE_SCORE_H2O_H = 2,
   KVE_SCORE_TOVA = 3,
   KVE_SCORE_MIN = 4,
-  KVE_SCORE_MIN_H = 5
+  KVE_SCORE_MIN_H = 5,
+  KVE_SCORE_KNORM = 6
 } kve_score_kind;
 typedef enum { KVE_POOL_MAX = 0, KVE_POOL_AVG = 1 } kve_pool_mode;
 kve_status kvevict_score_ex(const kve_layout* L, const void* q_win, const void* k,
@@ -170,6 +179,18 @@ kve_status kvevict_select(const kve_layout* L, const float* scores,
                           int32_t* idx, float* bias, double* m_out,
                           int32_t* status_out, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* kvevict_select with the proposal mixed with the uniform ([PI] App. D.1):
+ * in KVE_SAMPLE mode pi'_j = mix * pi_j + (1 - mix) / n_s replaces pi_j
+ * everywhere above (the search, q_j, and the Gumbel keys, which become
+ * log pi'_j - log(-log u_j)).  mix in [0, 1], else KVE_EINVAL; mix = 1 is
+ * kvevict_select bit for bit; ignored in KVE_TOPK mode. */
+kve_status kvevict_select_ex(const kve_layout* L, const float* scores,
+                             const int32_t* bud_off, const int32_t* bud_off_host,
+                             int32_t mode, float tau, float tau_w, float mix,
+                             uint64_t seed, int32_t* idx, float* bias,
+                             double* m_out, int32_t* status_out, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- compact
  * Gather of the kept entries ([PI] §2 Eq. 3: evicted attention uses the

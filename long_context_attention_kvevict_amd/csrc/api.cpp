@@ -46,11 +46,11 @@ kve_status kvevict_score_ex(const kve_layout* L, const void* q_win, const void* 
   if (!(sm_scale > 0.f) || sm_scale > 1e6f) return set_err(KVE_EINVAL, "kvevict_score: sm_scale must be in (0, 1e6]");
   if (pool_kernel < 1 || pool_kernel > 31 || pool_kernel % 2 == 0)
     return set_err(KVE_EINVAL, "kvevict_score: pool_kernel must be odd and in [1, 31]");
-  if (score_kind < KVE_SCORE_PERTURB || score_kind > KVE_SCORE_MIN_H)
+  if (score_kind < KVE_SCORE_PERTURB || score_kind > KVE_SCORE_KNORM)
     return set_err(KVE_EINVAL, "kvevict_score: unknown score kind");
   if (pool_mode != KVE_POOL_MAX && pool_mode != KVE_POOL_AVG)
     return set_err(KVE_EINVAL, "kvevict_score: unknown pool mode");
-  if (score_kind != KVE_SCORE_PERTURB && L->dtype != KVE_BF16)
+  if (score_kind != KVE_SCORE_PERTURB && score_kind != KVE_SCORE_KNORM && L->dtype != KVE_BF16)
     return set_err(KVE_ENOTSUP, "kvevict_score: attention-weight score kinds need bf16 inputs");
   if (!ws || ws_bytes < G.bytes)
     return set_err(KVE_EWORKSPACE, "kvevict_score: workspace smaller than kvevict_score_workspace()");
@@ -59,11 +59,18 @@ kve_status kvevict_score_ex(const kve_layout* L, const void* q_win, const void* 
   if (reinterpret_cast<uintptr_t>(ws) & 255)
     return set_err(KVE_EINVAL, "kvevict_score: workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = (L->dtype == KVE_BF16)
-                     ? kve::launch_score_bf16(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, score_kind, ws, s)
-                     : kve::launch_score_f32(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, ws, s);
+  hipError_t e;
+  int planes = G.pool_rg;
+  if (score_kind == KVE_SCORE_KNORM) {
+    e = kve::launch_knorm(G, k, ws, s);
+    planes = 1;
+  } else if (L->dtype == KVE_BF16) {
+    e = kve::launch_score_bf16(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, score_kind, ws, s);
+  } else {
+    e = kve::launch_score_f32(G, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, ws, s);
+  }
   if (e != hipSuccess) return hip_err(e, "kvevict_score");
-  e = kve::launch_pool(G, L->seq_off, pool_kernel, pool_mode, ws, scores, s);
+  e = kve::launch_pool(G, L->seq_off, pool_kernel, pool_mode, planes, ws, scores, s);
   if (e != hipSuccess) return hip_err(e, "kvevict_score (pool)");
   return KVE_OK;
 }
@@ -82,10 +89,10 @@ size_t kvevict_select_workspace(const kve_layout* L, const int32_t* bud_off_host
   return G.bytes;
 }
 
-kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_t* bud_off,
-                          const int32_t* bud_off_host, int32_t mode, float tau, float tau_w, uint64_t seed,
-                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                          size_t ws_bytes, void* stream) {
+kve_status kvevict_select_ex(const kve_layout* L, const float* scores, const int32_t* bud_off,
+                             const int32_t* bud_off_host, int32_t mode, float tau, float tau_w, float mix,
+                             uint64_t seed, int32_t* idx, float* bias, double* m_out, int32_t* status_out,
+                             void* ws, size_t ws_bytes, void* stream) {
   kve::SelectGeom G;
   std::string msg;
   kve_status st = kve::plan_select(L, bud_off_host, mode, &G, &msg);
@@ -93,14 +100,23 @@ kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_
   if (!scores || !bud_off || !idx || !bias) return set_err(KVE_EINVAL, "kvevict_select: null tensor pointer");
   if (mode == KVE_SAMPLE && (!(tau > 0.f) || !(tau_w > 0.f)))
     return set_err(KVE_EINVAL, "kvevict_select: tau and tau_w must be > 0");
+  if (!(mix >= 0.f && mix <= 1.f)) return set_err(KVE_EINVAL, "kvevict_select: mix must be in [0, 1]");
   if (!ws || ws_bytes < G.bytes)
     return set_err(KVE_EWORKSPACE, "kvevict_select: workspace smaller than kvevict_select_workspace()");
   if (reinterpret_cast<uintptr_t>(ws) & 255)
     return set_err(KVE_EINVAL, "kvevict_select: workspace must be 256-byte aligned");
-  hipError_t e = kve::launch_select(G, scores, L->seq_off, bud_off, tau, tau_w, seed, idx, bias, m_out,
+  hipError_t e = kve::launch_select(G, scores, L->seq_off, bud_off, tau, tau_w, mix, seed, idx, bias, m_out,
                                     status_out, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_err(e, "kvevict_select");
   return KVE_OK;
+}
+
+kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_t* bud_off,
+                          const int32_t* bud_off_host, int32_t mode, float tau, float tau_w, uint64_t seed,
+                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return kvevict_select_ex(L, scores, bud_off, bud_off_host, mode, tau, tau_w, 1.f, seed, idx, bias, m_out,
+                           status_out, ws, ws_bytes, stream);
 }
 
 kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v, const int32_t* bud_off,

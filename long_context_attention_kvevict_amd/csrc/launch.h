@@ -15,12 +15,14 @@ hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k
                             const int32_t* seq_off, float sm_scale, int causal, void* ws,
                             hipStream_t st);
 hipError_t launch_merge_f32(const ScoreGeom& G, const int32_t* seq_off, void* ws, hipStream_t st);
-hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode,
+hipError_t launch_knorm(const ScoreGeom& G, const void* k, void* ws, hipStream_t st);
+hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode, int planes,
                        const void* ws, float* scores, hipStream_t st);
 
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
-                         const int32_t* bud_off, float tau, float tau_w, uint64_t seed, int32_t* idx,
-                         float* bias, double* m_out, int32_t* status_out, void* ws, hipStream_t st);
+                         const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
+                         int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
+                         hipStream_t st);
 
 hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t totalB, int64_t totalC,
                           int maxB, const void* k, const void* v, const int32_t* seq_off,

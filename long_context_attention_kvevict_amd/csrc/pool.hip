@@ -52,18 +52,18 @@ __global__ __launch_bounds__(POOL_TILE) void pool_window(const float* __restrict
   out[static_cast<size_t>(h) * T + t] = m;
 }
 
-hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode,
+hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode, int planes,
                        const void* ws, float* scores, hipStream_t st) {
   const float* sraw = reinterpret_cast<const float*>(static_cast<const char*>(ws) + G.off_sraw);
   if ((pool_kernel - 1) / 2 > POOL_MAX_RADIUS) return hipErrorInvalidValue;
   dim3 grid((G.T + POOL_TILE - 1) / POOL_TILE, G.Hkv);
   stage_begin(ST_SCORE_POOL, st);
   if (pool_mode == KVE_POOL_AVG)
-    hipLaunchKernelGGL((pool_window<true>), grid, dim3(POOL_TILE), 0, st, sraw, seq_off, G.S, G.Hkv, G.T, G.pool_rg,
+    hipLaunchKernelGGL((pool_window<true>), grid, dim3(POOL_TILE), 0, st, sraw, seq_off, G.S, G.Hkv, G.T, planes,
                        (pool_kernel - 1) / 2, scores);
   else
     hipLaunchKernelGGL((pool_window<false>), grid, dim3(POOL_TILE), 0, st, sraw, seq_off, G.S, G.Hkv, G.T,
-                       G.pool_rg, (pool_kernel - 1) / 2, scores);
+                       planes, (pool_kernel - 1) / 2, scores);
   stage_end(ST_SCORE_POOL, st);
   return hipGetLastError();
 }

@@ -11,7 +11,8 @@
 // with-replacement draws m whose expected distinct count
 // E(m) = sum_j 1 - (1 - pi_j)^m lies within 0.5 of B, Gumbel keys from
 // Philox-4x64-10 (the B largest are kept), bias -log(q_j) / tau_w with
-// q_j = 1 - (1 - pi_j)^m.
+// q_j = 1 - (1 - pi_j)^m.  Optionally (App. D.1) the normalised proposal is
+// mixed with the uniform, pi' = alpha pi + (1 - alpha) / n, before all of it.
 //
 // Work is spread over workgroups of SEL_CHUNK keys of one (sequence, head),
 // one launch per pass; no launch waits on another workgroup of the same
@@ -410,6 +411,7 @@ struct SmpArgs {
   Search* state;      // [2][S*Hkv] search state (ping-pong)
   double* mvals;      // [S*Hkv] final m
   double inv_tau;
+  double mix;         // weight of the proposal against the uniform (1: unmixed)
   uint64_t seed;
 };
 
@@ -513,8 +515,15 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   for (int i = 0; i < SMP_PER; ++i) {
     const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
-      const double x = A.lp[row + j];
-      const double l = log1p(-exp(x - lse));
+      double x = A.lp[row + j];
+      double l;
+      if (A.mix < 1.0) {   // pi' = alpha pi + (1 - alpha) / n; the keys use log pi'
+        const double pm = A.mix * exp(x - lse) + (1.0 - A.mix) / n;
+        l = log1p(-pm);
+        x = log(pm);
+      } else {
+        l = log1p(-exp(x - lse));
+      }
       A.L[row + j] = l;
       const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h),
                                           static_cast<uint64_t>(s), 0ull, A.seed, 0ull);
@@ -744,8 +753,9 @@ __global__ __launch_bounds__(256) void sel_init(int* __restrict__ p, int n, doub
 }
 
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
-                         const int32_t* bud_off, float tau, float tau_w, uint64_t seed, int32_t* idx,
-                         float* bias, double* m_out, int32_t* status_out, void* ws, hipStream_t st) {
+                         const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
+                         int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
+                         hipStream_t st) {
   char* wsb = static_cast<char*>(ws);
   int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
   int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
@@ -782,6 +792,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.state = reinterpret_cast<Search*>(wsb + G.off_state);
     A.mvals = reinterpret_cast<double*>(wsb + G.off_mvals);
     A.inv_tau = 1.0 / static_cast<double>(tau);
+    A.mix = static_cast<double>(mix);
     A.seed = seed;
     const dim3 sgrid(G.nsmp, G.Hkv, G.S);
     hipLaunchKernelGGL(smp_logp, sgrid, dim3(SEL_THREADS), 0, st, A);

@@ -17,11 +17,12 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 KVE_OK, KVE_EINVAL, KVE_ENOTSUP, KVE_EWORKSPACE, KVE_EHIP, KVE_ENOCONV = range(6)
 KVE_BF16, KVE_F32 = 0, 1
 KVE_TOPK, KVE_SAMPLE = 0, 1
-SCORE_KINDS = {"perturb": 0, "h2o": 1, "h2o_h": 2, "tova": 3, "min": 4, "min_h": 5}
+SCORE_KINDS = {"perturb": 0, "h2o": 1, "h2o_h": 2, "tova": 3, "min": 4, "min_h": 5, "knorm": 6}
 POOL_MODES = {"max": 0, "avg": 1}
 
 EXPORTS = [
     "kvevict_score_workspace", "kvevict_score", "kvevict_score_ex", "kvevict_select_workspace", "kvevict_select",
+    "kvevict_select_ex",
     "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
@@ -69,6 +70,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_select_workspace.restype = SZ
     lib.kvevict_select.argtypes = [LP, P, P, P, I32, F32, F32, U64, P, P, P, P, P, SZ, P]
     lib.kvevict_select.restype = I32
+    lib.kvevict_select_ex.argtypes = [LP, P, P, P, I32, F32, F32, F32, U64, P, P, P, P, P, SZ, P]
+    lib.kvevict_select_ex.restype = I32
     lib.kvevict_compact.argtypes = [LP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.kvevict_compact.restype = I32
     lib.kvevict_decode_workspace.argtypes = [LP, I32]
@@ -195,8 +198,9 @@ class Batch:
         return out
 
     def select(self, scores, budgets, mode: int = KVE_TOPK, tau: float = 1.0, tau_w: float = 1.0,
-               seed: int = 0, out=None, stream=None, bud_offsets=None):
-        """budgets: per-sequence kept counts.  Returns (idx, bias, m, status)."""
+               seed: int = 0, out=None, stream=None, bud_offsets=None, mix: float = 1.0):
+        """budgets: per-sequence kept counts; mix < 1 mixes the sampling
+        proposal with the uniform.  Returns (idx, bias, m, status)."""
         bud_host, bud_dev = bud_offsets if bud_offsets is not None else self.offsets(budgets, self.device)
         lay = ctypes.byref(self.layout)
         nbytes = self._lib.kvevict_select_workspace(lay, bud_host.data_ptr(), int(mode)) or 256
@@ -209,10 +213,16 @@ class Batch:
             status = torch.empty((self.S, self.Hkv), dtype=torch.int32, device=self.device)
         else:
             idx, bias, m, status = out
-        _check(self._lib.kvevict_select(lay, _ptr(scores), _ptr(bud_dev), bud_host.data_ptr(), int(mode),
-                                        float(tau), float(tau_w), ctypes.c_uint64(seed & (2 ** 64 - 1)),
-                                        _ptr(idx), _ptr(bias), _ptr(m), _ptr(status), _ptr(ws),
-                                        ws.numel(), _stream(stream)))
+        seed64 = ctypes.c_uint64(seed & (2 ** 64 - 1))
+        if mix == 1.0:
+            st = self._lib.kvevict_select(lay, _ptr(scores), _ptr(bud_dev), bud_host.data_ptr(), int(mode),
+                                          float(tau), float(tau_w), seed64, _ptr(idx), _ptr(bias), _ptr(m),
+                                          _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+        else:
+            st = self._lib.kvevict_select_ex(lay, _ptr(scores), _ptr(bud_dev), bud_host.data_ptr(), int(mode),
+                                             float(tau), float(tau_w), float(mix), seed64, _ptr(idx), _ptr(bias),
+                                             _ptr(m), _ptr(status), _ptr(ws), ws.numel(), _stream(stream))
+        _check(st)
         self._bud = (bud_host, bud_dev)   # keep alive until the stream has consumed them
         return idx[:, :total], bias[:, :total], m, status
 

@@ -13,7 +13,7 @@ prior h_j = 1 / ((t - j + 1) H_t), H_t the t-th harmonic number.
 [PI] App. D (SnapKV): the column sums are smoothed by 1-D average pooling
 along the key axis.
 [PI] App. D, Eq. 18 (K-norm): a score from an L2 norm per entry and a
-softmax proposal; the related-work page describes the method as keeping the
+softmax proposal; [DK]'s related work describes the method as keeping the
 entries whose KEYS have the smaller norms.
 
 Readings (also in the design notes):

@@ -86,7 +86,7 @@ def _score_ex(lay, kind, pool_mode, ws_bytes=1 << 40):
 
 def test_score_ex_rejects_bad_kind_and_pool_mode():
     lay, keep = _layout()
-    assert _score_ex(lay, 6, 0) == K.KVE_EINVAL
+    assert _score_ex(lay, 7, 0) == K.KVE_EINVAL
     assert _score_ex(lay, -1, 0) == K.KVE_EINVAL
     assert _score_ex(lay, 1, 2) == K.KVE_EINVAL
     assert K.load_library().kvevict_last_error().startswith(b"kvevict_score")
@@ -94,8 +94,9 @@ def test_score_ex_rejects_bad_kind_and_pool_mode():
     lay32, keep32 = _layout(dtype=K.KVE_F32)
     for kind in range(1, 6):
         assert _score_ex(lay32, kind, 0) == K.KVE_ENOTSUP
+    assert _score_ex(lay32, 6, 1, ws_bytes=16) == K.KVE_EWORKSPACE   # K-norm takes fp32
     # every valid kind/mode pair reaches the workspace check
-    for kind in range(6):
+    for kind in range(7):
         for mode in range(2):
             assert _score_ex(lay, kind, mode, ws_bytes=16) == K.KVE_EWORKSPACE
 
@@ -150,3 +151,14 @@ def test_workspace_scales_with_shape():
     assert big > small > 0
     # O(w d + n) per head: far below the w x n x d intermediates of a naive scorer
     assert big < 8 * 131072 * 32 * 4 * 128 * 2 / 50
+
+
+def test_select_ex_rejects_bad_mix():
+    lib = K.load_library()
+    lay, keep = _layout(S=2, lens=(50, 60))
+    b = torch.tensor([0, 5, 10], dtype=torch.int32)
+    for mix, st in ((-0.1, K.KVE_EINVAL), (1.5, K.KVE_EINVAL), (float("nan"), K.KVE_EINVAL),
+                    (0.0, K.KVE_EWORKSPACE), (0.5, K.KVE_EWORKSPACE), (1.0, K.KVE_EWORKSPACE)):
+        r = lib.kvevict_select_ex(ctypes.byref(lay), DUMMY, DUMMY, b.data_ptr(), 1, 0.5, 1.0, mix, 0, DUMMY,
+                                  DUMMY, None, None, DUMMY, 16, None)
+        assert r == st, mix

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle.score import score_workload, max_pool_fast
-from oracle.proposals import group_proposal_scores, avg_pool
+from oracle.proposals import group_proposal_scores, avg_pool, knorm_scores
 from oracle.select import select_workload, expected_distinct, proposal, inclusion_prob
 from long_context_attention_kvevict_amd import kvevict as K
 from long_context_attention_kvevict_amd import synth, workloads
@@ -171,16 +171,33 @@ def test_score_kinds_noncausal_and_perturb_avg(runs):
             check_scores(got[h, a:b].cpu().numpy(), avg_pool(raw[h, a:b], 7), f"perturb/avg h{h} s{s}")
 
 
+@pytest.mark.parametrize("name,pool_mode", [("llama_n4099", "max"), ("ragged3", "avg"), ("tiny_fp32", "max"),
+                                            ("fp32_d128_gqa", "avg")])
+def test_score_knorm_parity(runs, name, pool_mode):
+    r = _run(runs, name)
+    got = r.b.score(r.q, r.k, r.v, r.wl.sm_scale, pool_kernel=r.wl.pool_kernel, score_kind="knorm",
+                    pool_mode=pool_mode)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    k = r.f64("k")
+    off = r.wl.seq_off()
+    pool = avg_pool if pool_mode == "avg" else max_pool_fast
+    for h in range(r.wl.Hkv):
+        for s in range(r.wl.S):
+            a, b = off[s], off[s + 1]
+            check_scores(got[h, a:b], pool(knorm_scores(k[h, a:b]), r.wl.pool_kernel), f"knorm {name} h{h} s{s}")
+
+
 # ---------------------------------------------------------------- select
-def _select_check(r, scores_f32, mode, tau, tau_w, seed):
+def _select_check(r, scores_f32, mode, tau, tau_w, seed, mix=1.0):
     wl = r.wl
     budgets = wl.budgets()
     sc_dev = torch.from_numpy(scores_f32).cuda()
-    idx, bias, m, st = r.b.select(sc_dev, budgets, mode=mode, tau=tau, tau_w=tau_w, seed=seed)
+    idx, bias, m, st = r.b.select(sc_dev, budgets, mode=mode, tau=tau, tau_w=tau_w, seed=seed, mix=mix)
     torch.cuda.synchronize()
     idx, bias, m, st = idx.cpu().numpy(), bias.cpu().numpy(), m.cpu().numpy(), st.cpu().numpy()
     ridx, rbias, rm, rst = select_workload(scores_f32.astype(np.float64), wl.seq_off(), budgets,
-                                           "topk" if mode == K.KVE_TOPK else "sample", tau, tau_w, seed)
+                                           "topk" if mode == K.KVE_TOPK else "sample", tau, tau_w, seed, mix=mix)
     assert np.array_equal(idx, ridx), "selected indices differ"
     if mode == K.KVE_TOPK:
         assert np.all(bias == 0.0)
@@ -193,7 +210,7 @@ def _select_check(r, scores_f32, mode, tau, tau_w, seed):
             if B == 0 or B >= n:
                 continue
             assert st[s, h] == rst[s, h]
-            pi = proposal(scores_f32[h, a:b].astype(np.float64), tau)
+            pi = proposal(scores_f32[h, a:b].astype(np.float64), tau, mix)
             if st[s, h] == 0:
                 assert abs(expected_distinct(pi, m[s, h]) - B) <= 0.5 + 1e-9 * n, (s, h, m[s, h])
             q = inclusion_prob(pi[idx[h, boff[s]:boff[s + 1]]], m[s, h])
@@ -215,6 +232,13 @@ def test_select_sample_on_oracle_scores(runs, name):
     r = _run(runs, name)
     ref = _oracle_scores(r).astype(np.float32)
     _select_check(r, ref, K.KVE_SAMPLE, r.wl.tau, r.wl.tau_w, r.wl.hash_seed)
+
+
+@pytest.mark.parametrize("mix", [0.0, 0.5, 0.9])
+def test_select_sample_mixed_with_uniform(runs, mix):
+    r = _run(runs, "ragged3")
+    ref = _oracle_scores(r).astype(np.float32)
+    _select_check(r, ref, K.KVE_SAMPLE, r.wl.tau, r.wl.tau_w, r.wl.hash_seed, mix=mix)
 
 
 @pytest.mark.parametrize("mode", [K.KVE_TOPK, K.KVE_SAMPLE])
