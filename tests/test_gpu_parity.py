@@ -260,6 +260,33 @@ def test_select_ties_nan_and_budget_edges(mode):
     _select_check(r, sc, mode, 0.5, 2.0, 12345)
 
 
+@pytest.mark.parametrize("case", ["one_bin", "all_equal", "two_bins"])
+def test_select_topk_crowded_threshold_bin(case):
+    # tens of thousands of keys share the threshold's leading digits (sign,
+    # exponent and the top mantissa bits), or are exactly equal: every radix
+    # level sees a crowded bin and the selection must stay exact
+    lens = [40000, 17000]
+    rng = np.random.default_rng(5)
+    T = sum(lens)
+    if case == "one_bin":
+        sc = rng.uniform(1.0, 1.19, size=(2, T))
+    elif case == "all_equal":
+        sc = np.full((2, T), 0.75)
+        sc[1, ::97] = 2.0
+    else:
+        sc = np.where(rng.random((2, T)) < 0.5, rng.uniform(1.0, 1.2, (2, T)), rng.uniform(4.0, 4.9, (2, T)))
+    sc = sc.astype(np.float32)
+    budgets = [30000, 1234]
+    wl = dataclasses.replace(workloads.tiny_fp32(), name="sel_crowded", S=2, Hq=2, Hkv=2, lens=lens,
+                             budget_frac=0.0)
+    r = type("R", (), {})()
+    r.wl = wl
+    r.b = K.Batch(lens, 2, 2, 64, 1, "f32")
+    wl.budgets = lambda: np.array(budgets, dtype=np.int32)
+    wl.bud_off = lambda: np.concatenate([[0], np.cumsum(budgets)]).astype(np.int32)
+    _select_check(r, sc, K.KVE_TOPK, 1.0, 1.0, 0)
+
+
 # ---------------------------------------------------------------- compact / decode
 @pytest.mark.parametrize("name", ["tiny_fp32", "ragged3"])
 def test_compact_bitwise_and_decode(runs, name):
