@@ -21,7 +21,7 @@ from .attention import window_attention, row_positions  # noqa: F401
 from .score import perturbation_scores, group_scores, max_pool, score_workload  # noqa: F401
 from .select import (  # noqa: F401
     topk_select, proposal_log, proposal, expected_distinct, expected_samples_search,
-    inclusion_prob, gumbel_keys, sample_select, select_workload,
+    inclusion_prob, gumbel_keys, sample_select, select_workload, global_search, global_sample_select,
 )
 from .philox import philox4x64_10, uniform53  # noqa: F401
 from .decode import compact, decode_attention, decode_alg1_literal  # noqa: F401

@@ -27,6 +27,11 @@ Readings:
  * B >= n keeps everything with bias 0 and reports m = 0;
  * if no m <= 10^12 reaches the band (E(10^12) < B - 0.5), m = 10^12 and the
    status is "not converged" (the Remark after Algorithm 2).
+ * soft per-sequence budget ([PI] App. F.1): one m for all KV heads of a
+   sequence, found by Algorithm 2 on the heads' mean E (Eq. 33); head h then
+   keeps B_h = floor(E_h(m) + 0.5) entries (its expected number of distinct
+   draws, clamped to the sequence length and the caller's capacity), chosen
+   and weighted as above; a head that keeps every entry has bias 0.
 E(m) is evaluated as sum(-expm1(m * log1p(-pi))), the same closed form
 written to keep precision for tiny pi.
 
@@ -128,6 +133,65 @@ def sample_select(s: np.ndarray, B: int, tau: float, tau_w: float, seed: int, se
     q = inclusion_prob(pi[idx], m)
     bias = -np.log(q) / tau_w
     return idx, bias, m, status
+
+
+def global_search(pis, target: float, eps: float = 0.5):
+    """[PI] App. F.1, Eq. 33: Algorithm 2 with E(m) replaced by the mean over
+    the heads, (1/H) sum_h E_h(m), all heads sharing one m.  Returns (m, status)."""
+    Ls = [np.log1p(-pi) for pi in pis]
+    H = len(pis)
+    low, high = 0, ALPHA_MAX
+    while low <= high:
+        mid = (low + high) // 2
+        e = sum(float(np.sum(-np.expm1(float(mid) * L))) for L in Ls) / H
+        if abs(e - target) <= eps:
+            return mid, STATUS_OK
+        if e < target:
+            low = mid + 1
+        else:
+            high = mid - 1
+    return ALPHA_MAX, STATUS_NOCONV
+
+
+def global_kept_count(pi: np.ndarray, m, cap: int) -> int:
+    """Kept entries of one head under the shared m: its expected number of
+    distinct draws rounded half up, clamped to [0, min(n, cap)]."""
+    e = expected_distinct(pi, m)
+    return int(min(max(np.floor(e + 0.5), 0), min(pi.shape[0], cap)))
+
+
+def global_sample_select(scores_heads, B: int, cap: int, tau: float, tau_w: float, seed: int, seq: int,
+                         mix: float = 1.0, m=None):
+    """Sampling selection of one sequence under a per-sequence soft budget
+    ([PI] §7 and App. F.1): one m for all heads with mean expected kept count
+    B (Eq. 33); head h keeps its own expected count B_h (global_kept_count)
+    by the same Gumbel top-B_h and weights as sample_select.  With m given,
+    the search is skipped (any m in the band is a valid result of it).
+    Returns ([(idx, bias)] per head, [B_h], m, status)."""
+    scores_heads = [np.asarray(sc, dtype=np.float64) for sc in scores_heads]
+    n = scores_heads[0].shape[0]
+    H = len(scores_heads)
+    if B >= n:
+        return [(np.arange(n), np.zeros(n)) for _ in range(H)], [n] * H, 0, STATUS_OK
+    if B <= 0:
+        return [(np.zeros(0, dtype=np.int64), np.zeros(0)) for _ in range(H)], [0] * H, 0, STATUS_OK
+    pis = [proposal(sc, tau, mix) for sc in scores_heads]
+    status = STATUS_OK
+    if m is None:
+        m, status = global_search(pis, float(B))
+    out, kept = [], []
+    for h, (sc, pi) in enumerate(zip(scores_heads, pis)):
+        Bh = global_kept_count(pi, m, cap)
+        kept.append(Bh)
+        if Bh >= n:
+            out.append((np.arange(n), np.zeros(n)))
+            continue
+        lp = proposal_log(sc, tau) if mix >= 1.0 else np.log(pi)
+        kappa = gumbel_keys(lp, seed, seq, h)
+        idx = np.sort(np.lexsort((np.arange(n), -kappa))[:Bh])
+        q = inclusion_prob(pi[idx], m)
+        out.append((idx, -np.log(q) / tau_w))
+    return out, kept, m, status
 
 
 def select_workload(scores: np.ndarray, seq_off, budgets, mode: str, tau: float = 1.0,

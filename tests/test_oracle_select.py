@@ -236,3 +236,70 @@ def test_uniform_mixing_of_the_proposal():
     q1 = S.inclusion_prob(S.proposal(s, 0.7, 0.5), m1)
     lo = np.argsort(pi)[:50]
     assert np.all(q1[lo] > q0[lo])
+
+
+# ------------------------------------------------- soft per-sequence budget
+def _heads(seed, n=400, H=4):
+    rng = np.random.default_rng(seed)
+    # head 0 peaked, head H-1 nearly flat, others in between
+    return [rng.exponential(size=n) ** (6.0 - 1.5 * h) for h in range(H)]
+
+
+def test_global_search_is_algorithm2_on_the_head_mean():
+    from oracle import select as S
+    heads = _heads(1)
+    pis = [S.proposal(sc, 1.0) for sc in heads]
+    for B in (20, 60, 150):
+        m, st = S.global_search(pis, float(B))
+        mean_e = np.mean([S.expected_distinct(pi, m) for pi in pis])
+        assert st == S.STATUS_OK and abs(mean_e - B) <= 0.5
+        # brute force: the band of integer m is non-empty and contains m
+        ms = np.arange(max(0, m - 50), m + 51)
+        e = np.array([np.mean([S.expected_distinct(pi, k) for pi in pis]) for k in ms])
+        assert np.all(np.diff(e) >= 0) and np.all(np.diff(e) <= 1 + 1e-12)   # Eq. 27-31 per head
+    # one head: the per-head search
+    for B in (20, 60):
+        assert S.global_search([pis[2]], float(B)) == S.expected_samples_search(pis[2], float(B))
+
+
+def test_global_select_one_head_is_sample_select():
+    from oracle import select as S
+    sc = _heads(2)[1]
+    out, kept, m, st = S.global_sample_select([sc], 50, 400, 0.7, 1.3, 9, 2)
+    idx, bias, m1, st1 = S.sample_select(sc, 50, 0.7, 1.3, 9, 2, 0)
+    assert m == m1 and kept == [50]
+    assert np.array_equal(out[0][0], idx) and np.allclose(out[0][1], bias, rtol=1e-15, atol=0)
+
+
+def test_global_select_adapts_per_head_budget():
+    from oracle import select as S
+    heads = _heads(3)
+    H, B = len(heads), 60
+    out, kept, m, st = S.global_sample_select(heads, B, 400, 1.0, 1.0, 4, 0)
+    pis = [S.proposal(sc, 1.0) for sc in heads]
+    # each head keeps its rounded expected count; they average to B
+    for pi, k in zip(pis, kept):
+        assert abs(k - S.expected_distinct(pi, m)) <= 0.5
+    assert abs(np.mean(kept) - B) <= 0.5 + 0.5
+    assert kept[0] < kept[-1]                       # the peaked head keeps fewer
+    for (idx, bias), k, h in zip(out, kept, range(H)):
+        assert len(idx) == k and np.all(np.diff(idx) > 0)
+    # capacity clamps a head's count
+    out2, kept2, m2, _ = S.global_sample_select(heads, B, 70, 1.0, 1.0, 4, 0)
+    assert m2 == m and max(kept2) <= 70
+
+
+def test_global_expected_count_monte_carlo():
+    # draws with replacement under the shared m: the mean distinct count
+    # over heads matches the target B (Eq. 33 by linearity)
+    from oracle import select as S
+    heads = _heads(5, n=200, H=3)
+    pis = [S.proposal(sc, 1.0) for sc in heads]
+    B = 40
+    m, st = S.global_search(pis, float(B))
+    rng = np.random.default_rng(0)
+    trials = 400
+    tot = 0.0
+    for _ in range(trials):
+        tot += np.mean([len(np.unique(rng.choice(len(pi), size=int(m), p=pi))) for pi in pis])
+    assert abs(tot / trials - B) < 0.5 + 4 * 1.0 / np.sqrt(trials) * 3
