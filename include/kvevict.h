@@ -192,6 +192,35 @@ kve_status kvevict_select_ex(const kve_layout* L, const float* scores,
                              double* m_out, int32_t* status_out, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Sampling selection under a soft per-sequence budget ([PI] §7 and App. F.1,
+ * Eq. 33): one m for all KV heads of sequence s, found by the same search on
+ * the heads' mean expected distinct count (1/Hkv) sum_h E_h(m), with target
+ * B_s = bud_off[s+1] - bud_off[s]; head h then keeps
+ * kept[s][h] = floor(E_h(m) + 0.5) entries, clamped to [0, min(n_s, cap_s)],
+ * chosen as in KVE_SAMPLE (the kept[s][h] largest Gumbel keys, ascending)
+ * with bias -log(q_j) / tau_w, q_j = 1 - (1 - pi_j)^m (bias 0 for a head
+ * that keeps all n_s).  Peaked heads keep fewer entries than flat ones.
+ *   cap_off    device [S+1], cap_off_host host [S+1]: output slots per head
+ *              of each sequence, cap_s = cap_off[s+1] - cap_off[s] in
+ *              [0, n_s], and cap_s = n_s where B_s = n_s (KVE_EINVAL
+ *              otherwise)
+ *   idx, bias  [Hkv][cap_off[S]] out; slots r >= kept[s][h] hold idx -1 and
+ *              bias -inf (kvevict_compact turns them into zero rows with
+ *              bias -inf, which the decode weighs 0)
+ *   kept       [S][Hkv] int32 out, or NULL
+ *   m_out      [S][Hkv] float64 out, the same m in every head of a sequence
+ *   status_out [S][Hkv] as kvevict_select
+ *   ws         at least kvevict_select_workspace(L, bud_off_host, KVE_SAMPLE)
+ * Compact with the capacities in place of the budgets (bud_off := cap_off)
+ * to carry the padded slots into the cache. */
+kve_status kvevict_select_soft(const kve_layout* L, const float* scores,
+                               const int32_t* bud_off, const int32_t* bud_off_host,
+                               const int32_t* cap_off, const int32_t* cap_off_host,
+                               float tau, float tau_w, float mix, uint64_t seed,
+                               int32_t* idx, float* bias, int32_t* kept,
+                               double* m_out, int32_t* status_out, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- compact
  * Gather of the kept entries ([PI] §2 Eq. 3: evicted attention uses the
  * rows of K and V indexed by the kept set; [PI] §5: evicted entries are
@@ -202,8 +231,9 @@ kve_status kvevict_select_ex(const kve_layout* L, const float* scores,
  *   k, v      [Hkv][T][d] dtype;      idx, bias as produced by select
  *   cap_off   device [S+1] with cap_s = cap_off[s+1]-cap_off[s] >= B_s
  *   k_c, v_c  [Hkv][cap_off[S]][d] dtype out;  bias_c [Hkv][cap_off[S]] out
- * An idx entry outside [0, n_s) is skipped on the device (its slot is left
- * untouched). */
+ * An idx entry of -1 (an empty slot of kvevict_select_soft; any negative
+ * value) gives a zero row with bias -inf; one at or past n_s is skipped on
+ * the device (its slot is left untouched). */
 kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v,
                            const int32_t* bud_off, const int32_t* bud_off_host,
                            const int32_t* idx, const float* bias,

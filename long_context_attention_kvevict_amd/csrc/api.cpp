@@ -111,6 +111,38 @@ kve_status kvevict_select_ex(const kve_layout* L, const float* scores, const int
   return KVE_OK;
 }
 
+kve_status kvevict_select_soft(const kve_layout* L, const float* scores, const int32_t* bud_off,
+                               const int32_t* bud_off_host, const int32_t* cap_off, const int32_t* cap_off_host,
+                               float tau, float tau_w, float mix, uint64_t seed, int32_t* idx, float* bias,
+                               int32_t* kept, double* m_out, int32_t* status_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  kve::SelectGeom G;
+  std::string msg;
+  kve_status st = kve::plan_select(L, bud_off_host, KVE_SAMPLE, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_select_soft: " + msg);
+  if (!scores || !bud_off || !idx || !bias || !cap_off || !cap_off_host)
+    return set_err(KVE_EINVAL, "kvevict_select_soft: null pointer");
+  if (cap_off_host[0] != 0) return set_err(KVE_EINVAL, "kvevict_select_soft: cap_off[0] must be 0");
+  for (int s = 0; s < L->S; ++s) {
+    const int64_t C = static_cast<int64_t>(cap_off_host[s + 1]) - cap_off_host[s];
+    const int64_t n = static_cast<int64_t>(L->seq_off_host[s + 1]) - L->seq_off_host[s];
+    if (C < 0 || C > n) return set_err(KVE_EINVAL, "kvevict_select_soft: capacity cap_s must be in [0, n_s]");
+    const int64_t B = static_cast<int64_t>(bud_off_host[s + 1]) - bud_off_host[s];
+    if (B >= n && C != n) return set_err(KVE_EINVAL, "kvevict_select_soft: B_s = n_s needs cap_s = n_s");
+  }
+  if (!(tau > 0.f) || !(tau_w > 0.f)) return set_err(KVE_EINVAL, "kvevict_select_soft: tau and tau_w must be > 0");
+  if (!(mix >= 0.f && mix <= 1.f)) return set_err(KVE_EINVAL, "kvevict_select_soft: mix must be in [0, 1]");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_select_soft: workspace smaller than kvevict_select_workspace()");
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return set_err(KVE_EINVAL, "kvevict_select_soft: workspace must be 256-byte aligned");
+  const kve::SoftBudget soft{cap_off, cap_off_host[L->S], kept};
+  hipError_t e = kve::launch_select(G, scores, L->seq_off, bud_off, tau, tau_w, mix, seed, idx, bias, m_out,
+                                    status_out, ws, static_cast<hipStream_t>(stream), &soft);
+  if (e != hipSuccess) return hip_err(e, "kvevict_select_soft");
+  return KVE_OK;
+}
+
 kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_t* bud_off,
                           const int32_t* bud_off_host, int32_t mode, float tau, float tau_w, uint64_t seed,
                           int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,

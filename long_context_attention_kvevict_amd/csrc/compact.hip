@@ -26,9 +26,16 @@ __global__ __launch_bounds__(256) void compact_rows(const uint8_t* __restrict__ 
   const int q = static_cast<int>(item % chunks);
   if (r >= B) return;
   const int j = idx[h * totalB + bud_off[s] + r];
-  if (j < 0 || j >= seq_off[s + 1] - seq_off[s]) return;   // out-of-range index: slot untouched
-  const int64_t src_row = static_cast<int64_t>(h) * T + seq_off[s] + j;
   const int64_t dst_row = static_cast<int64_t>(h) * totalC + cap_off[s] + r;
+  if (j < 0) {   // empty slot (a soft budget's unused capacity): zero row, weight 0
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(k_c + dst_row * row_bytes + 16 * q) = z;
+    *reinterpret_cast<u32x4*>(v_c + dst_row * row_bytes + 16 * q) = z;
+    if (q == 0) bias_c[dst_row] = -INFINITY;
+    return;
+  }
+  if (j >= seq_off[s + 1] - seq_off[s]) return;   // out-of-range index: slot untouched
+  const int64_t src_row = static_cast<int64_t>(h) * T + seq_off[s] + j;
   const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src_row * row_bytes + 16 * q);
   const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src_row * row_bytes + 16 * q);
   *reinterpret_cast<u32x4*>(k_c + dst_row * row_bytes + 16 * q) = kv;

@@ -19,10 +19,17 @@ hipError_t launch_knorm(const ScoreGeom& G, const void* k, void* ws, hipStream_t
 hipError_t launch_pool(const ScoreGeom& G, const int32_t* seq_off, int pool_kernel, int pool_mode, int planes,
                        const void* ws, float* scores, hipStream_t st);
 
+// Soft per-sequence budget of the sampling selection: output slots per
+// sequence (capacities) and the per-head kept counts returned to the caller.
+struct SoftBudget {
+  const int32_t* cap_off;   // device [S+1]
+  int64_t total_cap;        // cap_off[S]
+  int32_t* kept;            // device [S*Hkv] out, or NULL
+};
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                         hipStream_t st);
+                         hipStream_t st, const SoftBudget* soft = nullptr);
 
 hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t totalB, int64_t totalC,
                           int maxB, const void* k, const void* v, const int32_t* seq_off,

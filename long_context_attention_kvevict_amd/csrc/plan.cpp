@@ -134,6 +134,7 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.off_grid = off; off = align256(off + (smp ? SH * g.nsmp * kSelGrid * sizeof(float) : 0));
   g.off_state = off; off = align256(off + (smp ? 2 * SH * kSelSearchBytes : 0));
   g.off_mvals = off; off = align256(off + (smp ? SH * sizeof(double) : 0));
+  g.off_bsh = off; off = align256(off + (smp ? SH * sizeof(int32_t) : 0));
   g.bytes = off;
   *G = g;
   return KVE_OK;

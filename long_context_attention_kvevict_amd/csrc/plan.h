@@ -59,6 +59,7 @@ struct SelectGeom {
   size_t off_grid;                 // sampling: float [S*Hkv][nchunk][kSelGrid]
   size_t off_state;                // sampling: [2][S*Hkv] search state (kSelSearchBytes each)
   size_t off_mvals;                // sampling: double [S*Hkv] final m
+  size_t off_bsh;                  // sampling: int [S*Hkv] kept count per head (soft budget)
   size_t bytes;
 };
 

@@ -114,10 +114,17 @@ struct GumbelKeys {
 // Geometry shared by the selection kernels.
 struct SelArgs {
   const int32_t* seq_off;
-  const int32_t* bud_off;
+  const int32_t* bud_off;   // per-sequence budget B_s (the target under a soft budget)
+  const int32_t* out_off;   // output slots of each sequence (bud_off, or the capacities)
+  const int32_t* bsh;       // soft budget: kept count of each (sequence, head), else NULL
   int S, Hkv, T, nchunk;
-  int64_t totalB;
+  int64_t totalB;           // out_off[S]
 };
+
+// Kept count of (sequence s, head h).
+__device__ __forceinline__ int sel_budget(const SelArgs& a, int s, int sh) {
+  return a.bsh ? a.bsh[sh] : a.bud_off[s + 1] - a.bud_off[s];
+}
 
 // Scans the 8 bins a thread holds (thread t owns bins 2047-8t .. 2040-8t, in
 // that order) across the block from the top bin down; returns the bin at
@@ -186,11 +193,11 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
-  const int B = a.bud_off[s + 1] - a.bud_off[s];
+  const int sh = s * a.Hkv + h;
+  const int B = sel_budget(a, s, sh);
   const int j0 = ch * SEL_CHUNK;
   if (B <= 0 || B >= n || j0 >= n) return;
   const int SH = a.S * a.Hkv;
-  const int sh = s * a.Hkv + h;
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
   const size_t row = static_cast<size_t>(h) * a.T + base;
@@ -237,11 +244,11 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_count(Src src, SelArgs a, con
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
-  const int B = a.bud_off[s + 1] - a.bud_off[s];
+  const int sh = s * a.Hkv + h;
+  const int B = sel_budget(a, s, sh);
   const int j0 = ch * SEL_CHUNK;
   if (B <= 0 || B >= n || j0 >= n) return;
   const int SH = a.S * a.Hkv;
-  const int sh = s * a.Hkv + h;
   __shared__ int lds[8];
   const size_t row = static_cast<size_t>(h) * a.T + base;
   K u[SEL_PER];
@@ -299,12 +306,20 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
-  const int B = a.bud_off[s + 1] - a.bud_off[s];
   const int j0 = ch * SEL_CHUNK;
   const int sh = s * a.Hkv + h;
-  if (B <= 0 || j0 >= n) return;
-  int32_t* out = idx + h * a.totalB + a.bud_off[s];
-  float* bout = bias + h * a.totalB + a.bud_off[s];
+  const int B = sel_budget(a, s, sh);
+  if (j0 >= n) return;   // the chunks cover [0, n), which holds every output slot
+  int32_t* out = idx + h * a.totalB + a.out_off[s];
+  float* bout = bias + h * a.totalB + a.out_off[s];
+  if (a.bsh) {   // soft budget: slots past this head's count are empty
+    const int cap = a.out_off[s + 1] - a.out_off[s];
+    for (int p = max(B, j0) + threadIdx.x; p < min(cap, j0 + SEL_CHUNK); p += SEL_THREADS) {
+      out[p] = -1;
+      bout[p] = -INFINITY;
+    }
+  }
+  if (B <= 0) return;
   if (B >= n) {   // everything kept, weight 1
     for (int i = threadIdx.x; i < SEL_CHUNK; i += SEL_THREADS) {
       const int j = j0 + i;
@@ -413,6 +428,9 @@ struct SmpArgs {
   double inv_tau;
   double mix;         // weight of the proposal against the uniform (1: unmixed)
   uint64_t seed;
+  int global;         // soft budget: one m per sequence for all its heads (Eq. 33)
+  int32_t* bsh;       // soft budget: [S*Hkv] kept count per head (written by smp_decide)
+  int32_t* kept_out;  // [S*Hkv] kept counts for the caller, or NULL
 };
 
 __device__ __forceinline__ double* part_of(const SmpArgs& A, int buf, int sh, int ch) {
@@ -426,6 +444,16 @@ __device__ double sum_part(const SmpArgs& A, int buf, int sh, int nch, int c, do
   double v = 0.0;
   for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v += part_of(A, buf, sh, i)[c];
   return block_sum_d(v, dl);
+}
+// The search's view of the chunk sums: the head's own, or under a soft
+// budget the mean over the sequence's heads (heads in order, then chunks).
+__device__ double search_sum(const SmpArgs& A, int buf, int sh, int nch, int c, double* dl) {
+  if (!A.global) return sum_part(A, buf, sh, nch, c, dl);
+  const int s0 = (sh / A.g.Hkv) * A.g.Hkv;
+  double v = 0.0;
+  for (int h = 0; h < A.g.Hkv; ++h)
+    for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v += part_of(A, buf, s0 + h, i)[c];
+  return block_sum_d(v, dl) / A.g.Hkv;
 }
 __device__ double max_part(const SmpArgs& A, int buf, int sh, int nch, int c, double* dl) {
   double v = -INFINITY;
@@ -560,11 +588,14 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
     const double target = static_cast<double>(B);
     int kx = kSelGrid;   // first grid point with E >= B
     double Ek = 0.0, Ep = 0.0;
+    const int h0 = A.global ? (sh / A.g.Hkv) * A.g.Hkv : sh;
+    const int nh = A.global ? A.g.Hkv : 1;
     for (int k = 0; k < kSelGrid; ++k) {
       double v = 0.0;
-      for (int i = threadIdx.x; i < nch; i += SEL_THREADS)
-        v += static_cast<double>(A.grid[(static_cast<size_t>(sh) * A.nsmp + i) * kSelGrid + k]);
-      v = block_sum_d(v, dl);
+      for (int hh = 0; hh < nh; ++hh)
+        for (int i = threadIdx.x; i < nch; i += SEL_THREADS)
+          v += static_cast<double>(A.grid[(static_cast<size_t>(h0 + hh) * A.nsmp + i) * kSelGrid + k]);
+      v = block_sum_d(v, dl) / nh;
       if (v >= target) { kx = k; Ek = v; break; }
       Ep = v;
     }
@@ -585,11 +616,11 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
   Search st = A.state[(step & 1) * SH + sh];
   if (st.done != 0.0) return st;
   const int pb = (step - 1) & 1;
-  const double E = sum_part(A, pb, sh, nch, 0, dl);
-  const double dE = sum_part(A, pb, sh, nch, 1, dl);
+  const double E = search_sum(A, pb, sh, nch, 0, dl);
+  const double dE = search_sum(A, pb, sh, nch, 1, dl);
   const double target = static_cast<double>(B);
   if (step == 1) {
-    const double Eh = sum_part(A, pb, sh, nch, 2, dl);
+    const double Eh = search_sum(A, pb, sh, nch, 2, dl);
     if (Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
       st.done = 2.0;
       return st;
@@ -660,8 +691,9 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) 
   __shared__ double dl[4];
   const Search st = search_state(A, steps, sh, nch, B, dl);
   if (ch == 0 && threadIdx.x == 0) A.state[((steps + 1) & 1) * SH + sh] = st;
-  if (st.done == 2.0) return;
-  const double m0 = fmin(floor(exp(st.u)), kAlphaMax - 1.0);
+  // out of reach: E at 10^12 (the second value), which sets a head's count
+  // under a soft budget
+  const double m0 = (st.done == 2.0) ? kAlphaMax - 1.0 : fmin(floor(exp(st.u)), kAlphaMax - 1.0);
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   double e0 = 0.0, e1 = 0.0;
 #pragma unroll 4
@@ -685,7 +717,10 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) 
 
 // Final m and status per (sequence, head): the first of m0, m0 + 1 in the
 // band; 10^12 and KVE_ENOCONV if the target is out of reach; the closer one
-// and KVE_ENOCONV if the search ran out of steps.  One workgroup per head.
+// and KVE_ENOCONV if the search ran out of steps.  Under a soft budget the
+// band is on the heads' mean (every head of a sequence decides the same m)
+// and each head keeps floor(E_h(m) + 0.5) entries, clamped to its sequence
+// length and capacity.  One workgroup per head.
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, double* m_out, int32_t* status_out) {
   const int h = blockIdx.x, s = blockIdx.y;
   const int sh = s * A.g.Hkv + h;
@@ -693,33 +728,46 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
   const bool active = smp_active(A, s, 0, &n, &B, &base);
   double m = 0.0;
   int status = KVE_OK;
+  int kept = (B >= n) ? n : max(B, 0);
   if (active) {
     const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
     const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
     __shared__ double dl[4];
     const Search st = A.state[((steps + 1) & 1) * SH + sh];
+    const double E0 = search_sum(A, steps & 1, sh, nch, 0, dl);
+    const double E1 = search_sum(A, steps & 1, sh, nch, 1, dl);
+    bool upper;   // m is m0 + 1 (or 10^12)
     if (st.done == 2.0) {
       m = kAlphaMax;
+      upper = true;
       status = KVE_ENOCONV;
     } else {
       const double target = static_cast<double>(B);
       const double m0 = fmin(floor(exp(st.u)), kAlphaMax - 1.0);
-      const double E0 = sum_part(A, steps & 1, sh, nch, 0, dl);
-      const double E1 = sum_part(A, steps & 1, sh, nch, 1, dl);
       if (fabs(E0 - target) <= 0.5) {
-        m = m0;
+        upper = false;
       } else if (fabs(E1 - target) <= 0.5) {
-        m = m0 + 1.0;
+        upper = true;
       } else {
-        m = (fabs(E1 - target) < fabs(E0 - target)) ? m0 + 1.0 : m0;
+        upper = fabs(E1 - target) < fabs(E0 - target);
         status = KVE_ENOCONV;
       }
+      m = upper ? m0 + 1.0 : m0;
     }
+    if (A.global) {
+      const double Eh = sum_part(A, steps & 1, sh, nch, upper ? 1 : 0, dl);
+      const int cap = A.g.out_off[s + 1] - A.g.out_off[s];
+      kept = static_cast<int>(fmin(fmax(floor(Eh + 0.5), 0.0), static_cast<double>(min(n, cap))));
+    }
+  } else if (A.global) {
+    kept = min(kept, A.g.out_off[s + 1] - A.g.out_off[s]);
   }
   if (threadIdx.x == 0) {
     A.mvals[sh] = m;
     if (m_out) m_out[sh] = m;
     if (status_out) status_out[sh] = status;
+    if (A.bsh) A.bsh[sh] = kept;
+    if (A.kept_out) A.kept_out[sh] = kept;
   }
 }
 
@@ -755,7 +803,7 @@ __global__ __launch_bounds__(256) void sel_init(int* __restrict__ p, int n, doub
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                         hipStream_t st) {
+                         hipStream_t st, const SoftBudget* soft) {
   char* wsb = static_cast<char*>(ws);
   int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
   int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
@@ -765,11 +813,13 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   SelArgs a;
   a.seq_off = seq_off;
   a.bud_off = bud_off;
+  a.out_off = soft ? soft->cap_off : bud_off;
+  a.bsh = soft ? reinterpret_cast<int32_t*>(wsb + G.off_bsh) : nullptr;
   a.S = G.S;
   a.Hkv = G.Hkv;
   a.T = G.T;
   a.nchunk = G.nchunk;
-  a.totalB = G.total_B;
+  a.totalB = soft ? soft->total_cap : G.total_B;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
   // histograms start at zero; cleared by a kernel, so that a captured graph
   // holds no memset node
@@ -794,6 +844,9 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.inv_tau = 1.0 / static_cast<double>(tau);
     A.mix = static_cast<double>(mix);
     A.seed = seed;
+    A.global = soft ? 1 : 0;
+    A.bsh = soft ? reinterpret_cast<int32_t*>(wsb + G.off_bsh) : nullptr;
+    A.kept_out = soft ? soft->kept : nullptr;
     const dim3 sgrid(G.nsmp, G.Hkv, G.S);
     hipLaunchKernelGGL(smp_logp, sgrid, dim3(SEL_THREADS), 0, st, A);
     hipLaunchKernelGGL(smp_keys, sgrid, dim3(SEL_THREADS), 0, st, A);

@@ -162,3 +162,19 @@ def test_select_ex_rejects_bad_mix():
         r = lib.kvevict_select_ex(ctypes.byref(lay), DUMMY, DUMMY, b.data_ptr(), 1, 0.5, 1.0, mix, 0, DUMMY,
                                   DUMMY, None, None, DUMMY, 16, None)
         assert r == st, mix
+
+
+def test_select_soft_rejects_bad_capacities():
+    lib = K.load_library()
+    lay, keep = _layout(S=2, lens=(50, 60))
+    b = torch.tensor([0, 5, 65], dtype=torch.int32)          # B_1 = n_1 = 60
+
+    def call(caps, ws_bytes=16, tau=0.5):
+        c = torch.tensor(caps, dtype=torch.int32)
+        return lib.kvevict_select_soft(ctypes.byref(lay), DUMMY, DUMMY, b.data_ptr(), DUMMY, c.data_ptr(), tau,
+                                       1.0, 1.0, 0, DUMMY, DUMMY, None, None, None, DUMMY, ws_bytes, None)
+    assert call([0, 51, 111]) == K.KVE_EINVAL                 # cap_0 > n_0
+    assert call([0, 20, 70]) == K.KVE_EINVAL                  # B_1 = n_1 but cap_1 < n_1
+    assert call([1, 20, 80]) == K.KVE_EINVAL                  # cap_off[0] != 0
+    assert call([0, 20, 80], tau=0.0) == K.KVE_EINVAL
+    assert call([0, 20, 80]) == K.KVE_EWORKSPACE              # valid up to the workspace

@@ -11,7 +11,8 @@ import torch
 import oracle
 from oracle.score import score_workload, max_pool_fast
 from oracle.proposals import group_proposal_scores, avg_pool, knorm_scores
-from oracle.select import select_workload, expected_distinct, proposal, inclusion_prob
+from oracle.select import select_workload, expected_distinct, proposal, inclusion_prob, global_sample_select
+from oracle.decode import decode_attention
 from long_context_attention_kvevict_amd import kvevict as K
 from long_context_attention_kvevict_amd import synth, workloads
 from tests.gpu_util import Run, check_scores, say, DECODE_ATOL
@@ -239,6 +240,81 @@ def test_select_sample_mixed_with_uniform(runs, mix):
     r = _run(runs, "ragged3")
     ref = _oracle_scores(r).astype(np.float32)
     _select_check(r, ref, K.KVE_SAMPLE, r.wl.tau, r.wl.tau_w, r.wl.hash_seed, mix=mix)
+
+
+def test_select_soft_budget_compact_and_decode():
+    # one m per sequence for all KV heads (Eq. 33): peaked heads keep fewer
+    # entries; unused slots compact to zero rows with bias -inf, which the
+    # decode weighs 0
+    from oracle.select import global_kept_count
+    rng = np.random.default_rng(11)
+    lens = [300, 2049, 5000, 9000, 700]
+    budgets = [30, 205, 500, 0, 700]
+    caps = [120, 600, 2000, 50, 700]
+    S, Hq, Hkv, d = len(lens), 8, 4, 128
+    T = sum(lens)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    coff = np.concatenate([[0], np.cumsum(caps)])
+    sig = np.array([3.0, 2.0, 1.2, 0.5])[:, None]
+    sc = np.exp(rng.standard_normal((Hkv, T)) * sig - 10.0).astype(np.float32)
+    tau, tau_w, seed = 0.8, 1.0, 99
+    b = K.Batch(lens, Hq, Hkv, d, 8, "bf16")
+    idx, bias, kept, m, st = b.select_soft(torch.from_numpy(sc).cuda(), budgets, caps, tau=tau, tau_w=tau_w,
+                                           seed=seed)
+    torch.cuda.synchronize()
+    idx, bias, kept, m, st = (x.cpu().numpy() for x in (idx, bias, kept, m, st))
+    for s_ in range(S):
+        n, B, cap = lens[s_], budgets[s_], caps[s_]
+        heads = [sc[h, off[s_]:off[s_ + 1]].astype(np.float64) for h in range(Hkv)]
+        assert np.all(m[s_] == m[s_, 0]) and np.all(st[s_] == 0), (s_, m[s_], st[s_])
+        ms = float(m[s_, 0])
+        if 0 < B < n:
+            pis = [proposal(x, tau) for x in heads]
+            mean_e = np.mean([expected_distinct(pi, ms) for pi in pis])
+            assert abs(mean_e - B) <= 0.5 + 1e-9 * n, (s_, ms, mean_e)
+            for h in range(Hkv):
+                e = expected_distinct(pis[h], ms)
+                if abs(e - np.floor(e) - 0.5) > 1e-9:
+                    assert kept[s_, h] == global_kept_count(pis[h], ms, cap), (s_, h, kept[s_, h], e)
+        out, rkept, _, _ = global_sample_select(heads, B, cap, tau, tau_w, seed, s_, m=ms if 0 < B < n else None)
+        assert list(kept[s_]) == rkept, (s_, list(kept[s_]), rkept)
+        for h in range(Hkv):
+            kk = kept[s_, h]
+            gi = idx[h, coff[s_]:coff[s_ + 1]]
+            gb = bias[h, coff[s_]:coff[s_ + 1]].astype(np.float64)
+            assert np.array_equal(gi[:kk], out[h][0]), (s_, h)
+            assert np.all(np.abs(gb[:kk] - out[h][1]) <= 1e-6 * (1 + np.abs(out[h][1]))), (s_, h)
+            assert np.all(gi[kk:] == -1) and np.all(np.isneginf(gb[kk:])), (s_, h)
+    if len(set(kept[2])) > 1:
+        assert kept[2, 0] < kept[2, 3]          # the peaked head keeps fewer than the flat one
+    # compaction with the capacities as budgets, then one decode over the caches
+    kb = synth.f32_to_bf16_bits(rng.standard_normal((Hkv, T, d)).astype(np.float32))
+    vb = synth.f32_to_bf16_bits(rng.standard_normal((Hkv, T, d)).astype(np.float32))
+    qb = synth.f32_to_bf16_bits(rng.standard_normal((S, Hq, d)).astype(np.float32))
+    k, v, q = (K.to_device(x, "bf16") for x in (kb, vb, qb))
+    k_c, v_c, b_c = b.compact(k, v, caps, torch.from_numpy(idx).cuda(), torch.from_numpy(bias).cuda(), caps)
+    cache_len = torch.tensor(caps, dtype=torch.int32, device="cuda")
+    o = b.decode(q, k_c, v_c, b_c, caps, cache_len, max(caps), 1 / np.sqrt(d))
+    torch.cuda.synchronize()
+    kc = k_c.view(torch.int16).cpu().numpy().view(np.uint16)
+    bc, o = b_c.cpu().numpy(), o.cpu().numpy()
+    kf, vf = synth.to_f64(kb, "bf16"), synth.to_f64(vb, "bf16")
+    rk = np.zeros((Hkv, coff[-1], d))
+    rv = np.zeros((Hkv, coff[-1], d))
+    rb = np.full((Hkv, coff[-1]), -np.inf)
+    for s_ in range(S):
+        for h in range(Hkv):
+            kk = kept[s_, h]
+            rows = off[s_] + idx[h, coff[s_]:coff[s_] + kk]
+            rk[h, coff[s_]:coff[s_] + kk] = kf[h, rows]
+            rv[h, coff[s_]:coff[s_] + kk] = vf[h, rows]
+            rb[h, coff[s_]:coff[s_] + kk] = bias[h, coff[s_]:coff[s_] + kk]
+    assert np.array_equal(synth.to_f64(kc, "bf16"), rk)
+    assert np.array_equal(bc.astype(np.float64), rb.astype(np.float32).astype(np.float64))
+    live = [s_ for s_ in range(S) if kept[s_].min() > 0]
+    ref = decode_attention(synth.to_f64(qb, "bf16"), rk, rv, rb, coff, caps, Hq, 1 / np.sqrt(d))
+    for s_ in live:
+        assert np.abs(o[s_] - ref[s_]).max() < DECODE_ATOL, s_
 
 
 @pytest.mark.parametrize("mode", [K.KVE_TOPK, K.KVE_SAMPLE])
