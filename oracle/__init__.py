@@ -22,6 +22,7 @@ from .score import perturbation_scores, group_scores, max_pool, score_workload  
 from .select import (  # noqa: F401
     topk_select, proposal_log, proposal, expected_distinct, expected_samples_search,
     inclusion_prob, gumbel_keys, sample_select, select_workload, global_search, global_sample_select,
+    draw_counts, literal_select,
 )
 from .philox import philox4x64_10, uniform53  # noqa: F401
 from .decode import compact, decode_attention, decode_alg1_literal  # noqa: F401

@@ -67,3 +67,12 @@ def uniform53(seed: int, s: int, h: int, j: np.ndarray) -> np.ndarray:
     x0, _, _, _ = philox4x64_10(j, np.uint64(h), np.uint64(s), np.uint64(0),
                                 np.uint64(seed), np.uint64(0))
     return ((x0 >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+
+
+def uniform53_draws(seed: int, s: int, h: int, k: np.ndarray) -> np.ndarray:
+    """u_k in (0, 1) for the with-replacement draws k of (sequence s, KV
+    head h): the same generator on the counter (k, h, s, 1)."""
+    k = np.asarray(k, dtype=np.uint64)
+    x0, _, _, _ = philox4x64_10(k, np.uint64(h), np.uint64(s), np.uint64(1),
+                                np.uint64(seed), np.uint64(0))
+    return ((x0 >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53

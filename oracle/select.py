@@ -27,6 +27,9 @@ Readings:
  * B >= n keeps everything with bias 0 and reports m = 0;
  * if no m <= 10^12 reaches the band (E(10^12) < B - 0.5), m = 10^12 and the
    status is "not converged" (the Remark after Algorithm 2).
+ * literal estimator ([PI] §4, Algorithm 1, Eq. 10): m draws with
+   replacement by inverse CDF, draw k from u_k on the Philox counter
+   (k, h, s, 1); kept = drawn at least once; bias log(c_j / (m pi_j)) / tau_w;
  * soft per-sequence budget ([PI] App. F.1): one m for all KV heads of a
    sequence, found by Algorithm 2 on the heads' mean E (Eq. 33); head h then
    keeps B_h = floor(E_h(m) + 0.5) entries (its expected number of distinct
@@ -44,7 +47,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .philox import uniform53
+from .philox import uniform53, uniform53_draws
 
 FLT_MIN = 2.0 ** -126
 ALPHA_MAX = 10 ** 12
@@ -192,6 +195,33 @@ def global_sample_select(scores_heads, B: int, cap: int, tau: float, tau_w: floa
         q = inclusion_prob(pi[idx], m)
         out.append((idx, -np.log(q) / tau_w))
     return out, kept, m, status
+
+
+def draw_counts(pi: np.ndarray, m: int, seed: int, seq: int, head: int) -> np.ndarray:
+    """[PI] §4: m draws with replacement from pi; draw k takes u_k (Philox
+    counter (k, head, seq, 1)) and lands on the first entry whose cumulative
+    probability exceeds u_k times the total.  Returns the counts c_j."""
+    cdf = np.cumsum(pi)
+    u = uniform53_draws(seed, seq, head, np.arange(int(m)))
+    j = np.minimum(np.searchsorted(cdf, u * cdf[-1], side="right"), pi.shape[0] - 1)
+    return np.bincount(j, minlength=pi.shape[0])
+
+
+def literal_select(s: np.ndarray, m: int, cap: int, tau: float, tau_w: float, seed: int, seq: int, head: int,
+                   mix: float = 1.0):
+    """[PI] §4-§6 as the pages state it: the kept set is the entries drawn at
+    least once in m draws with replacement from pi, and entry j carries the
+    tempered importance weight exp(log(c_j / (m pi_j)) / tau_w) (Algorithm 1
+    step 4 and Eq. 10), i.e. the logit bias log(c_j / (m pi_j)) / tau_w.
+    Returns (idx ascending, bias, J = number kept); at most cap are returned
+    (the lowest indices) when J > cap."""
+    pi = proposal(s, tau, mix)
+    c = draw_counts(pi, m, seed, seq, head)
+    idx = np.nonzero(c)[0]
+    J = idx.shape[0]
+    idx = idx[:cap]
+    bias = (np.log(c[idx].astype(np.float64)) - np.log(float(m)) - np.log(pi[idx])) / tau_w
+    return idx, bias, J
 
 
 def select_workload(scores: np.ndarray, seq_off, budgets, mode: str, tau: float = 1.0,

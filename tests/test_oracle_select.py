@@ -303,3 +303,59 @@ def test_global_expected_count_monte_carlo():
     for _ in range(trials):
         tot += np.mean([len(np.unique(rng.choice(len(pi), size=int(m), p=pi))) for pi in pis])
     assert abs(tot / trials - B) < 0.5 + 4 * 1.0 / np.sqrt(trials) * 3
+
+
+# ------------------------------------------------------- literal estimator
+def test_draw_counts_brute_force_and_frequencies():
+    from oracle import select as S
+    from oracle.philox import uniform53_draws
+    rng = np.random.default_rng(8)
+    pi = rng.exponential(size=7)
+    pi /= pi.sum()
+    m = 3000
+    c = S.draw_counts(pi, m, 5, 1, 2)
+    assert c.sum() == m
+    # brute force: walk the cumulative sum for each draw
+    u = uniform53_draws(5, 1, 2, np.arange(m))
+    ref = np.zeros(7, dtype=np.int64)
+    for x in u:
+        acc, t = 0.0, x * np.cumsum(pi)[-1]
+        for j in range(7):
+            acc = np.cumsum(pi)[j]
+            if acc > t:
+                ref[j] += 1
+                break
+        else:
+            ref[6] += 1
+    assert np.array_equal(c, ref)
+    # the frequencies follow pi (chi-square, 6 dof, far from the tail)
+    big = S.draw_counts(pi, 200000, 6, 0, 0)
+    chi2 = ((big - 200000 * pi) ** 2 / (200000 * pi)).sum()
+    assert chi2 < 30.0
+
+
+def test_literal_estimator_kept_count_and_unbiased_weights():
+    # E[J] = E(m) (Eq. 24) and, with tau_w = 1, sum_j c_j/(m pi_j) f_j is an
+    # unbiased estimate of sum_j f_j (importance sampling, Algorithm 1)
+    from oracle import select as S
+    rng = np.random.default_rng(9)
+    s = rng.exponential(size=60) ** 3
+    pi = S.proposal(s, 1.0)
+    f = rng.standard_normal(60)
+    m = 40
+    Js, est = [], []
+    for seed in range(600):
+        idx, bias, J = S.literal_select(s, m, 60, 1.0, 1.0, seed, 0, 0)
+        Js.append(J)
+        est.append(np.sum(np.exp(bias) * f[idx]))
+        assert np.allclose(np.exp(bias), S.draw_counts(pi, m, seed, 0, 0)[idx] / (m * pi[idx]), rtol=1e-12)
+    E = S.expected_distinct(pi, m)
+    assert abs(np.mean(Js) - E) < 4 * np.std(Js) / np.sqrt(len(Js)) + 1e-9
+    assert abs(np.mean(est) - f.sum()) < 4 * np.std(est) / np.sqrt(len(est))
+    # the weight temperature divides the log weight
+    i1, b1, _ = S.literal_select(s, m, 60, 1.0, 2.0, 3, 0, 0)
+    i2, b2, _ = S.literal_select(s, m, 60, 1.0, 1.0, 3, 0, 0)
+    assert np.array_equal(i1, i2) and np.allclose(b1, b2 / 2.0, rtol=1e-14)
+    # capacity keeps the lowest indices and reports the full count
+    i3, b3, J3 = S.literal_select(s, m, 5, 1.0, 1.0, 3, 0, 0)
+    assert J3 == len(i2) and np.array_equal(i3, i2[:5])
