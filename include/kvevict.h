@@ -221,6 +221,35 @@ kve_status kvevict_select_soft(const kve_layout* L, const float* scores,
                                double* m_out, int32_t* status_out, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* The literal estimator of [PI] §4 (keep the entries drawn at least once in
+ * m draws with replacement from the proposal) with the weights of Algorithm 1
+ * step 4 tempered as Eq. 10: per (sequence, head) with m = m_in[s][h] draws
+ * (a whole number in [0, 2^26]; otherwise status KVE_ENOTSUP and nothing
+ * kept), draw k takes u_k = ((x >> 11) + 0.5) 2^-53, x the first word of
+ * Philox-4x64-10(counter = (k, h, s, 1), key = (seed, 0)), and lands on the
+ * first entry whose cumulative proposal exceeds u_k times the total (the
+ * proposal as in KVE_SAMPLE: tempered by tau, mixed with the uniform when
+ * mix < 1).  Every entry drawn (count c_j > 0) is kept, ascending, with bias
+ * log(c_j / (m pi_j)) / tau_w.  The kept count is random (its mean is
+ * E(m) of Eq. 24; m can come from kvevict_select's m_out).
+ *   m_in       device [S][Hkv] float64
+ *   cap_off    device [S+1], cap_off_host host [S+1]: output slots per head
+ *              of each sequence, cap_s in [0, n_s]
+ *   idx, bias  [Hkv][cap_off[S]] out; the first min(kept, cap_s) slots hold
+ *              the lowest-index drawn entries, the rest -1 / -inf
+ *   kept       [S][Hkv] int32 out (may exceed cap_s), or NULL
+ *   status_out [S][Hkv] int32 out (KVE_OK or KVE_ENOTSUP), or NULL
+ *   ws         at least kvevict_select_literal_workspace() bytes
+ * n_s above 4194304 is KVE_ENOTSUP. */
+size_t kvevict_select_literal_workspace(const kve_layout* L);
+kve_status kvevict_select_literal(const kve_layout* L, const float* scores,
+                                  const double* m_in, const int32_t* cap_off,
+                                  const int32_t* cap_off_host, float tau,
+                                  float tau_w, float mix, uint64_t seed,
+                                  int32_t* idx, float* bias, int32_t* kept,
+                                  int32_t* status_out, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- compact
  * Gather of the kept entries ([PI] §2 Eq. 3: evicted attention uses the
  * rows of K and V indexed by the kept set; [PI] §5: evicted entries are

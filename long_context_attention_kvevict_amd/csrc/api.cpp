@@ -143,6 +143,41 @@ kve_status kvevict_select_soft(const kve_layout* L, const float* scores, const i
   return KVE_OK;
 }
 
+size_t kvevict_select_literal_workspace(const kve_layout* L) {
+  kve::LiteralGeom G;
+  std::string msg;
+  if (kve::plan_literal(L, &G, &msg) != KVE_OK) return 0;
+  return G.bytes;
+}
+
+kve_status kvevict_select_literal(const kve_layout* L, const float* scores, const double* m_in,
+                                  const int32_t* cap_off, const int32_t* cap_off_host, float tau, float tau_w,
+                                  float mix, uint64_t seed, int32_t* idx, float* bias, int32_t* kept,
+                                  int32_t* status_out, void* ws, size_t ws_bytes, void* stream) {
+  kve::LiteralGeom G;
+  std::string msg;
+  kve_status st = kve::plan_literal(L, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_select_literal: " + msg);
+  if (!scores || !m_in || !idx || !bias || !cap_off || !cap_off_host)
+    return set_err(KVE_EINVAL, "kvevict_select_literal: null pointer");
+  if (cap_off_host[0] != 0) return set_err(KVE_EINVAL, "kvevict_select_literal: cap_off[0] must be 0");
+  for (int s = 0; s < L->S; ++s) {
+    const int64_t C = static_cast<int64_t>(cap_off_host[s + 1]) - cap_off_host[s];
+    const int64_t n = static_cast<int64_t>(L->seq_off_host[s + 1]) - L->seq_off_host[s];
+    if (C < 0 || C > n) return set_err(KVE_EINVAL, "kvevict_select_literal: capacity cap_s must be in [0, n_s]");
+  }
+  if (!(tau > 0.f) || !(tau_w > 0.f)) return set_err(KVE_EINVAL, "kvevict_select_literal: tau and tau_w must be > 0");
+  if (!(mix >= 0.f && mix <= 1.f)) return set_err(KVE_EINVAL, "kvevict_select_literal: mix must be in [0, 1]");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_select_literal: workspace smaller than kvevict_select_literal_workspace()");
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return set_err(KVE_EINVAL, "kvevict_select_literal: workspace must be 256-byte aligned");
+  hipError_t e = kve::launch_literal(G, L->seq_off, scores, m_in, cap_off, cap_off_host[L->S], tau, tau_w, mix, seed,
+                                     idx, bias, kept, status_out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "kvevict_select_literal");
+  return KVE_OK;
+}
+
 kve_status kvevict_select(const kve_layout* L, const float* scores, const int32_t* bud_off,
                           const int32_t* bud_off_host, int32_t mode, float tau, float tau_w, uint64_t seed,
                           int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,

@@ -31,6 +31,11 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
                          hipStream_t st, const SoftBudget* soft = nullptr);
 
+hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const float* scores, const double* m_in,
+                          const int32_t* cap_off, int64_t total_cap, float tau, float tau_w, float mix,
+                          uint64_t seed, int32_t* idx, float* bias, int32_t* kept, int32_t* status, void* ws,
+                          hipStream_t st);
+
 hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t totalB, int64_t totalC,
                           int maxB, const void* k, const void* v, const int32_t* seq_off,
                           const int32_t* bud_off, const int32_t* idx, const float* bias,

@@ -140,6 +140,28 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   return KVE_OK;
 }
 
+kve_status plan_literal(const kve_layout* L, LiteralGeom* G, std::string* msg) {
+  int max_len = 0;
+  int64_t T = 0;
+  kve_status st = check_layout(L, msg, &max_len, &T);
+  if (st != KVE_OK) return st;
+  if (max_len > kLitMaxLen) return fail(msg, KVE_ENOTSUP, "literal draws support n_s <= 4194304");
+  LiteralGeom g{};
+  g.S = L->S; g.Hkv = L->Hkv; g.T = static_cast<int>(T);
+  g.nch = (max_len + kSmpChunk - 1) / kSmpChunk;
+  const size_t SH = static_cast<size_t>(g.S) * g.Hkv;
+  const size_t plane = static_cast<size_t>(g.Hkv) * g.T;
+  size_t off = 0;
+  g.off_part = off; off = align256(off + SH * g.nch * 2 * sizeof(double));
+  g.off_pi = off; off = align256(off + plane * sizeof(double));
+  g.off_cdf = off; off = align256(off + plane * sizeof(double));
+  g.off_cnt = off; off = align256(off + plane * sizeof(int32_t));
+  g.off_nz = off; off = align256(off + SH * g.nch * sizeof(int32_t));
+  g.bytes = off;
+  *G = g;
+  return KVE_OK;
+}
+
 kve_status check_compact(const kve_layout* L, const int32_t* bud_off_host, const int32_t* cap_off_host,
                          std::string* msg) {
   int max_len = 0;

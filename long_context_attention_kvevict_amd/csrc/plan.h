@@ -63,6 +63,17 @@ struct SelectGeom {
   size_t bytes;
 };
 
+// Literal estimator: draws per head, and the longest sequence (its chunk
+// offsets are held in LDS).
+constexpr int64_t kLitMaxDraws = int64_t(1) << 26;
+constexpr int kLitMaxLen = 4096 * kSmpChunk;
+
+struct LiteralGeom {
+  int S, Hkv, T, nch;
+  size_t off_part, off_pi, off_cdf, off_cnt, off_nz;
+  size_t bytes;
+};
+
 // Cache entries per decode workgroup for bf16 caches: 4 waves, each two
 // blocks of 32 entries.
 constexpr int kDecodeChunkBf16 = 256;
@@ -80,6 +91,7 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
                        std::string* msg);
 kve_status check_compact(const kve_layout* L, const int32_t* bud_off_host, const int32_t* cap_off_host,
                          std::string* msg);
+kve_status plan_literal(const kve_layout* L, LiteralGeom* G, std::string* msg);
 kve_status plan_decode(const kve_layout* L, const int32_t* cap_off_host, int max_cache_len,
                        DecodeGeom* G, std::string* msg);
 

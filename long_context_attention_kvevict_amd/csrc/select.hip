@@ -771,6 +771,307 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
   }
 }
 
+// ------------------------------------------------------- literal estimator
+// "A Probabilistic Interpretation of KV Cache Eviction", §4 (keep the
+// entries drawn at least once in m draws with replacement from pi),
+// Algorithm 1 step 4 and Eq. 10 (weight c_j / (m pi_j), tempered): draw k
+// takes u_k from Philox-4x64-10 on counter (k, h, s, 1) and lands on the
+// first entry whose cumulative probability exceeds u_k times the total.
+// The cumulative sums are chunk-local fp64 scans plus chunk offsets summed
+// in chunk order; counts are integer atomics, so results are reproducible.
+struct LitArgs {
+  const int32_t* seq_off;
+  const int32_t* cap_off;
+  const float* scores;
+  const double* m_in;     // [S*Hkv] draws per head
+  int S, Hkv, T, nch;     // nch: chunks of SMP_CHUNK keys per (sequence, head), maximum
+  int64_t total_cap;
+  double inv_tau, mix, inv_tau_w;
+  uint64_t seed;
+  double* part;           // [S*Hkv][nch][2] chunk max and sum of exp, then [.][.][0] chunk mass
+  double* pi;             // [Hkv][T] proposal
+  double* cdf;            // [Hkv][T] chunk-local inclusive cumulative proposal
+  int* cnt;               // [Hkv][T] draw counts (cleared first)
+  int* nz;                // [S*Hkv][nch] drawn entries per chunk
+  int32_t* idx;
+  float* bias;
+  int32_t* kept;          // [S*Hkv] or NULL
+  int32_t* status;        // [S*Hkv] or NULL
+};
+
+// Draws of one head: m when it is a whole number in [0, kLitMaxDraws], else -1.
+__device__ __forceinline__ int64_t lit_draws(const LitArgs& A, int sh) {
+  const double m = A.m_in[sh];
+  if (!(m >= 0.0 && m <= static_cast<double>(kLitMaxDraws)) || m != floor(m)) return -1;
+  return static_cast<int64_t>(m);
+}
+
+// Inclusive scan of doubles over a 256-thread block in a fixed order; lds: 4.
+__device__ __forceinline__ double block_incl_scan256_d(double v, double* lds, double* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) lds[wave] = v;
+  __syncthreads();
+  double off = 0.0;
+  for (int wv = 0; wv < wave; ++wv) off += lds[wv];
+  *total = ((lds[0] + lds[1]) + lds[2]) + lds[3];
+  __syncthreads();
+  return v + off;
+}
+
+// Pass 1: log pi~ and the chunk's max and sum of exp (the normaliser in parts).
+__global__ __launch_bounds__(SEL_THREADS) void lit_logp(LitArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = A.seq_off[s], n = A.seq_off[s + 1] - base;
+  if (ch * SMP_CHUNK >= n) return;
+  const int sh = s * A.Hkv + h;
+  const size_t row = static_cast<size_t>(h) * A.T + base;
+  __shared__ double dl[4];
+  double x[SMP_PER];
+  double mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + SMP_PER * threadIdx.x + i;
+    x[i] = -INFINITY;
+    if (j < n) {
+      x[i] = log(static_cast<double>(fmaxf(A.scores[row + j], 1.17549435e-38f))) * A.inv_tau;
+      A.pi[row + j] = x[i];
+      mx = fmax(mx, x[i]);
+    }
+  }
+  mx = block_max_d(mx, dl);
+  double z = 0.0;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) z += exp(x[i] - mx);
+  z = block_sum_d(z, dl);
+  if (threadIdx.x == 0) {
+    double* p = A.part + (static_cast<size_t>(sh) * A.nch + ch) * 2;
+    p[0] = mx;
+    p[1] = z;
+  }
+}
+
+// Pass 2: pi (mixed with the uniform when mix < 1), its chunk-local
+// cumulative sums and the chunk's mass.
+__global__ __launch_bounds__(SEL_THREADS) void lit_cdf(LitArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = A.seq_off[s], n = A.seq_off[s + 1] - base;
+  if (ch * SMP_CHUNK >= n) return;
+  const int sh = s * A.Hkv + h;
+  const int nc = (n + SMP_CHUNK - 1) / SMP_CHUNK;
+  const size_t row = static_cast<size_t>(h) * A.T + base;
+  __shared__ double dl[4];
+  const double* pp = A.part + static_cast<size_t>(sh) * A.nch * 2;
+  double M = -INFINITY;
+  for (int i = threadIdx.x; i < nc; i += SEL_THREADS) M = fmax(M, pp[2 * i]);
+  M = block_max_d(M, dl);
+  double zp = 0.0;
+  for (int i = threadIdx.x; i < nc; i += SEL_THREADS) zp += pp[2 * i + 1] * exp(pp[2 * i] - M);
+  const double lse = M + log(block_sum_d(zp, dl));
+  double v[SMP_PER], acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + SMP_PER * threadIdx.x + i;
+    double p = 0.0;
+    if (j < n) {
+      p = exp(A.pi[row + j] - lse);
+      if (A.mix < 1.0) p = A.mix * p + (1.0 - A.mix) / n;
+    }
+    v[i] = p;
+    acc += p;
+  }
+  double tot;
+  double run = block_incl_scan256_d(acc, dl, &tot) - acc;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + SMP_PER * threadIdx.x + i;
+    run += v[i];
+    if (j < n) {
+      A.pi[row + j] = v[i];
+      A.cdf[row + j] = run;
+    }
+  }
+}
+
+// Pass 3: the draws.  Every workgroup of a head forms the chunk offsets
+// (masses summed in chunk order, from each chunk's last cumulative value),
+// then its threads take draws k = t, t + stride, ... below m.
+constexpr int LIT_DRAW_WGS = 256;    // workgroups per head
+constexpr int LIT_MAX_CHUNKS = 4096; // chunk offsets held in LDS (n <= 4M)
+__global__ __launch_bounds__(SEL_THREADS) void lit_draw(LitArgs A) {
+  const int h = blockIdx.y, s = blockIdx.z;
+  const int base = A.seq_off[s], n = A.seq_off[s + 1] - base;
+  const int sh = s * A.Hkv + h;
+  const int64_t m = lit_draws(A, sh);
+  if (n <= 0 || m <= 0) return;
+  const int nc = (n + SMP_CHUNK - 1) / SMP_CHUNK;
+  const size_t row = static_cast<size_t>(h) * A.T + base;
+  __shared__ double off[LIT_MAX_CHUNKS + 1];
+  __shared__ double dl[4];
+  // exclusive offsets of the chunks: a block scan per 256 chunks, carried in order
+  double carry = 0.0;
+  for (int c0 = 0; c0 < nc; c0 += SEL_THREADS) {
+    const int c = c0 + threadIdx.x;
+    const double mass = (c < nc) ? A.cdf[row + min(n, (c + 1) * SMP_CHUNK) - 1] : 0.0;
+    double tot;
+    const double incl = block_incl_scan256_d(mass, dl, &tot);
+    if (c < nc) off[c] = carry + (incl - mass);
+    carry += tot;
+  }
+  if (threadIdx.x == 0) off[nc] = carry;
+  __syncthreads();
+  const double total = off[nc];
+  const int64_t stride = static_cast<int64_t>(LIT_DRAW_WGS) * SEL_THREADS;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * SEL_THREADS + threadIdx.x; k < m; k += stride) {
+    const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(k), static_cast<uint64_t>(h),
+                                        static_cast<uint64_t>(s), 1ull, A.seed, 0ull);
+    const double t = ((static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53) * total;
+    // first chunk whose end exceeds t
+    int lo = 0, hi = nc - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid + 1] > t) hi = mid; else lo = mid + 1;
+    }
+    // first entry of that chunk whose cumulative value exceeds t
+    const int j0 = lo * SMP_CHUNK;
+    int a = j0, b = min(n, j0 + SMP_CHUNK) - 1;
+    while (a < b) {
+      const int mid = (a + b) >> 1;
+      if (off[lo] + A.cdf[row + mid] > t) b = mid; else a = mid + 1;
+    }
+    atomicAdd(&A.cnt[row + a], 1);
+  }
+}
+
+// Pass 4: entries drawn at least once, per chunk.
+__global__ __launch_bounds__(SEL_THREADS) void lit_count(LitArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = A.seq_off[s], n = A.seq_off[s + 1] - base;
+  if (ch * SMP_CHUNK >= n) return;
+  const int sh = s * A.Hkv + h;
+  const size_t row = static_cast<size_t>(h) * A.T + base;
+  __shared__ int lds[8];
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + SMP_PER * threadIdx.x + i;
+    c += (j < n) && A.cnt[row + j] > 0;
+  }
+  int tot;
+  block_incl_scan256(c, lds, &tot);
+  if (threadIdx.x == 0) A.nz[static_cast<size_t>(sh) * A.nch + ch] = tot;
+}
+
+// Pass 5: ordered write of the drawn entries into the head's capacity slots,
+// bias log(c_j / (m pi_j)) / tau_w; slots past the drawn count get -1 and
+// -inf; the chunk that holds the last entry reports the count and status.
+__global__ __launch_bounds__(SEL_THREADS) void lit_write(LitArgs A) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = A.seq_off[s], n = A.seq_off[s + 1] - base;
+  if (ch * SMP_CHUNK >= n) return;
+  const int sh = s * A.Hkv + h;
+  const int nc = (n + SMP_CHUNK - 1) / SMP_CHUNK;
+  const int cap = A.cap_off[s + 1] - A.cap_off[s];
+  const int64_t m = lit_draws(A, sh);
+  const size_t row = static_cast<size_t>(h) * A.T + base;
+  int32_t* out = A.idx + h * A.total_cap + A.cap_off[s];
+  float* bout = A.bias + h * A.total_cap + A.cap_off[s];
+  __shared__ int lds[8];
+  int before = 0, all = 0;
+  for (int c = threadIdx.x; c < nc; c += SEL_THREADS) {
+    const int v = A.nz[static_cast<size_t>(sh) * A.nch + c];
+    before += (c < ch) ? v : 0;
+    all += v;
+  }
+  int tot;
+  block_incl_scan256(before, lds, &tot);
+  before = tot;
+  block_incl_scan256(all, lds, &tot);
+  const int J = (m > 0) ? tot : 0;
+  int take = 0;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + SMP_PER * threadIdx.x + i;
+    take += (m > 0) && (j < n) && A.cnt[row + j] > 0;
+  }
+  int pos = before + block_incl_scan256(take, lds, &tot) - take;
+  if (m > 0) {
+    const double lm = log(static_cast<double>(m));
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int j = ch * SMP_CHUNK + SMP_PER * threadIdx.x + i;
+      if (j < n && A.cnt[row + j] > 0) {
+        if (pos < cap) {
+          out[pos] = j;
+          bout[pos] = static_cast<float>((log(static_cast<double>(A.cnt[row + j])) - lm - log(A.pi[row + j])) *
+                                         A.inv_tau_w);
+        }
+        ++pos;
+      }
+    }
+  }
+  for (int p = max(J, ch * SMP_CHUNK) + threadIdx.x; p < min(cap, (ch + 1) * SMP_CHUNK); p += SEL_THREADS) {
+    out[p] = -1;
+    bout[p] = -INFINITY;
+  }
+  if (ch == nc - 1 && threadIdx.x == 0) {
+    if (A.kept) A.kept[sh] = J;
+    if (A.status) A.status[sh] = (m < 0) ? KVE_ENOTSUP : KVE_OK;
+  }
+}
+
+__global__ __launch_bounds__(256) void lit_clear(int* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0;
+}
+
+hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const float* scores, const double* m_in,
+                          const int32_t* cap_off, int64_t total_cap, float tau, float tau_w, float mix,
+                          uint64_t seed, int32_t* idx, float* bias, int32_t* kept, int32_t* status, void* ws,
+                          hipStream_t st) {
+  char* wsb = static_cast<char*>(ws);
+  LitArgs A;
+  A.seq_off = seq_off;
+  A.cap_off = cap_off;
+  A.scores = scores;
+  A.m_in = m_in;
+  A.S = G.S;
+  A.Hkv = G.Hkv;
+  A.T = G.T;
+  A.nch = G.nch;
+  A.total_cap = total_cap;
+  A.inv_tau = 1.0 / static_cast<double>(tau);
+  A.mix = static_cast<double>(mix);
+  A.inv_tau_w = 1.0 / static_cast<double>(tau_w);
+  A.seed = seed;
+  A.part = reinterpret_cast<double*>(wsb + G.off_part);
+  A.pi = reinterpret_cast<double*>(wsb + G.off_pi);
+  A.cdf = reinterpret_cast<double*>(wsb + G.off_cdf);
+  A.cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
+  A.nz = reinterpret_cast<int*>(wsb + G.off_nz);
+  A.idx = idx;
+  A.bias = bias;
+  A.kept = kept;
+  A.status = status;
+  const int64_t ncnt = static_cast<int64_t>(G.Hkv) * G.T;
+  const dim3 grid(G.nch, G.Hkv, G.S);
+  stage_begin(ST_SELECT, st);
+  hipLaunchKernelGGL(lit_clear, dim3(static_cast<unsigned>((ncnt + 255) / 256 < 4096 ? (ncnt + 255) / 256 : 4096)), dim3(256), 0, st,
+                     A.cnt, ncnt);
+  hipLaunchKernelGGL(lit_logp, grid, dim3(SEL_THREADS), 0, st, A);
+  hipLaunchKernelGGL(lit_cdf, grid, dim3(SEL_THREADS), 0, st, A);
+  hipLaunchKernelGGL(lit_draw, dim3(LIT_DRAW_WGS, G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A);
+  hipLaunchKernelGGL(lit_count, grid, dim3(SEL_THREADS), 0, st, A);
+  hipLaunchKernelGGL(lit_write, grid, dim3(SEL_THREADS), 0, st, A);
+  stage_end(ST_SELECT, st);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------- launch
 template <class Src, class Bias>
 static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,

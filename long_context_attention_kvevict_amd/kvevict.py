@@ -22,7 +22,7 @@ POOL_MODES = {"max": 0, "avg": 1}
 
 EXPORTS = [
     "kvevict_score_workspace", "kvevict_score", "kvevict_score_ex", "kvevict_select_workspace", "kvevict_select",
-    "kvevict_select_ex", "kvevict_select_soft",
+    "kvevict_select_ex", "kvevict_select_soft", "kvevict_select_literal_workspace", "kvevict_select_literal",
     "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
@@ -74,6 +74,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_select_ex.restype = I32
     lib.kvevict_select_soft.argtypes = [LP, P, P, P, P, P, F32, F32, F32, U64, P, P, P, P, P, P, SZ, P]
     lib.kvevict_select_soft.restype = I32
+    lib.kvevict_select_literal_workspace.argtypes = [LP]
+    lib.kvevict_select_literal_workspace.restype = SZ
+    lib.kvevict_select_literal.argtypes = [LP, P, P, P, P, F32, F32, F32, U64, P, P, P, P, P, SZ, P]
+    lib.kvevict_select_literal.restype = I32
     lib.kvevict_compact.argtypes = [LP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.kvevict_compact.restype = I32
     lib.kvevict_decode_workspace.argtypes = [LP, I32]
@@ -252,6 +256,28 @@ class Batch:
                                              _stream(stream)))
         self._soft = (bud_host, bud_dev, cap_host, cap_dev)   # alive until the stream has used them
         return idx[:, :C], bias[:, :C], kept, m, status
+
+    def select_literal(self, scores, m, caps, tau: float = 1.0, tau_w: float = 1.0, seed: int = 0,
+                       mix: float = 1.0, stream=None):
+        """m draws with replacement per (sequence, head) (float64 [S][Hkv] on
+        the device, e.g. select()'s m); keeps the drawn entries.  Returns
+        (idx, bias, kept, status) with idx/bias [Hkv][sum caps]."""
+        cap_host, cap_dev = self.offsets(caps, self.device)
+        lay = ctypes.byref(self.layout)
+        nbytes = self._lib.kvevict_select_literal_workspace(lay) or 256
+        ws = self._workspace("literal", nbytes)
+        C = int(cap_host[-1])
+        m = m.to(device=self.device, dtype=torch.float64).contiguous()
+        idx = torch.empty((self.Hkv, max(C, 1)), dtype=torch.int32, device=self.device)
+        bias = torch.empty((self.Hkv, max(C, 1)), dtype=torch.float32, device=self.device)
+        kept = torch.empty((self.S, self.Hkv), dtype=torch.int32, device=self.device)
+        status = torch.empty((self.S, self.Hkv), dtype=torch.int32, device=self.device)
+        _check(self._lib.kvevict_select_literal(lay, _ptr(scores), _ptr(m), _ptr(cap_dev), cap_host.data_ptr(),
+                                                float(tau), float(tau_w), float(mix),
+                                                ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(idx), _ptr(bias),
+                                                _ptr(kept), _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
+        self._lit = (cap_host, cap_dev, m)
+        return idx[:, :C], bias[:, :C], kept, status
 
     def compact(self, k, v, budgets, idx, bias, caps, out=None, stream=None, bud_offsets=None,
                 cap_offsets=None):

@@ -178,3 +178,20 @@ def test_select_soft_rejects_bad_capacities():
     assert call([1, 20, 80]) == K.KVE_EINVAL                  # cap_off[0] != 0
     assert call([0, 20, 80], tau=0.0) == K.KVE_EINVAL
     assert call([0, 20, 80]) == K.KVE_EWORKSPACE              # valid up to the workspace
+
+
+def test_select_literal_rejects_bad_arguments():
+    lib = K.load_library()
+    lay, keep = _layout(S=2, lens=(50, 60))
+    assert lib.kvevict_select_literal_workspace(ctypes.byref(lay)) > 0
+
+    def call(caps, ws_bytes=16, tau=0.5, mix=1.0, m=DUMMY):
+        c = torch.tensor(caps, dtype=torch.int32)
+        return lib.kvevict_select_literal(ctypes.byref(lay), DUMMY, m, DUMMY, c.data_ptr(), tau, 1.0, mix, 0,
+                                          DUMMY, DUMMY, None, None, DUMMY, ws_bytes, None)
+    assert call([0, 51, 60]) == K.KVE_EINVAL                  # cap_0 > n_0
+    assert call([2, 20, 60]) == K.KVE_EINVAL                  # cap_off[0] != 0
+    assert call([0, 20, 60], tau=0.0) == K.KVE_EINVAL
+    assert call([0, 20, 60], mix=2.0) == K.KVE_EINVAL
+    assert call([0, 20, 60], m=None) == K.KVE_EINVAL
+    assert call([0, 20, 60]) == K.KVE_EWORKSPACE

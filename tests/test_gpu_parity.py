@@ -257,7 +257,7 @@ def test_select_soft_budget_compact_and_decode():
     coff = np.concatenate([[0], np.cumsum(caps)])
     sig = np.array([3.0, 2.0, 1.2, 0.5])[:, None]
     sc = np.exp(rng.standard_normal((Hkv, T)) * sig - 10.0).astype(np.float32)
-    tau, tau_w, seed = 0.8, 1.0, 99
+    tau, tau_w, seed = float(np.float32(0.8)), 1.0, 99   # fp32 parameters, as the library takes them
     b = K.Batch(lens, Hq, Hkv, d, 8, "bf16")
     idx, bias, kept, m, st = b.select_soft(torch.from_numpy(sc).cuda(), budgets, caps, tau=tau, tau_w=tau_w,
                                            seed=seed)
@@ -315,6 +315,45 @@ def test_select_soft_budget_compact_and_decode():
     ref = decode_attention(synth.to_f64(qb, "bf16"), rk, rv, rb, coff, caps, Hq, 1 / np.sqrt(d))
     for s_ in live:
         assert np.abs(o[s_] - ref[s_]).max() < DECODE_ATOL, s_
+
+
+@pytest.mark.parametrize("mix", [1.0, 0.5])
+def test_select_literal_draws(mix):
+    # m draws with replacement; the drawn entries are kept with bias
+    # log(c / (m pi)) / tau_w; counts are integers, so selections are exact
+    from oracle.select import literal_select
+    rng = np.random.default_rng(21)
+    lens = [300, 2049, 5000]
+    caps = [300, 400, 5000]
+    S, Hkv = len(lens), 2
+    T = sum(lens)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    coff = np.concatenate([[0], np.cumsum(caps)])
+    sc = np.exp(rng.standard_normal((Hkv, T)) * np.array([[2.5], [1.0]]) - 9.0).astype(np.float32)
+    m = np.array([[500.0, 3000.0], [2000.0, 0.0], [150000.0, 7.0e7]])   # 7e7 > 2^26: not drawn
+    # the library takes fp32 temperatures: the oracle gets the same values
+    tau, tau_w, seed = float(np.float32(0.7)), 1.5, 4242
+    b = K.Batch(lens, 4, Hkv, 128, 8, "bf16")
+    idx, bias, kept, st = b.select_literal(torch.from_numpy(sc).cuda(), torch.from_numpy(m), caps, tau=tau,
+                                           tau_w=tau_w, seed=seed, mix=mix)
+    torch.cuda.synchronize()
+    idx, bias, kept, st = (x.cpu().numpy() for x in (idx, bias, kept, st))
+    for s_ in range(S):
+        for h in range(Hkv):
+            gi = idx[h, coff[s_]:coff[s_ + 1]]
+            gb = bias[h, coff[s_]:coff[s_ + 1]].astype(np.float64)
+            if m[s_, h] > 2 ** 26:
+                assert st[s_, h] == K.KVE_ENOTSUP and kept[s_, h] == 0 and np.all(gi == -1)
+                continue
+            assert st[s_, h] == K.KVE_OK
+            ri, rb, J = literal_select(sc[h, off[s_]:off[s_ + 1]].astype(np.float64), int(m[s_, h]), caps[s_], tau,
+                                       tau_w, seed, s_, h, mix)
+            k = len(ri)
+            assert kept[s_, h] == J, (s_, h, kept[s_, h], J)
+            bad = np.nonzero(gi[:k] != ri)[0]
+            assert bad.size == 0, (s_, h, bad[:8], gi[bad[:8]], ri[bad[:8]], gi[:12], ri[:12])
+            assert np.all(np.abs(gb[:k] - rb) <= 1e-5 * (1 + np.abs(rb))), (s_, h)
+            assert np.all(gi[k:] == -1) and np.all(np.isneginf(gb[k:]))
 
 
 @pytest.mark.parametrize("mode", [K.KVE_TOPK, K.KVE_SAMPLE])
