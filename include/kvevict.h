@@ -15,6 +15,8 @@
  *   [PI] "A Probabilistic Interpretation of KV Cache Eviction"
  *   [DK] "DropKV: Decoupling Residual-Output Perturbation for Near-Optimal
  *        KV-Cache Eviction"
+ *   [IT] "Information-Theoretic Token Eviction and KV-Cache Compression for
+ *        Memory-Bounded Long-Context LLM Inference"
  *
  * Conventions shared by every call
  * --------------------------------
@@ -249,6 +251,32 @@ kve_status kvevict_select_literal(const kve_layout* L, const float* scores,
                                   int32_t* idx, float* bias, int32_t* kept,
                                   int32_t* status_out, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Partition-conserving merge ([IT] §4.1): for every (sequence, KV head),
+ * each evicted entry e (a position of the sequence not in the kept list)
+ * is assigned to the kept entry r* with the largest key cosine similarity
+ * cos(k_e, k_r) (the lowest list position on ties; a zero key has
+ * similarity 0), and merged into it when cos > tau_merge.  The kept entry's
+ * bias then grows by log(1 + number merged into it) (its multiplicity m_r,
+ * starting at 1); keys and values stay as they are, so an exact duplicate
+ * leaves the softmax normaliser unchanged.  Similarities are bf16 products
+ * accumulated in fp32 (MFMA); the argmax and the threshold are decided on
+ * those fp32 values.
+ *   k          [Hkv][T][128] bf16 (the full cache the selection read)
+ *   bud_off    device [S+1], bud_off_host host [S+1]: the kept counts
+ *   idx        [Hkv][bud_off[S]] kept positions as written by select
+ *   bias       [Hkv][bud_off[S]] float32, updated in place
+ *   merged     [Hkv][bud_off[S]] int32 out (entries merged into each), or NULL
+ *   target     [Hkv][T] int32 out: list position each entry merged into,
+ *              -1 if none (kept entries: -1), or NULL
+ *   ws         at least kvevict_merge_workspace() bytes
+ * bf16 with d = 128 only (KVE_ENOTSUP otherwise).  The result does not
+ * depend on workgroup order (integer counts, 64-bit atomic maximum). */
+size_t kvevict_merge_workspace(const kve_layout* L, const int32_t* bud_off_host);
+kve_status kvevict_merge(const kve_layout* L, const void* k, const int32_t* bud_off,
+                         const int32_t* bud_off_host, const int32_t* idx,
+                         float tau_merge, float* bias, int32_t* merged,
+                         int32_t* target, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- compact
  * Gather of the kept entries ([PI] §2 Eq. 3: evicted attention uses the

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libkvevict.so")
 
-SOURCES = ["api.cpp", "plan.cpp", "timing.cpp", "score_bf16.hip", "score_f32.hip", "pool.hip", "knorm.hip", "select.hip",
+SOURCES = ["api.cpp", "plan.cpp", "timing.cpp", "score_bf16.hip", "score_f32.hip", "pool.hip", "knorm.hip", "merge.hip", "select.hip",
            "compact.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -143,6 +143,32 @@ kve_status kvevict_select_soft(const kve_layout* L, const float* scores, const i
   return KVE_OK;
 }
 
+size_t kvevict_merge_workspace(const kve_layout* L, const int32_t* bud_off_host) {
+  kve::MergeGeom G;
+  std::string msg;
+  if (kve::plan_merge(L, bud_off_host, &G, &msg) != KVE_OK) return 0;
+  return G.bytes;
+}
+
+kve_status kvevict_merge(const kve_layout* L, const void* k, const int32_t* bud_off, const int32_t* bud_off_host,
+                         const int32_t* idx, float tau_merge, float* bias, int32_t* merged, int32_t* target,
+                         void* ws, size_t ws_bytes, void* stream) {
+  kve::MergeGeom G;
+  std::string msg;
+  kve_status st = kve::plan_merge(L, bud_off_host, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_merge: " + msg);
+  if (!k || !bud_off || !idx || !bias) return set_err(KVE_EINVAL, "kvevict_merge: null pointer");
+  if (!(tau_merge >= -1.f && tau_merge <= 1.f)) return set_err(KVE_EINVAL, "kvevict_merge: tau_merge must be in [-1, 1]");
+  if (reinterpret_cast<uintptr_t>(k) & 15) return set_err(KVE_EINVAL, "kvevict_merge: k must be 16-byte aligned");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_merge: workspace smaller than kvevict_merge_workspace()");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_err(KVE_EINVAL, "kvevict_merge: workspace must be 256-byte aligned");
+  hipError_t e = kve::launch_merge(G, k, L->seq_off, bud_off, idx, tau_merge, bias, merged, target, ws,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "kvevict_merge");
+  return KVE_OK;
+}
+
 size_t kvevict_select_literal_workspace(const kve_layout* L) {
   kve::LiteralGeom G;
   std::string msg;

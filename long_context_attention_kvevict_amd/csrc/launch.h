@@ -36,6 +36,10 @@ hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const fl
                           uint64_t seed, int32_t* idx, float* bias, int32_t* kept, int32_t* status, void* ws,
                           hipStream_t st);
 
+hipError_t launch_merge(const MergeGeom& G, const void* k, const int32_t* seq_off, const int32_t* bud_off,
+                        const int32_t* idx, float tau, float* bias, int32_t* merged, int32_t* target, void* ws,
+                        hipStream_t st);
+
 hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t totalB, int64_t totalC,
                           int maxB, const void* k, const void* v, const int32_t* seq_off,
                           const int32_t* bud_off, const int32_t* idx, const float* bias,

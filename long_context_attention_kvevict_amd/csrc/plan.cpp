@@ -140,6 +140,35 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   return KVE_OK;
 }
 
+kve_status plan_merge(const kve_layout* L, const int32_t* bud_off_host, MergeGeom* G, std::string* msg) {
+  int max_len = 0;
+  int64_t T = 0;
+  kve_status st = check_layout(L, msg, &max_len, &T);
+  if (st != KVE_OK) return st;
+  if (L->dtype != KVE_BF16 || L->d != 128) return fail(msg, KVE_ENOTSUP, "the merge supports bf16 keys with d = 128");
+  if (!bud_off_host) return fail(msg, KVE_EINVAL, "bud_off_host is NULL");
+  if (bud_off_host[0] != 0) return fail(msg, KVE_EINVAL, "bud_off[0] must be 0");
+  int maxB = 0;
+  for (int s = 0; s < L->S; ++s) {
+    const int64_t B = static_cast<int64_t>(bud_off_host[s + 1]) - bud_off_host[s];
+    const int64_t n = static_cast<int64_t>(L->seq_off_host[s + 1]) - L->seq_off_host[s];
+    if (B < 0 || B > n) return fail(msg, KVE_EINVAL, "budget B_s must be in [0, n_s]");
+    maxB = B > maxB ? static_cast<int>(B) : maxB;
+  }
+  MergeGeom g{};
+  g.S = L->S; g.Hkv = L->Hkv; g.T = static_cast<int>(T); g.max_len = max_len; g.maxB = maxB;
+  g.totalB = bud_off_host[L->S];
+  const size_t plane = static_cast<size_t>(g.Hkv) * g.T;
+  size_t off = 0;
+  g.off_invn = off; off = align256(off + plane * sizeof(float));
+  g.off_flag = off; off = align256(off + plane * sizeof(int32_t));
+  g.off_best = off; off = align256(off + plane * sizeof(uint64_t));
+  g.off_cnt = off; off = align256(off + static_cast<size_t>(g.Hkv) * g.totalB * sizeof(int32_t));
+  g.bytes = off;
+  *G = g;
+  return KVE_OK;
+}
+
 kve_status plan_literal(const kve_layout* L, LiteralGeom* G, std::string* msg) {
   int max_len = 0;
   int64_t T = 0;

@@ -74,6 +74,13 @@ struct LiteralGeom {
   size_t bytes;
 };
 
+struct MergeGeom {
+  int S, Hkv, T, max_len, maxB;
+  int64_t totalB;
+  size_t off_invn, off_flag, off_best, off_cnt;
+  size_t bytes;
+};
+
 // Cache entries per decode workgroup for bf16 caches: 4 waves, each two
 // blocks of 32 entries.
 constexpr int kDecodeChunkBf16 = 256;
@@ -91,6 +98,7 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
                        std::string* msg);
 kve_status check_compact(const kve_layout* L, const int32_t* bud_off_host, const int32_t* cap_off_host,
                          std::string* msg);
+kve_status plan_merge(const kve_layout* L, const int32_t* bud_off_host, MergeGeom* G, std::string* msg);
 kve_status plan_literal(const kve_layout* L, LiteralGeom* G, std::string* msg);
 kve_status plan_decode(const kve_layout* L, const int32_t* cap_off_host, int max_cache_len,
                        DecodeGeom* G, std::string* msg);

@@ -23,6 +23,7 @@ POOL_MODES = {"max": 0, "avg": 1}
 EXPORTS = [
     "kvevict_score_workspace", "kvevict_score", "kvevict_score_ex", "kvevict_select_workspace", "kvevict_select",
     "kvevict_select_ex", "kvevict_select_soft", "kvevict_select_literal_workspace", "kvevict_select_literal",
+    "kvevict_merge_workspace", "kvevict_merge",
     "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
@@ -78,6 +79,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_select_literal_workspace.restype = SZ
     lib.kvevict_select_literal.argtypes = [LP, P, P, P, P, F32, F32, F32, U64, P, P, P, P, P, SZ, P]
     lib.kvevict_select_literal.restype = I32
+    lib.kvevict_merge_workspace.argtypes = [LP, P]
+    lib.kvevict_merge_workspace.restype = SZ
+    lib.kvevict_merge.argtypes = [LP, P, P, P, P, F32, P, P, P, P, SZ, P]
+    lib.kvevict_merge.restype = I32
     lib.kvevict_compact.argtypes = [LP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.kvevict_compact.restype = I32
     lib.kvevict_decode_workspace.argtypes = [LP, I32]
@@ -278,6 +283,22 @@ class Batch:
                                                 _ptr(kept), _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
         self._lit = (cap_host, cap_dev, m)
         return idx[:, :C], bias[:, :C], kept, status
+
+    def merge(self, k, budgets, idx, bias, tau_merge: float, want_target: bool = False, stream=None):
+        """Partition-conserving merge: bias (updated in place) of the kept
+        entries grows by log(1 + merged).  Returns (bias, merged, target)."""
+        bud_host, bud_dev = self.offsets(budgets, self.device)
+        lay = ctypes.byref(self.layout)
+        nbytes = self._lib.kvevict_merge_workspace(lay, bud_host.data_ptr()) or 256
+        ws = self._workspace("merge", nbytes)
+        idx = idx.contiguous()
+        merged = torch.empty_like(idx)
+        target = torch.empty((self.Hkv, self.T), dtype=torch.int32, device=self.device) if want_target else None
+        _check(self._lib.kvevict_merge(lay, _ptr(k), _ptr(bud_dev), bud_host.data_ptr(), _ptr(idx), float(tau_merge),
+                                       _ptr(bias), _ptr(merged), _ptr(target) if target is not None else None,
+                                       _ptr(ws), ws.numel(), _stream(stream)))
+        self._mrg = (bud_host, bud_dev)
+        return bias, merged, target
 
     def compact(self, k, v, budgets, idx, bias, caps, out=None, stream=None, bud_offsets=None,
                 cap_offsets=None):

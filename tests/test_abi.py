@@ -195,3 +195,20 @@ def test_select_literal_rejects_bad_arguments():
     assert call([0, 20, 60], mix=2.0) == K.KVE_EINVAL
     assert call([0, 20, 60], m=None) == K.KVE_EINVAL
     assert call([0, 20, 60]) == K.KVE_EWORKSPACE
+
+
+def test_merge_rejects_bad_arguments():
+    lib = K.load_library()
+    lay, keep = _layout(S=2, lens=(50, 60))
+    b = torch.tensor([0, 5, 10], dtype=torch.int32)
+    assert lib.kvevict_merge_workspace(ctypes.byref(lay), b.data_ptr()) > 0
+
+    def call(lay_, bud, tau=0.5, ws_bytes=16, k=DUMMY):
+        return lib.kvevict_merge(ctypes.byref(lay_), k, DUMMY, bud.data_ptr(), DUMMY, tau, DUMMY, None, None, DUMMY,
+                                 ws_bytes, None)
+    assert call(lay, torch.tensor([0, 51, 60], dtype=torch.int32)) == K.KVE_EINVAL   # B_0 > n_0
+    assert call(lay, b, tau=1.5) == K.KVE_EINVAL
+    assert call(lay, b, k=DUMMY + 8) == K.KVE_EINVAL                                  # misaligned
+    assert call(lay, b) == K.KVE_EWORKSPACE
+    lay32, keep32 = _layout(S=2, lens=(50, 60), dtype=K.KVE_F32)
+    assert call(lay32, b) == K.KVE_ENOTSUP

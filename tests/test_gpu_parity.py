@@ -402,6 +402,70 @@ def test_select_topk_crowded_threshold_bin(case):
     _select_check(r, sc, K.KVE_TOPK, 1.0, 1.0, 0)
 
 
+# ---------------------------------------------------------------- merge
+def _merge_case(seed, lens, Hkv, frac, dup):
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    k = rng.standard_normal((Hkv, T, 128)).astype(np.float32)
+    budgets = [max(1, int(frac * n)) for n in lens]
+    idx = np.zeros((Hkv, sum(budgets)), dtype=np.int32)
+    boff = np.concatenate([[0], np.cumsum(budgets)])
+    for h in range(Hkv):
+        for s_, n in enumerate(lens):
+            kept = np.sort(rng.choice(n, budgets[s_], replace=False))
+            idx[h, boff[s_]:boff[s_ + 1]] = kept
+            if dup:   # a share of the evicted entries duplicate a kept key exactly
+                ev = np.setdiff1d(np.arange(n), kept)
+                cp = rng.choice(ev, int(dup * ev.size), replace=False)
+                k[h, off[s_] + cp] = k[h, off[s_] + rng.choice(kept, cp.size)]
+    kb = synth.f32_to_bf16_bits(k)
+    bias = rng.standard_normal((Hkv, sum(budgets))).astype(np.float32) * 0.1
+    return kb, idx, bias, budgets, off, boff
+
+
+@pytest.mark.parametrize("dup,tau", [(0.3, 0.9), (0.0, 0.25)])
+def test_merge_against_oracle(dup, tau):
+    from oracle.merge import merge_targets, cosine
+    lens = [700, 5000, 9000]
+    Hkv = 2
+    kb, idx, bias0, budgets, off, boff = _merge_case(3, lens, Hkv, 0.08, dup)
+    b = K.Batch(lens, 4, Hkv, 128, 8, "bf16")
+    k = K.to_device(kb, "bf16")
+    bias_d = torch.from_numpy(bias0.copy()).cuda()
+    _, merged, target = b.merge(k, budgets, torch.from_numpy(idx).cuda(), bias_d, tau, want_target=True)
+    torch.cuda.synchronize()
+    bias1, merged, target = bias_d.cpu().numpy(), merged.cpu().numpy(), target.cpu().numpy()
+    kf = synth.to_f64(kb, "bf16")
+    checked = 0
+    for h in range(Hkv):
+        for s_ in range(len(lens)):
+            kept = idx[h, boff[s_]:boff[s_ + 1]].astype(np.int64)
+            ks = kf[h, off[s_]:off[s_ + 1]]
+            rt, rc = merge_targets(ks, kept, tau)
+            gt = target[h, off[s_]:off[s_ + 1]]
+            ev = np.setdiff1d(np.arange(lens[s_]), kept)
+            assert np.all(gt[kept] == -1)
+            c = cosine(ks[ev], ks[kept])
+            srt = np.sort(c, axis=1)
+            gap = srt[:, -1] - srt[:, -2]
+            clear = (gap > 1e-4) & (np.abs(srt[:, -1] - tau) > 1e-4)
+            assert np.array_equal(gt[ev][clear], rt[ev][clear]), (h, s_)
+            amb = ~clear              # near-ties: any target within 1e-4 of the best is right
+            for i in np.nonzero(amb)[0]:
+                g = gt[ev][i]
+                if g >= 0:
+                    assert c[i, g] >= srt[i, -1] - 1e-4 and c[i, g] > tau - 1e-4
+                else:
+                    assert srt[i, -1] <= tau + 1e-4
+            checked += int(clear.sum())
+            cnt = np.bincount(gt[gt >= 0], minlength=kept.size)
+            assert np.array_equal(merged[h, boff[s_]:boff[s_ + 1]], cnt)
+            want = (bias0[h, boff[s_]:boff[s_ + 1]].astype(np.float64) + np.log1p(cnt)).astype(np.float32)
+            assert np.allclose(bias1[h, boff[s_]:boff[s_ + 1]], want, rtol=1e-6, atol=1e-6)
+    assert checked > 0.9 * sum(n - B for n, B in zip(lens, budgets)) * Hkv
+
+
 # ---------------------------------------------------------------- compact / decode
 @pytest.mark.parametrize("name", ["tiny_fp32", "ragged3"])
 def test_compact_bitwise_and_decode(runs, name):
