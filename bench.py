@@ -55,6 +55,7 @@ def _parse():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph instead of eager launches")
     ap.add_argument("--no-decode", action="store_true", help="skip the SNIS decode measurement")
+    ap.add_argument("--no-merge", action="store_true", help="skip the partition-conserving merge measurement")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (5 times) and exit")
@@ -163,6 +164,33 @@ def _cpu_baseline(wl, data, heads):
                       f"{dt:.1f} s, scaled by {wl.Hkv / heads:g}",
             "value_1thread": wl.T / (dt1 * wl.Hkv),
             "sample_1thread": f"1 of {wl.Hkv} KV heads, BLAS limited to 1 thread, {dt1:.1f} s, scaled by {wl.Hkv}"}
+
+
+def _merge_leg(b, k, budgets, idx, bias, wl, tau_merge=0.9, reps=10):
+    """kvevict_merge over the step's kept set: every evicted key against
+    every kept key of its head (cosine), on bf16 MFMAs.  Algorithmic work:
+    2 d B (n - B) flops per (sequence, KV head)."""
+    import torch
+    flops = sum(2.0 * wl.d * int(B) * (int(n) - int(B)) for n, B in zip(wl.lens, budgets)) * wl.Hkv
+    biases = [bias.clone() for _ in range(reps + 3)]
+    torch.cuda.synchronize()
+    for i in range(3):
+        b.merge(k, budgets, idx, biases[i], tau_merge)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(reps):
+        _, merged, _ = b.merge(k, budgets, idx, biases[3 + i], tau_merge)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    achieved = flops / (ms * 1e-3) / 1e12
+    evicted = sum(int(n) - int(B) for n, B in zip(wl.lens, budgets)) * wl.Hkv
+    return {"workload": wl.name, "tau_merge": tau_merge, "ms": ms,
+            "merged_fraction_of_evicted": float(merged.sum().item()) / max(evicted, 1),
+            "roofline": {"bound": "mfma", "kernel": "mrg_sim (with its prep/apply launches)",
+                         "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
+                         "traffic": None, "algorithmic_flops": flops}}
 
 
 def _decode_leg(steps_max, want_cpu):
@@ -424,6 +452,9 @@ def main():
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = _cpu_baseline(wl, data, max(1, min(args.cpu_heads, wl.Hkv)))
     del data
+    if not args.no_merge:
+        print("# merge leg", file=sys.stderr, flush=True)
+        result["merge"] = _merge_leg(b, k, budgets, sel[0][:, :total_B], sel[1][:, :total_B], wl)
     if not args.no_decode:
         print("# decode leg", file=sys.stderr, flush=True)
         result["decode"] = _decode_leg(args.decode_steps, not args.no_cpu_baseline)

@@ -7,20 +7,21 @@
 // normaliser unchanged.
 //
 // The similarity search is a dense contraction (evicted keys x retained
-// keys x d), done on bf16 MFMAs with fp32 accumulation: a workgroup holds 128
-// retained keys in registers (the A operand, 32 per wave) and streams 4096
-// tokens of the sequence in 32-token tiles (the B operand); per token it
-// keeps the best similarity over its 128 keys and folds it into the token's
-// running best with one 64-bit atomic max of (ordered similarity, inverted
-// position), which makes the result independent of workgroup order.
+// keys x d), done on bf16 MFMAs with fp32 accumulation: a workgroup holds 512
+// retained keys in registers (the A operands, 128 per wave) and streams 2048
+// tokens of the sequence through a 3-stage LDS ring of 32-token tiles (the B
+// operand); per token it keeps the best similarity over its 512 keys and
+// folds it into the token's running best with one 64-bit atomic max of
+// (ordered similarity, inverted position), which makes the result
+// independent of workgroup order.
 #include "common.h"
 #include "launch.h"
 
 namespace kve {
 
 constexpr int MRG_THREADS = 256;
-constexpr int MRG_KB = 128;      // retained keys per workgroup
-constexpr int MRG_TCH = 4096;    // tokens per workgroup
+constexpr int MRG_KB = 512;      // retained keys per workgroup (128 per wave)
+constexpr int MRG_TCH = 2048;    // tokens per workgroup
 constexpr int MRG_TT = 32;       // tokens per tile
 constexpr int MRG_D = 128;
 
@@ -87,72 +88,129 @@ __global__ __launch_bounds__(256) void mrg_mark(MergeArgs a) {
   if (j >= 0 && j < n) a.flag[static_cast<size_t>(h) * a.T + a.seq_off[s] + j] = 1;
 }
 
-// Best retained key per token over one block of 128 retained keys.
-__global__ __launch_bounds__(MRG_THREADS) void mrg_sim(MergeArgs a) {
+// ------------------------------------------------------------ LDS ring
+// Token tiles reach LDS through direct global->LDS loads issued from inline
+// assembly, with explicit waits, so the compiler's in-order wait counting
+// does not drain the ring before every read.  Row k of a tile stores its
+// 16-byte chunk c at c ^ (k & 15): the 16 rows a group of lanes reads at one
+// chunk land on distinct banks.
+__device__ __forceinline__ void mrg_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "s"(lds_base) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void mrg_wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+__device__ __forceinline__ void mrg_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ uint32_t mrg_lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+template <typename T>
+__device__ __forceinline__ void mrg_settle(const T& x) { asm volatile("" :: "v"(x)); }
+
+constexpr int MRG_NST = 3;                      // ring stages
+constexpr int MRG_TILE_BYTES = MRG_TT * MRG_D * 2;
+
+// Best retained key per token: a workgroup holds MRG_KB retained keys (each
+// wave 4 blocks of 32 as MFMA A operands) and streams MRG_TCH tokens.
+__global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
   const int kb = blockIdx.x % a.nkb, tc = blockIdx.x / a.nkb;
   const int h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
   const int B = a.bud_off[s + 1] - a.bud_off[s];
   if (kb * MRG_KB >= B || tc * MRG_TCH >= n || B >= n) return;
-  __shared__ float kinv[MRG_KB];
+  __shared__ __align__(1024) char ring[MRG_NST * MRG_TILE_BYTES];
+  __shared__ __align__(16) float kinv[MRG_KB];   // 1 / ||k_r|| (0 for a missing key)
+  __shared__ __align__(16) float kpen[MRG_KB];   // 0, or -inf for a missing key
   __shared__ float wbest[4][MRG_TT];
   __shared__ int wrow[4][MRG_TT];
+  __shared__ float cbest[MRG_TCH];
+  __shared__ int crow[MRG_TCH];
+  __shared__ float tinvs[MRG_TCH];   // 1 / ||k|| of the range's tokens (no global loads in the loop)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
   const size_t hrow = static_cast<size_t>(h) * a.T + base;
   const int32_t* kid = a.idx + h * a.totalB + a.bud_off[s];
-  // A operand: retained key kb*128 + 32*wave + col
-  const int rr = kb * MRG_KB + 32 * wave + col;
-  const bool rr_ok = rr < B;
-  int jr = rr_ok ? kid[rr] : 0;
-  if (jr < 0 || jr >= n) jr = 0;
-  bf16x8 qa[MRG_D / 16];
+  // A operands: retained keys kb*MRG_KB + 128*wave + 32*rb + col
+  bf16x8 qa[4][MRG_D / 16];
 #pragma unroll
-  for (int kk = 0; kk < MRG_D / 16; ++kk) {
-    u32x4 t = {0u, 0u, 0u, 0u};
-    if (rr_ok) t = *reinterpret_cast<const u32x4*>(a.k + (hrow + jr) * MRG_D + 16 * kk + 8 * hl);
-    qa[kk] = as_bf16x8(t);
+  for (int rb = 0; rb < 4; ++rb) {
+    const int rr = kb * MRG_KB + 128 * wave + 32 * rb + col;
+    int jr = rr < B ? kid[rr] : -1;
+    const bool ok = jr >= 0 && jr < n;
+#pragma unroll
+    for (int kk = 0; kk < MRG_D / 16; ++kk) {
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (ok) t = *reinterpret_cast<const u32x4*>(a.k + (hrow + jr) * MRG_D + 16 * kk + 8 * hl);
+      qa[rb][kk] = as_bf16x8(t);
+    }
   }
-  if (tid < MRG_KB) {
-    const int r2 = kb * MRG_KB + tid;
-    int j2 = r2 < B ? kid[r2] : -1;
-    kinv[tid] = (j2 >= 0 && j2 < n) ? a.invn[hrow + j2] : -1.f;   // -1 marks a missing key
+  for (int i = tid; i < MRG_KB; i += MRG_THREADS) {
+    const int r2 = kb * MRG_KB + i;
+    const int j2 = r2 < B ? kid[r2] : -1;
+    const bool ok = j2 >= 0 && j2 < n;
+    kinv[i] = ok ? a.invn[hrow + j2] : 0.f;
+    kpen[i] = ok ? 0.f : -INFINITY;
   }
+  const int t_begin = tc * MRG_TCH;
+  const int t_end = min(n, t_begin + MRG_TCH);
+  for (int i = tid; i < MRG_TCH; i += MRG_THREADS) tinvs[i] = (t_begin + i < t_end) ? a.invn[hrow + t_begin + i] : 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < MRG_D / 16; ++kk) mrg_settle(qa[rb][kk]);
   __syncthreads();
-  float kiv[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) kiv[r] = kinv[32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3)];
 
-  const int t1 = min(n, (tc + 1) * MRG_TCH);
-  for (int t0 = tc * MRG_TCH; t0 < t1; t0 += MRG_TT) {
-    const int tok = t0 + col;
-    const int tk = tok < n ? tok : n - 1;
+  // ring fill: tile rows 8*wave .. 8*wave+7 (two 1 KiB blocks per wave)
+  const int ntile = (t_end - t_begin + MRG_TT - 1) / MRG_TT;
+  const uint32_t ring0 = mrg_lds_addr(ring);
+  auto issue = [&](int t) {   // tile t of the range into stage t % MRG_NST (rows past the end repeat the last)
+    const uint32_t sb = ring0 + static_cast<uint32_t>((t % MRG_NST) * MRG_TILE_BYTES);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = 2 * wave + i;                  // rows 4*blk .. 4*blk+3
+      const int row = 4 * blk + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);        // logical chunk for this physical slot
+      const int tok = min(t_begin + t * MRG_TT + row, n - 1);
+      mrg_dma16(a.k + (hrow + tok) * MRG_D + 8 * c, __builtin_amdgcn_readfirstlane(sb + blk * 1024));
+    }
+  };
+  issue(0);
+  issue(1);
+  for (int t = 0; t < ntile; ++t) {
+    mrg_wait_vm<2>();          // this wave's part of tile t has landed (tile t+1 may be in flight)
+    mrg_lds_barrier();         // every wave's part; stage (t+2) % 3 is free
+    issue(t + 2);
+    const char* tl = ring + (t % MRG_NST) * MRG_TILE_BYTES;
     bf16x8 kop[MRG_D / 16];
 #pragma unroll
     for (int kk = 0; kk < MRG_D / 16; ++kk)
-      kop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.k + (hrow + tk) * MRG_D + 16 * kk + 8 * hl));
-    const float tinv = a.invn[hrow + tk];
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < MRG_D / 16; ++kk) acc = mfma32(qa[kk], kop[kk], acc);
-    // best over this lane's 16 retained rows, in increasing row order
-    float bv = -INFINITY;
+      kop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(tl + col * (MRG_D * 2) + (((2 * kk + hl) ^ (col & 15)) << 4)));
+    float bv = -INFINITY;   // best of k_r.k_t / ||k_r|| (the token's 1 / ||k_t|| is applied after)
     int br = 0x7fffffff;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float kv = kiv[r];
-      const float c = (kv >= 0.f) ? acc[r] * kv * tinv : -INFINITY;
-      const int row = 32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3);
-      if (c > bv || (c == bv && row < br)) { bv = c; br = row; }
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < MRG_D / 16; ++kk) acc = mfma32(qa[rb][kk], kop[kk], acc);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {   // rows in increasing order: strict > keeps the lowest
+        const int row0 = 128 * wave + 32 * rb + 8 * q4 + 4 * hl;
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&kinv[row0]);
+        const f32x4 pn = *reinterpret_cast<const f32x4*>(&kpen[row0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float c = fmaf(acc[4 * q4 + e], kv[e], pn[e]);   // missing keys: 0 * 0 - inf
+          if (c > bv) { bv = c; br = row0 + e; }
+        }
+      }
     }
     const float ov = __shfl_xor(bv, 32, 64);
     const int orow = __shfl_xor(br, 32, 64);
     if (ov > bv || (ov == bv && orow < br)) { bv = ov; br = orow; }
     if (hl == 0) {
-      wbest[wave][col] = bv;
+      wbest[wave][col] = (bv == -INFINITY) ? bv : bv * tinvs[t * MRG_TT + col];   // the cosine
       wrow[wave][col] = br;
     }
-    __syncthreads();
+    mrg_lds_barrier();
     if (tid < MRG_TT) {
       float v = wbest[0][tid];
       int rw = wrow[0][tid];
@@ -161,15 +219,22 @@ __global__ __launch_bounds__(MRG_THREADS) void mrg_sim(MergeArgs a) {
         const float v2 = wbest[w][tid];
         if (v2 > v) { v = v2; rw = wrow[w][tid]; }   // later waves hold higher rows: ties stay
       }
-      const int t = t0 + tid;
-      if (t < n && v > -INFINITY && a.flag[hrow + t] == 0) {
-        const uint32_t pos = static_cast<uint32_t>(kb * MRG_KB + rw);
-        const unsigned long long key =
-            (static_cast<unsigned long long>(mrg_order(v)) << 32) | static_cast<unsigned long long>(0xffffffffu - pos);
-        atomicMax(&a.best[hrow + t], key);
-      }
+      cbest[t * MRG_TT + tid] = v;
+      crow[t * MRG_TT + tid] = rw;
     }
-    __syncthreads();
+  }
+  mrg_wait_vm<0>();
+  __syncthreads();
+  // fold the range into the tokens' running bests (one 64-bit atomic max per
+  // evicted token); kept tokens and tokens past the end take no part
+  for (int i = tid; i < t_end - t_begin; i += MRG_THREADS) {
+    const float v = cbest[i];
+    if (v > -INFINITY && a.flag[hrow + t_begin + i] == 0) {
+      const uint32_t pos = static_cast<uint32_t>(kb * MRG_KB + crow[i]);
+      const unsigned long long key =
+          (static_cast<unsigned long long>(mrg_order(v)) << 32) | static_cast<unsigned long long>(0xffffffffu - pos);
+      atomicMax(&a.best[hrow + t_begin + i], key);
+    }
   }
 }
 
