@@ -99,6 +99,32 @@ def test_llama_layer_n128k_topk():
     kbits = r.data["k"].view(np.int16)
     for h in (0, 7):
         assert np.array_equal(k_c[h].cpu().view(torch.int16).numpy(), kbits[h, idx[h]])
+    # partition-conserving merge at full size: sampled evicted tokens of head
+    # 0 against all kept keys (fp64 cosines; near-ties within 1e-4 accepted)
+    say(f"[gpu] full {wl.name}: merge")
+    from oracle.merge import cosine
+    tau = 0.3
+    bias_d = torch.from_numpy(bias.copy()).cuda()
+    _, merged, target = r.b.merge(r.k, budgets, torch.from_numpy(idx).cuda(), bias_d, tau, want_target=True)
+    torch.cuda.synchronize()
+    merged, target, bias1 = merged.cpu().numpy(), target.cpu().numpy(), bias_d.cpu().numpy()
+    kept = idx[0].astype(np.int64)
+    ev = np.setdiff1d(np.arange(wl.T), kept)
+    smp = np.random.default_rng(3).choice(ev, 200, replace=False)
+    kf = synth.to_f64(r.data["k"][0], wl.dtype)
+    c = cosine(kf[smp], kf[kept])
+    srt = np.sort(c, axis=1)
+    for i, e in enumerate(smp):
+        g = target[0, e]
+        if g >= 0:
+            assert c[i, g] >= srt[i, -1] - 1e-4 and c[i, g] > tau - 1e-4, (e, g)
+        else:
+            assert srt[i, -1] <= tau + 1e-4, e
+    assert np.all(target[0, kept] == -1)
+    cnt = np.bincount(target[0][target[0] >= 0], minlength=kept.size)
+    assert np.array_equal(merged[0], cnt)
+    assert np.allclose(bias1[0], (bias[0].astype(np.float64) + np.log1p(cnt)).astype(np.float32), rtol=1e-6,
+                       atol=1e-6)
 
 
 def test_qwen_layer_n128k_sample():
