@@ -56,6 +56,9 @@ def _parse():
                     help="time replays of the step captured in a HIP graph instead of eager launches")
     ap.add_argument("--no-decode", action="store_true", help="skip the SNIS decode measurement")
     ap.add_argument("--no-merge", action="store_true", help="skip the partition-conserving merge measurement")
+    ap.add_argument("--score-kind", default="perturb", choices=["perturb", "h2o", "h2o_h", "tova", "min", "min_h"],
+                    help="score of the step (the default is the output-perturbation score)")
+    ap.add_argument("--pool-mode", default="max", choices=["max", "avg"])
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (5 times) and exit")
@@ -102,16 +105,20 @@ def _copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
 
 
-def _stage_bytes(wl, esize):
+def _stage_bytes(wl, esize, score_kind="perturb"):
     """Algorithmic HBM bytes per launch of each stage (what the method has to
     move, not implementation scratch)."""
     T, Hkv, d = wl.T, wl.Hkv, wl.d
     kv = 2 * Hkv * T * d * esize            # K and V read once
     planes = ((wl.Hq // wl.Hkv) * wl.w + 127) // 128 if wl.dtype == "bf16" else 1
     B = int(sum(wl.budgets()))
+    if score_kind == "perturb":
+        p2 = kv + 4 * Hkv * T + 4 * Hkv * T * planes          # + ||v||^2 read, raw scores written
+    else:                                                    # attention weights: K only (+ ||v||^2 for the min kinds)
+        p2 = kv // 2 + 4 * Hkv * T * planes + (4 * Hkv * T if score_kind in ("min", "min_h") else 0)
     return {
         "score_pass1": kv + 4 * Hkv * T,                       # + ||v||^2 written
-        "score_pass2": kv + 4 * Hkv * T + 4 * Hkv * T * planes,  # + ||v||^2 read, raw scores written
+        "score_pass2": p2,
         "score_pool": 4 * Hkv * T * planes + 4 * Hkv * T,
         "select": 4 * Hkv * T + 8 * Hkv * B,
         "compact": 2 * (2 * Hkv * B * d * esize) + 12 * Hkv * B,
@@ -315,7 +322,8 @@ def main():
            torch.empty((wl.Hkv, total_C), dtype=torch.float32, device=dev))
 
     def step():
-        b.score(q, k, v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel, out=scores)
+        b.score(q, k, v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel, out=scores, score_kind=args.score_kind,
+                pool_mode=args.pool_mode)
         idx, bias, _, _ = b.select(scores, budgets, mode=mode, tau=wl.tau, tau_w=wl.tau_w, seed=wl.hash_seed,
                                    out=sel, bud_offsets=bud)
         b.compact(k, v, budgets, idx, bias, caps, out=cmp, bud_offsets=bud, cap_offsets=cap)
@@ -338,7 +346,7 @@ def main():
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     esize = 2 if wl.dtype == "bf16" else 4
-    sbytes = _stage_bytes(wl, esize)
+    sbytes = _stage_bytes(wl, esize, args.score_kind)
 
     def timed(stages_timed):
         """K steps between two events; the library records HIP events on its
@@ -396,7 +404,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "S": wl.S, "n": int(max(wl.lens)), "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "d": wl.d, "w": wl.w, "budget_frac": wl.budget_frac, "mode": wl.mode,
-                   "pool_kernel": wl.pool_kernel, "parallelism": "none (1 GPU)",
+                   "pool_kernel": wl.pool_kernel, "score_kind": args.score_kind, "pool_mode": args.pool_mode,
+                   "parallelism": "none (1 GPU)",
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dominant, wl.name),
