@@ -226,8 +226,8 @@ kve_status kvevict_select_soft(const kve_layout* L, const float* scores,
 /* The literal estimator of [PI] §4 (keep the entries drawn at least once in
  * m draws with replacement from the proposal) with the weights of Algorithm 1
  * step 4 tempered as Eq. 10: per (sequence, head) with m = m_in[s][h] draws
- * (a whole number in [0, 2^26]; otherwise status KVE_ENOTSUP and nothing
- * kept), draw k takes u_k = ((x >> 11) + 0.5) 2^-53, x the first word of
+ * (a whole number in [0, 2^31 - 1]; otherwise status KVE_ENOTSUP and nothing
+ * kept; the draws cost time in proportion to m), draw k takes u_k = ((x >> 11) + 0.5) 2^-53, x the first word of
  * Philox-4x64-10(counter = (k, h, s, 1), key = (seed, 0)), and lands on the
  * first entry whose cumulative proposal exceeds u_k times the total (the
  * proposal as in KVE_SAMPLE: tempered by tau, mixed with the uniform when

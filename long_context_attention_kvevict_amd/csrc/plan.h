@@ -63,9 +63,9 @@ struct SelectGeom {
   size_t bytes;
 };
 
-// Literal estimator: draws per head, and the longest sequence (its chunk
-// offsets are held in LDS).
-constexpr int64_t kLitMaxDraws = int64_t(1) << 26;
+// Literal estimator: draws per head (the per-entry counts are int32), and
+// the longest sequence (its chunk offsets are held in LDS).
+constexpr int64_t kLitMaxDraws = (int64_t(1) << 31) - 1;
 constexpr int kLitMaxLen = 4096 * kSmpChunk;
 
 struct LiteralGeom {

@@ -137,7 +137,45 @@ def test_qwen_layer_n128k_sample():
     say(f"[gpu] full {wl.name}: oracle head 0")
     _check_sampled_scores(r, got, 0, 0, rng)
     say(f"[gpu] full {wl.name}: select")
-    _select_parity(r, got)
+    idx, bias, m, st = _select_parity(r, got)
+    say(f"[gpu] full {wl.name}: per-head m {m[0].tolist()}")
+    # one m for all heads (soft budget) at full size, capacity 2 B
+    from oracle.select import global_sample_select
+    budgets = wl.budgets()
+    caps = [min(int(n), 2 * int(B)) for n, B in zip(wl.lens, budgets)]
+    tau = float(np.float32(wl.tau))
+    sidx, sbias, kept, sm, sst = r.b.select_soft(torch.from_numpy(got).cuda(), budgets, caps, tau=tau,
+                                                 tau_w=wl.tau_w, seed=wl.hash_seed)
+    torch.cuda.synchronize()
+    sidx, sbias, kept, sm, sst = (x.cpu().numpy() for x in (sidx, sbias, kept, sm, sst))
+    heads = [got[h].astype(np.float64) for h in range(wl.Hkv)]
+    ms = float(sm[0, 0])
+    assert np.all(sm[0] == ms) and np.all(sst[0] == 0)
+    pis = [proposal(x, tau) for x in heads]
+    assert abs(np.mean([expected_distinct(pi, ms) for pi in pis]) - budgets[0]) <= 0.5 + 1e-9 * wl.T
+    say(f"[gpu] full {wl.name}: soft budget m {ms:.4g}, kept {kept[0].tolist()}")
+    out, rkept, _, _ = global_sample_select(heads, int(budgets[0]), caps[0], tau, wl.tau_w, wl.hash_seed, 0, m=ms)
+    assert list(kept[0]) == rkept
+    for h in range(wl.Hkv):
+        kk = kept[0, h]
+        assert np.array_equal(sidx[h, :kk], out[h][0])
+        assert np.all(np.abs(sbias[h, :kk] - out[h][1]) <= 1e-6 * (1 + np.abs(out[h][1])))
+        assert np.all(sidx[h, kk:] == -1)
+    # the literal estimator with head 0's searched m (about 1.5e7 draws)
+    from oracle.select import literal_select
+    say(f"[gpu] full {wl.name}: literal draws, m = {m[0, 0]:.4g}")
+    mm = np.zeros_like(m)
+    mm[0, 0] = m[0, 0]
+    lcap = [int(wl.lens[0])]
+    lidx, lbias, lkept, lst = r.b.select_literal(torch.from_numpy(got).cuda(), torch.from_numpy(mm), lcap, tau=tau,
+                                                 tau_w=wl.tau_w, seed=wl.hash_seed)
+    torch.cuda.synchronize()
+    lidx, lbias, lkept, lst = (x.cpu().numpy() for x in (lidx, lbias, lkept, lst))
+    ri, rb, J = literal_select(heads[0], int(m[0, 0]), lcap[0], tau, wl.tau_w, wl.hash_seed, 0, 0)
+    assert lst[0, 0] == 0 and lkept[0, 0] == J
+    assert np.array_equal(lidx[0, :J], ri)
+    assert np.all(np.abs(lbias[0, :J] - rb) <= 1e-5 * (1 + np.abs(rb)))
+    say(f"[gpu] full {wl.name}: literal kept {J}")
 
 
 def test_mistral_ragged_batch_with_decode():

@@ -330,7 +330,7 @@ def test_select_literal_draws(mix):
     off = np.concatenate([[0], np.cumsum(lens)])
     coff = np.concatenate([[0], np.cumsum(caps)])
     sc = np.exp(rng.standard_normal((Hkv, T)) * np.array([[2.5], [1.0]]) - 9.0).astype(np.float32)
-    m = np.array([[500.0, 3000.0], [2000.0, 0.0], [150000.0, 7.0e7]])   # 7e7 > 2^26: not drawn
+    m = np.array([[500.0, 3000.0], [2000.0, 0.0], [150000.0, 2.5e9]])   # 2.5e9 > 2^31 - 1: not drawn
     # the library takes fp32 temperatures: the oracle gets the same values
     tau, tau_w, seed = float(np.float32(0.7)), 1.5, 4242
     b = K.Batch(lens, 4, Hkv, 128, 8, "bf16")
@@ -342,7 +342,7 @@ def test_select_literal_draws(mix):
         for h in range(Hkv):
             gi = idx[h, coff[s_]:coff[s_ + 1]]
             gb = bias[h, coff[s_]:coff[s_ + 1]].astype(np.float64)
-            if m[s_, h] > 2 ** 26:
+            if m[s_, h] > 2 ** 31 - 1:
                 assert st[s_, h] == K.KVE_ENOTSUP and kept[s_, h] == 0 and np.all(gi == -1)
                 continue
             assert st[s_, h] == K.KVE_OK
