@@ -173,6 +173,29 @@ def _cpu_baseline(wl, data, heads):
             "sample_1thread": f"1 of {wl.Hkv} KV heads, BLAS limited to 1 thread, {dt1:.1f} s, scaled by {wl.Hkv}"}
 
 
+def _merge_cpu(data, wl, idx_np, budgets, tau_merge, sample=16384):
+    """The oracle's merge (fp64 cosines, argmax, threshold) for a sample of the
+    evicted tokens of KV head 0, scaled to all evicted tokens of all heads."""
+    import numpy as np
+    from oracle.merge import merge_targets
+    from long_context_attention_kvevict_amd import synth
+    n, B = int(wl.lens[0]), int(budgets[0])
+    kept = idx_np[0, :B].astype(np.int64)
+    ev = np.setdiff1d(np.arange(n), kept)
+    pick = np.sort(np.random.default_rng(0).choice(ev, min(sample, ev.size), replace=False))
+    k = synth.to_f64(data["k"][0], wl.dtype)
+    rows = np.sort(np.concatenate([kept, pick]))
+    pos = np.searchsorted(rows, kept)
+    t0 = time.perf_counter()
+    merge_targets(k[rows], pos, tau_merge)
+    dt = time.perf_counter() - t0
+    evicted = sum(int(x) - int(y) for x, y in zip(wl.lens, budgets)) * wl.Hkv
+    flops = 2.0 * wl.d * B * pick.size
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{pick.size} evicted tokens of KV head 0 against its {B} kept keys, {dt:.2f} s "
+                      f"(all {evicted} evicted tokens would take {dt * evicted / pick.size:.0f} s)"}
+
+
 def _merge_leg(b, k, budgets, idx, bias, wl, tau_merge=0.9, reps=10):
     """kvevict_merge over the step's kept set: every evicted key against
     every kept key of its head (cosine), on bf16 MFMAs.  Algorithmic work:
@@ -460,10 +483,14 @@ def main():
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = _cpu_baseline(wl, data, max(1, min(args.cpu_heads, wl.Hkv)))
+    merge_data = {"k": data["k"][:1].copy()}   # KV head 0 for the merge leg's oracle sample
     del data
     if not args.no_merge:
         print("# merge leg", file=sys.stderr, flush=True)
         result["merge"] = _merge_leg(b, k, budgets, sel[0][:, :total_B], sel[1][:, :total_B], wl)
+        if not args.no_cpu_baseline:
+            result["merge"]["cpu_baseline"] = _merge_cpu(merge_data, wl, sel[0][:, :total_B].cpu().numpy(), budgets,
+                                                         result["merge"]["tau_merge"])
     if not args.no_decode:
         print("# decode leg", file=sys.stderr, flush=True)
         result["decode"] = _decode_leg(args.decode_steps, not args.no_cpu_baseline)
