@@ -23,6 +23,7 @@ kernel and workload or when the kernel's source has changed since.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -443,6 +444,9 @@ def main():
             rows[st] = {"ms": round(rec[0], 5), "algorithmic_bytes": sbytes[st], "GB/s": round(gbs, 1),
                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     result["rows"] = rows
+    # device scratch of the scorer (the pages quote the scoring path's
+    # intermediate memory at n = 128K); caller-owned, reused every step
+    result["score_workspace_bytes"] = int(b._lib.kvevict_score_workspace(ctypes.byref(b.layout)))
     # Per-step times with the L2 / Infinity Cache flushed before every step
     # (a 512 MiB device write between steps), median over K steps.
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
