@@ -92,3 +92,20 @@ def test_knorm_closed_form_and_softmax_proposal():
     assert set(topk_select(P.knorm_scores(kk), 5)) == set(np.argsort(norms)[:5])
     for tau in (1.0, 0.5, 3.0):
         assert np.allclose(proposal(P.knorm_scores(kk), tau), softmax(-norms / tau), rtol=1e-12, atol=0)
+
+
+def test_tova_is_the_last_row_brute_force():
+    # TOVA: the last window row's softmax weights, summed over the group's
+    # q-heads (a plain loop; the last row sees every key under the mask)
+    q, k, v, g, w = _case(5, n=11, d=4, w=4, g=3, Hkv=1)
+    n = k.shape[0]
+    ref = np.zeros(n)
+    for qh in range(g):
+        logits = [0.7 * float(np.dot(q[qh, w - 1], k[j])) for j in range(n)]
+        m = max(logits)
+        e = [np.exp(x - m) for x in logits]
+        for j in range(n):
+            ref[j] += e[j] / sum(e)
+    for causal in (True, False):
+        got = P.group_proposal_scores("tova", q, k, v, 0, g, 0.7, causal)
+        assert np.allclose(got, ref, rtol=1e-13, atol=1e-16)
