@@ -260,8 +260,9 @@ kve_status kvevict_select_literal(const kve_layout* L, const float* scores,
  * bias then grows by log(1 + number merged into it) (its multiplicity m_r,
  * starting at 1); keys and values stay as they are, so an exact duplicate
  * leaves the softmax normaliser unchanged.  Similarities are bf16 products
- * accumulated in fp32 (MFMA); the argmax and the threshold are decided on
- * those fp32 values.
+ * accumulated in fp32 (MFMA), kept to about 2^-16 (the argmax packs the
+ * candidate's position into the low bits of the value): candidates or a
+ * threshold closer than that are resolved by position / may go either way.
  *   k          [Hkv][T][128] bf16 (the full cache the selection read)
  *   bud_off    device [S+1], bud_off_host host [S+1]: the kept counts
  *   idx        [Hkv][bud_off[S]] kept positions as written by select

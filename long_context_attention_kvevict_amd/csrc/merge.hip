@@ -119,8 +119,7 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
   const int B = a.bud_off[s + 1] - a.bud_off[s];
   if (kb * MRG_KB >= B || tc * MRG_TCH >= n || B >= n) return;
   __shared__ __align__(1024) char ring[MRG_NST * MRG_TILE_BYTES];
-  __shared__ __align__(16) float kinv[MRG_KB];   // 1 / ||k_r|| (0 for a missing key)
-  __shared__ __align__(16) float kpen[MRG_KB];   // 0, or -inf for a missing key
+  __shared__ __align__(16) float kinv[MRG_KB];   // 1 / ||k_r||
   __shared__ float wbest[4][MRG_TT];
   __shared__ int wrow[4][MRG_TT];
   __shared__ float cbest[MRG_TCH];
@@ -129,27 +128,22 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
   const size_t hrow = static_cast<size_t>(h) * a.T + base;
   const int32_t* kid = a.idx + h * a.totalB + a.bud_off[s];
-  // A operands: retained keys kb*MRG_KB + 128*wave + 32*rb + col
+  // A operands: retained keys kb*MRG_KB + 128*wave + 32*rb + col; rows past
+  // the kept count repeat the last kept key (equal values, higher row: they
+  // never win)
+  auto kept_pos = [&](int r) {
+    const int j = kid[min(r, B - 1)];
+    return min(max(j, 0), n - 1);
+  };
   bf16x8 qa[4][MRG_D / 16];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    const int rr = kb * MRG_KB + 128 * wave + 32 * rb + col;
-    int jr = rr < B ? kid[rr] : -1;
-    const bool ok = jr >= 0 && jr < n;
+    const int jr = kept_pos(kb * MRG_KB + 128 * wave + 32 * rb + col);
 #pragma unroll
-    for (int kk = 0; kk < MRG_D / 16; ++kk) {
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (ok) t = *reinterpret_cast<const u32x4*>(a.k + (hrow + jr) * MRG_D + 16 * kk + 8 * hl);
-      qa[rb][kk] = as_bf16x8(t);
-    }
+    for (int kk = 0; kk < MRG_D / 16; ++kk)
+      qa[rb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.k + (hrow + jr) * MRG_D + 16 * kk + 8 * hl));
   }
-  for (int i = tid; i < MRG_KB; i += MRG_THREADS) {
-    const int r2 = kb * MRG_KB + i;
-    const int j2 = r2 < B ? kid[r2] : -1;
-    const bool ok = j2 >= 0 && j2 < n;
-    kinv[i] = ok ? a.invn[hrow + j2] : 0.f;
-    kpen[i] = ok ? 0.f : -INFINITY;
-  }
+  for (int i = tid; i < MRG_KB; i += MRG_THREADS) kinv[i] = a.invn[hrow + kept_pos(kb * MRG_KB + i)];
   const int t_begin = tc * MRG_TCH;
   const int t_end = min(n, t_begin + MRG_TCH);
   for (int i = tid; i < MRG_TCH; i += MRG_THREADS) tinvs[i] = (t_begin + i < t_end) ? a.invn[hrow + t_begin + i] : 0.f;
@@ -184,30 +178,37 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
 #pragma unroll
     for (int kk = 0; kk < MRG_D / 16; ++kk)
       kop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(tl + col * (MRG_D * 2) + (((2 * kk + hl) ^ (col & 15)) << 4)));
-    float bv = -INFINITY;   // best of k_r.k_t / ||k_r|| (the token's 1 / ||k_t|| is applied after)
-    int br = 0x7fffffff;
+    // c = k_r.k_t / ||k_r|| + 2 ||k_t|| lies in [||k_t||, 3 ||k_t||] (a zero
+    // token key: 1), so its fp32 bits order like unsigned integers; the low
+    // 6 bits are replaced by 63 - e (e = 16 rb + r, increasing row order) and
+    // one unsigned maximum keeps the best value and, on ties, the lowest row
+    const float tinv = tinvs[t * MRG_TT + col];
+    const float sh = tinv > 0.f ? 2.f / tinv : 1.f;
+    uint32_t best = 0u;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < MRG_D / 16; ++kk) acc = mfma32(qa[rb][kk], kop[kk], acc);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {   // rows in increasing order: strict > keeps the lowest
-        const int row0 = 128 * wave + 32 * rb + 8 * q4 + 4 * hl;
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(&kinv[row0]);
-        const f32x4 pn = *reinterpret_cast<const f32x4*>(&kpen[row0]);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&kinv[128 * wave + 32 * rb + 8 * q4 + 4 * hl]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float c = fmaf(acc[4 * q4 + e], kv[e], pn[e]);   // missing keys: 0 * 0 - inf
-          if (c > bv) { bv = c; br = row0 + e; }
+          const float c = fmaf(acc[4 * q4 + e], kv[e], sh);
+          const uint32_t key = (__float_as_uint(c) & 0xffffffc0u) | static_cast<uint32_t>(63 - (16 * rb + 4 * q4 + e));
+          best = max(best, key);
         }
       }
     }
+    const int eb = 63 - static_cast<int>(best & 63u);
+    float bv = (__uint_as_float(best & 0xffffffc0u) - sh) * tinv;   // the cosine, to about 2^-16
+    int br = 128 * wave + 32 * (eb >> 4) + 8 * ((eb >> 2) & 3) + 4 * hl + (eb & 3);
     const float ov = __shfl_xor(bv, 32, 64);
     const int orow = __shfl_xor(br, 32, 64);
     if (ov > bv || (ov == bv && orow < br)) { bv = ov; br = orow; }
     if (hl == 0) {
-      wbest[wave][col] = (bv == -INFINITY) ? bv : bv * tinvs[t * MRG_TT + col];   // the cosine
+      wbest[wave][col] = bv;
       wrow[wave][col] = br;
     }
     mrg_lds_barrier();
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
   for (int i = tid; i < t_end - t_begin; i += MRG_THREADS) {
     const float v = cbest[i];
     if (v > -INFINITY && a.flag[hrow + t_begin + i] == 0) {
-      const uint32_t pos = static_cast<uint32_t>(kb * MRG_KB + crow[i]);
+      const uint32_t pos = static_cast<uint32_t>(min(kb * MRG_KB + crow[i], B - 1));
       const unsigned long long key =
           (static_cast<unsigned long long>(mrg_order(v)) << 32) | static_cast<unsigned long long>(0xffffffffu - pos);
       atomicMax(&a.best[hrow + t_begin + i], key);
