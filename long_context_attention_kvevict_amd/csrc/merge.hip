@@ -107,6 +107,7 @@ template <typename T>
 __device__ __forceinline__ void mrg_settle(const T& x) { asm volatile("" :: "v"(x)); }
 
 constexpr int MRG_NST = 3;                      // ring stages
+constexpr int MRG_GRP = 4;                      // tiles per cross-wave combine
 constexpr int MRG_TILE_BYTES = MRG_TT * MRG_D * 2;
 
 // Best retained key per token: a workgroup holds MRG_KB retained keys (each
@@ -120,8 +121,8 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
   if (kb * MRG_KB >= B || tc * MRG_TCH >= n || B >= n) return;
   __shared__ __align__(1024) char ring[MRG_NST * MRG_TILE_BYTES];
   __shared__ __align__(16) float kinv[MRG_KB];   // 1 / ||k_r||
-  __shared__ float wbest[4][MRG_TT];
-  __shared__ int wrow[4][MRG_TT];
+  __shared__ float wbest[4][MRG_GRP * MRG_TT];   // per wave, the last MRG_GRP tiles
+  __shared__ int wrow[4][MRG_GRP * MRG_TT];
   __shared__ float cbest[MRG_TCH];
   __shared__ int crow[MRG_TCH];
   __shared__ float tinvs[MRG_TCH];   // 1 / ||k|| of the range's tokens (no global loads in the loop)
@@ -207,21 +208,25 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
     const float ov = __shfl_xor(bv, 32, 64);
     const int orow = __shfl_xor(br, 32, 64);
     if (ov > bv || (ov == bv && orow < br)) { bv = ov; br = orow; }
+    const int gs = (t % MRG_GRP) * MRG_TT;
     if (hl == 0) {
-      wbest[wave][col] = bv;
-      wrow[wave][col] = br;
+      wbest[wave][gs + col] = bv;
+      wrow[wave][gs + col] = br;
     }
-    mrg_lds_barrier();
-    if (tid < MRG_TT) {
-      float v = wbest[0][tid];
-      int rw = wrow[0][tid];
+    if (t % MRG_GRP == MRG_GRP - 1 || t == ntile - 1) {   // combine the waves over the group's tiles
+      mrg_lds_barrier();
+      const int g0 = t - t % MRG_GRP;
+      if (tid < (t - g0 + 1) * MRG_TT) {
+        float v = wbest[0][tid];
+        int rw = wrow[0][tid];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        const float v2 = wbest[w][tid];
-        if (v2 > v) { v = v2; rw = wrow[w][tid]; }   // later waves hold higher rows: ties stay
+        for (int w = 1; w < 4; ++w) {
+          const float v2 = wbest[w][tid];
+          if (v2 > v) { v = v2; rw = wrow[w][tid]; }   // later waves hold higher rows: ties stay
+        }
+        cbest[g0 * MRG_TT + tid] = v;
+        crow[g0 * MRG_TT + tid] = rw;
       }
-      cbest[t * MRG_TT + tid] = v;
-      crow[t * MRG_TT + tid] = rw;
     }
   }
   mrg_wait_vm<0>();
