@@ -55,13 +55,18 @@ __device__ __forceinline__ int p1_key_of(int r, int hl) {
   return (r & 3) + 4 * ((r >> 2) & 1) + 8 * hl + 16 * (r >> 3);
 }
 
-// Chunk swizzle of a tile row: chunk c of key k is stored at chunk c ^ swz(k).
-// swz permutes the 16 residues of k (16 consecutive keys hit 16 distinct
-// chunks: the MFMA operand reads), gives the four keys 4a..4a+3 distinct
-// swz >> 1 (the transposing reads touch chunk pairs 2m, 2m+1 of four keys)
-// and flips bit 0 between keys 2a and 2a+1 (the ||v||^2 reads).
+// Chunk swizzle of a tile row: chunk c of key k is stored at chunk c ^ swz(k),
+// with key bits b3..b0 mapped to swz = (b1, b0, b1^b3, b2^b3).  The 16-byte
+// reads of one chunk (MFMA operands, ||v||^2) hit distinct slots whether the
+// LDS serves 8 or 16 lanes per cycle, for 16 consecutive keys and for pass
+// 1's keymap order alike: swz is a permutation of the 16 residues of k, and
+// eight consecutive keys, or keymap(0..7), keymap(8..15), differ mod 8.  The
+// transposing 8-byte reads of pass 1 touch four keys 4a..4a+3 at chunks
+// 4m..4m+3 per 32 lanes; the four keys have distinct swz >> 2, so those 16
+// chunks are distinct too (and, per 16 lanes, chunk pairs 2m, 2m+1 of the
+// four keys, distinct by swz >> 1).
 __device__ __forceinline__ int swz(int key) {
-  return (key & 8) | ((key & 3) << 1) | (((key >> 2) ^ key) & 1);
+  return ((key & 3) << 2) | ((((key >> 1) ^ (key >> 3)) & 1) << 1) | (((key >> 2) ^ (key >> 3)) & 1);
 }
 // Byte offset of 16-byte chunk c of row `key` inside a swizzled tile.
 __device__ __forceinline__ int tile_off(int key, int c) { return key * ROWB + ((c ^ swz(key)) << 4); }
