@@ -668,6 +668,9 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
     // halves; each half's operands are read in one batch so the LDS
     // latency is paid once per chain rather than once per MFMA
     f32x16 sacc[2], gacc[2];
+    // the MFMA section runs at raised wave priority, so that the other wave
+    // of the SIMD tends to be in its vector-ALU section meanwhile
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 kop[D / 16];
@@ -700,6 +703,7 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // x = log2 p in place of the logits; hidden pairs get x = -inf (p = 0)
     float xmax = -INFINITY;
 #pragma unroll
