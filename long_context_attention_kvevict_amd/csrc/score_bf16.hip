@@ -233,6 +233,10 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   // this lane's query row (N index of the K.Q^T MFMA)
   const int row = rg * ROWS + wave * 32 + col;
   const bool row_ok = row < R;
+  // A wave of the last row group can hold no window row (R not a multiple
+  // of 128, e.g. 7 query heads x 64 rows): it still loads its share of the
+  // tiles and forms its keys' ||v||^2, but skips the attention arithmetic.
+  const bool wave_rows = __builtin_amdgcn_readfirstlane(rg * ROWS + wave * 32 < R ? 1 : 0) != 0;
   const int qh = h * g + (row_ok ? row / a.w : 0);
   const int wi = row_ok ? row % a.w : 0;
   const int pos = n - a.w + wi;   // causal horizon of this row
@@ -321,6 +325,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
       }
       if (gdiag) vn[t * KT + gkey] = gram[lane & 3];
     }
+    if (!wave_rows) return;   // no window row in this wave (last row group)
     // S^T = K . Q^T for both 32-key halves (slot order through keymap)
     f32x16 sacc[2];
 #pragma unroll
@@ -607,6 +612,10 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   // A operands: rows wave*32 + col (M index)
   const int arow = rg * ROWS + wave * 32 + col;
   const bool arow_ok = arow < R;
+  // a wave of the last row group with no window row loads its share of the
+  // tiles but skips the arithmetic; its partials stay zero
+  const bool wave_rows = __builtin_amdgcn_readfirstlane(rg * ROWS + wave * 32 < R ? 1 : 0) != 0;
+  if (!wave_rows) red[0][wave][lane] = red[1][wave][lane] = 0.f;
   bf16x8 qa[D / 16], oha[D / 16];
   {
     const int qh = h * g + (arow_ok ? arow / a.w : 0);
@@ -769,13 +778,22 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   };
 
   const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;   // first key of an edge tile
-  for (int t = 0; t < ntile; ++t) {
-    wait_vm<0>();
-    lds_barrier();
-    if (t > 0) reduce_tile(t - 1);
-    if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
-    if (c0 + t * KT > edge_from) tile(t, std::true_type{});
-    else tile(t, std::false_type{});
+  if (wave_rows) {
+    for (int t = 0; t < ntile; ++t) {
+      wait_vm<0>();
+      lds_barrier();
+      if (t > 0) reduce_tile(t - 1);
+      if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+      if (c0 + t * KT > edge_from) tile(t, std::true_type{});
+      else tile(t, std::false_type{});
+    }
+  } else {   // the same loads, barriers and reductions, no arithmetic
+    for (int t = 0; t < ntile; ++t) {
+      wait_vm<0>();
+      lds_barrier();
+      if (t > 0) reduce_tile(t - 1);
+      if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+    }
   }
   lds_barrier();
   if (ntile > 0) reduce_tile(ntile - 1);
@@ -828,6 +846,10 @@ __global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
 
   const int arow = rg * ROWS + wave * 32 + col;
   const bool arow_ok = arow < R;
+  // a wave of the last row group with no window row loads its share of the
+  // tiles but skips the arithmetic; its partials stay zero
+  const bool wave_rows = __builtin_amdgcn_readfirstlane(rg * ROWS + wave * 32 < R ? 1 : 0) != 0;
+  if (!wave_rows) red[0][wave][lane] = red[1][wave][lane] = 0.f;
   bf16x8 qa[D / 16];
   {
     const int qh = h * g + (arow_ok ? arow / a.w : 0);
@@ -873,6 +895,7 @@ __global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
   const bool causal = a.causal != 0;
 
   auto tile = [&](const int t, auto edge_tag) {
+    if (!wave_rows) return;
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int kt0 = c0 + t * KT;
     const char* Kt = ring + (t & 1) * TILE_BYTES;
