@@ -35,7 +35,7 @@ struct ScoreGeom {
 // grid that brackets the search, and the step budget of the search that
 // follows (a safeguarded Newton iteration in log m; started from the grid
 // it needs at most 3 evaluations on the score distributions tried).
-constexpr int kSelChunk = 4096;
+constexpr int kSelChunk = 1024;
 constexpr int kSmpChunk = 1024;       // keys per workgroup of the sampling passes
 constexpr int kSelBins = 2048;
 constexpr int kSelLevels32 = 3;

@@ -32,7 +32,7 @@
 namespace kve {
 
 constexpr int SEL_THREADS = 256;
-constexpr int SEL_PER = 16;
+constexpr int SEL_PER = 4;
 constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER;
 constexpr int SEL_BINS = 2048;
 static_assert(SEL_CHUNK == kSelChunk && SEL_BINS == kSelBins, "host and device select geometry disagree");
