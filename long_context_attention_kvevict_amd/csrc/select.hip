@@ -227,6 +227,67 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   }
 }
 
+// Last digit level of the fp32 top-k, which also leaves the ordered write
+// what a separate count launch would: per chunk, the number of keys whose
+// leading digits (levels 0 .. LEVELS-2) exceed those of the threshold, and
+// per (sequence, head) a list of the keys that share them (index, last
+// digit).  Such keys are few unless many scores tie; the list has room for
+// every key of the head.
+template <class Src>
+__global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a, int* __restrict__ hist,
+                                                             int* __restrict__ ncand, int2* __restrict__ cand,
+                                                             int cap, int* __restrict__ cnt) {
+  typedef typename Src::K K;
+  constexpr int LV = Radix<K>::LEVELS - 1;
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int sh = s * a.Hkv + h;
+  const int B = sel_budget(a, s, sh);
+  const int j0 = ch * SEL_CHUNK;
+  if (B <= 0 || B >= n || j0 >= n) return;
+  const int SH = a.S * a.Hkv;
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  K u[SEL_PER];
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = j0 + i * SEL_THREADS + threadIdx.x;
+    u[i] = (j < n) ? src.key(row + j) : K(0);
+  }
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+  K prefix, mask;
+  int need;
+  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need);
+  __syncthreads();
+  const int sft = Radix<K>::shift(LV);
+  const K dm = Radix<K>::wmask(LV);
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int j = j0 + i * SEL_THREADS + threadIdx.x;
+    if (j >= n) continue;
+    const K lead = u[i] & mask;
+    if (lead > prefix) {
+      ++above;
+    } else if (lead == prefix) {
+      const int dg = static_cast<int>((u[i] >> sft) & dm);
+      atomicAdd(&lh[dg], 1);
+      const int slot = atomicAdd(&ncand[sh], 1);   // < n <= cap: each key is listed once
+      cand[static_cast<size_t>(sh) * cap + slot] = make_int2(j, dg);
+    }
+  }
+  int tot;
+  block_incl_scan256(above, lds, &tot);   // its barriers also complete lh
+  if (threadIdx.x == 0) cnt[(static_cast<size_t>(sh) * a.nchunk + ch) * 2] = tot;
+  int* gh = hist + (static_cast<size_t>(LV) * SH + sh) * SEL_BINS;
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) {
+    const int c = lh[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
 // Threshold (the B-th largest key) and the number of keys equal to it that
 // are kept, per (sequence, head).
 struct RState {
@@ -340,6 +401,95 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
   for (int c = threadIdx.x; c < ch; c += SEL_THREADS) {
     gt_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2 + 0];
     eq_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2 + 1];
+  }
+  int tot;
+  block_incl_scan256(gt_b, lds, &tot);
+  gt_b = tot;
+  block_incl_scan256(eq_b, lds, &tot);
+  eq_b = tot;
+  int neq = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) neq += (jt + i < n) && (u[i] == thr);
+  int eq_tot;
+  int eq_rank = eq_b + block_incl_scan256(neq, lds, &eq_tot) - neq;
+  int ntake = 0;
+  uint32_t take_bits = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const bool in = jt + i < n;
+    const bool gt = in && u[i] > thr;
+    const bool eq = in && u[i] == thr;
+    const bool take = gt || (eq && eq_rank < need);
+    eq_rank += eq;
+    take_bits |= static_cast<uint32_t>(take) << i;
+    ntake += take;
+  }
+  int take_tot;
+  int pos = gt_b + min(eq_b, need) + block_incl_scan256(ntake, lds, &take_tot) - ntake;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    if ((take_bits >> i) & 1u) {
+      if (pos < B) {   // bounded even if the counts were inconsistent
+        out[pos] = jt + i;
+        bout[pos] = bias_of(sh, row + jt + i);
+      }
+      ++pos;
+    }
+  }
+}
+
+// Ordered write of the fp32 top-k from sel_hist_last's counts: the
+// threshold is resolved here from the finished histograms (as sel_count
+// does), the keys above it in earlier chunks are the per-chunk counts of
+// larger leading digits plus the listed keys with a larger last digit, and
+// the keys equal to it are the listed keys with the same last digit.  The
+// rest is sel_write's; the output is the same.
+template <class Src, class Bias>
+__global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bias_of, SelArgs a,
+                                                                const int* __restrict__ hist,
+                                                                const int* __restrict__ cnt,
+                                                                const int* __restrict__ ncand,
+                                                                const int2* __restrict__ cand, int cap,
+                                                                int32_t* __restrict__ idx,
+                                                                float* __restrict__ bias) {
+  typedef typename Src::K K;
+  constexpr int NLV = Radix<K>::LEVELS;
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int j0 = ch * SEL_CHUNK;
+  const int sh = s * a.Hkv + h;
+  const int B = sel_budget(a, s, sh);
+  if (j0 >= n) return;   // the chunks cover [0, n), which holds every output slot
+  int32_t* out = idx + h * a.totalB + a.out_off[s];
+  float* bout = bias + h * a.totalB + a.out_off[s];
+  if (B <= 0) return;
+  if (B >= n) {   // everything kept, weight 1
+    for (int i = threadIdx.x; i < SEL_CHUNK; i += SEL_THREADS) {
+      const int j = j0 + i;
+      if (j < n) { out[j] = j; bout[j] = 0.f; }
+    }
+    return;
+  }
+  __shared__ int lds[8];
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  const int jt = j0 + SEL_PER * threadIdx.x;
+  K u[SEL_PER];
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) u[i] = (jt + i < n) ? src.key(row + jt + i) : K(0);
+  K thr, mask;
+  int need;
+  resolve<K, NLV>(hist, a.S * a.Hkv, sh, B, lds, &thr, &mask, &need);
+  const int dlast = static_cast<int>((thr >> Radix<K>::shift(NLV - 1)) & Radix<K>::wmask(NLV - 1));
+  int gt_b = 0, eq_b = 0;
+  for (int c = threadIdx.x; c < ch; c += SEL_THREADS) gt_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2];
+  const int nc = ncand[sh];
+  for (int i = threadIdx.x; i < nc; i += SEL_THREADS) {
+    const int2 e = cand[static_cast<size_t>(sh) * cap + i];
+    if (e.x < j0) {
+      gt_b += e.y > dlast;
+      eq_b += e.y == dlast;
+    }
   }
   int tot;
   block_incl_scan256(gt_b, lds, &tot);
@@ -1075,9 +1225,19 @@ hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const fl
 // ----------------------------------------------------------------- launch
 template <class Src, class Bias>
 static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,
-                         RState* rs, int32_t* idx, float* bias, hipStream_t st) {
+                         RState* rs, int32_t* idx, float* bias, hipStream_t st, int* ncand = nullptr,
+                         int2* cand = nullptr) {
   typedef typename Src::K K;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
+  if (Radix<K>::LEVELS == 3 && ncand && a.bsh == nullptr) {   // fp32 top-k: no count launch
+    hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    hipLaunchKernelGGL((sel_hist<Src, 1>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    hipLaunchKernelGGL((sel_hist_last<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, ncand, cand, G.max_len,
+                       cnt);
+    hipLaunchKernelGGL((sel_write_listed<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, hist, cnt,
+                       ncand, cand, G.max_len, idx, bias);
+    return;
+  }
   hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
   hipLaunchKernelGGL((sel_hist<Src, 1>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
   hipLaunchKernelGGL((sel_hist<Src, 2>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
@@ -1130,7 +1290,8 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   hipLaunchKernelGGL(sel_init, dim3((max(nzero, SH) + 255) / 256), dim3(256), 0, st, hist, nzero,
                      topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
   if (topk) {
-    launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st);
+    launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st,
+                 reinterpret_cast<int*>(wsb + G.off_ncand), reinterpret_cast<int2*>(wsb + G.off_cand));
   } else {
     SmpArgs A;
     A.g = a;
