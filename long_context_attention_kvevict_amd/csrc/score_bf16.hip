@@ -400,15 +400,16 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
     pv(pb);
     // A dominant weight is where the bf16 rounding of P matters: it moves o
     // by 2^-9 a v_j for a key of final weight a, against ||o - v_j|| of about
-    // (1 - a) ||v_j||.  This lane's running sum is a lower bound on the row's
-    // final sum, so a tile whose weights all stay within half of it has
+    // (1 - a) ||v_j||.  The running sum of the row (this lane's half plus its
+    // partner's) is a lower bound on its final sum, so a tile whose weights
+    // all stay within half of it has
     // a <= 1/2 for every key and the rounding moves ||o - v_j||^2 by at most
     // 2^-9 * 2 relative (0.39 %).  Tiles with a larger weight also contract
     // the rounding residual of P, which makes the weights exact to about
     // 2^-17.  (Early tiles of a chunk, where the running sum is still small,
     // are the ones that take this path.)
     const float pmax = __builtin_amdgcn_exp2f(tmax - m_use);
-    if (__any(2.f * pmax > l_run)) {
+    if (__any(2.f * pmax > sum_xor32(l_run))) {
       bf16x8 pr[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
