@@ -658,9 +658,9 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   fill.init(lds_addr(ring), wave, lane);
   const int ntile = (c1 - c0 + KT - 1) / KT;
 
-  auto reduce_tile = [&](int t) {   // 4 row-block partials -> sbuf
+  auto reduce_tile = [&](int t, int st) {   // 4 row-block partials of tile t (ring stage st) -> sbuf
     if (tid < KT) {
-      const float* rr = &red[t & 1][0][0];
+      const float* rr = &red[st][0][0];
       sbuf[t * KT + tid] = (rr[tid] + rr[KT + tid]) + (rr[2 * KT + tid] + rr[3 * KT + tid]);
     }
   };
@@ -669,14 +669,17 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   for (int kk = 0; kk < D / 16; ++kk) koff[kk] = tile_off(col, 2 * kk + hl);
   const bool causal = a.causal != 0;
 
-  if (ntile > 0) fill.issue(kb8, vb8, c0, c1, 0);
+  // Tiles are taken from the chunk's end back to its start: pass 1 streamed
+  // each chunk front to back, so the tiles it read last are the likeliest to
+  // still be in the Infinity Cache.  The ring stage follows the step count.
+  if (ntile > 0) fill.issue(kb8, vb8, c0 + (ntile - 1) * KT, c1, 0);
 
   // One tile; EDGE tiles mask keys past the chunk end or a row's causal
   // horizon, interior tiles carry no masking code.
-  auto tile = [&](const int t, auto edge_tag) {
+  auto tile = [&](const int t, const int st, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int kt0 = c0 + t * KT;
-    const char* Kt = ring + (t & 1) * STAGE_BYTES;
+    const char* Kt = ring + st * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
     // S = Q K^T and G = ||o_h||^2 + ||v||^2 - 2 O_h V^T for both 32-key
     // halves; each half's operands are read in one batch so the LDS
@@ -778,30 +781,33 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const float tot = sum_xor32(sc[kb]);
-      if (hl == 0) red[t & 1][wave][kb * 32 + col] = tot;
+      if (hl == 0) red[st][wave][kb * 32 + col] = tot;
     }
   };
 
   const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;   // first key of an edge tile
+  // step i takes tile t = ntile - 1 - i from ring stage i % 2
   if (wave_rows) {
-    for (int t = 0; t < ntile; ++t) {
+    for (int i = 0; i < ntile; ++i) {
+      const int t = ntile - 1 - i;
       wait_vm<0>();
       lds_barrier();
-      if (t > 0) reduce_tile(t - 1);
-      if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
-      if (c0 + t * KT > edge_from) tile(t, std::true_type{});
-      else tile(t, std::false_type{});
+      if (i > 0) reduce_tile(t + 1, (i - 1) & 1);
+      if (i + 1 < ntile) fill.issue(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
+      if (c0 + t * KT > edge_from) tile(t, i & 1, std::true_type{});
+      else tile(t, i & 1, std::false_type{});
     }
   } else {   // the same loads, barriers and reductions, no arithmetic
-    for (int t = 0; t < ntile; ++t) {
+    for (int i = 0; i < ntile; ++i) {
+      const int t = ntile - 1 - i;
       wait_vm<0>();
       lds_barrier();
-      if (t > 0) reduce_tile(t - 1);
-      if (t + 1 < ntile) fill.issue(kb8, vb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+      if (i > 0) reduce_tile(t + 1, (i - 1) & 1);
+      if (i + 1 < ntile) fill.issue(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
     }
   }
   lds_barrier();
-  if (ntile > 0) reduce_tile(ntile - 1);
+  if (ntile > 0) reduce_tile(0, (ntile - 1) & 1);
   lds_barrier();
   float* sout = a.sraw + (static_cast<size_t>(rg) * a.Hkv + h) * a.T + base;
   for (int i = tid; i < c1 - c0; i += WG) sout[c0 + i] = sbuf[i];
