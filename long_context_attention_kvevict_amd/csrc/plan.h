@@ -52,9 +52,9 @@ struct SelectGeom {
   int64_t total_B;
   size_t off_a, off_b;             // sampling: fp64 planes [Hkv][T]
   size_t off_hist;                 // int [levels][S*Hkv][kSelBins]
-  size_t off_ncand;                // top-k: int [S*Hkv] keys sharing the threshold's leading digits
+  size_t off_ncand;                // int [S*Hkv] keys sharing the threshold's leading digits
   size_t zero_end;                 // [off_hist, zero_end) is cleared on entry
-  size_t off_cand;                 // top-k: int [S*Hkv][max_len][2] those keys (index, last digit)
+  size_t off_cand;                 // int [S*Hkv][max_len][2] those keys (index, last digit)
   size_t off_cnt;                  // int [S*Hkv][nchunk][2]
   size_t off_rstate;               // [S*Hkv] radix threshold state (kSelRStateBytes each)
   size_t off_part;                 // sampling: double [2][S*Hkv][nchunk][3]

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   }
 }
 
-// Last digit level of the fp32 top-k, which also leaves the ordered write
+// Last digit level of the radix select, which also leaves the ordered write
 // what a separate count launch would: per chunk, the number of keys whose
 // leading digits (levels 0 .. LEVELS-2) exceed those of the threshold, and
 // per (sequence, head) a list of the keys that share them (index, last
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
   }
 }
 
-// Ordered write of the fp32 top-k from sel_hist_last's counts: the
+// Ordered write from sel_hist_last's counts: the
 // threshold is resolved here from the finished histograms (as sel_count
 // does), the keys above it in earlier chunks are the per-chunk counts of
 // larger leading digits plus the listed keys with a larger last digit, and
@@ -1229,9 +1229,14 @@ static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bi
                          int2* cand = nullptr) {
   typedef typename Src::K K;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
-  if (Radix<K>::LEVELS == 3 && ncand && a.bsh == nullptr) {   // fp32 top-k: no count launch
+  if (ncand && a.bsh == nullptr) {   // no count launch (not under a soft budget)
     hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     hipLaunchKernelGGL((sel_hist<Src, 1>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    if (Radix<K>::LEVELS > 3) {
+      hipLaunchKernelGGL((sel_hist<Src, 2>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+      hipLaunchKernelGGL((sel_hist<Src, 3>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+      hipLaunchKernelGGL((sel_hist<Src, 4>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    }
     hipLaunchKernelGGL((sel_hist_last<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, ncand, cand, G.max_len,
                        cnt);
     hipLaunchKernelGGL((sel_write_listed<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, hist, cnt,
@@ -1318,7 +1323,8 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     hipLaunchKernelGGL(smp_decide, dim3(G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
                        status_out);
     const SnisBias bias_of{A.L, A.mvals, 1.0 / static_cast<double>(tau_w)};
-    launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st);
+    launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st,
+                 reinterpret_cast<int*>(wsb + G.off_ncand), reinterpret_cast<int2*>(wsb + G.off_cand));
   }
   stage_end(ST_SELECT, st);
   return hipGetLastError();
