@@ -58,8 +58,10 @@ int32_t kvevict_timing_enable(int32_t stage_mask) {
   if (stage_mask && g.pool.empty()) {
     g.pool.reserve(kPool);
     for (size_t i = 0; i < kPool; ++i) {
+      // Timing only: no system-scope fence (cache write-back and invalidate)
+      // when an event is recorded, which would slow the kernel after it.
       hipEvent_t e;
-      if (hipEventCreate(&e) != hipSuccess) return KVE_EHIP;
+      if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return KVE_EHIP;
       g.pool.push_back(e);
     }
   }
