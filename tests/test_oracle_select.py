@@ -151,30 +151,76 @@ def _exact_inclusion(pi, B):
 
 @pytest.mark.parametrize("n,B", [(4, 1), (5, 2), (6, 3)])
 def test_gumbel_topB_is_sampling_without_replacement(n, B):
+    # [PI] §4: the kept set is B draws without replacement from the tempered
+    # proposal.  The oracle's own gumbel_keys, evaluated for 2e5 seeds at
+    # once (its Philox counter takes the seed as a broadcast array), must
+    # give inclusion frequencies of its top B equal to the exact inclusion
+    # probabilities of sequential draws without replacement (enumerated).
+    from oracle.select import gumbel_keys, proposal_log
     rng = np.random.default_rng(n * 10 + B)
     s = rng.uniform(0.05, 1.0, size=n)
     tau = 0.5
     pi = proposal(s, tau)
     exact = _exact_inclusion(pi, B)
     seeds = 200000
-    from oracle.select import proposal_log
-    lp = proposal_log(s, tau)
-    # draw u for every seed in one vectorised Philox call
-    j = np.tile(np.arange(n, dtype=np.uint64), seeds)
-    sd = np.repeat(np.arange(seeds, dtype=np.uint64), n)
-    x0 = philox4x64_10(j, np.uint64(0), np.uint64(0), np.uint64(0), sd, np.uint64(0))[0]
-    u = ((x0 >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
-    kappa = (lp[None, :] - np.log(-np.log(u.reshape(seeds, n))))
+    kappa = gumbel_keys(proposal_log(s, tau), np.arange(seeds, dtype=np.uint64)[:, None], 0, 0)
+    assert kappa.shape == (seeds, n)
     top = np.argsort(-kappa, axis=1, kind="stable")[:, :B]
+    freq = np.bincount(top.ravel(), minlength=n) / seeds
+    sigma = np.sqrt(exact * (1 - exact) / seeds)
+    assert np.all(np.abs(freq - exact) <= 4 * sigma + 1e-9), (freq, exact)
+
+
+def test_sample_select_kept_set_law():
+    # The same law through sample_select itself (one call per seed): its
+    # kept sets over 12000 seeds have the exact without-replacement
+    # inclusion probabilities, and each one is the top B of that seed's keys.
+    from oracle.select import gumbel_keys, proposal_log
+    n, B, tau = 5, 2, 0.5
+    s = np.random.default_rng(52).uniform(0.05, 1.0, size=n)
+    exact = _exact_inclusion(proposal(s, tau), B)
+    seeds = 12000
     freq = np.zeros(n)
-    for b in range(B):
-        freq += np.bincount(top[:, b], minlength=n)
+    lp = proposal_log(s, tau)
+    for sd in range(seeds):
+        idx, _, _, st = sample_select(s, B, tau, 1.0, sd, 0, 0)
+        assert st == 0 and len(idx) == B and np.all(np.diff(idx) > 0)
+        freq[idx] += 1
+        if sd < 200:
+            kap = gumbel_keys(lp, sd, 0, 0)
+            assert set(idx) == set(np.argsort(-kap, kind="stable")[:B])
     freq /= seeds
     sigma = np.sqrt(exact * (1 - exact) / seeds)
     assert np.all(np.abs(freq - exact) <= 4 * sigma + 1e-9), (freq, exact)
-    # the oracle's sample_select uses the same keys
-    idx, _, _, _ = sample_select(s, B, tau, 1.0, 7, 0, 0)
-    assert len(idx) == B and np.all(np.diff(idx) > 0)
+
+
+def test_sample_select_weight_temperature():
+    # [PI] §6 Eq. 10: the importance weight w is tempered as exp(log(w) /
+    # tau_w).  The weight of a kept entry is 1/q_j with q_j the chance that
+    # j shows up in m draws with replacement; estimate q_j by simulating
+    # those draws, and check bias * tau_w = -log q_j for several tau_w
+    # (tau_w = inf would give every entry weight 1).
+    rng = np.random.default_rng(17)
+    n, B, tau = 12, 4, 0.8
+    s = rng.uniform(0.01, 1.0, size=n)
+    pi = proposal(s, tau)
+    biases = {}
+    for tw in (1.0, 0.5, 2.0, 3.0):
+        idx, bias, m, st = sample_select(s, B, tau, tw, 9, 0, 0)
+        assert st == 0
+        biases[tw] = (idx, bias, m)
+    idx1, b1, m1 = biases[1.0]
+    for tw, (idx, bias, m) in biases.items():
+        assert np.array_equal(idx, idx1) and m == m1   # tau_w changes weights only
+        assert np.allclose(bias * tw, b1, rtol=1e-13, atol=0)
+    trials = 200000
+    draws = rng.choice(n, size=(trials, int(m1)), p=pi)
+    seen = np.zeros((trials, n), dtype=bool)
+    seen[np.arange(trials)[:, None], draws] = True
+    q_mc = seen.mean(axis=0)[idx1]
+    sig = np.sqrt(q_mc * (1 - q_mc) / trials)
+    q_or = np.exp(-b1)
+    assert np.all(np.abs(q_or - q_mc) <= 4 * sig + 1e-9), (q_or, q_mc)
 
 
 # ---------------------------------------------------------------- weights
