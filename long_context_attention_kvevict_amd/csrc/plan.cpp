@@ -83,7 +83,7 @@ kve_status plan_score(const kve_layout* L, ScoreGeom* G, std::string* msg) {
   g.pool_rg = (L->dtype == KVE_BF16) ? g.RG : 1;
   const size_t groups = static_cast<size_t>(g.S) * g.Hkv * g.RG;
   size_t off = 0;
-  g.off_part_ml = off; off = align256(off + groups * g.P * 128 * 2 * sizeof(float));
+  g.off_part_ml = off; off = align256(off + groups * g.P * 128 * kScoreRec * sizeof(float));
   g.off_part_o = off;  off = align256(off + groups * g.P * 128 * static_cast<size_t>(g.d) * sizeof(float));
   g.off_vnorm = off;   off = align256(off + static_cast<size_t>(g.Hkv) * g.T * sizeof(float));
   g.off_lse2 = off;    off = align256(off + groups * 128 * sizeof(float));
@@ -94,6 +94,8 @@ kve_status plan_score(const kve_layout* L, ScoreGeom* G, std::string* msg) {
   g.off_ohi = off;     off = align256(off + groups * 128 * static_cast<size_t>(g.d) * oel);
   g.off_olo = off;     off = align256(off + groups * 128 * static_cast<size_t>(g.d) * 2);
   g.off_sraw = off;    off = align256(off + static_cast<size_t>(g.pool_rg) * g.Hkv * g.T * sizeof(float));
+  g.off_jstar = off;   off = align256(off + groups * 128 * sizeof(int32_t));
+  g.off_cstar = off;   off = align256(off + groups * 128 * sizeof(float));
   g.bytes = off;
   *G = g;
   return KVE_OK;

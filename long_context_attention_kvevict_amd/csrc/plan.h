@@ -15,6 +15,12 @@ namespace kve {
 // are sized for it).
 constexpr int kScoreChunkMax = 2048;
 
+// Floats per (window row, key chunk) record of the scorer's first pass: the
+// softmax reference m, the weight sum of every key but the row's candidate
+// for a dominant key, that candidate's weight and key (int bits), and the
+// rounding error of the weight its P.V contraction used; 3 spare.
+constexpr int kScoreRec = 8;
+
 // Geometry of one kvevict_score call; the workspace is carved into the
 // regions below (byte offsets, each 256-byte aligned).
 struct ScoreGeom {
@@ -25,7 +31,8 @@ struct ScoreGeom {
   int CH;       // keys per chunk (multiple of 256)
   int P;        // chunks per sequence (grid x), ceil(max_len / CH)
   int pool_rg;  // partial score planes summed by the pool kernel
-  size_t off_part_ml, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw;
+  size_t off_part_ml, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw, off_jstar,
+      off_cstar;
   size_t bytes;
 };
 

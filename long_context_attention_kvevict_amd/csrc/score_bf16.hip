@@ -41,6 +41,7 @@ constexpr int ROWB = D * 2;     // bytes per K/V row
 constexpr int TILE_BYTES = KT * ROWB;          // one K (or V) tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // K tile then V tile
 static_assert(kScoreChunkMax % KT == 0, "chunk bound must be a multiple of the tile");
+static_assert(kScoreChunkMax / KT <= 32, "pass 2 marks a chunk's tiles in a 32-bit mask");
 
 // Slot s of a 32-key block holds key keymap(s): bits 2 and 3 swapped.  With
 // this order the P values a lane holds after the K.Q^T MFMA are 8
@@ -78,7 +79,7 @@ struct ScoreArgs {
   const int32_t* seq_off;  // [S+1]
   int S, Hq, Hkv, w, T, RG, CH, P, causal;
   float c2;                // sm_scale * log2(e)
-  float* part_ml;          // [S*Hkv*RG][P][ROWS][2]
+  float* part_ml;          // [S*Hkv*RG][P][ROWS][kScoreRec]
   float* part_o;           // [S*Hkv*RG][P][ROWS][D]
   float* vnorm;            // [Hkv][T]
   float* lse2;             // [S*Hkv*RG][ROWS]
@@ -87,6 +88,8 @@ struct ScoreArgs {
   uint16_t* ohi;           // [S*Hkv*RG][ROWS][D]  bf16 of -2 o
   uint16_t* olo;           // residual
   float* sraw;             // [RG][Hkv][T]
+  int32_t* jstar;          // [S*Hkv*RG][ROWS]  key holding over half of the row's weight, or -1
+  float* cstar;            // [S*Hkv*RG][ROWS]  that pair's exact term (a / (1 - a))^2 ||o - v||^2
 };
 
 // Work item of a workgroup of either pass.  The RG row groups of one
@@ -140,6 +143,12 @@ __device__ __forceinline__ float sum_xor32(float v) {
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// The values lanes l % 32 and l % 32 + 32 hold, in that order, on both.
+__device__ __forceinline__ void halves(uint32_t v, uint32_t* h0, uint32_t* h1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  *h0 = r[0];
+  *h1 = r[1];
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -221,6 +230,10 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 
   __shared__ __align__(1024) char ring[NSTAGE * STAGE_BYTES];
   __shared__ __align__(16) float vn[kScoreChunkMax];
+  // per lane: candidate key, its weight's rounding error, and l_run before
+  // the current tile (kept out of registers; only rare paths read them)
+  __shared__ int cand_j[WG];
+  __shared__ float cand_e[WG], cand_lb[WG];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -268,6 +281,17 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   // rescaled only when the max climbs by more than 8 (log2 units).
   float m_run = -INFINITY;
   float l_run = 0.f;
+  // A key can hold over half of its row's final weight only if, on its
+  // tile, its weight exceeds half of the row's running sum; such tiles take
+  // the residual branch below, which makes this lane's largest weight of the
+  // tile the lane's candidate when it exceeds the recorded one.  The
+  // candidate's weight pc is kept out of l_run (so the sum of the other
+  // keys, 1 - a up to the row sum, carries no cancellation), together with
+  // its key (cand_j) and the rounding error (cand_e) of the weight P.V used
+  // for it.
+  float pc = 0.f;
+  cand_j[tid] = -1;
+  cand_e[tid] = 0.f;
 
   // loop-invariant LDS offsets (the second 32-key half adds 32 rows = 8 KiB;
   // the swizzle depends on the row mod 16 only)
@@ -359,9 +383,12 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) oacc[i] *= scale;
       l_run *= scale;
+      pc *= scale;
+      cand_e[tid] *= scale;
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    cand_lb[tid] = l_run;
 
     f32x8 pf[2][2];
     bf16x8 pb[2][2];
@@ -409,7 +436,28 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
     // 2^-17.  (Early tiles of a chunk, where the running sum is still small,
     // are the ones that take this path.)
     const float pmax = __builtin_amdgcn_exp2f(tmax - m_use);
-    if (__any(2.f * pmax > sum_xor32(l_run))) {
+    if (__any(2.f * pmax > sum_xor32(l_run + pc))) {
+      float pm = 0.f;   // this lane's largest weight of the tile
+#pragma unroll
+      for (int i = 0; i < 32; ++i) pm = fmaxf(pm, pf[i >> 4][(i >> 3) & 1][i & 7]);
+      if (pm > pc) {
+        // new candidate: the first of this lane's keys (in key order) with
+        // that weight; the previous one joins the other keys
+        int eb = 0;
+#pragma unroll
+        for (int i = 31; i >= 0; --i) eb = (pf[i >> 4][(i >> 3) & 1][i & 7] == pm) ? i : eb;
+        float lsum = cand_lb[tid] + pc;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) lsum += (i == eb) ? 0.f : pf[i >> 4][(i >> 3) & 1][i & 7];
+        // P.V used its weight as the bf16 value plus the bf16 residual,
+        // formed exactly as above
+        const float wh = static_cast<float>(static_cast<__bf16>(pm));
+        const float wl = static_cast<float>(static_cast<__bf16>(pm - wh));
+        l_run = lsum;
+        pc = pm;
+        cand_e[tid] = (wh + wl) - pm;
+        cand_j[tid] = kt0 + (eb >> 4) * 32 + p1_key_of(eb & 15, hl);
+      }
       bf16x8 pr[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -423,6 +471,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
           pr[kb][k2] = __builtin_convertvector(rem, bf16x8);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       pv(pr);
     }
   };
@@ -440,13 +489,24 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   // ||v||^2 of the chunk
   for (int i = tid; i < c1 - c0; i += WG) a.vnorm[static_cast<size_t>(h) * a.T + base + c0 + i] = vn[i];
 
-  const float l_tot = sum_xor32(l_run);
+  // The row's candidate is the larger weight of its two halves' (the lower
+  // key on equal weights); the other half's candidate joins the other keys.
+  uint32_t p0, p1, e0, e1, j0, j1, l0, l1;
+  halves(__float_as_uint(pc), &p0, &p1);
+  halves(__float_as_uint(cand_e[tid]), &e0, &e1);
+  halves(static_cast<uint32_t>(cand_j[tid]), &j0, &j1);
+  halves(__float_as_uint(l_run), &l0, &l1);
   if (!row_ok) return;
   const size_t part = (static_cast<size_t>((s * a.Hkv + h) * a.RG + rg)) * a.P + c;
   const int rl = wave * 32 + col;
   if (hl == 0) {
-    a.part_ml[(part * ROWS + rl) * 2 + 0] = m_run;
-    a.part_ml[(part * ROWS + rl) * 2 + 1] = l_tot;
+    const float pa = __uint_as_float(p0), pb = __uint_as_float(p1);
+    const bool first = (pa > pb) || (pa == pb && static_cast<int>(j0) <= static_cast<int>(j1));
+    const float lo = (__uint_as_float(l0) + __uint_as_float(l1)) + (first ? pb : pa);
+    float* rec = a.part_ml + (part * ROWS + rl) * kScoreRec;
+    *reinterpret_cast<f32x4*>(rec) =
+        f32x4{m_run, lo, first ? pa : pb, __uint_as_float(first ? j0 : j1)};
+    *reinterpret_cast<f32x4*>(rec + 4) = f32x4{__uint_as_float(first ? e0 : e1), 0.f, 0.f, 0.f};
   }
   float* op = a.part_o + (part * ROWS + rl) * D;
 #pragma unroll
@@ -465,6 +525,15 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 // (lane = DD/32 consecutive features), then combine through LDS in a fixed
 // order.  Chunks wholly beyond a row's causal horizon carry max = -inf and
 // weight 0.
+//
+// A row whose best candidate key (largest weight over the chunks'
+// candidates, the lower key on equal weights) holds over half of the row's weight takes
+// the exact form of its term ("DropKV" page, §3.2: the perturbation of
+// dropping one key is a / (1 - a) ||o - v_j||): 1 - a is the summed weight
+// of every other key, o loses the rounding error of the candidate's weight,
+// and ||o - v_j||^2 is summed from the explicit difference.  Any key with a
+// weight above one half has the row's unique largest weight and was
+// recorded as a candidate on its tile, so this covers every such row.
 template <int DD, bool BF16OUT>
 __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   constexpr int F = DD / 32;
@@ -475,8 +544,10 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   const int tid = threadIdx.x;
   const int st = tid >> 5, ln = tid & 31;
   const int s = grp / (a.Hkv * a.RG);
+  const int h = (grp / a.RG) % a.Hkv;
   const int rg = grp % a.RG;
-  const int n = a.seq_off[s + 1] - a.seq_off[s];
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
   const int nch = (n + a.CH - 1) / a.CH;
   const int R = (a.Hq / a.Hkv) * a.w;
   const size_t ro = static_cast<size_t>(gr);
@@ -484,7 +555,11 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
     if (tid == 0) {
       a.lse2[ro] = INFINITY;
       a.no2[ro] = 0.f;
-      if (BF16OUT) a.no2d[ro] = 0.f;
+      if (BF16OUT) {
+        a.no2d[ro] = 0.f;
+        a.jstar[ro] = -1;
+        a.cstar[ro] = 0.f;
+      }
     }
     if (tid < 32) {
 #pragma unroll
@@ -496,11 +571,11 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
     return;
   }
   __shared__ float red_o[NSTR][DD];
-  __shared__ float red_l[NSTR];
+  __shared__ float red_l[NSTR][4];   // others' sum, candidate weight, key, rounding error
   __shared__ float red_m[4];
-  const size_t cstride_ml = static_cast<size_t>(ROWS) * 2;
+  const size_t cstride_ml = static_cast<size_t>(ROWS) * kScoreRec;
   const size_t cstride_o = static_cast<size_t>(ROWS) * DD;
-  const float* ml = a.part_ml + (static_cast<size_t>(grp) * a.P * ROWS + rl) * 2;
+  const float* ml = a.part_ml + (static_cast<size_t>(grp) * a.P * ROWS + rl) * kScoreRec;
   const float* po = a.part_o + (static_cast<size_t>(grp) * a.P * ROWS + rl) * DD + ln * F;
   float M = -INFINITY;
   for (int c = tid; c < nch; c += 256) M = fmaxf(M, ml[c * cstride_ml]);
@@ -508,16 +583,30 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   if ((tid & 63) == 0) red_m[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  float L = 0.f;
+  // per stream: sum of the non-candidate weights (the candidates that lose
+  // to a better one included) and the best candidate (weight, key, rounding
+  // error), all scaled to the reference M
+  float L = 0.f, cp = 0.f, ce = 0.f;
+  int cj = -1;
   float acc[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
 #pragma unroll 4
   for (int c = st; c < nch; c += NSTR) {
-    const float m = ml[c * cstride_ml];
-    const float l = ml[c * cstride_ml + 1];
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(ml + c * cstride_ml);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(ml + c * cstride_ml + 4);
+    const float m = r0[0];
     const float wgt = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    L = fmaf(l, wgt, L);
+    L = fmaf(r0[1], wgt, L);
+    const int jk = static_cast<int>(__float_as_uint(r0[3]));
+    const float pk = r0[2] * wgt, ek = r1[0] * wgt;
+    // chunks come in key order, so on equal weights the earlier key stays
+    if (pk > cp) {
+      L += cp;
+      cp = pk; cj = jk; ce = ek;
+    } else {
+      L += pk;
+    }
     if (F == 4) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(po + c * cstride_o);
 #pragma unroll
@@ -529,25 +618,55 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   }
 #pragma unroll
   for (int f = 0; f < F; ++f) red_o[st][ln * F + f] = acc[f];
-  if (ln == 0) red_l[st] = L;
+  if (ln == 0) {
+    red_l[st][0] = L;
+    red_l[st][1] = cp;
+    red_l[st][2] = __uint_as_float(static_cast<uint32_t>(cj));
+    red_l[st][3] = ce;
+  }
   __syncthreads();
   if (tid >= 32) return;
   L = 0.f;
+  cp = 0.f; ce = 0.f; cj = -1;
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
 #pragma unroll
   for (int k = 0; k < NSTR; ++k) {
-    L += red_l[k];
+    L += red_l[k][0];
+    const float pk = red_l[k][1];
+    const int jk = static_cast<int>(__float_as_uint(red_l[k][2]));
+    if (pk > cp || (pk == cp && jk >= 0 && jk < cj)) {
+      L += cp;
+      cp = pk; cj = jk; ce = red_l[k][3];
+    } else {
+      L += pk;
+    }
 #pragma unroll
     for (int f = 0; f < F; ++f) acc[f] += red_o[k][ln * F + f];
   }
-  const float inv = 1.f / L;
-  float sq = 0.f, sqh = 0.f;
+  const float Lt = L + cp;
+  // the candidate's exact term needs its weight above half of the row's
+  const bool dom = BF16OUT && cj >= 0 && 2.f * cp > Lt;
+  float vs[F];
+  if (dom) {
+    const uint16_t* vr = a.v + (static_cast<size_t>(h) * a.T + base + cj) * DD + ln * F;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      vs[f] = bf16_to_f32(vr[f]);
+      acc[f] = fmaf(-ce, vs[f], acc[f]);
+    }
+  }
+  const float inv = 1.f / Lt;
+  float sq = 0.f, sqh = 0.f, dd = 0.f;
   uint16_t hi[F], lo[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) {
     acc[f] *= inv;
     sq = fmaf(acc[f], acc[f], sq);
+    if (dom) {
+      const float df = acc[f] - vs[f];
+      dd = fmaf(df, df, dd);
+    }
     if (BF16OUT) {
       const float x = -2.f * acc[f];
       hi[f] = f32_to_bf16(x);
@@ -559,12 +678,18 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   for (int o = 16; o > 0; o >>= 1) {
     sq += __shfl_xor(sq, o, 32);
     if (BF16OUT) sqh += __shfl_xor(sqh, o, 32);
+    if (dom) dd += __shfl_xor(dd, o, 32);
   }
   if (ln == 0) {
-    a.lse2[ro] = M + log2f(L);
+    a.lse2[ro] = M + log2f(Lt);
     if (BF16OUT) {
       a.no2[ro] = sqh;
       a.no2d[ro] = sq - sqh;
+      // (a / (1 - a))^2 = (cp / L)^2; a row with a single visible key
+      // (L = 0) contributes nothing for it
+      const float y = (L > 0.f) ? cp / L : 0.f;
+      a.jstar[ro] = dom ? cj : -1;
+      a.cstar[ro] = dom ? y * y * dd : 0.f;
     } else {
       a.no2[ro] = sq;
     }
@@ -592,9 +717,11 @@ constexpr float kResidX = -6.f;   // log2 p above this <=> p > 2^-6
 __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   ScoreWork wk;
   if (!score_work(a, blockIdx.x, &wk)) return;
-  const int c = wk.c, h = wk.h, rg = wk.rg, s = wk.s;
-  const int base = a.seq_off[s];
-  const int n = a.seq_off[s + 1] - base;
+  // wave-uniform work indices, held in scalar registers
+  const int c = __builtin_amdgcn_readfirstlane(wk.c), h = __builtin_amdgcn_readfirstlane(wk.h);
+  const int rg = __builtin_amdgcn_readfirstlane(wk.rg), s = __builtin_amdgcn_readfirstlane(wk.s);
+  const int base = __builtin_amdgcn_readfirstlane(a.seq_off[s]);
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_off[s + 1]) - base;
   const int c0 = c * a.CH;
   if (c0 >= n) return;
   const int c1 = min(c0 + a.CH, n);
@@ -604,6 +731,9 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   __shared__ __align__(16) float red[2][4][KT];
   __shared__ __align__(16) float rowc[2 * ROWS];
   __shared__ int rowhz[ROWS];   // causal horizon (last visible key) of each row
+  __shared__ int rowj[ROWS];      // key with over half of the row's weight, or -1
+  __shared__ float rowcs[ROWS];   // that pair's exact term
+  __shared__ uint32_t dmask[WG / 64];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -642,6 +772,18 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
     rowc[ROWS + i] = a.no2[grp * ROWS + i];
     const int rrow = rg * ROWS + i;
     rowhz[i] = (rrow < R) ? n - a.w + rrow % a.w : -1;
+    rowj[i] = a.jstar[grp * ROWS + i];
+    rowcs[i] = a.cstar[grp * ROWS + i];
+  }
+  {
+    // tiles of this chunk holding some row's dominant key (one bit each)
+    uint32_t bit = 0;
+    if (tid < ROWS) {
+      const int j = a.jstar[grp * ROWS + tid];
+      if (j >= c0 && j < c1) bit = 1u << ((j - c0) / KT);
+    }
+    for (int o = 32; o > 0; o >>= 1) bit |= __shfl_xor(bit, o, 64);
+    if (lane == 0) dmask[wave] = bit;
   }
   const float* vnb = a.vnorm + static_cast<size_t>(h) * a.T + base;
   for (int i = tid; i < c1 - c0; i += WG) sbuf[i] = vnb[c0 + i];
@@ -732,11 +874,13 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
         for (int e = 0; e < 4; ++e) sacc[kb][4 * q4 + e] = fmaf(sacc[kb][4 * q4 + e], a.c2, -lv[e]);
       }
       if constexpr (EDGE) {
+        // also hides each row's dominant key: its exact term is added after
+        // the tiles
         const int key = kt0 + kb * 32 + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int hz = rowhz[wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
-          const bool hidden = (key >= c1) | (causal & (key > hz));
+          const int ri = wave * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool hidden = (key >= c1) | (causal & (key > rowhz[ri])) | (key == rowj[ri]);
           sacc[kb][r] = hidden ? -INFINITY : sacc[kb][r];
         }
       }
@@ -786,6 +930,8 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   };
 
   const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;   // first key of an edge tile
+  // tiles holding some row's dominant key take the masking tile body
+  const uint32_t dtiles = __builtin_amdgcn_readfirstlane(dmask[0] | dmask[1] | dmask[2] | dmask[3]);
   // step i takes tile t = ntile - 1 - i from ring stage i % 2
   if (wave_rows) {
     for (int i = 0; i < ntile; ++i) {
@@ -794,7 +940,7 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
       lds_barrier();
       if (i > 0) reduce_tile(t + 1, (i - 1) & 1);
       if (i + 1 < ntile) fill.issue(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
-      if (c0 + t * KT > edge_from) tile(t, i & 1, std::true_type{});
+      if (c0 + t * KT > edge_from || ((dtiles >> t) & 1u)) tile(t, i & 1, std::true_type{});
       else tile(t, i & 1, std::false_type{});
     }
   } else {   // the same loads, barriers and reductions, no arithmetic
@@ -808,6 +954,14 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   }
   lds_barrier();
   if (ntile > 0) reduce_tile(0, (ntile - 1) & 1);
+  lds_barrier();
+  // the exact terms of the rows' dominant keys in this chunk, in row order
+  if (tid == 0) {
+    for (int i = 0; i < ROWS; ++i) {
+      const int j = rowj[i];
+      if (j >= c0 && j < c1) sbuf[j - c0] += rowcs[i];
+    }
+  }
   lds_barrier();
   float* sout = a.sraw + (static_cast<size_t>(rg) * a.Hkv + h) * a.T + base;
   for (int i = tid; i < c1 - c0; i += WG) sout[c0 + i] = sbuf[i];
@@ -833,9 +987,11 @@ template <bool VNORM>
 __global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
   ScoreWork wk;
   if (!score_work(a, blockIdx.x, &wk)) return;
-  const int c = wk.c, h = wk.h, rg = wk.rg, s = wk.s;
-  const int base = a.seq_off[s];
-  const int n = a.seq_off[s + 1] - base;
+  // wave-uniform work indices, held in scalar registers
+  const int c = __builtin_amdgcn_readfirstlane(wk.c), h = __builtin_amdgcn_readfirstlane(wk.h);
+  const int rg = __builtin_amdgcn_readfirstlane(wk.rg), s = __builtin_amdgcn_readfirstlane(wk.s);
+  const int base = __builtin_amdgcn_readfirstlane(a.seq_off[s]);
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_off[s + 1]) - base;
   const int c0 = c * a.CH;
   if (c0 >= n) return;
   const int c1 = min(c0 + a.CH, n);
@@ -980,6 +1136,8 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   a.ohi = reinterpret_cast<uint16_t*>(base + G.off_ohi);
   a.olo = reinterpret_cast<uint16_t*>(base + G.off_olo);
   a.sraw = reinterpret_cast<float*>(base + G.off_sraw);
+  a.jstar = reinterpret_cast<int32_t*>(base + G.off_jstar);
+  a.cstar = reinterpret_cast<float*>(base + G.off_cstar);
 
   const int items = G.S * G.Hkv * G.P;
   dim3 grid(8 * ((items + 7) / 8) * G.RG);

@@ -98,9 +98,13 @@ __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
     ored[tid] = o_part;
     __syncthreads();
     const size_t pr = (grp * a.P + c) * ROWS32 + rl;
-    if (tid == 0) {
-      a.part_ml[pr * 2] = m_run;
-      a.part_ml[pr * 2 + 1] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (tid == 0) {   // the record of the bf16 path with no dominant-key candidate
+      float* rec = a.part_ml + pr * kScoreRec;
+      rec[0] = m_run;
+      rec[1] = (red[0] + red[1]) + (red[2] + red[3]);
+      rec[2] = 0.f;
+      rec[3] = __uint_as_float(0xffffffffu);   // key -1
+      for (int i = 4; i < kScoreRec; ++i) rec[i] = 0.f;
     }
     if (tid < DD) {
       float o = 0.f;

@@ -99,10 +99,89 @@ def test_score_window_equals_length():
     check_scores(got, ref, "w=n")
 
 
-def test_score_dominant_key_is_finite():
-    # one key takes almost all of a row's weight (alpha -> 1).  The kernel
-    # clamps 1 - alpha at ~2^-20, so only finiteness is checked for that key
-    # (parity unpinned there); every other key must still match.
+def _plant_dominant(wl, alphas, shared_head=None, shared_alpha=0.99):
+    """Inputs where one key holds a planted share a of a window row's weight
+    ("DropKV" page, §3.2: the term a / (1 - a) ||o - v_j|| is steepest as a
+    -> 1).  KV head h < len(alphas) gets one key aligned with the query of
+    window row 7 of its group's second q-head, its norm set so that row's
+    weight on it is alphas[h]; `shared_head` gets one key aligned with the
+    group's mean query whose largest weight over the group's window rows is
+    about shared_alpha (many rows then share the dominant key, at weights
+    spread below that)."""
+    data = synth.generate(wl)
+    q = synth.to_f64(data["q_win"], wl.dtype)
+    k = synth.to_f64(data["k"], wl.dtype)
+    n, w, g, sm = wl.lens[0], wl.w, wl.g, wl.sm_scale
+    planted = {}
+    for h, a in enumerate(alphas):
+        qv = q[0, h * g + 1, 7]
+        pos = n - w + 7
+        j = 500 + 700 * h
+        x = sm * (k[h, :pos + 1] @ qv)
+        x[j] = -np.inf
+        z = np.exp(x - x.max()).sum()
+        target = x.max() + np.log(z * a / (1 - a))        # logit giving weight a
+        k[h, j] = qv * target / (sm * (qv @ qv))
+        planted[h] = (j, a)
+    if shared_head is not None:
+        h = shared_head
+        rows = q[0, h * g:(h + 1) * g].reshape(g * w, -1)
+        qm = rows.mean(0)
+        qm /= np.linalg.norm(qm)
+        j = 333
+        proj = rows @ qm
+        x_other = np.log(np.exp(sm * (rows @ k[h, :n - w].T)).sum(1))
+        need = x_other + np.log(shared_alpha / (1 - shared_alpha))
+        k[h, j] = qm * np.min((need / (sm * proj))[proj > 0])
+        planted[h] = (j, shared_alpha)
+    if wl.dtype == "bf16":
+        data["k"] = synth.f32_to_bf16_bits(k.astype(np.float32))
+    else:
+        data["k"] = k.astype(np.float32)
+    return data, planted
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_score_dominant_key(dtype):
+    # a in {0.9, 0.99, 0.997, 0.999} for one row of KV heads 0..3, and a key
+    # of KV head 4 holding up to 0.999 of many rows' weight; every key
+    # compared, with and without pooling (no mask)
+    wl = dataclasses.replace(workloads.llama8b_32k(), name=f"dominant_{dtype}", Hq=20, Hkv=5, lens=[4099],
+                             needles=0, sinks=0, dtype=dtype)
+    alphas = [0.9, 0.99, 0.997, 0.999]
+    data, planted = _plant_dominant(wl, alphas, shared_head=4, shared_alpha=0.999)
+    r = Run(wl, data)
+    from oracle.attention import window_attention, row_positions
+    q, k, v = r.f64("q_win"), r.f64("k"), r.f64("v")
+    g, n, w = wl.g, wl.lens[0], wl.w
+    for h, a in enumerate(alphas):      # the planted weights after rounding the key
+        att = window_attention(q[0, h * g + 1, 7][None], k[h], v[h], [n - w + 7], wl.sm_scale)
+        got_a = att["alpha"][0, planted[h][0]]
+        say(f"[gpu] planted head {h}: weight {got_a:.6f} (target {a})")
+        assert abs(np.log((1 - got_a) / (1 - a))) < 0.3
+    rows = q[0, 4 * g:5 * g].reshape(g * w, -1)
+    att = window_attention(rows, k[4], v[4], np.tile(row_positions(n, w), g), wl.sm_scale)
+    sa = att["alpha"][:, planted[4][0]]
+    say(f"[gpu] shared key weights: min {sa.min():.4f} median {np.median(sa):.4f} max {sa.max():.6f}, "
+        f"{(sa > 0.5).sum()} rows above 1/2")
+    assert (sa > 0.5).sum() >= 16 and sa.max() < 0.9995
+    for pool in (1, 7):
+        got = r.b.score(r.q, r.k, r.v, wl.sm_scale, pool_kernel=pool)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        ref = score_workload(q, k, v, wl.seq_off(), wl.Hq, wl.Hkv, wl.sm_scale, True, pool, pooled=pool > 1)
+        for h in range(wl.Hkv):
+            j = planted[h][0]
+            worst, _ = check_scores(got[h], ref[h], f"dominant {dtype} pool {pool} h{h}")
+            say(f"[gpu] dominant {dtype} pool {pool} h{h}: max rel {worst:.2e}, planted key rel "
+                f"{abs(got[h, j] - ref[h, j]) / ref[h, j]:.2e}")
+
+
+def test_score_dominant_key_underflow_is_finite():
+    # a key whose logit exceeds every other of its row by ~440 nats: in fp32
+    # the other keys' weights underflow beside it, so the pair's term (which
+    # the oracle gives as the squared distance of that value from the others'
+    # average) is not formed; outputs stay finite and every other key matches
     wl = dataclasses.replace(workloads.llama8b_32k(), name="dominant", lens=[1024], needles=0, sinks=0)
     data = synth.generate(wl)
     q = synth.to_f64(data["q_win"], "bf16")
