@@ -17,9 +17,10 @@ constexpr int kScoreChunkMax = 2048;
 
 // Floats per (window row, key chunk) record of the scorer's first pass: the
 // softmax reference m, the weight sum of every key but the row's candidate
-// for a dominant key, that candidate's weight and key (int bits), and the
-// rounding error of the weight its P.V contraction used; 3 spare.
-constexpr int kScoreRec = 8;
+// for a dominant key, and that candidate's weight and key (int bits).  The
+// rounding error of the weight its P.V contraction used has a plane of its
+// own (only the merge of a row with a dominant key reads it).
+constexpr int kScoreRec = 4;
 
 // Geometry of one kvevict_score call; the workspace is carved into the
 // regions below (byte offsets, each 256-byte aligned).
@@ -31,7 +32,7 @@ struct ScoreGeom {
   int CH;       // keys per chunk (multiple of 256)
   int P;        // chunks per sequence (grid x), ceil(max_len / CH)
   int pool_rg;  // partial score planes summed by the pool kernel
-  size_t off_part_ml, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw, off_jstar,
+  size_t off_part_ml, off_part_e, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw, off_jstar,
       off_cstar;
   size_t bytes;
 };
@@ -41,14 +42,15 @@ struct ScoreGeom {
 // keys, per-head state slots, the points of the coarse expected-samples
 // grid that brackets the search, and the step budget of the search that
 // follows (a safeguarded Newton iteration in log m; started from the grid
-// it needs at most 3 evaluations on the score distributions tried).
+// it needed at most 3 updates on the proposals tried; a head still outside
+// the band afterwards finishes with the pages' integer binary search).
 constexpr int kSelChunk = 1024;
 constexpr int kSmpChunk = 1024;       // keys per workgroup of the sampling passes
 constexpr int kSelBins = 2048;
 constexpr int kSelLevels32 = 3;
 constexpr int kSelLevels64 = 6;
 constexpr int kSelGrid = 32;
-constexpr int kSelSearchSteps = 5;
+constexpr int kSelSearchSteps = 3;
 constexpr int kSelRStateBytes = 16;   // per-head radix threshold and count of equal keys kept
 constexpr int kSelSearchBytes = 32;   // per-head search state
 

@@ -80,6 +80,7 @@ struct ScoreArgs {
   int S, Hq, Hkv, w, T, RG, CH, P, causal;
   float c2;                // sm_scale * log2(e)
   float* part_ml;          // [S*Hkv*RG][P][ROWS][kScoreRec]
+  float* part_e;           // [S*Hkv*RG][P][ROWS] rounding error of the candidate's weight
   float* part_o;           // [S*Hkv*RG][P][ROWS][D]
   float* vnorm;            // [Hkv][T]
   float* lse2;             // [S*Hkv*RG][ROWS]
@@ -503,10 +504,9 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
     const float pa = __uint_as_float(p0), pb = __uint_as_float(p1);
     const bool first = (pa > pb) || (pa == pb && static_cast<int>(j0) <= static_cast<int>(j1));
     const float lo = (__uint_as_float(l0) + __uint_as_float(l1)) + (first ? pb : pa);
-    float* rec = a.part_ml + (part * ROWS + rl) * kScoreRec;
-    *reinterpret_cast<f32x4*>(rec) =
+    *reinterpret_cast<f32x4*>(a.part_ml + (part * ROWS + rl) * kScoreRec) =
         f32x4{m_run, lo, first ? pa : pb, __uint_as_float(first ? j0 : j1)};
-    *reinterpret_cast<f32x4*>(rec + 4) = f32x4{__uint_as_float(first ? e0 : e1), 0.f, 0.f, 0.f};
+    a.part_e[part * ROWS + rl] = __uint_as_float(first ? e0 : e1);
   }
   float* op = a.part_o + (part * ROWS + rl) * D;
 #pragma unroll
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
     return;
   }
   __shared__ float red_o[NSTR][DD];
-  __shared__ float red_l[NSTR][4];   // others' sum, candidate weight, key, rounding error
+  __shared__ float red_l[NSTR][4];   // others' sum, candidate weight, key, chunk
   __shared__ float red_m[4];
   const size_t cstride_ml = static_cast<size_t>(ROWS) * kScoreRec;
   const size_t cstride_o = static_cast<size_t>(ROWS) * DD;
@@ -584,26 +584,25 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   __syncthreads();
   M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   // per stream: sum of the non-candidate weights (the candidates that lose
-  // to a better one included) and the best candidate (weight, key, rounding
-  // error), all scaled to the reference M
-  float L = 0.f, cp = 0.f, ce = 0.f;
-  int cj = -1;
+  // to a better one included) and the best candidate (weight, key, chunk),
+  // all scaled to the reference M
+  float L = 0.f, cp = 0.f;
+  int cj = -1, cc = 0;
   float acc[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
 #pragma unroll 4
   for (int c = st; c < nch; c += NSTR) {
     const f32x4 r0 = *reinterpret_cast<const f32x4*>(ml + c * cstride_ml);
-    const f32x4 r1 = *reinterpret_cast<const f32x4*>(ml + c * cstride_ml + 4);
     const float m = r0[0];
     const float wgt = (m == -INFINITY) ? 0.f : exp2f(m - M);
     L = fmaf(r0[1], wgt, L);
     const int jk = static_cast<int>(__float_as_uint(r0[3]));
-    const float pk = r0[2] * wgt, ek = r1[0] * wgt;
+    const float pk = r0[2] * wgt;
     // chunks come in key order, so on equal weights the earlier key stays
     if (pk > cp) {
       L += cp;
-      cp = pk; cj = jk; ce = ek;
+      cp = pk; cj = jk; cc = c;
     } else {
       L += pk;
     }
@@ -622,12 +621,12 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
     red_l[st][0] = L;
     red_l[st][1] = cp;
     red_l[st][2] = __uint_as_float(static_cast<uint32_t>(cj));
-    red_l[st][3] = ce;
+    red_l[st][3] = __uint_as_float(static_cast<uint32_t>(cc));
   }
   __syncthreads();
   if (tid >= 32) return;
   L = 0.f;
-  cp = 0.f; ce = 0.f; cj = -1;
+  cp = 0.f; cj = -1; cc = 0;
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
 #pragma unroll
@@ -637,7 +636,7 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
     const int jk = static_cast<int>(__float_as_uint(red_l[k][2]));
     if (pk > cp || (pk == cp && jk >= 0 && jk < cj)) {
       L += cp;
-      cp = pk; cj = jk; ce = red_l[k][3];
+      cp = pk; cj = jk; cc = static_cast<int>(__float_as_uint(red_l[k][3]));
     } else {
       L += pk;
     }
@@ -649,6 +648,9 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   const bool dom = BF16OUT && cj >= 0 && 2.f * cp > Lt;
   float vs[F];
   if (dom) {
+    // the candidate's rounding error, in the reference M
+    const float mc = ml[cc * cstride_ml];
+    const float ce = a.part_e[(static_cast<size_t>(grp) * a.P + cc) * ROWS + rl] * exp2f(mc - M);
     const uint16_t* vr = a.v + (static_cast<size_t>(h) * a.T + base + cj) * DD + ln * F;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
@@ -956,13 +958,15 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   if (ntile > 0) reduce_tile(0, (ntile - 1) & 1);
   lds_barrier();
   // the exact terms of the rows' dominant keys in this chunk, in row order
-  if (tid == 0) {
-    for (int i = 0; i < ROWS; ++i) {
-      const int j = rowj[i];
-      if (j >= c0 && j < c1) sbuf[j - c0] += rowcs[i];
+  if (dtiles) {
+    if (tid == 0) {
+      for (int i = 0; i < ROWS; ++i) {
+        const int j = rowj[i];
+        if (j >= c0 && j < c1) sbuf[j - c0] += rowcs[i];
+      }
     }
+    lds_barrier();
   }
-  lds_barrier();
   float* sout = a.sraw + (static_cast<size_t>(rg) * a.Hkv + h) * a.T + base;
   for (int i = tid; i < c1 - c0; i += WG) sout[c0 + i] = sbuf[i];
 }
@@ -1128,6 +1132,7 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   a.c2 = sm_scale * kLog2e;
   char* base = static_cast<char*>(ws);
   a.part_ml = reinterpret_cast<float*>(base + G.off_part_ml);
+  a.part_e = reinterpret_cast<float*>(base + G.off_part_e);
   a.part_o = reinterpret_cast<float*>(base + G.off_part_o);
   a.vnorm = reinterpret_cast<float*>(base + G.off_vnorm);
   a.lse2 = reinterpret_cast<float*>(base + G.off_lse2);

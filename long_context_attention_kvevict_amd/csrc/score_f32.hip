@@ -104,7 +104,6 @@ __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
       rec[1] = (red[0] + red[1]) + (red[2] + red[3]);
       rec[2] = 0.f;
       rec[3] = __uint_as_float(0xffffffffu);   // key -1
-      for (int i = 4; i < kScoreRec; ++i) rec[i] = 0.f;
     }
     if (tid < DD) {
       float o = 0.f;

@@ -865,12 +865,30 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) 
   }
 }
 
+// E(m) = sum_j -expm1(m log1p(-pi_j)) of the head (fp64, fixed order), or
+// with `mean` the mean over the sequence's heads (the soft budget, Eq. 33).
+__device__ double expected_at(const SmpArgs& A, bool mean, int s, int sh, int n, int base, double m, double* dl) {
+  const int h0 = mean ? 0 : sh - s * A.g.Hkv;
+  const int nh = mean ? A.g.Hkv : 1;
+  double v = 0.0;
+  for (int hh = 0; hh < nh; ++hh) {
+    const double* L = A.L + static_cast<size_t>(h0 + hh) * A.g.T + base;
+    for (int j = threadIdx.x; j < n; j += SEL_THREADS) v -= expm1(m * L[j]);
+  }
+  return block_sum_d(v, dl) / nh;
+}
+
 // Final m and status per (sequence, head): the first of m0, m0 + 1 in the
-// band; 10^12 and KVE_ENOCONV if the target is out of reach; the closer one
-// and KVE_ENOCONV if the search ran out of steps.  Under a soft budget the
-// band is on the heads' mean (every head of a sequence decides the same m)
-// and each head keeps floor(E_h(m) + 0.5) entries, clamped to its sequence
-// length and capacity.  One workgroup per head.
+// band; 10^12 and KVE_ENOCONV if the target is out of reach.  If neither
+// integer is in the band (the Newton steps ran out), the pages' integer
+// binary search ("A Probabilistic Interpretation of KV Cache Eviction",
+// App. F, Algorithm 2) continues on the search's bracket, widened to [0,
+// 10^12] if its ends do not straddle the target; since E rises by at most 1
+// per unit step and E(10^12) reaches the band, it ends in the band (at most
+// about 40 evaluations, in this workgroup).  Under a soft budget the band is
+// on the heads' mean (every head of a sequence decides the same m) and each
+// head keeps floor(E_h(m) + 0.5) entries, clamped to its sequence length and
+// capacity.  One workgroup per head.
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, double* m_out, int32_t* status_out) {
   const int h = blockIdx.x, s = blockIdx.y;
   const int sh = s * A.g.Hkv + h;
@@ -886,26 +904,45 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
     const Search st = A.state[((steps + 1) & 1) * SH + sh];
     const double E0 = search_sum(A, steps & 1, sh, nch, 0, dl);
     const double E1 = search_sum(A, steps & 1, sh, nch, 1, dl);
-    bool upper;   // m is m0 + 1 (or 10^12)
+    int which;   // 0: m0, 1: m0 + 1 (or 10^12), 2: found by the binary search
     if (st.done == 2.0) {
       m = kAlphaMax;
-      upper = true;
+      which = 1;
       status = KVE_ENOCONV;
     } else {
       const double target = static_cast<double>(B);
       const double m0 = fmin(floor(exp(st.u)), kAlphaMax - 1.0);
       if (fabs(E0 - target) <= 0.5) {
-        upper = false;
+        which = 0;
+        m = m0;
       } else if (fabs(E1 - target) <= 0.5) {
-        upper = true;
+        which = 1;
+        m = m0 + 1.0;
       } else {
-        upper = fabs(E1 - target) < fabs(E0 - target);
-        status = KVE_ENOCONV;
+        which = 2;
+        double lo = fmax(floor(exp(st.lo)), 0.0), hi = fmin(ceil(exp(st.hi)), kAlphaMax);
+        if (expected_at(A, A.global, s, sh, n, base, lo, dl) > target + 0.5) lo = 0.0;
+        if (expected_at(A, A.global, s, sh, n, base, hi, dl) < target - 0.5) hi = kAlphaMax;
+        m = -1.0;
+        while (lo <= hi) {
+          const double mid = floor(0.5 * (lo + hi));
+          const double e = expected_at(A, A.global, s, sh, n, base, mid, dl);
+          if (fabs(e - target) <= 0.5) {
+            m = mid;
+            break;
+          }
+          if (e < target) lo = mid + 1.0;
+          else hi = mid - 1.0;
+        }
+        if (m < 0.0) {   // unreachable when E(10^12) reaches the band
+          m = kAlphaMax;
+          status = KVE_ENOCONV;
+        }
       }
-      m = upper ? m0 + 1.0 : m0;
     }
     if (A.global) {
-      const double Eh = sum_part(A, steps & 1, sh, nch, upper ? 1 : 0, dl);
+      const double Eh = (which == 2) ? expected_at(A, false, s, sh, n, base, m, dl)
+                                     : sum_part(A, steps & 1, sh, nch, which, dl);
       const int cap = A.g.out_off[s + 1] - A.g.out_off[s];
       kept = static_cast<int>(fmin(fmax(floor(Eh + 0.5), 0.0), static_cast<double>(min(n, cap))));
     }

@@ -454,6 +454,31 @@ def test_select_ties_nan_and_budget_edges(mode):
     _select_check(r, sc, mode, 0.5, 2.0, 12345)
 
 
+def test_select_sample_search_runs_out_of_newton_steps():
+    # Uniform proposals with budgets of 99-99.9 % of n: the expected-distinct
+    # curve E(m) is flattest there, and a safeguarded Newton iteration from
+    # the coarse grid needs 3-4 updates (n = 10000, B = 9990 takes 4), more
+    # than the kernel's 3 launches.  The search must still return an m in
+    # the band of the pages' Algorithm 2 ("A Probabilistic Interpretation of
+    # KV Cache Eviction", App. F) with status OK, not KVE_ENOCONV.
+    lens = [10000, 3000, 1000, 300]
+    budgets = [9990, 2985, 990, 299]
+    wl = dataclasses.replace(workloads.tiny_fp32(), name="sel_newton", S=4, Hq=2, Hkv=2, lens=lens,
+                             budget_frac=0.0)
+    sc = np.full((2, sum(lens)), 0.37, dtype=np.float32)
+    r = type("R", (), {})()
+    r.wl = wl
+    r.b = K.Batch(lens, 2, 2, 64, 1, "f32")
+    wl.budgets = lambda: np.array(budgets, dtype=np.int32)
+    wl.bud_off = lambda: np.concatenate([[0], np.cumsum(budgets)]).astype(np.int32)
+    sc_dev = torch.from_numpy(sc).cuda()
+    _, _, m, st = r.b.select(sc_dev, budgets, mode=K.KVE_SAMPLE, tau=0.5, tau_w=1.0, seed=3)
+    torch.cuda.synchronize()
+    say(f"[gpu] newton-limit m {m.cpu().numpy().ravel()} status {st.cpu().numpy().ravel()}")
+    assert np.all(st.cpu().numpy() == 0)
+    _select_check(r, sc, K.KVE_SAMPLE, 0.5, 1.0, 3)
+
+
 @pytest.mark.parametrize("case", ["one_bin", "all_equal", "two_bins"])
 def test_select_topk_crowded_threshold_bin(case):
     # tens of thousands of keys share the threshold's leading digits (sign,
