@@ -6,12 +6,23 @@ the workload (inputs resident in HBM before timing starts).  The default
 workload is the Llama-3.1-8B-shaped layer at n = 131072 (32 q-heads, 8 KV
 heads, d = 128, w = 32, bf16, 5 % top-k budget, max-pool 7).
 
+Every timed step starts with cold caches: a 1 GiB streaming read of an
+unrelated buffer (clean lines, nothing left to write back) evicts the L2s
+and the Infinity Cache first.  `value` and `ms_per_step` are the median
+over K such steps; the back-to-back (warm) figures and those after a 512 MiB
+device write (whose dirty lines are written back during the step) are extra
+keys.
+
 Prints one JSON line with the throughput (scored tokens / s per layer), a
 roofline entry for the dominant kernel (per-launch HIP-event durations
-recorded on the launch stream over the timed steps) and the fp64 oracle timed
-on a bounded sample of the same workload on the host cores.
+recorded on the launch stream over K cold-cache steps), the HBM read
+ceiling of the device for the same bytes (plain streaming read, and the
+scorer's LDS ring with no arithmetic), the other four workloads timed the
+same way, the SNIS decode loop (eager and as one HIP graph), the merge, and
+the fp64 oracle timed on a bounded sample of the workload on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs all|none|a,b]
+                    [--no-cpu-baseline]
     python bench.py --copy-probe MIB     # plain device copy of known size (counter calibration)
 
 roofline.traffic is the HBM traffic per launch of the dominant kernel from
@@ -51,7 +62,9 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama128k")
+    ap.add_argument("--workload", default="llama128k", help="headline workload (workloads.ALL)")
+    ap.add_argument("--configs", default="all",
+                    help="further workloads timed in the same line: 'all', 'none' or a comma list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="KV heads the oracle baseline scores")
     ap.add_argument("--graph", action="store_true",
@@ -64,6 +77,9 @@ def _parse():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (5 times) and exit")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only the headline workload's K cold-cache steps, no events in the library "
+                         "(for a kernel trace whose averages are those of the roofline)")
     return ap.parse_args()
 
 
@@ -208,10 +224,12 @@ def _merge_cpu(data, wl, idx_np, budgets, tau_merge, sample=16384):
                       f"(all {evicted} evicted tokens would take {dt * evicted / pick.size:.0f} s)"}
 
 
-def _merge_leg(b, k, budgets, idx, bias, wl, tau_merge=0.9, reps=10):
+def _merge_leg(b, k, budgets, idx, bias, wl, tau_merge=0.33, reps=10):
     """kvevict_merge over the step's kept set: every evicted key against
     every kept key of its head (cosine), on bf16 MFMAs.  Algorithmic work:
-    2 d B (n - B) flops per (sequence, KV head)."""
+    2 d B (n - B) flops per (sequence, KV head).  The keys are random
+    N(0, 1) rows in 128 dimensions, whose best cosine against 6553 kept keys
+    is about 0.34: tau_merge = 0.33 merges a part of the evicted tokens."""
     import torch
     flops = sum(2.0 * wl.d * int(B) * (int(n) - int(B)) for n, B in zip(wl.lens, budgets)) * wl.Hkv
     biases = [bias.clone() for _ in range(reps + 3)]
@@ -261,29 +279,59 @@ def _decode_leg(steps_max, want_cpu):
     max_len = int(caps.max())
     out = torch.empty((wl.S, wl.Hq, wl.d), dtype=torch.float32, device=dev)
 
-    def run():
-        k_c, v_c, b_c = k0.clone(), v0.clone(), b0.clone()
-        cache_len = torch.from_numpy(budgets.copy()).to(dev)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
+    k_c, v_c, b_c = k0.clone(), v0.clone(), b0.clone()
+    cache_len = torch.from_numpy(budgets.copy()).to(dev)
+
+    def reset():
+        k_c.copy_(k0)
+        v_c.copy_(v0)
+        b_c.copy_(b0)
+        cache_len.copy_(torch.from_numpy(budgets.copy()))
+
+    def loop():
         for t in range(steps):
             rows = coff + cache_len
             k_c.index_copy_(1, rows, kd[t])
             v_c.index_copy_(1, rows, vd[t])
             b_c.index_fill_(1, rows, 0.0)
-            cache_len += 1
+            cache_len.add_(1)
             b.decode(qd[t], k_c, v_c, b_c, caps, cache_len, max_len, wl.sm_scale, out=out, cap_offsets=cap)
+
+    def run():
+        reset()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        loop()
         ev1.record()
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps
 
     run()                                    # warmup
     ms = run()
+    out_eager = out.clone()
     K.timing_enable(["decode_split", "decode_merge"])
     run()
     stages = K.timing_summary()
     K.timing_enable(False)
+    # the same loop captured as one HIP graph (appends and decode calls of
+    # every step) and replayed; the last step's output must equal the eager one
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop()
+    torch.cuda.synchronize()
+    graph_ms = []
+    for _ in range(3):
+        reset()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms.append(g0.elapsed_time(g1) / steps)
+    graph_equal = bool(torch.equal(out, out_eager))
+    del graph
     esize = 2 if wl.dtype == "bf16" else 4
     # entries read per step, averaged over the steps: sum_s (B_s + t + 1)
     entries = float(budgets.sum()) * wl.Hkv + wl.S * wl.Hkv * (steps + 1) / 2.0
@@ -295,6 +343,9 @@ def _decode_leg(steps_max, want_cpu):
         "cache_len": [int(x) for x in budgets], "steps": steps,
         "cache": "synthetic compacted cache of the batch's capacities (N(0,1) rows, sample-mode biases)",
         "ms_per_step": ms, "tokens_per_s": wl.S / (ms * 1e-3),
+        "ms_per_step_graph": float(np.median(graph_ms)), "tokens_per_s_graph": wl.S / (np.median(graph_ms) * 1e-3),
+        "graph_output_equals_eager": graph_equal,
+        "launch": f"eager: 3 appends + kvevict_decode_snis per step; graph: the {steps} steps captured as one HIP graph",
         "kernel_ms": {"decode_split": split_ms, "decode_merge": merge_ms},
         "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic("decode_split", wl.name),
@@ -319,21 +370,83 @@ def _decode_leg(steps_max, want_cpu):
     return res
 
 
-def main():
-    args = _parse()
-    if args.copy_probe:
-        _copy_probe(args.copy_probe)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
+class Probe:
+    """The memory-system probes of libkveprobe.so: a plain streaming read
+    (the HBM read ceiling; also used to evict the caches with clean lines
+    before each cold-cache step) and the scorer's ring structure with no
+    arithmetic."""
+
+    def __init__(self, dev):
+        import torch
+        path = os.path.join(ROOT, "long_context_attention_kvevict_amd", "lib", "libkveprobe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} not found; build with `python -m long_context_attention_kvevict_amd.build`")
+        self.lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        self.lib.kvp_read.argtypes = [P, ctypes.c_size_t, P, P]
+        self.lib.kvp_read_ring.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+        self.sink = torch.zeros(self.lib.kvp_read_sink_words(), dtype=torch.int32, device=dev)
+        # 1 GiB of clean lines, four times the Infinity Cache
+        self.evict_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+
+    def _st(self):
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def evict(self):
+        rc = self.lib.kvp_read(self.evict_buf.data_ptr(), self.evict_buf.numel(), self.sink.data_ptr(), self._st())
+        assert rc == 0, rc
+
+    def read(self, ptr, nbytes):
+        rc = self.lib.kvp_read(ptr, nbytes, self.sink.data_ptr(), self._st())
+        assert rc == 0, rc
+
+    def ring(self, k, v, Hkv, n, chunk):
+        rc = self.lib.kvp_read_ring(k.data_ptr(), v.data_ptr(), Hkv, n, chunk, self.sink.data_ptr(), self._st())
+        assert rc == 0, rc
+
+
+def _cold_times(probe, fn, steps):
+    """Per-call times (ms) of fn() with the caches evicted before each call:
+    the eviction read, then events around fn, all on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    evs = []
+    for _ in range(steps):
+        probe.evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def _read_ceiling(probe, k, v, wl, chunk):
+    """Cold-cache read rate of K and V of the workload: a plain streaming
+    read, and the scorer's ring structure (its grid and tiles, no arithmetic)."""
+    import numpy as np
+    nbytes = k.numel() * k.element_size()
+    assert v.numel() * v.element_size() == nbytes
+    plain = np.median(_cold_times(probe, lambda: (probe.read(k.data_ptr(), nbytes), probe.read(v.data_ptr(), nbytes)), 7))
+    n = int(wl.lens[0])
+    ring = np.median(_cold_times(probe, lambda: probe.ring(k, v, wl.Hkv, n, chunk), 7))
+    return {"plain_read_GBs": 2 * nbytes / (plain * 1e-3) / 1e9, "scorer_ring_GBs": 2 * nbytes / (ring * 1e-3) / 1e9,
+            "bytes": 2 * nbytes, "ring_chunk_keys": chunk,
+            "note": "K and V of the workload read once with the caches evicted by a 1 GiB read; plain: 16-byte "
+                    "loads from 2048 workgroups; ring: the scorer's 2-stage LDS ring of 64-key tiles, one 4-wave "
+                    "workgroup per (KV head, key chunk), no arithmetic"}
+
+
+def _eviction_leg(wl, args, probe, headline=False):
+    """Score + select + compact of one layer of `wl`, timed with the caches
+    evicted before every step (the headline figures) and back to back."""
     import numpy as np
     import torch
     from long_context_attention_kvevict_amd import kvevict as K
-    from long_context_attention_kvevict_amd import synth, workloads
+    from long_context_attention_kvevict_amd import synth
 
-    wl = workloads.ALL[args.workload]()
     print(f"# generating {wl.name}", file=sys.stderr, flush=True)
     data = synth.generate(wl)
     dev = torch.device("cuda:0")
@@ -355,22 +468,25 @@ def main():
     cmp = (torch.empty((wl.Hkv, total_C, wl.d), dtype=k.dtype, device=dev),
            torch.empty((wl.Hkv, total_C, wl.d), dtype=v.dtype, device=dev),
            torch.empty((wl.Hkv, total_C), dtype=torch.float32, device=dev))
+    score_kind = args.score_kind if headline else "perturb"
+    pool_mode = args.pool_mode if headline else "max"
 
     def step():
-        b.score(q, k, v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel, out=scores, score_kind=args.score_kind,
-                pool_mode=args.pool_mode)
+        b.score(q, k, v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel, out=scores, score_kind=score_kind,
+                pool_mode=pool_mode)
         idx, bias, _, _ = b.select(scores, budgets, mode=mode, tau=wl.tau, tau_w=wl.tau_w, seed=wl.hash_seed,
                                    out=sel, bud_offsets=bud)
         b.compact(k, v, budgets, idx, bias, caps, out=cmp, bud_offsets=bud, cap_offsets=cap)
 
-    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # The timed step is the library's eager launches, or with --graph one
-    # HIP-graph replay of them (every kernel of the step still runs).
+    if args.cold_only:
+        cold = _cold_times(probe, step, args.steps)
+        return {"workload": wl.name, "ms_per_step": float(np.median(cold)), "steps": args.steps,
+                "timing": "cold caches (1 GiB read before each step), no library events"}, None
     run = step
-    if args.graph:
+    if args.graph and headline:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
@@ -381,49 +497,53 @@ def main():
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     esize = 2 if wl.dtype == "bf16" else 4
-    sbytes = _stage_bytes(wl, esize, args.score_kind)
+    sbytes = _stage_bytes(wl, esize, score_kind)
+    K_ = args.steps
 
-    def timed(stages_timed):
-        """K steps between two events; the library records HIP events on its
-        launch stream around the kernels of `stages_timed` (None: no events)."""
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        K.timing_enable(stages_timed or False)
-        ev0.record(stream)
-        for _ in range(args.steps):
-            run()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        stages = K.timing_summary() if stages_timed else None
+    def cold_stages(stages):
+        """Mean per-launch time of `stages` over K cold steps (library events
+        on its launch stream around those kernels only)."""
+        K.timing_enable(stages)
+        _cold_times(probe, step, K_)
+        out = K.timing_summary()
         K.timing_enable(False)
-        return ev0.elapsed_time(ev1) / args.steps, stages
+        return out
 
-    # Per-stage durations of every kernel (events around all launches, eager:
-    # graph replays cannot carry the library's events); names the dominant one.
-    timed_run = run
-    run = step
-    _, stages = timed(list(K.STAGES))
-    dominant = max((s for s in stages if s in sbytes), key=lambda s: stages[s][0])
-    run = timed_run
-    if args.graph:
-        ms, _ = timed(None)
-        ms_plain = ms
-        run = step
-        _, dom = timed([dominant])
-    else:
-        # The timed region: K eager steps with HIP events around the dominant
-        # kernel only (its per-launch duration for the roofline comes from
-        # these same steps), then K steps without any events, for reference.
-        ms, dom = timed([dominant])
-        ms_plain, _ = timed(None)
-    dom_ms = dom[dominant][0]
-    print(f"# {args.steps} steps: {ms:.3f} ms/step ({'graph replay' if args.graph else 'eager'}, events around "
-          f"{dominant}); {ms_plain:.3f} ms/step without events; all-stage timing {stages}",
-          file=sys.stderr, flush=True)
+    # 1. every stage, cold: names the dominant kernel and gives the rows
+    stages = cold_stages(list(K.STAGES))
+    dominant = max((st for st in stages if st in sbytes), key=lambda st: stages[st][0])
+    # 2. the step, cold, no library events: the headline step time
+    cold = _cold_times(probe, run, K_)
+    ms = float(np.median(cold))
+    # 3. the dominant kernel alone, cold: the roofline's launch time
+    dom_ms = cold_stages([dominant])[dominant][0]
+    # 4. back to back (warm caches; the next step re-reads what the last left)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K_):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / K_
+    # 5. the previous round's flush (a 512 MiB device write before each step):
+    # its dirty lines are written back while the step runs
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    wf = []
+    for i in range(K_):
+        scratch.fill_(i & 0xff)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        run()
+        a1.record(stream)
+        wf.append((a0, a1))
+    torch.cuda.synchronize()
+    ms_write_flushed = float(np.median([x.elapsed_time(y) for x, y in wf]))
+    del scratch
+    print(f"# {wl.name}: {ms:.4f} ms/step cold (median of {K_}), {ms_warm:.4f} warm; dominant {dominant} "
+          f"{dom_ms * 1e3:.1f} us cold; stages {stages}", file=sys.stderr, flush=True)
 
     achieved = sbytes[dominant] / (dom_ms * 1e-3) / 1e9
-    # The dominant kernel's roof: HBM below the bf16 ridge (peak flops / peak
-    # bytes), the matrix cores above it (many window rows per KV head).
-    flops = _stage_flops(wl, args.score_kind).get(dominant) if wl.dtype == "bf16" else None
+    flops = _stage_flops(wl, score_kind).get(dominant) if wl.dtype == "bf16" else None
     tflops = flops / (dom_ms * 1e-3) / 1e12 if flops else None
     if flops and flops / sbytes[dominant] > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "mfma", "kernel": dominant, "achieved": tflops, "peak": MFMA_PEAK_TFLOPS,
@@ -437,17 +557,84 @@ def main():
         if flops:
             roof["algorithmic_flops"] = flops
             roof["mfma_frac"] = tflops / MFMA_PEAK_TFLOPS
-    step_bytes = sum(sbytes[s] for s in ("score_pass1", "score_pass2", "score_pool", "select", "compact"))
-    tokens_per_s = wl.T / (ms * 1e-3)
+    roof["timing"] = f"mean per-launch time over {K_} cold-cache steps, HIP events on the launch stream"
+    step_bytes = sum(sbytes[st] for st in ("score_pass1", "score_pass2", "score_pool", "select", "compact"))
+    rows = {}
+    for st, rec in stages.items():
+        if st in sbytes:
+            gbs = sbytes[st] / (rec[0] * 1e-3) / 1e9
+            rows[st] = {"ms": round(rec[0], 5), "algorithmic_bytes": sbytes[st], "GB/s": round(gbs, 1),
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            f = _stage_flops(wl, score_kind).get(st) if wl.dtype == "bf16" else None
+            if f:
+                rows[st]["mfma_frac"] = round(f / (rec[0] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
+    res = {
+        "workload": wl.name, "S": wl.S, "n": int(max(wl.lens)), "T": int(wl.T), "Hq": wl.Hq, "Hkv": wl.Hkv,
+        "d": wl.d, "w": wl.w, "dtype": wl.dtype, "mode": wl.mode, "budget_frac": wl.budget_frac,
+        "ms_per_step": ms, "tokens_per_s": wl.T / (ms * 1e-3),
+        "ms_per_step_cold_min": float(np.min(cold)),
+        "ms_per_step_warm": ms_warm, "tokens_per_s_warm": wl.T / (ms_warm * 1e-3),
+        "ms_per_step_write_flushed_median": ms_write_flushed,
+        "roofline": roof,
+        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stage_ms": {name: round(rec[0], 5) for name, rec in stages.items()},
+        "rows": rows,
+    }
+    extra = {"b": b, "k": k, "v": v, "q": q, "sel": sel, "budgets": budgets, "data": data,
+             "score_ws": int(b._lib.kvevict_score_workspace(ctypes.byref(b.layout)))}
+    return res, extra
+
+
+def _decode_graph(b, run_once, steps):
+    """The decode loop of `steps` steps captured as one HIP graph; returns ms
+    per step of its replay (appends + decode, every kernel of every step)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_once()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps / steps
+
+
+def main():
+    args = _parse()
+    if args.copy_probe:
+        _copy_probe(args.copy_probe)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from long_context_attention_kvevict_amd import workloads
+
+    dev = torch.device("cuda:0")
+    probe = Probe(dev)
+    wl = workloads.ALL[args.workload]()
+    head, ex = _eviction_leg(wl, args, probe, headline=True)
+    if args.cold_only:
+        print(json.dumps(head), flush=True)
+        return
+    b, k, v = ex["b"], ex["k"], ex["v"]
+    roof = head["roofline"]
     result = {
         "metric": "scored KV tokens/sec per layer (score+select+compact) at n=128K; % HBM peak",
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
-        "ms_per_step_without_kernel_events": ms_plain,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -457,51 +644,24 @@ def main():
                    "d": wl.d, "w": wl.w, "budget_frac": wl.budget_frac, "mode": wl.mode,
                    "pool_kernel": wl.pool_kernel, "score_kind": args.score_kind, "pool_mode": args.pool_mode,
                    "parallelism": "none (1 GPU)",
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "timing": f"median of {args.steps} steps, caches evicted before each step by a 1 GiB read"},
         "roofline": roof,
-        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stage_ms": {name: round(rec[0], 5) for name, rec in stages.items()},
     }
-    rows = {}
-    for st, rec in stages.items():
-        if st in sbytes:
-            gbs = sbytes[st] / (rec[0] * 1e-3) / 1e9
-            rows[st] = {"ms": round(rec[0], 5), "algorithmic_bytes": sbytes[st], "GB/s": round(gbs, 1),
-                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    result["rows"] = rows
+    for key in ("ms_per_step_cold_min", "ms_per_step_warm", "tokens_per_s_warm", "ms_per_step_write_flushed_median",
+                "step_hbm_frac", "stage_ms", "rows"):
+        result[key] = head[key]
     # device scratch of the scorer (the pages quote the scoring path's
     # intermediate memory at n = 128K); caller-owned, reused every step
-    result["score_workspace_bytes"] = int(b._lib.kvevict_score_workspace(ctypes.byref(b.layout)))
-    # Per-step times with the L2 / Infinity Cache flushed before every step
-    # (a 512 MiB device write between steps), median over K steps.
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    flushed = []
-    for i in range(args.steps):
-        scratch.fill_(i & 0xff)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        flushed.append(e0.elapsed_time(e1))
-    result["ms_per_step_flushed_median"] = float(np.median(flushed))
-    # device copy bandwidth on this GPU (1 GiB read + 1 GiB written)
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del scratch, src, dst
-    result["copy_GBs"] = copy_gbs
-    result["step_frac_of_copy"] = step_bytes / (ms * 1e-3) / 1e9 / copy_gbs
+    result["score_workspace_bytes"] = ex["score_ws"]
+    if wl.dtype == "bf16" and wl.S == 1 and wl.lens[0] % 2048 == 0:
+        result["read_ceiling"] = _read_ceiling(probe, k, v, wl, 2048)
+        result["read_ceiling"]["dominant_frac_of_plain_read"] = (
+            roof["algorithmic_bytes"] / (roof["launch_ms"] * 1e-3) / 1e9 / result["read_ceiling"]["plain_read_GBs"])
     # needles planted by the generator that the selection kept (context only)
+    data = ex["data"]
     if data.get("needle_pos"):
-        idx_h = sel[0].cpu().numpy()
+        idx_h = ex["sel"][0].cpu().numpy()
         boff = wl.bud_off()
         kept = tot = 0
         for (s_, h_), pos in data["needle_pos"].items():
@@ -513,13 +673,27 @@ def main():
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = _cpu_baseline(wl, data, max(1, min(args.cpu_heads, wl.Hkv)))
     merge_data = {"k": data["k"][:1].copy()}   # KV head 0 for the merge leg's oracle sample
-    del data
+    del data, ex["data"]
     if not args.no_merge:
         print("# merge leg", file=sys.stderr, flush=True)
+        sel, budgets = ex["sel"], ex["budgets"]
+        total_B = int(budgets.sum())
         result["merge"] = _merge_leg(b, k, budgets, sel[0][:, :total_B], sel[1][:, :total_B], wl)
         if not args.no_cpu_baseline:
             result["merge"]["cpu_baseline"] = _merge_cpu(merge_data, wl, sel[0][:, :total_B].cpu().numpy(), budgets,
                                                          result["merge"]["tau_merge"])
+    del ex, b, k, v
+    torch.cuda.empty_cache()
+    # the other workloads, each timed the same way (cold-cache median)
+    names = [] if args.configs == "none" else (
+        [n for n in workloads.ALL if n != args.workload] if args.configs == "all" else args.configs.split(","))
+    if names:
+        result["configs"] = {}
+        for name in names:
+            res, ex2 = _eviction_leg(workloads.ALL[name](), args, probe)
+            result["configs"][name] = res
+            del ex2
+            torch.cuda.empty_cache()
     if not args.no_decode:
         print("# decode leg", file=sys.stderr, flush=True)
         result["decode"] = _decode_leg(args.decode_steps, not args.no_cpu_baseline)
