@@ -321,6 +321,26 @@ kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k
                                float sm_scale, float* out, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------- decode_snis_noalloc
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as kvevict_decode_snis, with the same arguments except the
+ * workspace, and the same results bit for bit.  Its split partials live in
+ * a device array the library holds per GPU, kvevict_decode_scratch_max()
+ * bytes (8 MiB: S * Hq * ceil(max_cache_len / 256) * (d + 2) * 4 bytes plus
+ * alignment must fit, e.g. 8 sequences x 32 q-heads at d = 128 up to caches
+ * of about 15000 entries).  A larger batch returns KVE_EWORKSPACE with a
+ * message and launches nothing.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); the first call on a device looks
+ * up the array's address there once.  Calls on one GPU share the array:
+ * calls that overlap on one GPU (other streams, other threads) race. */
+size_t kvevict_decode_scratch_max(void);
+kve_status kvevict_decode_snis_noalloc(const kve_layout* L, const void* q, const void* k_c,
+                                       const void* v_c, const float* bias_c,
+                                       const int32_t* cap_off, const int32_t* cap_off_host,
+                                       const int32_t* cache_len, int32_t max_cache_len,
+                                       float sm_scale, float* out, void* stream);
+
 /* ------------------------------------------------------- instrumentation
  * Not part of the eviction path.  Opt-in per-kernel timing with HIP events
  * recorded on the launch stream around every kernel the four calls enqueue.

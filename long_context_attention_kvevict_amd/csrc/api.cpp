@@ -264,4 +264,32 @@ kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k
   return KVE_OK;
 }
 
+size_t kvevict_decode_scratch_max(void) { return kve::kDecodeScratchBytes; }
+
+kve_status kvevict_decode_snis_noalloc(const kve_layout* L, const void* q, const void* k_c, const void* v_c,
+                                       const float* bias_c, const int32_t* cap_off, const int32_t* cap_off_host,
+                                       const int32_t* cache_len, int32_t max_cache_len, float sm_scale,
+                                       float* out, void* stream) {
+  kve::DecodeGeom G;
+  std::string msg;
+  if (!cap_off_host) return set_err(KVE_EINVAL, "kvevict_decode_snis_noalloc: cap_off_host is NULL");
+  kve_status st = kve::plan_decode(L, cap_off_host, max_cache_len, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_decode_snis_noalloc: " + msg);
+  if (!q || !k_c || !v_c || !bias_c || !cap_off || !cache_len || !out)
+    return set_err(KVE_EINVAL, "kvevict_decode_snis_noalloc: null tensor pointer");
+  if (!(sm_scale > 0.f)) return set_err(KVE_EINVAL, "kvevict_decode_snis_noalloc: sm_scale must be > 0");
+  if (G.bytes > kve::kDecodeScratchBytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_decode_snis_noalloc: this batch needs " + std::to_string(G.bytes) +
+                                       " bytes of decode scratch, more than the " +
+                                       std::to_string(kve::kDecodeScratchBytes) +
+                                       " the library holds per device (use kvevict_decode_snis)");
+  void* ws = nullptr;
+  hipError_t e = kve::decode_scratch(&ws);
+  if (e != hipSuccess) return hip_err(e, "kvevict_decode_snis_noalloc: scratch address");
+  e = kve::launch_decode(G, cap_off_host[L->S], q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws,
+                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "kvevict_decode_snis_noalloc");
+  return KVE_OK;
+}
+
 }  // extern "C"

@@ -14,9 +14,37 @@
 #include "launch.h"
 #include "timing.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace kve {
+
+// Device scratch of the allocation-free decode entry point: the split
+// partials live here instead of in a caller workspace.  Every GPU the
+// library runs on holds its own copy for the life of the process; calls on
+// one GPU share it.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  // The array's name is a host-side stand-in; its device address is looked
+  // up once per device, with that device current, and kept.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 template <typename T>
 __device__ __forceinline__ float ld_elem(const T* p);

@@ -46,6 +46,9 @@ hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t total
                           const int32_t* cap_off, void* k_c, void* v_c, float* bias_c,
                           hipStream_t st);
 
+// Device address of the decode scratch array on the current device.
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_decode(const DecodeGeom& G, int64_t totalC, const void* q, const void* k_c,
                          const void* v_c, const float* bias_c, const int32_t* cap_off,
                          const int32_t* cache_len, float sm_scale, float* out, void* ws,

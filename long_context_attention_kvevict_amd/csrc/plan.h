@@ -96,6 +96,10 @@ struct MergeGeom {
 // blocks of 32 entries.
 constexpr int kDecodeChunkBf16 = 256;
 
+// Device scratch the allocation-free decode entry point holds per GPU (its
+// split partials: S * Hq * splits * (d + 2) floats, 256-byte aligned parts).
+constexpr size_t kDecodeScratchBytes = static_cast<size_t>(8) << 20;
+
 struct DecodeGeom {
   int S, Hq, Hkv, d, dtype, splits, split_len;
   size_t off_ml, off_o;

@@ -24,7 +24,8 @@ EXPORTS = [
     "kvevict_score_workspace", "kvevict_score", "kvevict_score_ex", "kvevict_select_workspace", "kvevict_select",
     "kvevict_select_ex", "kvevict_select_soft", "kvevict_select_literal_workspace", "kvevict_select_literal",
     "kvevict_merge_workspace", "kvevict_merge",
-    "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_last_error",
+    "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_decode_scratch_max",
+    "kvevict_decode_snis_noalloc", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
 
@@ -89,6 +90,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_decode_workspace.restype = SZ
     lib.kvevict_decode_snis.argtypes = [LP, P, P, P, P, P, P, P, I32, F32, P, P, SZ, P]
     lib.kvevict_decode_snis.restype = I32
+    lib.kvevict_decode_scratch_max.argtypes = []
+    lib.kvevict_decode_scratch_max.restype = SZ
+    lib.kvevict_decode_snis_noalloc.argtypes = [LP, P, P, P, P, P, P, P, I32, F32, P, P]
+    lib.kvevict_decode_snis_noalloc.restype = I32
     lib.kvevict_last_error.argtypes = []
     lib.kvevict_last_error.restype = ctypes.c_char_p
     lib.kvevict_version.argtypes = []
@@ -337,6 +342,18 @@ class Batch:
                                              float(sm_scale), _ptr(out), _ptr(ws), ws.numel(),
                                              _stream(stream)))
         self._dec = (cap_host, cap_dev)
+        return out
+
+    def decode_noalloc(self, q, k_c, v_c, bias_c, cap_offsets, cache_len, max_cache_len: int, sm_scale: float,
+                       out, stream=None):
+        """kvevict_decode_snis_noalloc: the same decode with the library's
+        per-device scratch instead of a workspace; nothing is allocated
+        (the caller passes `out` and the capacity offsets (host, device))."""
+        cap_host, cap_dev = cap_offsets
+        _check(self._lib.kvevict_decode_snis_noalloc(ctypes.byref(self.layout), _ptr(q), _ptr(k_c), _ptr(v_c),
+                                                     _ptr(bias_c), _ptr(cap_dev), cap_host.data_ptr(),
+                                                     _ptr(cache_len), int(max_cache_len), float(sm_scale),
+                                                     _ptr(out), _stream(stream)))
         return out
 
 

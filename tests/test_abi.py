@@ -212,3 +212,19 @@ def test_merge_rejects_bad_arguments():
     assert call(lay, b) == K.KVE_EWORKSPACE
     lay32, keep32 = _layout(S=2, lens=(50, 60), dtype=K.KVE_F32)
     assert call(lay32, b) == K.KVE_ENOTSUP
+
+
+def test_noalloc_decode_rejects_batches_beyond_its_scratch():
+    # 8 sequences x 32 q-heads with caches of 20000 entries need about 10 MiB
+    # of split partials, more than the 8 MiB the allocation-free decode
+    # holds: the host check refuses before any launch (pointers unused)
+    lib = K.load_library()
+    assert lib.kvevict_decode_scratch_max() == 8 << 20
+    lay, host = _layout(S=8, Hq=32, Hkv=8, lens=(200000,) * 8)
+    cap = torch.tensor([20016 * i for i in range(9)], dtype=torch.int32)
+    st = lib.kvevict_decode_snis_noalloc(ctypes.byref(lay), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, cap.data_ptr(),
+                                         DUMMY, 20000, 0.1, DUMMY, None)
+    assert st == K.KVE_EWORKSPACE
+    assert "scratch" in lib.kvevict_last_error().decode()
+    # the workspace entry point takes the same batch
+    assert lib.kvevict_decode_workspace(ctypes.byref(lay), 20000) > (8 << 20)
