@@ -1,13 +1,13 @@
 """GPU tier at full workload sizes, in the launch configuration the benchmark
-times.  The oracle is evaluated on sampled keys (every row's softmax still
-spans all n keys), on every head's selection given the GPU's scores, and on
-sampled decode steps."""
+times.  The oracle scores every key of two KV heads per workload (all
+window rows, all n keys), checks every head's selection given the GPU's
+scores, and sampled decode steps."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from oracle.score import group_scores_at
+from oracle.score import max_pool_fast
 from oracle.select import select_workload, expected_distinct, proposal, inclusion_prob
 from long_context_attention_kvevict_amd import kvevict as K
 from long_context_attention_kvevict_amd import synth, workloads
@@ -16,28 +16,17 @@ from tests.gpu_util import Run, check_scores, say, DECODE_ATOL
 pytestmark = pytest.mark.gpu
 
 
-def _sample_keys(rng, n, needles, count=1536):
-    base = rng.choice(n, size=min(count, n), replace=False)
-    special = np.concatenate([np.arange(min(8, n)), np.arange(max(0, n - 40), n), needles])
-    return np.unique(np.concatenate([base, special]))
-
-
-def _check_sampled_scores(r, got, s, h, rng):
+def _check_full_scores(r, got, s, h):
+    """Every key of (sequence s, KV head h) against the oracle's pooled
+    group score (all window rows of the group's q-heads, all n keys)."""
     wl = r.wl
     a, b = wl.seq_off()[s], wl.seq_off()[s + 1]
-    n = b - a
-    rad = (wl.pool_kernel - 1) // 2
-    needles = r.data["needle_pos"].get((s, h), np.zeros(0, np.int64))
-    centers = _sample_keys(rng, n, needles)
-    need = np.unique(np.clip((centers[:, None] + np.arange(-rad, rad + 1)[None, :]).ravel(), 0, n - 1))
-    q = r.f64_q()[s]
-    raw = group_scores_at(q, r.f64_kv("k", h, a, b), r.f64_kv("v", h, a, b), h, wl.g, wl.sm_scale, True, need)
-    lut = dict(zip(need.tolist(), raw.tolist()))
-    ref = np.array([max(lut[j] for j in range(max(0, c - rad), min(n, c + rad + 1))) for c in centers])
-    # the floor of the tolerance uses the head's max, which the sample contains
-    # (needles and sinks are sampled); guard with the GPU's own max as well
-    got_c = got[h, a + centers]
-    return check_scores(got_c, ref, f"{wl.name} s{s} h{h}")
+    raw = oracle.group_scores(r.f64_q()[s], r.f64_kv("k", h, a, b), r.f64_kv("v", h, a, b), h, wl.g,
+                              wl.sm_scale, True)
+    ref = max_pool_fast(raw, wl.pool_kernel)
+    worst, small = check_scores(got[h, a:b], ref, f"{wl.name} s{s} h{h}")
+    say(f"[gpu] full {wl.name} s{s} h{h}: all {b - a} keys, max rel err {worst:.2e}")
+    return worst
 
 
 class BigRun(Run):
@@ -83,10 +72,8 @@ def test_llama_layer_n128k_topk():
     say(f"[gpu] full {wl.name}: score")
     got = r.score().cpu().numpy()
     assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(0)
     for h in (0, 5):
-        say(f"[gpu] full {wl.name}: oracle head {h}")
-        _check_sampled_scores(r, got, 0, h, rng)
+        _check_full_scores(r, got, 0, h)
     say(f"[gpu] full {wl.name}: select")
     idx, bias, _, _ = _select_parity(r, got)
     # needle recall (context, not parity)
@@ -127,15 +114,34 @@ def test_llama_layer_n128k_topk():
                        atol=1e-6)
 
 
+def test_llama_layer_n32k_topk():
+    # the Llama layer at n = 32768 (10 % budget): the key chunk and grid the
+    # benchmark runs at this length
+    wl = workloads.llama8b_32k()
+    say(f"[gpu] full {wl.name}: generating")
+    r = BigRun(wl)
+    got = r.score().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    for h in (2, 7):
+        _check_full_scores(r, got, 0, h)
+    idx, bias, _, _ = _select_parity(r, got)
+    budgets = wl.budgets()
+    k_c, v_c, b_c = r.b.compact(r.k, r.v, budgets, torch.from_numpy(idx).cuda(), torch.from_numpy(bias).cuda(),
+                                budgets)
+    torch.cuda.synchronize()
+    vbits = r.data["v"].view(np.int16)
+    for h in range(wl.Hkv):
+        assert np.array_equal(v_c[h].cpu().view(torch.int16).numpy(), vbits[h, idx[h]])
+
+
 def test_qwen_layer_n128k_sample():
     wl = workloads.qwen7b_128k_sample()
     say(f"[gpu] full {wl.name}: generating")
     r = BigRun(wl)
     got = r.score().cpu().numpy()
     assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(1)
-    say(f"[gpu] full {wl.name}: oracle head 0")
-    _check_sampled_scores(r, got, 0, 0, rng)
+    for h in (0, 3):
+        _check_full_scores(r, got, 0, h)
     say(f"[gpu] full {wl.name}: select")
     idx, bias, m, st = _select_parity(r, got)
     say(f"[gpu] full {wl.name}: per-head m {m[0].tolist()}")
@@ -183,9 +189,8 @@ def test_mistral_ragged_batch_with_decode():
     say(f"[gpu] full {wl.name}: generating lens={wl.lens}")
     r = BigRun(wl)
     got = r.score().cpu().numpy()
-    rng = np.random.default_rng(2)
-    for s in (0, 3, 7):
-        _check_sampled_scores(r, got, s, s % wl.Hkv, rng)
+    for s, h in ((0, 0), (3, 3), (7, 6)):
+        _check_full_scores(r, got, s, h)
     say(f"[gpu] full {wl.name}: select")
     idx, bias, m, st = _select_parity(r, got)
     budgets = wl.budgets()
