@@ -23,7 +23,7 @@ def test_no_scratch_spills(src, tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     text = out.read_text()
-    kernels = re.findall(r"^(_Z\w+):", text, re.M)
+    kernels = re.findall(r"^(_Z\w+):\s+; @", text, re.M)   # function labels (not data symbols)
     scratch = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", text)]
     assert kernels and len(scratch) >= len(kernels)
     assert all(x == 0 for x in scratch), f"{src}: scratch sizes {scratch}"
