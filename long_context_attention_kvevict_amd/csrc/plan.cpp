@@ -85,6 +85,7 @@ kve_status plan_score(const kve_layout* L, ScoreGeom* G, std::string* msg) {
   size_t off = 0;
   g.off_part_ml = off; off = align256(off + groups * g.P * 128 * kScoreRec * sizeof(float));
   g.off_part_e = off;  off = align256(off + groups * g.P * 128 * sizeof(float));
+  g.off_part_x = off;  off = align256(off + groups * g.P * 128 * sizeof(float));
   g.off_part_o = off;  off = align256(off + groups * g.P * 128 * static_cast<size_t>(g.d) * sizeof(float));
   g.off_vnorm = off;   off = align256(off + static_cast<size_t>(g.Hkv) * g.T * sizeof(float));
   g.off_lse2 = off;    off = align256(off + groups * 128 * sizeof(float));

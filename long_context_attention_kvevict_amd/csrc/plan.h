@@ -32,7 +32,7 @@ struct ScoreGeom {
   int CH;       // keys per chunk (multiple of 256)
   int P;        // chunks per sequence (grid x), ceil(max_len / CH)
   int pool_rg;  // partial score planes summed by the pool kernel
-  size_t off_part_ml, off_part_e, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw, off_jstar,
+  size_t off_part_ml, off_part_e, off_part_x, off_part_o, off_vnorm, off_lse2, off_no2, off_no2d, off_ohi, off_olo, off_sraw, off_jstar,
       off_cstar;
   size_t bytes;
 };

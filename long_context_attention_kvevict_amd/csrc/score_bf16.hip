@@ -81,6 +81,7 @@ struct ScoreArgs {
   float c2;                // sm_scale * log2(e)
   float* part_ml;          // [S*Hkv*RG][P][ROWS][kScoreRec]
   float* part_e;           // [S*Hkv*RG][P][ROWS] rounding error of the candidate's weight
+  float* part_x;           // [S*Hkv*RG][P][ROWS] largest logit of the row in the chunk (log2 units)
   float* part_o;           // [S*Hkv*RG][P][ROWS][D]
   float* vnorm;            // [Hkv][T]
   float* lse2;             // [S*Hkv*RG][ROWS]
@@ -291,6 +292,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   // its key (cand_j) and the rounding error (cand_e) of the weight P.V used
   // for it.
   float pc = 0.f;
+  float cmax = -INFINITY;   // the row's largest logit in the chunk, log2 units
   cand_j[tid] = -1;
   cand_e[tid] = 0.f;
 
@@ -377,6 +379,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 #pragma unroll
     for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(sacc[0][r], sacc[1][r]));
     tmax = max_xor32(tmax) * a.c2;
+    cmax = fmaxf(cmax, tmax);
     const bool raise = tmax > m_run + 8.f;
     if (__any(raise)) {
       const float m_new = raise ? tmax : m_run;
@@ -507,6 +510,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
     *reinterpret_cast<f32x4*>(a.part_ml + (part * ROWS + rl) * kScoreRec) =
         f32x4{m_run, lo, first ? pa : pb, __uint_as_float(first ? j0 : j1)};
     a.part_e[part * ROWS + rl] = __uint_as_float(first ? e0 : e1);
+    a.part_x[part * ROWS + rl] = cmax;
   }
   float* op = a.part_o + (part * ROWS + rl) * D;
 #pragma unroll
@@ -753,6 +757,11 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   // tiles but skips the arithmetic; its partials stay zero
   const bool wave_rows = __builtin_amdgcn_readfirstlane(rg * ROWS + wave * 32 < R ? 1 : 0) != 0;
   if (!wave_rows) red[0][wave][lane] = red[1][wave][lane] = 0.f;
+  // Whether some row of this wave has a weight above 2^-6 in this chunk
+  // (pass 1's largest logit of the row in the chunk against its log-sum-exp):
+  // only then do the tiles look for such weights at all.
+  const bool wave_big = __any(arow_ok && a.part_x[(grp * a.P + c) * ROWS + wave * 32 + col] -
+                                             a.lse2[grp * ROWS + wave * 32 + col] > kResidX);
   bf16x8 qa[D / 16], oha[D / 16];
   {
     const int qh = h * g + (arow_ok ? arow / a.w : 0);
@@ -820,8 +829,9 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
 
   // One tile; EDGE tiles mask keys past the chunk end or a row's causal
   // horizon, interior tiles carry no masking code.
-  auto tile = [&](const int t, const int st, auto edge_tag) {
+  auto tile = [&](const int t, const int st, auto edge_tag, auto big_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr bool BIG = decltype(big_tag)::value;
     const int kt0 = c0 + t * KT;
     const char* Kt = ring + st * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
@@ -886,11 +896,13 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
           sacc[kb][r] = hidden ? -INFINITY : sacc[kb][r];
         }
       }
+      if constexpr (BIG) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xmax = fmaxf(xmax, sacc[kb][r]);
+        for (int r = 0; r < 16; ++r) xmax = fmaxf(xmax, sacc[kb][r]);
+      }
     }
     float sc[2] = {0.f, 0.f};
-    if (__any(xmax > kResidX)) {
+    if (BIG && __any(xmax > kResidX)) {
       // some weight above 2^-6 (uniform): add the residual plane of o and
       // use the exact weight factor 1 / y^2, y = (1 - p) / p = 2^-x - 1
       const uint16_t* lp = a.olo + (grp * ROWS + wave * 32 + col) * D;
@@ -942,8 +954,14 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
       lds_barrier();
       if (i > 0) reduce_tile(t + 1, (i - 1) & 1);
       if (i + 1 < ntile) fill.issue(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
-      if (c0 + t * KT > edge_from || ((dtiles >> t) & 1u)) tile(t, i & 1, std::true_type{});
-      else tile(t, i & 1, std::false_type{});
+      const bool edge = c0 + t * KT > edge_from || ((dtiles >> t) & 1u);
+      if (wave_big) {
+        if (edge) tile(t, i & 1, std::true_type{}, std::true_type{});
+        else tile(t, i & 1, std::false_type{}, std::true_type{});
+      } else {
+        if (edge) tile(t, i & 1, std::true_type{}, std::false_type{});
+        else tile(t, i & 1, std::false_type{}, std::false_type{});
+      }
     }
   } else {   // the same loads, barriers and reductions, no arithmetic
     for (int i = 0; i < ntile; ++i) {
@@ -1133,6 +1151,7 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   char* base = static_cast<char*>(ws);
   a.part_ml = reinterpret_cast<float*>(base + G.off_part_ml);
   a.part_e = reinterpret_cast<float*>(base + G.off_part_e);
+  a.part_x = reinterpret_cast<float*>(base + G.off_part_x);
   a.part_o = reinterpret_cast<float*>(base + G.off_part_o);
   a.vnorm = reinterpret_cast<float*>(base + G.off_vnorm);
   a.lse2 = reinterpret_cast<float*>(base + G.off_lse2);

@@ -71,6 +71,44 @@ __device__ __forceinline__ double block_sum_d(double v, double* lds) {
   __syncthreads();
   return t;
 }
+// Block sums of three fp64 values at once (same order as block_sum_d);
+// lds: 12 doubles.  Two barriers.
+__device__ __forceinline__ void block_sum3_d(double* a, double* b, double* c, double* lds) {
+  double x = wave_sum_d(*a), y = wave_sum_d(*b), z = wave_sum_d(*c);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    lds[wave] = x;
+    lds[4 + wave] = y;
+    lds[8 + wave] = z;
+  }
+  __syncthreads();
+  *a = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+  *b = (lds[4] + lds[5]) + (lds[6] + lds[7]);
+  *c = (lds[8] + lds[9]) + (lds[10] + lds[11]);
+  __syncthreads();
+}
+
+// Block sums of G values per thread (G * 8 == 256 threads): every thread
+// writes its G values, then 8 threads per value each sum 32 entries and
+// combine in a fixed tree.  Returns the total of value threadIdx.x / 8 on
+// the thread with threadIdx.x % 8 == 0 (0 elsewhere).  lds: [G][257].
+template <int G>
+__device__ __forceinline__ float block_sum_many(const float (&v)[G], float (*lds)[257]) {
+  static_assert(G * 8 == 256, "eight threads per value");
+#pragma unroll
+  for (int k = 0; k < G; ++k) lds[k][threadIdx.x] = v[k];
+  __syncthreads();
+  const int k = threadIdx.x >> 3, part = threadIdx.x & 7;
+  float t = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) t += lds[k][part * 32 + i];
+  t += __shfl_xor(t, 1, 8);
+  t += __shfl_xor(t, 2, 8);
+  t += __shfl_xor(t, 4, 8);
+  __syncthreads();
+  return part == 0 ? t : 0.f;
+}
+
 __device__ __forceinline__ double block_max_d(double v, double* lds) {
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -605,6 +643,24 @@ __device__ double search_sum(const SmpArgs& A, int buf, int sh, int nch, int c, 
     for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v += part_of(A, buf, s0 + h, i)[c];
   return block_sum_d(v, dl) / A.g.Hkv;
 }
+// The three components of search_sum at once (one block reduction).
+__device__ void search_sum3(const SmpArgs& A, int buf, int sh, int nch, double* e, double* de, double* eh,
+                            double* dl) {
+  const int h0 = A.global ? (sh / A.g.Hkv) * A.g.Hkv : sh;
+  const int nh = A.global ? A.g.Hkv : 1;
+  double a = 0.0, b = 0.0, c = 0.0;
+  for (int h = 0; h < nh; ++h)
+    for (int i = threadIdx.x; i < nch; i += SEL_THREADS) {
+      const double* p = part_of(A, buf, h0 + h, i);
+      a += p[0];
+      b += p[1];
+      c += p[2];
+    }
+  block_sum3_d(&a, &b, &c, dl);
+  *e = a / nh;
+  *de = b / nh;
+  *eh = c / nh;
+}
 __device__ double max_part(const SmpArgs& A, int buf, int sh, int nch, int c, double* dl) {
   double v = -INFINITY;
   for (int i = threadIdx.x; i < nch; i += SEL_THREADS) v = fmax(v, part_of(A, buf, sh, i)[c]);
@@ -655,11 +711,14 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
   }
 }
 
-// Grid of the expected-samples start: u_k = log B + k (log 10^12 - log B) /
-// (kSelGrid - 1), k = 0 .. kSelGrid - 1, in log m.
+// Grid of the expected-samples start: m_k = B 2^k, k = 0 .. kSelGrid - 1
+// (u_k = log m_k).  A key's term d_k = 1 - (1 - pi)^(m_k) then follows
+// d_(k+1) = d_k (2 - d_k) (the square of 1 - d_k), which keeps full
+// relative precision when d_k is tiny, so the grid costs one expm1 per key.
+// Points beyond 10^12 are clamped there (E >= B is then out of the search's
+// range).
 __device__ __forceinline__ double grid_u(int k, int B) {
-  const double lo = log(static_cast<double>(B));
-  return lo + k * ((log(kAlphaMax) - lo) / (kSelGrid - 1));
+  return fmin(log(static_cast<double>(B)) + k * 0.69314718055994531, log(kAlphaMax));
 }
 
 // Pass B: log1p(-pi_j) and the Gumbel keys kappa_j = log pi~_j - log(-log u_j),
@@ -683,9 +742,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
     zp += p[1] * exp(p[0] - M);
   }
   const double lse = M + log(block_sum_d(zp, dl));
-  float mk[kSelGrid];
-#pragma unroll
-  for (int k = 0; k < kSelGrid; ++k) mk[k] = static_cast<float>(exp(grid_u(k, B)) * 1.4426950408889634);
+  // per grid point, this thread's share of the chunk's E(m_k)
   float e[kSelGrid];
 #pragma unroll
   for (int k = 0; k < kSelGrid; ++k) e[k] = 0.f;
@@ -707,20 +764,18 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
                                           static_cast<uint64_t>(s), 0ull, A.seed, 0ull);
       const double uu = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
       A.lp[row + j] = x - log(-log(uu));
-      const float lf = static_cast<float>(l);
+      float dk = -expm1f(static_cast<float>(static_cast<double>(B) * l));
 #pragma unroll
-      for (int k = 0; k < kSelGrid; ++k) e[k] += 1.f - exp2f(mk[k] * lf);
+      for (int k = 0; k < kSelGrid; ++k) {
+        e[k] += dk;
+        dk *= 2.f - dk;
+      }
     }
   }
-  // per grid point, the chunk sum in a fixed order (column of threads)
-#pragma unroll
-  for (int k = 0; k < kSelGrid; ++k) eg[k][threadIdx.x] = e[k];
-  __syncthreads();
-  if (threadIdx.x < kSelGrid) {
-    float t = 0.f;
-    for (int i = 0; i < SEL_THREADS; ++i) t += eg[threadIdx.x][i];
-    A.grid[(static_cast<size_t>(sh) * A.nsmp + ch) * kSelGrid + threadIdx.x] = t;
-  }
+  // per grid point, the chunk sum in a fixed order
+  const float t = block_sum_many<kSelGrid>(e, eg);
+  if ((threadIdx.x & 7) == 0)
+    A.grid[(static_cast<size_t>(sh) * A.nsmp + ch) * kSelGrid + (threadIdx.x >> 3)] = t;
 }
 
 // The search state after step `step`: step 0 starts from the state smp_keys
@@ -729,26 +784,42 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
 // safeguarded Newton step in log m on E(e^u) - B (bisection of the bracket
 // when the step leaves it), or stop once |E - B| <= 0.5, or -- on step 1,
 // from E(10^12) -- stop with the target out of reach.
-__device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int B, double* dl) {
+__device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int B, double* dl,
+                               float (*eg)[257]) {
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   if (step == 0) {
     // start from the grid: the first point whose E reaches B, and a bracket
     // one grid cell wider on each side than the crossing (the grid sums are
     // fp32); log B is a true lower bound since E(m) <= m
     const double target = static_cast<double>(B);
-    int kx = kSelGrid;   // first grid point with E >= B
-    double Ek = 0.0, Ep = 0.0;
     const int h0 = A.global ? (sh / A.g.Hkv) * A.g.Hkv : sh;
     const int nh = A.global ? A.g.Hkv : 1;
-    for (int k = 0; k < kSelGrid; ++k) {
-      double v = 0.0;
+    // every grid point's head (or heads') total in one block reduction
+    float v[kSelGrid];
+    {
+      double acc[kSelGrid];
+#pragma unroll
+      for (int k = 0; k < kSelGrid; ++k) acc[k] = 0.0;
       for (int hh = 0; hh < nh; ++hh)
-        for (int i = threadIdx.x; i < nch; i += SEL_THREADS)
-          v += static_cast<double>(A.grid[(static_cast<size_t>(h0 + hh) * A.nsmp + i) * kSelGrid + k]);
-      v = block_sum_d(v, dl) / nh;
-      if (v >= target) { kx = k; Ek = v; break; }
-      Ep = v;
+        for (int i = threadIdx.x; i < nch; i += SEL_THREADS) {
+          const float* gp = A.grid + (static_cast<size_t>(h0 + hh) * A.nsmp + i) * kSelGrid;
+#pragma unroll
+          for (int k = 0; k < kSelGrid; ++k) acc[k] += static_cast<double>(gp[k]);
+        }
+#pragma unroll
+      for (int k = 0; k < kSelGrid; ++k) v[k] = static_cast<float>(acc[k]);
     }
+    const float t = block_sum_many<kSelGrid>(v, eg);
+    if ((threadIdx.x & 7) == 0) eg[0][256 - kSelGrid + (threadIdx.x >> 3)] = t;   // totals, in a free column
+    __syncthreads();
+    int kx = kSelGrid;   // first grid point with E >= B
+    double Ek = 0.0, Ep = 0.0;
+    for (int k = 0; k < kSelGrid; ++k) {
+      const double e = static_cast<double>(eg[0][256 - kSelGrid + k]) / nh;
+      if (e >= target) { kx = k; Ek = e; break; }
+      Ep = e;
+    }
+    __syncthreads();
     Search st;
     st.done = 0.0;
     if (kx == 0) {
@@ -766,11 +837,10 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
   Search st = A.state[(step & 1) * SH + sh];
   if (st.done != 0.0) return st;
   const int pb = (step - 1) & 1;
-  const double E = search_sum(A, pb, sh, nch, 0, dl);
-  const double dE = search_sum(A, pb, sh, nch, 1, dl);
+  double E, dE, Eh;
+  search_sum3(A, pb, sh, nch, &E, &dE, &Eh, dl);
   const double target = static_cast<double>(B);
   if (step == 1) {
-    const double Eh = search_sum(A, pb, sh, nch, 2, dl);
     if (Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
       st.done = 2.0;
       return st;
@@ -799,8 +869,9 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
   const int sh = s * A.g.Hkv + h;
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
-  __shared__ double dl[4];
-  const Search st = search_state(A, step, sh, nch, B, dl);
+  __shared__ double dl[12];
+  __shared__ float eg[kSelGrid][257];
+  const Search st = search_state(A, step, sh, nch, B, dl, eg);
   if (ch == 0 && threadIdx.x == 0) A.state[((step + 1) & 1) * SH + sh] = st;
   if (st.done != 0.0) return;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
@@ -838,8 +909,8 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) 
   const int sh = s * A.g.Hkv + h;
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
-  __shared__ double dl[4];
-  const Search st = search_state(A, steps, sh, nch, B, dl);
+  __shared__ double dl[12];
+  const Search st = search_state(A, steps, sh, nch, B, dl, nullptr);   // steps >= 1: no grid
   if (ch == 0 && threadIdx.x == 0) A.state[((steps + 1) & 1) * SH + sh] = st;
   // out of reach: E at 10^12 (the second value), which sets a head's count
   // under a soft budget
@@ -900,10 +971,10 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
   if (active) {
     const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
     const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
-    __shared__ double dl[4];
+    __shared__ double dl[12];
     const Search st = A.state[((steps + 1) & 1) * SH + sh];
-    const double E0 = search_sum(A, steps & 1, sh, nch, 0, dl);
-    const double E1 = search_sum(A, steps & 1, sh, nch, 1, dl);
+    double E0, E1, unused;
+    search_sum3(A, steps & 1, sh, nch, &E0, &E1, &unused, dl);
     int which;   // 0: m0, 1: m0 + 1 (or 10^12), 2: found by the binary search
     if (st.done == 2.0) {
       m = kAlphaMax;
