@@ -225,8 +225,10 @@ __device__ void resolve(const int* __restrict__ hist, int SH, int sh, int B, int
 }
 
 // One digit level: histogram of the keys matching the prefix resolved so far.
+// lh: SEL_BINS ints of LDS, lds: 8 ints of LDS (the caller's, so that fused
+// kernels can share one allocation between their parts).
 template <class Src, int LV>
-__global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int* __restrict__ hist) {
+__device__ __forceinline__ void sel_hist_body(Src src, const SelArgs& a, int* __restrict__ hist, int* lh, int* lds) {
   typedef typename Src::K K;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
@@ -236,8 +238,6 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   const int j0 = ch * SEL_CHUNK;
   if (B <= 0 || B >= n || j0 >= n) return;
   const int SH = a.S * a.Hkv;
-  __shared__ int lh[SEL_BINS];
-  __shared__ int lds[8];
   const size_t row = static_cast<size_t>(h) * a.T + base;
   K u[SEL_PER];
 #pragma unroll
@@ -263,6 +263,12 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
     const int c = lh[i];
     if (c) atomicAdd(&gh[i], c);
   }
+}
+template <class Src, int LV>
+__global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int* __restrict__ hist) {
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  sel_hist_body<Src, LV>(src, a, hist, lh, lds);
 }
 
 // Last digit level of the radix select, which also leaves the ordered write
@@ -862,7 +868,8 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
 // One step of the expected-samples search: brings the state up to date,
 // then (if still searching) writes the chunk's E(m), dE/dm at m = e^u, and
 // on the first step also E(10^12).
-__global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
+// eg: kSelGrid x 257 floats of LDS, used on step 0 only (may be NULL after).
+__device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257]) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -870,7 +877,6 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[12];
-  __shared__ float eg[kSelGrid][257];
   const Search st = search_state(A, step, sh, nch, B, dl, eg);
   if (ch == 0 && threadIdx.x == 0) A.state[((step + 1) & 1) * SH + sh] = st;
   if (st.done != 0.0) return;
@@ -902,7 +908,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
 // Brings the state up to date after the last step, then writes the chunk's
 // E at m0 = floor(e^u) and m0 + 1 (one of them lies in the band when the
 // search converged: E rises by at most 1 per unit step).
-__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) {
+__device__ void smp_finish_body(const SmpArgs& A, int steps) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -960,8 +966,7 @@ __device__ double expected_at(const SmpArgs& A, bool mean, int s, int sh, int n,
 // on the heads' mean (every head of a sequence decides the same m) and each
 // head keeps floor(E_h(m) + 0.5) entries, clamped to its sequence length and
 // capacity.  One workgroup per head.
-__global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, double* m_out, int32_t* status_out) {
-  const int h = blockIdx.x, s = blockIdx.y;
+__device__ void smp_decide_body(const SmpArgs& A, int steps, double* m_out, int32_t* status_out, int h, int s) {
   const int sh = s * A.g.Hkv + h;
   int n, B, base;
   const bool active = smp_active(A, s, 0, &n, &B, &base);
@@ -1027,6 +1032,54 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
     if (A.bsh) A.bsh[sh] = kept;
     if (A.kept_out) A.kept_out[sh] = kept;
   }
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
+  __shared__ float eg[kSelGrid][257];
+  smp_search_body(A, step, eg);
+}
+__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) { smp_finish_body(A, steps); }
+__global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, double* m_out, int32_t* status_out) {
+  smp_decide_body(A, steps, m_out, status_out, blockIdx.x, blockIdx.y);
+}
+
+// The Gumbel keys' radix digit levels do not depend on m (the kept set is
+// the top B of the keys whatever m the search returns), so with a per-head
+// budget each search launch also makes one histogram level of the keys over
+// the same chunk (the sampling and radix chunks are both 1024 keys):
+// search steps with levels 0 .. steps-1, the finish with level steps, and
+// the decision (in the first chunk's workgroup of each head) with the next.
+// Step 0 (which sums the start grid) shares one LDS block between its two
+// parts; the others hold only the histogram's.
+template <int LV>
+__global__ __launch_bounds__(SEL_THREADS) void smp_search_hist(SmpArgs A, int step, int* __restrict__ hist) {
+  __shared__ int lds[8];
+  if constexpr (LV == 0) {
+    __shared__ __align__(16) float eg[kSelGrid][257];
+    static_assert(sizeof(eg) >= SEL_BINS * sizeof(int), "the grid block holds the histogram");
+    smp_search_body(A, step, eg);
+    __syncthreads();
+    sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, reinterpret_cast<int*>(&eg[0][0]), lds);
+  } else {
+    __shared__ int lh[SEL_BINS];
+    smp_search_body(A, step, nullptr);
+    sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
+  }
+}
+template <int LV>
+__global__ __launch_bounds__(SEL_THREADS) void smp_finish_hist(SmpArgs A, int steps, int* __restrict__ hist) {
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  smp_finish_body(A, steps);
+  sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
+}
+template <int LV>
+__global__ __launch_bounds__(SEL_THREADS) void smp_decide_hist(SmpArgs A, int steps, double* m_out,
+                                                               int32_t* status_out, int* __restrict__ hist) {
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  if (blockIdx.x == 0) smp_decide_body(A, steps, m_out, status_out, blockIdx.y, blockIdx.z);
+  sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
 }
 
 // ------------------------------------------------------- literal estimator
@@ -1425,14 +1478,34 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     const dim3 sgrid(G.nsmp, G.Hkv, G.S);
     hipLaunchKernelGGL(smp_logp, sgrid, dim3(SEL_THREADS), 0, st, A);
     hipLaunchKernelGGL(smp_keys, sgrid, dim3(SEL_THREADS), 0, st, A);
-    for (int it = 0; it < kSelSearchSteps; ++it)
-      hipLaunchKernelGGL(smp_search, sgrid, dim3(SEL_THREADS), 0, st, A, it);
-    hipLaunchKernelGGL(smp_finish, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps);
-    hipLaunchKernelGGL(smp_decide, dim3(G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
-                       status_out);
     const SnisBias bias_of{A.L, A.mvals, 1.0 / static_cast<double>(tau_w)};
-    launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st,
-                 reinterpret_cast<int*>(wsb + G.off_ncand), reinterpret_cast<int2*>(wsb + G.off_cand));
+    int* ncand = reinterpret_cast<int*>(wsb + G.off_ncand);
+    int2* cand = reinterpret_cast<int2*>(wsb + G.off_cand);
+    if (!soft) {
+      // the search launches carry the keys' histogram levels 0 .. 4
+      static_assert(kSelSearchSteps == 3 && Radix<uint64_t>::LEVELS == 6 && kSmpChunk == kSelChunk,
+                    "the fused launches pair 3 search steps, the finish and the decision with levels 0..4");
+      hipLaunchKernelGGL((smp_search_hist<0>), sgrid, dim3(SEL_THREADS), 0, st, A, 0, hist);
+      hipLaunchKernelGGL((smp_search_hist<1>), sgrid, dim3(SEL_THREADS), 0, st, A, 1, hist);
+      hipLaunchKernelGGL((smp_search_hist<2>), sgrid, dim3(SEL_THREADS), 0, st, A, 2, hist);
+      hipLaunchKernelGGL((smp_finish_hist<3>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, hist);
+      hipLaunchKernelGGL((smp_decide_hist<4>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
+                         status_out, hist);
+      const dim3 grid(G.nchunk, G.Hkv, G.S);
+      hipLaunchKernelGGL((sel_hist_last<GumbelKeys>), grid, dim3(SEL_THREADS), 0, st, GumbelKeys{A.lp}, a, hist,
+                         ncand, cand, G.max_len, cnt);
+      hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias>), grid, dim3(SEL_THREADS), 0, st, GumbelKeys{A.lp},
+                         bias_of, a, hist, cnt, ncand, cand, G.max_len, idx, bias);
+    } else {
+      // a soft budget decides each head's kept count first (its radix
+      // levels need it)
+      for (int it = 0; it < kSelSearchSteps; ++it)
+        hipLaunchKernelGGL(smp_search, sgrid, dim3(SEL_THREADS), 0, st, A, it);
+      hipLaunchKernelGGL(smp_finish, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps);
+      hipLaunchKernelGGL(smp_decide, dim3(G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
+                         status_out);
+      launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st, ncand, cand);
+    }
   }
   stage_end(ST_SELECT, st);
   return hipGetLastError();
