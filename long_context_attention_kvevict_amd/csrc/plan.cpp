@@ -136,6 +136,7 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.off_cand = off; off = align256(off + SH * static_cast<size_t>(max_len) * 2 * sizeof(int32_t));
   g.off_cnt = off; off = align256(off + SH * g.nchunk * 2 * sizeof(int32_t));
   g.off_rstate = off; off = align256(off + SH * kSelRStateBytes);
+  g.off_rcache = off; off = align256(off + SH * kSelLevels64 * kSelRCacheBytes);
   g.off_part = off; off = align256(off + (smp ? 2 * SH * g.nsmp * 3 * sizeof(double) : 0));
   g.off_grid = off; off = align256(off + (smp ? SH * g.nsmp * kSelGrid * sizeof(float) : 0));
   g.off_state = off; off = align256(off + (smp ? 2 * SH * kSelSearchBytes : 0));

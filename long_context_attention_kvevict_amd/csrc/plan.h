@@ -53,6 +53,7 @@ constexpr int kSelGrid = 32;
 constexpr int kSelSearchSteps = 3;
 constexpr int kSelRStateBytes = 16;   // per-head radix threshold and count of equal keys kept
 constexpr int kSelSearchBytes = 32;   // per-head search state
+constexpr int kSelRCacheBytes = 16;   // per-head, per-level resolved threshold digits
 
 struct SelectGeom {
   int S, Hkv, T, max_len, mode;
@@ -66,6 +67,7 @@ struct SelectGeom {
   size_t off_cand;                 // int [S*Hkv][max_len][2] those keys (index, last digit)
   size_t off_cnt;                  // int [S*Hkv][nchunk][2]
   size_t off_rstate;               // [S*Hkv] radix threshold state (kSelRStateBytes each)
+  size_t off_rcache;               // [S*Hkv][kSelLevels64] resolved digits (kSelRCacheBytes each)
   size_t off_part;                 // sampling: double [2][S*Hkv][nchunk][3]
   size_t off_grid;                 // sampling: float [S*Hkv][nchunk][kSelGrid]
   size_t off_state;                // sampling: [2][S*Hkv] search state (kSelSearchBytes each)

@@ -157,7 +157,16 @@ struct SelArgs {
   const int32_t* bsh;       // soft budget: kept count of each (sequence, head), else NULL
   int S, Hkv, T, nchunk;
   int64_t totalB;           // out_off[S]
+  struct RCache* rcache;    // [S*Hkv][kSelLevels64] threshold digits resolved so far
 };
+
+// Threshold digits resolved so far for one (sequence, head): the key prefix
+// of levels 0 .. L and the count still needed among keys carrying it.
+struct RCache {
+  uint64_t prefix;
+  int32_t need, pad;
+};
+static_assert(sizeof(RCache) == kSelRCacheBytes, "host and device cache entry size disagree");
 
 // Kept count of (sequence s, head h).
 __device__ __forceinline__ int sel_budget(const SelArgs& a, int s, int sh) {
@@ -197,27 +206,35 @@ __device__ void pick_bin(const int (&c)[8], int need, int* lds, int* digit, int*
 
 // Resolves digit levels 0 .. NLV-1 from the finished histograms: key prefix,
 // its mask and the count still needed among the keys carrying that prefix.
-// The histograms of all levels are loaded at once.
+// Levels 0 .. NLV-2 come from the per-head cache the previous launch of the
+// chain left (the launches resolve one more level each), so only level
+// NLV-1 is picked from its histogram here; the first chunk's workgroup of
+// the head then caches levels 0 .. NLV-1 for the next launch.
 template <typename K, int NLV>
-__device__ void resolve(const int* __restrict__ hist, int SH, int sh, int B, int* lds, K* prefix, K* mask, int* need) {
+__device__ void resolve(const int* __restrict__ hist, int SH, int sh, int B, int* lds, K* prefix, K* mask, int* need,
+                        RCache* cache) {
   K p = 0, m = 0;
   int nd = B;
   if (NLV > 0) {
-    int c[NLV > 0 ? NLV : 1][8];
+    constexpr int lv = NLV - 1;
+    int c[8];
+    const int* gh = hist + (static_cast<size_t>(lv) * SH + sh) * SEL_BINS;
 #pragma unroll
-    for (int lv = 0; lv < NLV; ++lv) {
-      const int* gh = hist + (static_cast<size_t>(lv) * SH + sh) * SEL_BINS;
+    for (int i = 0; i < 8; ++i) c[i] = gh[SEL_BINS - 1 - 8 * threadIdx.x - i];
+    if (NLV > 1) {
+      const RCache r = cache[static_cast<size_t>(sh) * kSelLevels64 + (NLV - 2)];
+      p = static_cast<K>(r.prefix);
+      nd = r.need;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[lv][i] = gh[SEL_BINS - 1 - 8 * threadIdx.x - i];
+      for (int l = 0; l < NLV - 1; ++l) m |= Radix<K>::wmask(l) << Radix<K>::shift(l);
     }
-#pragma unroll
-    for (int lv = 0; lv < NLV; ++lv) {
-      int dg, ab;
-      pick_bin(c[lv], nd, lds, &dg, &ab);
-      p |= static_cast<K>(dg) << Radix<K>::shift(lv);
-      m |= Radix<K>::wmask(lv) << Radix<K>::shift(lv);
-      nd -= ab;
-    }
+    int dg, ab;
+    pick_bin(c, nd, lds, &dg, &ab);
+    p |= static_cast<K>(dg) << Radix<K>::shift(lv);
+    m |= Radix<K>::wmask(lv) << Radix<K>::shift(lv);
+    nd -= ab;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+      cache[static_cast<size_t>(sh) * kSelLevels64 + (NLV - 1)] = RCache{static_cast<uint64_t>(p), nd, 0};
   }
   *prefix = p;
   *mask = m;
@@ -248,7 +265,7 @@ __device__ __forceinline__ void sel_hist_body(Src src, const SelArgs& a, int* __
   for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
   K prefix, mask;
   int need;
-  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need);
+  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need, a.rcache);
   __syncthreads();   // lh cleared (level 0 resolves nothing and has no barrier of its own)
   const int sft = Radix<K>::shift(LV);
   const K dm = Radix<K>::wmask(LV);
@@ -303,7 +320,7 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a,
   for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
   K prefix, mask;
   int need;
-  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need);
+  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need, a.rcache);
   __syncthreads();
   const int sft = Radix<K>::shift(LV);
   const K dm = Radix<K>::wmask(LV);
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_count(Src src, SelArgs a, con
   }
   K thr, mask;
   int need;
-  resolve<K, NLV>(hist, SH, sh, B, lds, &thr, &mask, &need);
+  resolve<K, NLV>(hist, SH, sh, B, lds, &thr, &mask, &need, a.rcache);
   int gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < SEL_PER; ++i) {
@@ -523,7 +540,7 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bi
   for (int i = 0; i < SEL_PER; ++i) u[i] = (jt + i < n) ? src.key(row + jt + i) : K(0);
   K thr, mask;
   int need;
-  resolve<K, NLV>(hist, a.S * a.Hkv, sh, B, lds, &thr, &mask, &need);
+  resolve<K, NLV>(hist, a.S * a.Hkv, sh, B, lds, &thr, &mask, &need, a.rcache);
   const int dlast = static_cast<int>((thr >> Radix<K>::shift(NLV - 1)) & Radix<K>::wmask(NLV - 1));
   int gt_b = 0, eq_b = 0;
   for (int c = threadIdx.x; c < ch; c += SEL_THREADS) gt_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2];
@@ -827,7 +844,10 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
     }
     __syncthreads();
     Search st;
-    st.done = 0.0;
+    // -1: still searching, and a grid point below 10^12 already exceeds the
+    // target by more than the fp32 grid's error, so E(10^12) reaches the
+    // band (E is increasing) and need not be evaluated
+    st.done = (kx < kSelGrid && grid_u(kx, B) < log(kAlphaMax) && Ek >= target * (1.0 + 1e-5) + 1.0) ? -1.0 : 0.0;
     if (kx == 0) {
       st.u = grid_u(0, B);
     } else if (kx == kSelGrid) {
@@ -841,12 +861,12 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
     return st;
   }
   Search st = A.state[(step & 1) * SH + sh];
-  if (st.done != 0.0) return st;
+  if (st.done > 0.0) return st;
   const int pb = (step - 1) & 1;
   double E, dE, Eh;
   search_sum3(A, pb, sh, nch, &E, &dE, &Eh, dl);
   const double target = static_cast<double>(B);
-  if (step == 1) {
+  if (step == 1 && st.done == 0.0) {
     if (Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
       st.done = 2.0;
       return st;
@@ -879,7 +899,8 @@ __device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257]) {
   __shared__ double dl[12];
   const Search st = search_state(A, step, sh, nch, B, dl, eg);
   if (ch == 0 && threadIdx.x == 0) A.state[((step + 1) & 1) * SH + sh] = st;
-  if (st.done != 0.0) return;
+  if (st.done > 0.0) return;
+  const bool want_eh = step == 0 && st.done == 0.0;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   const double m = exp(st.u);
   double e = 0.0, de = 0.0, eh = 0.0;
@@ -891,12 +912,10 @@ __device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257]) {
       const double x = expm1(m * l);
       e -= x;
       de -= l * (x + 1.0);
-      if (step == 0) eh -= expm1(kAlphaMax * l);
+      if (want_eh) eh -= expm1(kAlphaMax * l);
     }
   }
-  e = block_sum_d(e, dl);
-  de = block_sum_d(de, dl);
-  if (step == 0) eh = block_sum_d(eh, dl);
+  block_sum3_d(&e, &de, &eh, dl);
   if (threadIdx.x == 0) {
     double* p = part_of(A, step & 1, sh, ch);
     p[0] = e;
@@ -1447,6 +1466,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   a.T = G.T;
   a.nchunk = G.nchunk;
   a.totalB = soft ? soft->total_cap : G.total_B;
+  a.rcache = reinterpret_cast<RCache*>(wsb + G.off_rcache);
   const dim3 grid(G.nchunk, G.Hkv, G.S);
   // histograms start at zero; cleared by a kernel, so that a captured graph
   // holds no memset node
