@@ -262,11 +262,11 @@ __device__ __forceinline__ void sel_hist_body(Src src, const SelArgs& a, int* __
     const int j = j0 + i * SEL_THREADS + threadIdx.x;
     u[i] = (j < n) ? src.key(row + j) : K(0);
   }
-  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
   K prefix, mask;
   int need;
-  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need, a.rcache);
-  __syncthreads();   // lh cleared (level 0 resolves nothing and has no barrier of its own)
+  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need, a.rcache);   // its loads overlap the keys'
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+  __syncthreads();   // lh cleared
   const int sft = Radix<K>::shift(LV);
   const K dm = Radix<K>::wmask(LV);
 #pragma unroll
@@ -294,10 +294,11 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
 // per (sequence, head) a list of the keys that share them (index, last
 // digit).  Such keys are few unless many scores tie; the list has room for
 // every key of the head.
+// lh: SEL_BINS ints of LDS, lds: 8 ints of LDS.
 template <class Src>
-__global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a, int* __restrict__ hist,
-                                                             int* __restrict__ ncand, int2* __restrict__ cand,
-                                                             int cap, int* __restrict__ cnt) {
+__device__ __forceinline__ void sel_hist_last_body(Src src, const SelArgs& a, int* __restrict__ hist,
+                                                   int* __restrict__ ncand, int2* __restrict__ cand, int cap,
+                                                   int* __restrict__ cnt, int* lh, int* lds) {
   typedef typename Src::K K;
   constexpr int LV = Radix<K>::LEVELS - 1;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -308,8 +309,6 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a,
   const int j0 = ch * SEL_CHUNK;
   if (B <= 0 || B >= n || j0 >= n) return;
   const int SH = a.S * a.Hkv;
-  __shared__ int lh[SEL_BINS];
-  __shared__ int lds[8];
   const size_t row = static_cast<size_t>(h) * a.T + base;
   K u[SEL_PER];
 #pragma unroll
@@ -317,11 +316,11 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a,
     const int j = j0 + i * SEL_THREADS + threadIdx.x;
     u[i] = (j < n) ? src.key(row + j) : K(0);
   }
-  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
   K prefix, mask;
   int need;
-  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need, a.rcache);
-  __syncthreads();
+  resolve<K, LV>(hist, SH, sh, B, lds, &prefix, &mask, &need, a.rcache);   // its loads overlap the keys'
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+  __syncthreads();   // lh cleared
   const int sft = Radix<K>::shift(LV);
   const K dm = Radix<K>::wmask(LV);
   int above = 0;
@@ -347,6 +346,14 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a,
     const int c = lh[i];
     if (c) atomicAdd(&gh[i], c);
   }
+}
+template <class Src>
+__global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a, int* __restrict__ hist,
+                                                             int* __restrict__ ncand, int2* __restrict__ cand,
+                                                             int cap, int* __restrict__ cnt) {
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  sel_hist_last_body<Src>(src, a, hist, ncand, cand, cap, cnt, lh, lds);
 }
 
 // Threshold (the B-th largest key) and the number of keys equal to it that
@@ -701,9 +708,33 @@ __device__ __forceinline__ bool smp_active(const SmpArgs& A, int s, int ch, int*
   return B > 0 && B < n && ch * SMP_CHUNK < n;
 }
 
+// log pi~ of key j of a row: log(max(s, 2^-126)) / tau.
+__device__ __forceinline__ double smp_logpt(const SmpArgs& A, size_t i) {
+  return log(static_cast<double>(fmaxf(A.scores[i], 1.17549435e-38f))) * A.inv_tau;
+}
+// Gumbel key of key j of (sequence s, head h) with log-proposal x:
+// x - log(-log u_j), u_j = ((w >> 11) + 0.5) 2^-53 with w the Philox word 0
+// of counter (j, h, s, 0).
+__device__ __forceinline__ double smp_gumbel(const SmpArgs& A, double x, int j, int h, int s) {
+  const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h), static_cast<uint64_t>(s),
+                                      0ull, A.seed, 0ull);
+  const double uu = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
+  return x - log(-log(uu));
+}
+
 // Pass A: log pi~ = log(max(s, 2^-126)) / tau, its per-chunk maximum and
 // the chunk's sum of exp(log pi~ - maximum) (the normaliser in parts).
-__global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
+// KEYS (unmixed proposal): the Gumbel keys need no normaliser, so this pass
+// writes them in place of log pi~, and it also clears the selection's
+// counters ([0, nzero) of `zero`: every digit level's histogram and the
+// candidate counts), which no workgroup of this launch touches otherwise.
+template <bool KEYS>
+__global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A, int* __restrict__ zero, int nzero) {
+  if constexpr (KEYS) {
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    const int wg = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    for (int i = wg * SEL_THREADS + threadIdx.x; i < nzero; i += nwg * SEL_THREADS) zero[i] = 0;
+  }
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -717,8 +748,13 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A) {
     const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     x[i] = -INFINITY;
     if (j < n) {
-      x[i] = log(static_cast<double>(fmaxf(A.scores[row + j], 1.17549435e-38f))) * A.inv_tau;
-      A.lp[row + j] = x[i];
+      x[i] = smp_logpt(A, row + j);
+      if (KEYS) {   // log pi~ waits in the log1p(-pi) plane for the next pass
+        A.lp[row + j] = smp_gumbel(A, x[i], j, h, s);
+        A.L[row + j] = x[i];
+      } else {
+        A.lp[row + j] = x[i];
+      }
       mx = fmax(mx, x[i]);
     }
   }
@@ -744,11 +780,14 @@ __device__ __forceinline__ double grid_u(int k, int B) {
   return fmin(log(static_cast<double>(B)) + k * 0.69314718055994531, log(kAlphaMax));
 }
 
-// Pass B: log1p(-pi_j) and the Gumbel keys kappa_j = log pi~_j - log(-log u_j),
-// u_j = ((x >> 11) + 0.5) 2^-53 with x the Philox word 0 of counter (j, h, s, 0).
-// Also the chunk's E(m) = sum 1 - (1 - pi_j)^m on the start grid, in fp32
-// (it only brackets the search; every value the search accepts is fp64).
-__global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
+// Pass B: log1p(-pi_j) and (KEYS) the Gumbel keys of the proposal's
+// logarithm, mixed or not (smp_gumbel); without KEYS pass A already wrote
+// them and left log pi~ in the log1p(-pi) plane, which this pass overwrites.  Also the chunk's
+// E(m) = sum 1 - (1 - pi_j)^m on the start grid, in fp32 (it only brackets
+// the search; every value the search accepts is fp64).
+// eg: kSelGrid x 257 floats of LDS.
+template <bool KEYS>
+__device__ void smp_keys_body(const SmpArgs& A, float (*eg)[SEL_THREADS + 1]) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -756,13 +795,31 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t row = static_cast<size_t>(h) * A.g.T + base;
   __shared__ double dl[4];
-  __shared__ float eg[kSelGrid][SEL_THREADS + 1];
+  // every load first (their latencies overlap): this thread's log pi~ and,
+  // with at most one chunk per thread, its chunk's part of the normaliser
+  double xin[SMP_PER];
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
+    xin[i] = (j < n) ? (KEYS ? A.lp[row + j] : A.L[row + j]) : 0.0;
+  }
+  const bool one = nch <= SEL_THREADS;
+  double pm0 = -INFINITY, pz0 = 0.0;
+  if (one && threadIdx.x < nch) {
+    const double* p = part_of(A, 0, sh, threadIdx.x);
+    pm0 = fmax(pm0, p[0]);   // as max_part folds it
+    pz0 = p[1];
+  }
   // log-sum-exp of the whole row from the chunk parts, in chunk order
-  const double M = max_part(A, 0, sh, nch, 0, dl);
+  const double M = one ? block_max_d(pm0, dl) : max_part(A, 0, sh, nch, 0, dl);
   double zp = 0.0;
-  for (int i = threadIdx.x; i < nch; i += SEL_THREADS) {
-    const double* p = part_of(A, 0, sh, i);
-    zp += p[1] * exp(p[0] - M);
+  if (one) {
+    if (threadIdx.x < nch) zp = pz0 * exp(pm0 - M);
+  } else {
+    for (int i = threadIdx.x; i < nch; i += SEL_THREADS) {
+      const double* p = part_of(A, 0, sh, i);
+      zp += p[1] * exp(p[0] - M);
+    }
   }
   const double lse = M + log(block_sum_d(zp, dl));
   // per grid point, this thread's share of the chunk's E(m_k)
@@ -773,9 +830,9 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   for (int i = 0; i < SMP_PER; ++i) {
     const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
-      double x = A.lp[row + j];
+      double x = xin[i];
       double l;
-      if (A.mix < 1.0) {   // pi' = alpha pi + (1 - alpha) / n; the keys use log pi'
+      if (KEYS && A.mix < 1.0) {   // pi' = alpha pi + (1 - alpha) / n; the keys use log pi'
         const double pm = A.mix * exp(x - lse) + (1.0 - A.mix) / n;
         l = log1p(-pm);
         x = log(pm);
@@ -783,10 +840,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
         l = log1p(-exp(x - lse));
       }
       A.L[row + j] = l;
-      const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h),
-                                          static_cast<uint64_t>(s), 0ull, A.seed, 0ull);
-      const double uu = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
-      A.lp[row + j] = x - log(-log(uu));
+      if (KEYS) A.lp[row + j] = smp_gumbel(A, x, j, h, s);
       float dk = -expm1f(static_cast<float>(static_cast<double>(B) * l));
 #pragma unroll
       for (int k = 0; k < kSelGrid; ++k) {
@@ -800,16 +854,62 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
   if ((threadIdx.x & 7) == 0)
     A.grid[(static_cast<size_t>(sh) * A.nsmp + ch) * kSelGrid + (threadIdx.x >> 3)] = t;
 }
+__global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
+  __shared__ float eg[kSelGrid][SEL_THREADS + 1];
+  smp_keys_body<true>(A, eg);
+}
 
-// The search state after step `step`: step 0 starts from the state smp_keys
-// wrote; later steps apply the update of the previous step's partials (every
+// What a search step (or the finish) reads, loaded at the start of its
+// launch so that the latencies overlap each other and the histogram's.  With
+// a head-local search and at most one chunk per thread (`one`), thread t
+// holds chunk t's grid values (step 0) or partials (later steps); otherwise
+// the state update reads them itself.
+struct SearchIn {
+  double l[SMP_PER];   // log1p(-pi) of this thread's keys (0 past the end)
+  float g[kSelGrid];   // step 0: chunk threadIdx.x's E(m) on the start grid
+  double p[3];         // later steps: chunk threadIdx.x's partials of the previous step
+  Search st;           // later steps: the state the previous step left
+  bool one;
+};
+__device__ __forceinline__ void search_load(const SmpArgs& A, int step, int sh, int nch, int n, size_t row,
+                                            SearchIn* in) {
+  const int ch = blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
+    in->l[i] = (j < n) ? A.L[row + j] : 0.0;
+  }
+  in->one = !A.global && nch <= SEL_THREADS;
+  const bool mine = in->one && static_cast<int>(threadIdx.x) < nch;
+#pragma unroll
+  for (int k = 0; k < kSelGrid; ++k) in->g[k] = 0.f;
+  in->p[0] = in->p[1] = in->p[2] = 0.0;
+  if (step == 0) {
+    if (mine) {
+      const float* gp = A.grid + (static_cast<size_t>(sh) * A.nsmp + threadIdx.x) * kSelGrid;
+#pragma unroll
+      for (int k = 0; k < kSelGrid; ++k) in->g[k] = gp[k];
+    }
+  } else {
+    const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
+    in->st = A.state[(step & 1) * SH + sh];
+    if (mine) {
+      const double* q = part_of(A, (step - 1) & 1, sh, threadIdx.x);
+      in->p[0] = q[0];
+      in->p[1] = q[1];
+      in->p[2] = q[2];
+    }
+  }
+}
+
+// The search state after step `step`: step 0 starts from the grid the keys
+// pass wrote; later steps apply the update of the previous step's partials (every
 // workgroup computes the same update, in the same order).  The update is a
 // safeguarded Newton step in log m on E(e^u) - B (bisection of the bracket
 // when the step leaves it), or stop once |E - B| <= 0.5, or -- on step 1,
 // from E(10^12) -- stop with the target out of reach.
 __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int B, double* dl,
-                               float (*eg)[257]) {
-  const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
+                               float (*eg)[257], const SearchIn& in) {
   if (step == 0) {
     // start from the grid: the first point whose E reaches B, and a bracket
     // one grid cell wider on each side than the crossing (the grid sums are
@@ -819,7 +919,10 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
     const int nh = A.global ? A.g.Hkv : 1;
     // every grid point's head (or heads') total in one block reduction
     float v[kSelGrid];
-    {
+    if (in.one) {   // one chunk per thread: its fp32 values as they are
+#pragma unroll
+      for (int k = 0; k < kSelGrid; ++k) v[k] = in.g[k];
+    } else {
       double acc[kSelGrid];
 #pragma unroll
       for (int k = 0; k < kSelGrid; ++k) acc[k] = 0.0;
@@ -860,11 +963,18 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
     st.hi = (kx + 1 < kSelGrid) ? grid_u(kx + 1, B) : log(kAlphaMax);
     return st;
   }
-  Search st = A.state[(step & 1) * SH + sh];
+  Search st = in.st;
   if (st.done > 0.0) return st;
   const int pb = (step - 1) & 1;
   double E, dE, Eh;
-  search_sum3(A, pb, sh, nch, &E, &dE, &Eh, dl);
+  if (in.one) {   // the same sums as search_sum3's for one chunk per thread
+    E = in.p[0];
+    dE = in.p[1];
+    Eh = in.p[2];
+    block_sum3_d(&E, &dE, &Eh, dl);
+  } else {
+    search_sum3(A, pb, sh, nch, &E, &dE, &Eh, dl);
+  }
   const double target = static_cast<double>(B);
   if (step == 1 && st.done == 0.0) {
     if (Eh < target - 0.5) {   // no m in [0, 10^12] reaches the band
@@ -888,8 +998,9 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
 // One step of the expected-samples search: brings the state up to date,
 // then (if still searching) writes the chunk's E(m), dE/dm at m = e^u, and
 // on the first step also E(10^12).
-// eg: kSelGrid x 257 floats of LDS, used on step 0 only (may be NULL after).
-__device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257]) {
+// eg: kSelGrid x 257 floats of LDS, used on step 0 only (may be NULL after);
+// in: search_load's values for this workgroup.
+__device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257], const SearchIn& in) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -897,18 +1008,17 @@ __device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257]) {
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[12];
-  const Search st = search_state(A, step, sh, nch, B, dl, eg);
+  const Search st = search_state(A, step, sh, nch, B, dl, eg, in);
   if (ch == 0 && threadIdx.x == 0) A.state[((step + 1) & 1) * SH + sh] = st;
   if (st.done > 0.0) return;
   const bool want_eh = step == 0 && st.done == 0.0;
-  const size_t row = static_cast<size_t>(h) * A.g.T + base;
   const double m = exp(st.u);
   double e = 0.0, de = 0.0, eh = 0.0;
 #pragma unroll 4
   for (int i = 0; i < SMP_PER; ++i) {
     const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
-      const double l = A.L[row + j];
+      const double l = in.l[i];
       const double x = expm1(m * l);
       e -= x;
       de -= l * (x + 1.0);
@@ -927,7 +1037,7 @@ __device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257]) {
 // Brings the state up to date after the last step, then writes the chunk's
 // E at m0 = floor(e^u) and m0 + 1 (one of them lies in the band when the
 // search converged: E rises by at most 1 per unit step).
-__device__ void smp_finish_body(const SmpArgs& A, int steps) {
+__device__ void smp_finish_body(const SmpArgs& A, int steps, const SearchIn& in) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -935,18 +1045,17 @@ __device__ void smp_finish_body(const SmpArgs& A, int steps) {
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[12];
-  const Search st = search_state(A, steps, sh, nch, B, dl, nullptr);   // steps >= 1: no grid
+  const Search st = search_state(A, steps, sh, nch, B, dl, nullptr, in);   // steps >= 1: no grid
   if (ch == 0 && threadIdx.x == 0) A.state[((steps + 1) & 1) * SH + sh] = st;
   // out of reach: E at 10^12 (the second value), which sets a head's count
   // under a soft budget
   const double m0 = (st.done == 2.0) ? kAlphaMax - 1.0 : fmin(floor(exp(st.u)), kAlphaMax - 1.0);
-  const size_t row = static_cast<size_t>(h) * A.g.T + base;
   double e0 = 0.0, e1 = 0.0;
 #pragma unroll 4
   for (int i = 0; i < SMP_PER; ++i) {
     const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
     if (j < n) {
-      const double l = A.L[row + j];
+      const double l = in.l[i];
       e0 -= expm1(m0 * l);
       e1 -= expm1((m0 + 1.0) * l);
     }
@@ -1053,11 +1162,27 @@ __device__ void smp_decide_body(const SmpArgs& A, int steps, double* m_out, int3
   }
 }
 
+// search_load for this workgroup's chunk; false if the chunk takes no part.
+__device__ __forceinline__ bool search_load_wg(const SmpArgs& A, int step, SearchIn* in) {
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  int n, B, base;
+  if (!smp_active(A, s, ch, &n, &B, &base)) return false;
+  search_load(A, step, s * A.g.Hkv + h, (n + SMP_CHUNK - 1) / SMP_CHUNK, n, static_cast<size_t>(h) * A.g.T + base,
+              in);
+  return true;
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
   __shared__ float eg[kSelGrid][257];
-  smp_search_body(A, step, eg);
+  SearchIn in;
+  if (!search_load_wg(A, step, &in)) return;
+  smp_search_body(A, step, eg, in);
 }
-__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) { smp_finish_body(A, steps); }
+__global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) {
+  SearchIn in;
+  if (!search_load_wg(A, steps, &in)) return;
+  smp_finish_body(A, steps, in);
+}
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, double* m_out, int32_t* status_out) {
   smp_decide_body(A, steps, m_out, status_out, blockIdx.x, blockIdx.y);
 }
@@ -1070,27 +1195,34 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
 // the decision (in the first chunk's workgroup of each head) with the next.
 // Step 0 (which sums the start grid) shares one LDS block between its two
 // parts; the others hold only the histogram's.
-template <int LV>
+// The search's loads go out first, then the histogram runs (its own loads
+// overlap them), then the search step; a chunk outside the search (budget
+// 0, at least n, or past the end) is outside the histograms too.
+template <int LV, bool FIRST>
 __global__ __launch_bounds__(SEL_THREADS) void smp_search_hist(SmpArgs A, int step, int* __restrict__ hist) {
   __shared__ int lds[8];
-  if constexpr (LV == 0) {
+  SearchIn in;
+  if (!search_load_wg(A, step, &in)) return;
+  if constexpr (FIRST) {
     __shared__ __align__(16) float eg[kSelGrid][257];
     static_assert(sizeof(eg) >= SEL_BINS * sizeof(int), "the grid block holds the histogram");
-    smp_search_body(A, step, eg);
-    __syncthreads();
     sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, reinterpret_cast<int*>(&eg[0][0]), lds);
+    __syncthreads();   // the histogram's LDS is the grid's
+    smp_search_body(A, step, eg, in);
   } else {
     __shared__ int lh[SEL_BINS];
-    smp_search_body(A, step, nullptr);
     sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
+    smp_search_body(A, step, nullptr, in);
   }
 }
 template <int LV>
 __global__ __launch_bounds__(SEL_THREADS) void smp_finish_hist(SmpArgs A, int steps, int* __restrict__ hist) {
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
-  smp_finish_body(A, steps);
+  SearchIn in;
+  if (!search_load_wg(A, steps, &in)) return;
   sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
+  smp_finish_body(A, steps, in);
 }
 template <int LV>
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide_hist(SmpArgs A, int steps, double* m_out,
@@ -1099,6 +1231,25 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide_hist(SmpArgs A, int st
   __shared__ int lds[8];
   if (blockIdx.x == 0) smp_decide_body(A, steps, m_out, status_out, blockIdx.y, blockIdx.z);
   sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
+}
+// Pass B without the keys (pass A wrote them), with the keys' level 0.
+__global__ __launch_bounds__(SEL_THREADS) void smp_grid_hist(SmpArgs A, int* __restrict__ hist) {
+  __shared__ int lds[8];
+  __shared__ __align__(16) float eg[kSelGrid][SEL_THREADS + 1];
+  static_assert(sizeof(eg) >= SEL_BINS * sizeof(int), "the grid block holds the histogram");
+  smp_keys_body<false>(A, eg);
+  __syncthreads();
+  sel_hist_body<GumbelKeys, 0>(GumbelKeys{A.lp}, A.g, hist, reinterpret_cast<int*>(&eg[0][0]), lds);
+}
+// The decision with the keys' last level (its candidate list and counts).
+__global__ __launch_bounds__(SEL_THREADS) void smp_decide_last(SmpArgs A, int steps, double* m_out,
+                                                               int32_t* status_out, int* __restrict__ hist,
+                                                               int* __restrict__ ncand, int2* __restrict__ cand,
+                                                               int cap, int* __restrict__ cnt) {
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  if (blockIdx.x == 0) smp_decide_body(A, steps, m_out, status_out, blockIdx.y, blockIdx.z);
+  sel_hist_last_body<GumbelKeys>(GumbelKeys{A.lp}, A.g, hist, ncand, cand, cap, cnt, lh, lds);
 }
 
 // ------------------------------------------------------- literal estimator
@@ -1472,9 +1623,13 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   // holds no memset node
   const int nzero = static_cast<int>((G.zero_end - G.off_hist) / sizeof(int));
   const bool topk = G.mode == KVE_TOPK;
+  // sampling with a per-head budget and the unmixed proposal: the first
+  // pass also writes the Gumbel keys and clears the counters
+  const bool chain = !topk && !soft && mix >= 1.0f;
   stage_begin(ST_SELECT, st);
-  hipLaunchKernelGGL(sel_init, dim3((max(nzero, SH) + 255) / 256), dim3(256), 0, st, hist, nzero,
-                     topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
+  if (!chain)
+    hipLaunchKernelGGL(sel_init, dim3((max(nzero, SH) + 255) / 256), dim3(256), 0, st, hist, nzero,
+                       topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
   if (topk) {
     launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st,
                  reinterpret_cast<int*>(wsb + G.off_ncand), reinterpret_cast<int2*>(wsb + G.off_cand));
@@ -1496,18 +1651,36 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.bsh = soft ? reinterpret_cast<int32_t*>(wsb + G.off_bsh) : nullptr;
     A.kept_out = soft ? soft->kept : nullptr;
     const dim3 sgrid(G.nsmp, G.Hkv, G.S);
-    hipLaunchKernelGGL(smp_logp, sgrid, dim3(SEL_THREADS), 0, st, A);
-    hipLaunchKernelGGL(smp_keys, sgrid, dim3(SEL_THREADS), 0, st, A);
     const SnisBias bias_of{A.L, A.mvals, 1.0 / static_cast<double>(tau_w)};
     int* ncand = reinterpret_cast<int*>(wsb + G.off_ncand);
     int2* cand = reinterpret_cast<int2*>(wsb + G.off_cand);
+    // the search launches carry the keys' histogram levels
+    static_assert(kSelSearchSteps == 3 && Radix<uint64_t>::LEVELS == 6 && kSmpChunk == kSelChunk,
+                  "the fused launches pair 3 search steps, the finish and the decision with the 6 levels");
+    if (chain) {
+      // keys first: levels 0 .. 5 ride on the grid pass, the 3 search steps,
+      // the finish and the decision
+      hipLaunchKernelGGL((smp_logp<true>), sgrid, dim3(SEL_THREADS), 0, st, A, hist, nzero);
+      hipLaunchKernelGGL(smp_grid_hist, sgrid, dim3(SEL_THREADS), 0, st, A, hist);
+      hipLaunchKernelGGL((smp_search_hist<1, true>), sgrid, dim3(SEL_THREADS), 0, st, A, 0, hist);
+      hipLaunchKernelGGL((smp_search_hist<2, false>), sgrid, dim3(SEL_THREADS), 0, st, A, 1, hist);
+      hipLaunchKernelGGL((smp_search_hist<3, false>), sgrid, dim3(SEL_THREADS), 0, st, A, 2, hist);
+      hipLaunchKernelGGL((smp_finish_hist<4>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, hist);
+      hipLaunchKernelGGL(smp_decide_last, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out, status_out,
+                         hist, ncand, cand, G.max_len, cnt);
+      hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias>), sgrid, dim3(SEL_THREADS), 0, st,
+                         GumbelKeys{A.lp}, bias_of, a, hist, cnt, ncand, cand, G.max_len, idx, bias);
+      stage_end(ST_SELECT, st);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((smp_logp<false>), sgrid, dim3(SEL_THREADS), 0, st, A, nullptr, 0);
+    hipLaunchKernelGGL(smp_keys, sgrid, dim3(SEL_THREADS), 0, st, A);
     if (!soft) {
-      // the search launches carry the keys' histogram levels 0 .. 4
-      static_assert(kSelSearchSteps == 3 && Radix<uint64_t>::LEVELS == 6 && kSmpChunk == kSelChunk,
-                    "the fused launches pair 3 search steps, the finish and the decision with levels 0..4");
-      hipLaunchKernelGGL((smp_search_hist<0>), sgrid, dim3(SEL_THREADS), 0, st, A, 0, hist);
-      hipLaunchKernelGGL((smp_search_hist<1>), sgrid, dim3(SEL_THREADS), 0, st, A, 1, hist);
-      hipLaunchKernelGGL((smp_search_hist<2>), sgrid, dim3(SEL_THREADS), 0, st, A, 2, hist);
+      // (mixed proposal) the keys need the normaliser: levels 0 .. 4 ride
+      // on the search steps, the finish and the decision
+      hipLaunchKernelGGL((smp_search_hist<0, true>), sgrid, dim3(SEL_THREADS), 0, st, A, 0, hist);
+      hipLaunchKernelGGL((smp_search_hist<1, false>), sgrid, dim3(SEL_THREADS), 0, st, A, 1, hist);
+      hipLaunchKernelGGL((smp_search_hist<2, false>), sgrid, dim3(SEL_THREADS), 0, st, A, 2, hist);
       hipLaunchKernelGGL((smp_finish_hist<3>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, hist);
       hipLaunchKernelGGL((smp_decide_hist<4>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
                          status_out, hist);
