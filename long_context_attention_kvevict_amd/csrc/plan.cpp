@@ -131,9 +131,8 @@ kve_status plan_select(const kve_layout* L, const int32_t* bud_off_host, int mod
   g.off_a = off; off = align256(off + plane);
   g.off_b = off; off = align256(off + plane);
   g.off_hist = off; off = align256(off + levels * SH * kSelBins * sizeof(int32_t));
-  g.off_ncand = off; off = align256(off + SH * sizeof(int32_t));
   g.zero_end = off;
-  g.off_cand = off; off = align256(off + SH * static_cast<size_t>(max_len) * 2 * sizeof(int32_t));
+  g.off_cand = off; off = align256(off + SH * g.nchunk * static_cast<size_t>(kSelChunk) * sizeof(int32_t));
   g.off_cnt = off; off = align256(off + SH * g.nchunk * 2 * sizeof(int32_t));
   g.off_rstate = off; off = align256(off + SH * kSelRStateBytes);
   g.off_rcache = off; off = align256(off + SH * kSelLevels64 * kSelRCacheBytes);

@@ -54,6 +54,10 @@ constexpr int kSelSearchSteps = 3;
 constexpr int kSelRStateBytes = 16;   // per-head radix threshold and count of equal keys kept
 constexpr int kSelSearchBytes = 32;   // per-head search state
 constexpr int kSelRCacheBytes = 16;   // per-head, per-level resolved threshold digits
+// Keys of one selection chunk that share the threshold's leading digits are
+// listed (their last digits) when at most this many; a chunk with more
+// stores the suffix sums of their last-digit histogram instead.
+constexpr int kSelListMax = 64;
 
 struct SelectGeom {
   int S, Hkv, T, max_len, mode;
@@ -62,9 +66,8 @@ struct SelectGeom {
   int64_t total_B;
   size_t off_a, off_b;             // sampling: fp64 planes [Hkv][T]
   size_t off_hist;                 // int [levels][S*Hkv][kSelBins]
-  size_t off_ncand;                // int [S*Hkv] keys sharing the threshold's leading digits
   size_t zero_end;                 // [off_hist, zero_end) is cleared on entry
-  size_t off_cand;                 // int [S*Hkv][max_len][2] those keys (index, last digit)
+  size_t off_cand;                 // int [S*Hkv][nchunk][kSelChunk] per chunk: listed last digits or suffix sums
   size_t off_cnt;                  // int [S*Hkv][nchunk][2]
   size_t off_rstate;               // [S*Hkv] radix threshold state (kSelRStateBytes each)
   size_t off_rcache;               // [S*Hkv][kSelLevels64] resolved digits (kSelRCacheBytes each)

@@ -125,12 +125,14 @@ struct Radix;
 template <>
 struct Radix<uint32_t> {   // digits of 11 + 11 + 10 bits
   static constexpr int LEVELS = 3;
+  static constexpr int LAST_BINS = 1024;
   __device__ static int shift(int lv) { return lv == 0 ? 21 : (lv == 1 ? 10 : 0); }
   __device__ static uint32_t wmask(int lv) { return lv == 2 ? 0x3ffu : 0x7ffu; }
 };
 template <>
 struct Radix<uint64_t> {   // digits of 5 x 11 + 9 bits
   static constexpr int LEVELS = 6;
+  static constexpr int LAST_BINS = 512;
   __device__ static int shift(int lv) { return lv < 5 ? 53 - 11 * lv : 0; }
   __device__ static uint64_t wmask(int lv) { return lv < 5 ? 0x7ffull : 0x1ffull; }
 };
@@ -289,18 +291,21 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
 }
 
 // Last digit level of the radix select, which also leaves the ordered write
-// what a separate count launch would: per chunk, the number of keys whose
-// leading digits (levels 0 .. LEVELS-2) exceed those of the threshold, and
-// per (sequence, head) a list of the keys that share them (index, last
-// digit).  Such keys are few unless many scores tie; the list has room for
-// every key of the head.
+// what a separate count launch would.  Per chunk: the number of keys whose
+// leading digits (levels 0 .. LEVELS-2) exceed those of the threshold, and,
+// for the keys that share them, their last digits in the chunk's own region
+// of `cand` (kSelChunk ints) -- listed when at most kSelListMax, otherwise as
+// suffix sums S[d] = (keys with a last digit >= d), so that the write reads
+// a bounded amount per earlier chunk however many keys tie.  cnt[.][1] holds
+// the listed count, or -1 for suffix sums.
 // lh: SEL_BINS ints of LDS, lds: 8 ints of LDS.
 template <class Src>
 __device__ __forceinline__ void sel_hist_last_body(Src src, const SelArgs& a, int* __restrict__ hist,
-                                                   int* __restrict__ ncand, int2* __restrict__ cand, int cap,
-                                                   int* __restrict__ cnt, int* lh, int* lds) {
+                                                   int* __restrict__ cand, int* __restrict__ cnt, int* lh, int* lds) {
   typedef typename Src::K K;
   constexpr int LV = Radix<K>::LEVELS - 1;
+  constexpr int NB = Radix<K>::LAST_BINS;
+  static_assert(NB % SEL_THREADS == 0 && NB <= SEL_CHUNK, "a chunk's region holds the suffix sums");
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
@@ -323,24 +328,55 @@ __device__ __forceinline__ void sel_hist_last_body(Src src, const SelArgs& a, in
   __syncthreads();   // lh cleared
   const int sft = Radix<K>::shift(LV);
   const K dm = Radix<K>::wmask(LV);
-  int above = 0;
+  int above = 0, nmine = 0;
+  int dg[SEL_PER];
 #pragma unroll
   for (int i = 0; i < SEL_PER; ++i) {
     const int j = j0 + i * SEL_THREADS + threadIdx.x;
+    dg[i] = -1;
     if (j >= n) continue;
     const K lead = u[i] & mask;
     if (lead > prefix) {
       ++above;
     } else if (lead == prefix) {
-      const int dg = static_cast<int>((u[i] >> sft) & dm);
-      atomicAdd(&lh[dg], 1);
-      const int slot = atomicAdd(&ncand[sh], 1);   // < n <= cap: each key is listed once
-      cand[static_cast<size_t>(sh) * cap + slot] = make_int2(j, dg);
+      dg[i] = static_cast<int>((u[i] >> sft) & dm);
+      atomicAdd(&lh[dg[i]], 1);
+      ++nmine;
     }
   }
+  // both counts in one scan (each field stays below 2^16)
+  const int packed = (above << 16) | nmine;
   int tot;
-  block_incl_scan256(above, lds, &tot);   // its barriers also complete lh
-  if (threadIdx.x == 0) cnt[(static_cast<size_t>(sh) * a.nchunk + ch) * 2] = tot;
+  const int incl = block_incl_scan256(packed, lds, &tot);   // its barriers also complete lh
+  const int nl = tot & 0xffff;
+  const size_t ci = static_cast<size_t>(sh) * a.nchunk + ch;
+  int* reg = cand + ci * SEL_CHUNK;
+  if (nl <= kSelListMax) {
+    int pos = (incl - packed) & 0xffff;
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i)
+      if (dg[i] >= 0) reg[pos++] = dg[i];
+  } else {
+    // thread t holds bins NB-1-Q t .. NB-Q(t+1), top down
+    constexpr int Q = NB / SEL_THREADS;
+    int v[Q], sum = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      v[q] = lh[NB - 1 - (threadIdx.x * Q + q)];
+      sum += v[q];
+    }
+    int t2;
+    int run = block_incl_scan256(sum, lds, &t2) - sum;   // keys in the bins above this thread's
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      run += v[q];
+      reg[NB - 1 - (threadIdx.x * Q + q)] = run;
+    }
+  }
+  if (threadIdx.x == 0) {
+    cnt[ci * 2] = tot >> 16;
+    cnt[ci * 2 + 1] = (nl <= kSelListMax) ? nl : -1;
+  }
   int* gh = hist + (static_cast<size_t>(LV) * SH + sh) * SEL_BINS;
   for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) {
     const int c = lh[i];
@@ -349,11 +385,10 @@ __device__ __forceinline__ void sel_hist_last_body(Src src, const SelArgs& a, in
 }
 template <class Src>
 __global__ __launch_bounds__(SEL_THREADS) void sel_hist_last(Src src, SelArgs a, int* __restrict__ hist,
-                                                             int* __restrict__ ncand, int2* __restrict__ cand,
-                                                             int cap, int* __restrict__ cnt) {
+                                                             int* __restrict__ cand, int* __restrict__ cnt) {
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
-  sel_hist_last_body<Src>(src, a, hist, ncand, cand, cap, cnt, lh, lds);
+  sel_hist_last_body<Src>(src, a, hist, cand, cnt, lh, lds);
 }
 
 // Threshold (the B-th largest key) and the number of keys equal to it that
@@ -506,18 +541,17 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
   }
 }
 
-// Ordered write from sel_hist_last's counts: the
-// threshold is resolved here from the finished histograms (as sel_count
-// does), the keys above it in earlier chunks are the per-chunk counts of
-// larger leading digits plus the listed keys with a larger last digit, and
-// the keys equal to it are the listed keys with the same last digit.  The
-// rest is sel_write's; the output is the same.
+// Ordered write from sel_hist_last's counts: the threshold is resolved here
+// from the finished histograms (as sel_count does); the keys above it in an
+// earlier chunk are that chunk's count of larger leading digits plus its
+// keys with the same leading digits and a larger last digit, and the keys
+// equal to it are those with the same last digit (from the chunk's list or
+// suffix sums).  The rest is sel_write's; the output is the same.
 template <class Src, class Bias>
 __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bias_of, SelArgs a,
                                                                 const int* __restrict__ hist,
                                                                 const int* __restrict__ cnt,
-                                                                const int* __restrict__ ncand,
-                                                                const int2* __restrict__ cand, int cap,
+                                                                const int* __restrict__ cand,
                                                                 int32_t* __restrict__ idx,
                                                                 float* __restrict__ bias) {
   typedef typename Src::K K;
@@ -549,14 +583,23 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bi
   int need;
   resolve<K, NLV>(hist, a.S * a.Hkv, sh, B, lds, &thr, &mask, &need, a.rcache);
   const int dlast = static_cast<int>((thr >> Radix<K>::shift(NLV - 1)) & Radix<K>::wmask(NLV - 1));
+  constexpr int NB = Radix<K>::LAST_BINS;
   int gt_b = 0, eq_b = 0;
-  for (int c = threadIdx.x; c < ch; c += SEL_THREADS) gt_b += cnt[(static_cast<size_t>(sh) * a.nchunk + c) * 2];
-  const int nc = ncand[sh];
-  for (int i = threadIdx.x; i < nc; i += SEL_THREADS) {
-    const int2 e = cand[static_cast<size_t>(sh) * cap + i];
-    if (e.x < j0) {
-      gt_b += e.y > dlast;
-      eq_b += e.y == dlast;
+  for (int c = threadIdx.x; c < ch; c += SEL_THREADS) {
+    const size_t ci = static_cast<size_t>(sh) * a.nchunk + c;
+    const int* reg = cand + ci * SEL_CHUNK;
+    const int m = cnt[ci * 2 + 1];
+    gt_b += cnt[ci * 2];
+    if (m >= 0) {
+      for (int i = 0; i < m; ++i) {
+        const int d = reg[i];
+        gt_b += d > dlast;
+        eq_b += d == dlast;
+      }
+    } else {
+      const int ge = reg[dlast], gt = (dlast + 1 < NB) ? reg[dlast + 1] : 0;
+      gt_b += gt;
+      eq_b += ge - gt;
     }
   }
   int tot;
@@ -726,8 +769,8 @@ __device__ __forceinline__ double smp_gumbel(const SmpArgs& A, double x, int j, 
 // the chunk's sum of exp(log pi~ - maximum) (the normaliser in parts).
 // KEYS (unmixed proposal): the Gumbel keys need no normaliser, so this pass
 // writes them in place of log pi~, and it also clears the selection's
-// counters ([0, nzero) of `zero`: every digit level's histogram and the
-// candidate counts), which no workgroup of this launch touches otherwise.
+// histograms ([0, nzero) of `zero`: every digit level's), which no
+// workgroup of this launch touches otherwise.
 template <bool KEYS>
 __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A, int* __restrict__ zero, int nzero) {
   if constexpr (KEYS) {
@@ -1244,12 +1287,11 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_grid_hist(SmpArgs A, int* __r
 // The decision with the keys' last level (its candidate list and counts).
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide_last(SmpArgs A, int steps, double* m_out,
                                                                int32_t* status_out, int* __restrict__ hist,
-                                                               int* __restrict__ ncand, int2* __restrict__ cand,
-                                                               int cap, int* __restrict__ cnt) {
+                                                               int* __restrict__ cand, int* __restrict__ cnt) {
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
   if (blockIdx.x == 0) smp_decide_body(A, steps, m_out, status_out, blockIdx.y, blockIdx.z);
-  sel_hist_last_body<GumbelKeys>(GumbelKeys{A.lp}, A.g, hist, ncand, cand, cap, cnt, lh, lds);
+  sel_hist_last_body<GumbelKeys>(GumbelKeys{A.lp}, A.g, hist, cand, cnt, lh, lds);
 }
 
 // ------------------------------------------------------- literal estimator
@@ -1556,11 +1598,10 @@ hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const fl
 // ----------------------------------------------------------------- launch
 template <class Src, class Bias>
 static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,
-                         RState* rs, int32_t* idx, float* bias, hipStream_t st, int* ncand = nullptr,
-                         int2* cand = nullptr) {
+                         RState* rs, int32_t* idx, float* bias, hipStream_t st, int* cand) {
   typedef typename Src::K K;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
-  if (ncand && a.bsh == nullptr) {   // no count launch (not under a soft budget)
+  if (a.bsh == nullptr) {   // no count launch (not under a soft budget)
     hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     hipLaunchKernelGGL((sel_hist<Src, 1>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     if (Radix<K>::LEVELS > 3) {
@@ -1568,10 +1609,9 @@ static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bi
       hipLaunchKernelGGL((sel_hist<Src, 3>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
       hipLaunchKernelGGL((sel_hist<Src, 4>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     }
-    hipLaunchKernelGGL((sel_hist_last<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, ncand, cand, G.max_len,
-                       cnt);
+    hipLaunchKernelGGL((sel_hist_last<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, cand, cnt);
     hipLaunchKernelGGL((sel_write_listed<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, hist, cnt,
-                       ncand, cand, G.max_len, idx, bias);
+                       cand, idx, bias);
     return;
   }
   hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
@@ -1624,7 +1664,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   const int nzero = static_cast<int>((G.zero_end - G.off_hist) / sizeof(int));
   const bool topk = G.mode == KVE_TOPK;
   // sampling with a per-head budget and the unmixed proposal: the first
-  // pass also writes the Gumbel keys and clears the counters
+  // pass also writes the Gumbel keys and clears the histograms
   const bool chain = !topk && !soft && mix >= 1.0f;
   stage_begin(ST_SELECT, st);
   if (!chain)
@@ -1632,7 +1672,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
                        topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
   if (topk) {
     launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st,
-                 reinterpret_cast<int*>(wsb + G.off_ncand), reinterpret_cast<int2*>(wsb + G.off_cand));
+                 reinterpret_cast<int*>(wsb + G.off_cand));
   } else {
     SmpArgs A;
     A.g = a;
@@ -1652,8 +1692,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     A.kept_out = soft ? soft->kept : nullptr;
     const dim3 sgrid(G.nsmp, G.Hkv, G.S);
     const SnisBias bias_of{A.L, A.mvals, 1.0 / static_cast<double>(tau_w)};
-    int* ncand = reinterpret_cast<int*>(wsb + G.off_ncand);
-    int2* cand = reinterpret_cast<int2*>(wsb + G.off_cand);
+    int* cand = reinterpret_cast<int*>(wsb + G.off_cand);
     // the search launches carry the keys' histogram levels
     static_assert(kSelSearchSteps == 3 && Radix<uint64_t>::LEVELS == 6 && kSmpChunk == kSelChunk,
                   "the fused launches pair 3 search steps, the finish and the decision with the 6 levels");
@@ -1667,9 +1706,9 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
       hipLaunchKernelGGL((smp_search_hist<3, false>), sgrid, dim3(SEL_THREADS), 0, st, A, 2, hist);
       hipLaunchKernelGGL((smp_finish_hist<4>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, hist);
       hipLaunchKernelGGL(smp_decide_last, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out, status_out,
-                         hist, ncand, cand, G.max_len, cnt);
+                         hist, cand, cnt);
       hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias>), sgrid, dim3(SEL_THREADS), 0, st,
-                         GumbelKeys{A.lp}, bias_of, a, hist, cnt, ncand, cand, G.max_len, idx, bias);
+                         GumbelKeys{A.lp}, bias_of, a, hist, cnt, cand, idx, bias);
       stage_end(ST_SELECT, st);
       return hipGetLastError();
     }
@@ -1686,9 +1725,9 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
                          status_out, hist);
       const dim3 grid(G.nchunk, G.Hkv, G.S);
       hipLaunchKernelGGL((sel_hist_last<GumbelKeys>), grid, dim3(SEL_THREADS), 0, st, GumbelKeys{A.lp}, a, hist,
-                         ncand, cand, G.max_len, cnt);
+                         cand, cnt);
       hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias>), grid, dim3(SEL_THREADS), 0, st, GumbelKeys{A.lp},
-                         bias_of, a, hist, cnt, ncand, cand, G.max_len, idx, bias);
+                         bias_of, a, hist, cnt, cand, idx, bias);
     } else {
       // a soft budget decides each head's kept count first (its radix
       // levels need it)
@@ -1697,7 +1736,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
       hipLaunchKernelGGL(smp_finish, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps);
       hipLaunchKernelGGL(smp_decide, dim3(G.Hkv, G.S), dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out,
                          status_out);
-      launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st, ncand, cand);
+      launch_radix(G, a, GumbelKeys{A.lp}, bias_of, hist, cnt, rs, idx, bias, st, cand);
     }
   }
   stage_end(ST_SELECT, st);

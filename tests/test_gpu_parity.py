@@ -506,6 +506,52 @@ def test_select_topk_crowded_threshold_bin(case):
     _select_check(r, sc, K.KVE_TOPK, 1.0, 1.0, 0)
 
 
+@pytest.mark.parametrize("mode", [K.KVE_TOPK, K.KVE_SAMPLE])
+@pytest.mark.parametrize("case", ["all_equal", "one_bin"])
+def test_select_crowded_full_length_is_exact_and_bounded(case, mode):
+    # Two heads of n = 131072 keys whose scores all tie (or share the
+    # threshold's leading digits): every 1024-key chunk holds far more than
+    # 64 keys with the threshold's leading digits, so each records the
+    # suffix sums of their last digits and the ordered write reads two values
+    # per earlier chunk.  Exact against the oracle, and the selection stays
+    # within the time of an uncrowded one (a write that scanned every tied
+    # key per chunk would take milliseconds here).
+    n = 131072
+    rng = np.random.default_rng(11)
+    if case == "all_equal":
+        sc = np.full((2, n), 0.75)
+    else:
+        sc = rng.uniform(1.0, 1.0001, size=(2, n))
+    sc = sc.astype(np.float32)
+    budgets = [13107]
+    wl = dataclasses.replace(workloads.tiny_fp32(), name="sel_crowded_128k", S=1, Hq=2, Hkv=2, lens=[n],
+                             budget_frac=0.0)
+    r = type("R", (), {})()
+    r.wl = wl
+    r.b = K.Batch([n], 2, 2, 64, 1, "f32")
+    wl.budgets = lambda: np.array(budgets, dtype=np.int32)
+    wl.bud_off = lambda: np.concatenate([[0], np.cumsum(budgets)]).astype(np.int32)
+    _select_check(r, sc, mode, 0.5, 1.0, 7)
+    dev = torch.from_numpy(sc).cuda()
+    plain = torch.from_numpy(rng.standard_normal((2, n)).astype(np.float32) ** 2).cuda()
+
+    def timed(x):
+        for _ in range(3):
+            r.b.select(x, budgets, mode=mode, tau=0.5, tau_w=1.0, seed=7)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            r.b.select(x, budgets, mode=mode, tau=0.5, tau_w=1.0, seed=7)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 10 * 1e3
+
+    t_crowded, t_plain = timed(dev), timed(plain)
+    say(f"[gpu] crowded select {case} mode {mode}: {t_crowded:.1f} us per call, uncrowded {t_plain:.1f} us")
+    assert t_crowded < 2.0 * t_plain + 50.0, (t_crowded, t_plain)
+
+
 # ---------------------------------------------------------------- merge
 def _merge_case(seed, lens, Hkv, frac, dup):
     rng = np.random.default_rng(seed)
