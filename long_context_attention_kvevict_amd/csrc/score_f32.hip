@@ -28,11 +28,22 @@ struct F32Args {
   float* sraw;
 };
 
+// One wave per window row, four rows per workgroup (blockIdx.y = (KV head,
+// row group, block of 4 rows)): the wave's lanes take 64 keys per step, each
+// forming its key's logit against the row's query (broadcast a feature at a
+// time from the lane that holds it), then the wave's online softmax and
+// o += p v, where lane l owns features l, l + 64, ...
+constexpr int P1F32_ROWS = 4;
+
 template <int DD>
 __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
+  static_assert(DD % 64 == 0, "whole features per lane");
+  constexpr int F = DD / 64;
   const int c = blockIdx.x;
-  const int h = blockIdx.y / a.RG;
-  const int rg = blockIdx.y % a.RG;
+  const int rb = blockIdx.y % (ROWS32 / P1F32_ROWS);
+  const int hg = blockIdx.y / (ROWS32 / P1F32_ROWS);
+  const int h = hg / a.RG;
+  const int rg = hg % a.RG;
   const int s = blockIdx.z;
   const int base = a.seq_off[s];
   const int n = a.seq_off[s + 1] - base;
@@ -41,76 +52,80 @@ __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
   const int c1 = min(c0 + a.CH, n);
   const int g = a.Hq / a.Hkv;
   const int R = g * a.w;
-  const int tid = threadIdx.x;
-  constexpr int NP = 256 / DD;          // key partitions of the o update
-
-  __shared__ float qs[DD];
-  __shared__ float ps[256];
-  __shared__ float red[256 / 64];
-  __shared__ float ored[256];
-
+  const int lane = threadIdx.x & 63;
+  const int rl = rb * P1F32_ROWS + (threadIdx.x >> 6);
+  const int row = rg * ROWS32 + rl;
+  if (row >= R) return;   // whole waves; no workgroup barrier below
+  const int qh = h * g + row / a.w;
+  const int wi = row % a.w;
+  const int pos = n - a.w + wi;
   const float* kb = a.k + (static_cast<size_t>(h) * a.T + base) * DD;
   const float* vb = a.v + (static_cast<size_t>(h) * a.T + base) * DD;
-  const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rg);
+  const float* qp = a.q_win + ((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * DD;
+  float qv[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) qv[f] = qp[64 * f + lane];
 
-  for (int rl = 0; rl < ROWS32; ++rl) {
-    const int row = rg * ROWS32 + rl;
-    if (row >= R) break;
-    const int qh = h * g + row / a.w;
-    const int wi = row % a.w;
-    const int pos = n - a.w + wi;
-    __syncthreads();
-    if (tid < DD) qs[tid] = a.q_win[((static_cast<size_t>(s) * a.Hq + qh) * a.w + wi) * DD + tid];
-    __syncthreads();
-    float m_run = -INFINITY, l_run = 0.f, o_part = 0.f;
-    const int d = tid % DD, part = tid / DD;
-    for (int t0 = c0; t0 < c1; t0 += 256) {
-      const int key = t0 + tid;
-      float x = -INFINITY;
-      if (key < c1 && !(a.causal && key > pos)) {
-        const float* kr = kb + static_cast<size_t>(key) * DD;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int e = 0; e < DD; ++e) acc = fmaf(qs[e], kr[e], acc);
-        x = acc * a.c2;
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) o[f] = 0.f;
+  for (int t0 = c0; t0 < c1; t0 += 64) {
+    const int key = t0 + lane;
+    float x = -INFINITY;
+    if (key < c1 && !(a.causal && key > pos)) {
+      const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<size_t>(key) * DD);
+      float acc = 0.f;
+#pragma unroll
+      for (int e4 = 0; e4 < DD / 4; ++e4) {
+        const float4 kk = kr[e4];
+        const int e = 4 * e4;
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv[e / 64]), e % 64)), kk.x, acc);
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv[e / 64]), e % 64 + 1)), kk.y, acc);
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv[e / 64]), e % 64 + 2)), kk.z, acc);
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv[e / 64]), e % 64 + 3)), kk.w, acc);
       }
-      float tm = wave_max(x);
-      __syncthreads();
-      if ((tid & 63) == 0) red[tid >> 6] = tm;
-      __syncthreads();
-      tm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      const float m_new = fmaxf(m_run, tm);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float scale = exp2f(m_run - m_use);
-      const float p = exp2f(x - m_use);
-      ps[tid] = p;
-      l_run = l_run * scale + p;       // per-thread partial, combined at the end
-      o_part *= scale;
-      m_run = m_new;
-      __syncthreads();
-      const int kn = min(256, c1 - t0);
-      for (int j = part; j < kn; j += NP) o_part = fmaf(ps[j], vb[static_cast<size_t>(t0 + j) * DD + d], o_part);
+      x = acc * a.c2;
     }
-    // combine l over all threads, o over partitions
-    float lt = wave_sum(l_run);
-    __syncthreads();
-    if ((tid & 63) == 0) red[tid >> 6] = lt;
-    ored[tid] = o_part;
-    __syncthreads();
-    const size_t pr = (grp * a.P + c) * ROWS32 + rl;
-    if (tid == 0) {   // the record of the bf16 path with no dominant-key candidate
-      float* rec = a.part_ml + pr * kScoreRec;
-      rec[0] = m_run;
-      rec[1] = (red[0] + red[1]) + (red[2] + red[3]);
-      rec[2] = 0.f;
-      rec[3] = __uint_as_float(0xffffffffu);   // key -1
-    }
-    if (tid < DD) {
-      float o = 0.f;
-      for (int q = 0; q < NP; ++q) o += ored[q * DD + tid];
-      a.part_o[pr * DD + tid] = o;
+    const float m_new = fmaxf(m_run, wave_max(x));
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float scale = exp2f(m_run - m_use);
+    const float p = exp2f(x - m_use);
+    l_run = l_run * scale + p;       // per-lane partial, summed at the end
+#pragma unroll
+    for (int f = 0; f < F; ++f) o[f] *= scale;
+    m_run = m_new;
+    // 16 value rows' loads in flight at a time; keys past the chunk (or
+    // hidden) have p = 0 and read the chunk's last row instead
+    const int kn = min(64, c1 - t0);
+    for (int j0 = 0; j0 < kn; j0 += 16) {
+      float vv[16][F];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float* vr = vb + static_cast<size_t>(min(t0 + j0 + jj, c1 - 1)) * DD;
+#pragma unroll
+        for (int f = 0; f < F; ++f) vv[jj][f] = vr[64 * f + lane];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j0 + jj));
+#pragma unroll
+        for (int f = 0; f < F; ++f) o[f] = fmaf(pj, vv[jj][f], o[f]);
+      }
     }
   }
+  const float lt = wave_sum(l_run);
+  const size_t grp = static_cast<size_t>((s * a.Hkv + h) * a.RG + rg);
+  const size_t pr = (grp * a.P + c) * ROWS32 + rl;
+  if (lane == 0) {   // the record of the bf16 path with no dominant-key candidate
+    float* rec = a.part_ml + pr * kScoreRec;
+    rec[0] = m_run;
+    rec[1] = lt;
+    rec[2] = 0.f;
+    rec[3] = __uint_as_float(0xffffffffu);   // key -1
+  }
+#pragma unroll
+  for (int f = 0; f < F; ++f) a.part_o[pr * DD + 64 * f + lane] = o[f];
 }
 
 // One thread per key; rows of the group staged in LDS 32 at a time.
@@ -211,7 +226,7 @@ hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k
   a.no2 = reinterpret_cast<float*>(base + G.off_no2);
   a.o32 = reinterpret_cast<float*>(base + G.off_ohi);
   a.sraw = reinterpret_cast<float*>(base + G.off_sraw);
-  dim3 grid(G.P, G.Hkv * G.RG, G.S);
+  dim3 grid(G.P, G.Hkv * G.RG * (ROWS32 / P1F32_ROWS), G.S);
   stage_begin(ST_SCORE_P1, st);
   if (G.d == 64) hipLaunchKernelGGL(score_p1_f32<64>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(score_p1_f32<128>, grid, dim3(256), 0, st, a);
