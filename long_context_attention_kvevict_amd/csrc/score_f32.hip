@@ -128,10 +128,12 @@ __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
   for (int f = 0; f < F; ++f) a.part_o[pr * DD + 64 * f + lane] = o[f];
 }
 
-// One thread per key; rows of the group staged in LDS 32 at a time.
+// One key per lane, 64 keys per workgroup slice (blockIdx.x = chunk x 4
+// slices); the 4 waves take the same keys and every 4th row of the group
+// (rows staged in LDS 32 at a time), and their sums are added in wave order.
 template <int DD>
 __global__ __launch_bounds__(256) void score_p2_f32(F32Args a) {
-  const int c = blockIdx.x;
+  const int c = blockIdx.x >> 2, slice = blockIdx.x & 3;
   const int h = blockIdx.y;
   const int s = blockIdx.z;
   const int base = a.seq_off[s];
@@ -142,17 +144,19 @@ __global__ __launch_bounds__(256) void score_p2_f32(F32Args a) {
   const int g = a.Hq / a.Hkv;
   const int R = g * a.w;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
 
   __shared__ float qs[32 * DD];
   __shared__ float os[32 * DD];
   __shared__ float ls[32];
   __shared__ int ps[32];
+  __shared__ float part[4][64];
 
   const float* kb = a.k + (static_cast<size_t>(h) * a.T + base) * DD;
   const float* vb = a.v + (static_cast<size_t>(h) * a.T + base) * DD;
 
-  for (int t0 = c0; t0 < c1; t0 += 256) {
-    const int key = t0 + tid;
+  for (int t0 = c0 + 64 * slice; t0 < c1; t0 += 256) {
+    const int key = t0 + lane;
     const bool kok = key < c1;
     float kr[DD], vr[DD];
 #pragma unroll
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(256) void score_p2_f32(F32Args a) {
       __syncthreads();
       if (!kok) continue;
       const int rn = min(32, R - r0);
-      for (int r = 0; r < rn; ++r) {
+      for (int r = wave; r < rn; r += 4) {
         if (a.causal && key > ps[r]) continue;
         float dot = 0.f, d2 = 0.f;
 #pragma unroll
@@ -204,7 +208,11 @@ __global__ __launch_bounds__(256) void score_p2_f32(F32Args a) {
         sc = fmaf(d2, 1.f / y2, sc);
       }
     }
-    if (kok) a.sraw[static_cast<size_t>(h) * a.T + base + key] = sc;
+    __syncthreads();   // every wave's rows of these keys done
+    part[wave][lane] = sc;
+    __syncthreads();
+    if (wave == 0 && kok)
+      a.sraw[static_cast<size_t>(h) * a.T + base + key] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
   }
 }
 
@@ -237,7 +245,7 @@ hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k
   e = launch_merge_f32(G, seq_off, ws, st);
   stage_end(ST_SCORE_MERGE, st);
   if (e != hipSuccess) return e;
-  dim3 grid2(G.P, G.Hkv, G.S);
+  dim3 grid2(G.P * 4, G.Hkv, G.S);
   stage_begin(ST_SCORE_P2, st);
   if (G.d == 64) hipLaunchKernelGGL(score_p2_f32<64>, grid2, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(score_p2_f32<128>, grid2, dim3(256), 0, st, a);
