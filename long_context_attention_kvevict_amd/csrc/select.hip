@@ -18,13 +18,18 @@
 // one launch per pass; no launch waits on another workgroup of the same
 // launch.  Selection is a radix select over the order-preserving integer
 // image of the keys (11-bit digits, most significant first): histogram
-// launches count one digit each (integer atomics), the next launch reads the
-// finished histograms and fixes the digits of the B-th largest key, a count
-// launch tallies the keys above / equal to it per chunk, and the write launch
-// places each chunk's kept indices after those of earlier chunks, so the
-// output is ascending.  Cross-chunk sums of the sampling pass (the proposal's
-// normaliser, E(m) and its derivative) are per-chunk partials that the next
-// launch adds up in chunk order: results are bit-reproducible.
+// launches count one digit each (integer atomics) and the next launch reads
+// the finished histograms and fixes the digits of the B-th largest key.  The
+// last digit's launch also leaves, per chunk, the count of keys above the
+// threshold's leading digits and the last digits of those that share them,
+// from which the write launch places each chunk's kept indices after those
+// of earlier chunks, so the output is ascending (under a soft budget a count
+// launch tallies the keys above / equal to the threshold per chunk instead).
+// With a per-head budget the sampling passes carry the digit levels of the
+// Gumbel keys, which do not depend on m.  Cross-chunk sums of the sampling
+// passes (the proposal's normaliser, E(m) and its derivative) are per-chunk
+// partials that the next launch adds up in chunk order: results are
+// bit-reproducible.
 #include "common.h"
 #include "launch.h"
 #include "timing.h"
