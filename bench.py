@@ -288,7 +288,9 @@ def _decode_leg(steps_max, want_cpu):
         b_c.copy_(b0)
         cache_len.copy_(torch.from_numpy(budgets.copy()))
 
-    def loop():
+    def loop_host_append():
+        # the caller appends each step's token (four small torch launches),
+        # then kvevict_decode_snis
         for t in range(steps):
             rows = coff + cache_len
             k_c.index_copy_(1, rows, kd[t])
@@ -297,19 +299,30 @@ def _decode_leg(steps_max, want_cpu):
             cache_len.add_(1)
             b.decode(qd[t], k_c, v_c, b_c, caps, cache_len, max_len, wl.sm_scale, out=out, cap_offsets=cap)
 
-    def run():
+    def loop():
+        # kvevict_decode_snis_append: the decode attends to and stores the
+        # step's token itself (two launches per step)
+        for t in range(steps):
+            b.decode_append(qd[t], kd[t], vd[t], k_c, v_c, b_c, caps, cache_len, max_len, wl.sm_scale, out=out,
+                            cap_offsets=cap)
+
+    def run(fn=loop):
         reset()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
-        loop()
+        fn()
         ev1.record()
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps
 
+    run(loop_host_append)                    # warmup
+    ms_host = run(loop_host_append)
+    out_host = out.clone()
     run()                                    # warmup
     ms = run()
     out_eager = out.clone()
+    append_equal = bool(torch.equal(out_eager, out_host))
     K.timing_enable(["decode_split", "decode_merge"])
     run()
     stages = K.timing_summary()
@@ -345,7 +358,11 @@ def _decode_leg(steps_max, want_cpu):
         "ms_per_step": ms, "tokens_per_s": wl.S / (ms * 1e-3),
         "ms_per_step_graph": float(np.median(graph_ms)), "tokens_per_s_graph": wl.S / (np.median(graph_ms) * 1e-3),
         "graph_output_equals_eager": graph_equal,
-        "launch": f"eager: 3 appends + kvevict_decode_snis per step; graph: the {steps} steps captured as one HIP graph",
+        "ms_per_step_host_append": ms_host, "tokens_per_s_host_append": wl.S / (ms_host * 1e-3),
+        "host_append_output_equal": append_equal,
+        "launch": (f"eager: kvevict_decode_snis_append per step (the token appended by the decode); graph: the "
+                   f"{steps} steps captured as one HIP graph; host_append: 4 torch appends + kvevict_decode_snis "
+                   f"per step"),
         "kernel_ms": {"decode_split": split_ms, "decode_merge": merge_ms},
         "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic("decode_split", wl.name),

@@ -9,7 +9,9 @@
  *   kvevict_compact      gather of the kept K/V rows and their logit bias
  *   kvevict_decode_snis  decode attention over the compacted cache with a
  *                        per-entry logit bias (self-normalised importance
- *                        sampling correction)
+ *                        sampling correction); kvevict_decode_snis_append
+ *                        is the same step with the step's own token
+ *                        appended to the cache on the device
  *
  * Pages cited:
  *   [PI] "A Probabilistic Interpretation of KV Cache Eviction"
@@ -320,6 +322,33 @@ kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k
                                const int32_t* cache_len, int32_t max_cache_len,
                                float sm_scale, float* out, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------- decode_snis_append
+ * One decode step that also appends the step's token ([PI] §5 Algorithm 1:
+ * each new token enters the cache uncorrected, weight 1): for every sequence
+ * s with cache_len[s] < cap_s, the token (k_new[h][s], v_new[h][s], bias 0)
+ * is attended at slot cache_len[s] of every KV head h together with the
+ * cache's first cache_len[s] entries -- the output of kvevict_decode_snis
+ * after the caller's own append, bit for bit -- and is then stored there
+ * (k_c, v_c, bias_c = 0) and cache_len[s] advanced by one, all on the
+ * device, so that a decode loop takes two launches per step and can be
+ * captured in a graph.  A sequence whose cache is full (cache_len[s] >=
+ * cap_s) attends to its cap_s entries only; its token is neither attended
+ * nor stored and its cache_len is left as it is.
+ *   q              [S][Hq][d] dtype
+ *   k_new, v_new   [Hkv][S][d] dtype, the step's token per (KV head, sequence)
+ *   k_c, v_c, bias_c, cap_off  the compacted cache, as for decode_snis (written
+ *                  at the appended slots only)
+ *   cache_len      device [S], 0 <= cache_len[s]; read, then advanced
+ *   max_cache_len  host upper bound of the entries attended, cache_len[s] + 1
+ *                  for a sequence with room (grid sizing)
+ *   ws             at least kvevict_decode_workspace() bytes
+ * Errors as for kvevict_decode_snis.  Outputs must not alias inputs. */
+kve_status kvevict_decode_snis_append(const kve_layout* L, const void* q, const void* k_new,
+                                      const void* v_new, void* k_c, void* v_c, float* bias_c,
+                                      const int32_t* cap_off, const int32_t* cap_off_host,
+                                      int32_t* cache_len, int32_t max_cache_len, float sm_scale,
+                                      float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------- decode_snis_noalloc
  * For callers that cannot allocate device memory (code under HIP graph

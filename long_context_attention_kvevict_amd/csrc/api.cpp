@@ -264,6 +264,27 @@ kve_status kvevict_decode_snis(const kve_layout* L, const void* q, const void* k
   return KVE_OK;
 }
 
+kve_status kvevict_decode_snis_append(const kve_layout* L, const void* q, const void* k_new, const void* v_new,
+                                      void* k_c, void* v_c, float* bias_c, const int32_t* cap_off,
+                                      const int32_t* cap_off_host, int32_t* cache_len, int32_t max_cache_len,
+                                      float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  kve::DecodeGeom G;
+  std::string msg;
+  if (!cap_off_host) return set_err(KVE_EINVAL, "kvevict_decode_snis_append: cap_off_host is NULL");
+  kve_status st = kve::plan_decode(L, cap_off_host, max_cache_len, &G, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_decode_snis_append: " + msg);
+  if (!q || !k_new || !v_new || !k_c || !v_c || !bias_c || !cap_off || !cache_len || !out)
+    return set_err(KVE_EINVAL, "kvevict_decode_snis_append: null tensor pointer");
+  if (!(sm_scale > 0.f)) return set_err(KVE_EINVAL, "kvevict_decode_snis_append: sm_scale must be > 0");
+  if (!ws || ws_bytes < G.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_decode_snis_append: workspace smaller than kvevict_decode_workspace()");
+  const kve::DecodeAppendArgs ap{k_new, v_new, k_c, v_c, bias_c, cache_len};
+  hipError_t e = kve::launch_decode(G, cap_off_host[L->S], q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale,
+                                    out, ws, static_cast<hipStream_t>(stream), &ap);
+  if (e != hipSuccess) return hip_err(e, "kvevict_decode_snis_append");
+  return KVE_OK;
+}
+
 size_t kvevict_decode_scratch_max(void) { return kve::kDecodeScratchBytes; }
 
 kve_status kvevict_decode_snis_noalloc(const kve_layout* L, const void* q, const void* k_c, const void* v_c,

@@ -53,18 +53,55 @@ __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) { return b
 template <>
 __device__ __forceinline__ float ld_elem<float>(const float* p) { return *p; }
 
+// The step's own token, appended by the decode itself (kvevict_decode_snis_append):
+// the split kernels attend to it from k_new / v_new (bias 0) at slot
+// cache_len[s], and the merge kernel, which runs after every split has read
+// the cache, stores it there and advances cache_len[s].  All NULL for the
+// plain decode.
+struct DecAppend {
+  const void* k_new;    // [Hkv][S][d]
+  const void* v_new;
+  void* k_c;            // the cache, written at the appended slot
+  void* v_c;
+  float* bias_c;
+  int32_t* cache_len;   // advanced by one where the token was stored
+  int32_t* app;         // [S][2] workspace: entries attended, appended slot or -1
+};
+
+// Entries the split kernels attend to for sequence s, and the slot of the
+// appended token (-1: none).  Never past the sequence's capacity, whatever
+// cache_len holds; a full cache attends to its entries only.
+__device__ __forceinline__ int dec_len(const int32_t* cache_len, const int32_t* cap_off, int s, bool append,
+                                       int* app) {
+  const int cap = cap_off[s + 1] - cap_off[s];
+  const int c = cache_len[s];
+  if (append && c >= 0 && c < cap) {
+    *app = c;
+    return c + 1;
+  }
+  *app = -1;
+  return min(c, cap);
+}
+
 template <typename T, int DD, int GMAX>
 __global__ __launch_bounds__(256) void decode_split(const T* __restrict__ q, const T* __restrict__ k_c,
                                                     const T* __restrict__ v_c, const float* __restrict__ bias_c,
                                                     const int32_t* __restrict__ cap_off,
                                                     const int32_t* __restrict__ cache_len, int Hq, int Hkv,
                                                     int64_t totalC, int split_len, int splits, float c2,
-                                                    float* __restrict__ part_ml, float* __restrict__ part_o) {
+                                                    float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                    DecAppend ap) {
   constexpr int CPL = DD / 16;   // features per lane
   const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int g = Hq / Hkv;
-  // never read past this sequence's capacity, whatever cache_len holds
-  const int len = min(cache_len[s], cap_off[s + 1] - cap_off[s]);
+  int app;
+  const int len = dec_len(cache_len, cap_off, s, ap.k_new != nullptr, &app);
+  if (ap.k_new && sp == 0 && h == 0 && threadIdx.x == 0) {
+    ap.app[2 * s] = len;
+    ap.app[2 * s + 1] = app;
+  }
+  const T* knew = ap.k_new ? static_cast<const T*>(ap.k_new) + (static_cast<size_t>(h) * gridDim.z + s) * DD : nullptr;
+  const T* vnew = ap.k_new ? static_cast<const T*>(ap.v_new) + (static_cast<size_t>(h) * gridDim.z + s) * DD : nullptr;
   const int e0 = sp * split_len;
   const int e1 = min(e0 + split_len, len);
   const int tid = threadIdx.x;
@@ -92,12 +129,16 @@ __global__ __launch_bounds__(256) void decode_split(const T* __restrict__ q, con
   const size_t rowbase = static_cast<size_t>(h) * totalC + cap_off[s];
   for (int e = e0 + sub; e < e1; e += 16) {
     float kr[CPL], vr[CPL];
+    const bool isnew = e == app;   // the step's token: from k_new / v_new, bias 0
+    const T* kp = isnew ? knew : k_c + (rowbase + e) * DD;
+    const T* vp = isnew ? vnew : v_c + (rowbase + e) * DD;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      kr[c] = ld_elem<T>(k_c + (rowbase + e) * DD + fl * CPL + c);
-      vr[c] = ld_elem<T>(v_c + (rowbase + e) * DD + fl * CPL + c);
+      kr[c] = ld_elem<T>(kp + fl * CPL + c);
+      vr[c] = ld_elem<T>(vp + fl * CPL + c);
     }
-    const float bl2 = bias_c[rowbase + e] * kLog2e;
+    const float bv = bias_c[rowbase + e];   // within the capacity in every case
+    const float bl2 = isnew ? 0.f : bv * kLog2e;
 #pragma unroll
     for (int i = 0; i < GMAX; ++i) {
       if (i < g) {
@@ -196,12 +237,12 @@ __device__ __forceinline__ int dec_swz(int row) {
   return (row & (DD / 16 - 1)) << 1;   // keeps 16-byte chunk pairs together
 }
 
-template <int DD>
+template <int DD, bool APPEND>
 __global__ __launch_bounds__(256, 2) void decode_split_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_c, const uint16_t* __restrict__ v_c,
     const float* __restrict__ bias_c, const int32_t* __restrict__ cap_off,
     const int32_t* __restrict__ cache_len, int Hq, int Hkv, int64_t totalC, int splits, float c2,
-    float* __restrict__ part_ml, float* __restrict__ part_o) {
+    float* __restrict__ part_ml, float* __restrict__ part_o, DecAppend ap) {
   constexpr int KS = DD / 32;             // k-steps of S = K . Q^T
   constexpr int DT = DD / 16;             // 16-feature tiles of O
   constexpr int ROWB = DD * 2;            // bytes per cache row
@@ -212,8 +253,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma(
 
   const int sp = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int g = Hq / Hkv;
-  // never read past this sequence's capacity, whatever cache_len holds
-  const int len = min(cache_len[s], cap_off[s + 1] - cap_off[s]);
+  int app;
+  const int len = dec_len(cache_len, cap_off, s, APPEND, &app);
+  if (APPEND && sp == 0 && h == 0 && threadIdx.x == 0) {
+    ap.app[2 * s] = len;
+    ap.app[2 * s + 1] = app;
+  }
+  const char* knew =
+      APPEND ? static_cast<const char*>(ap.k_new) + (static_cast<size_t>(h) * gridDim.z + s) * (DD * 2) : nullptr;
+  const char* vnew =
+      APPEND ? static_cast<const char*>(ap.v_new) + (static_cast<size_t>(h) * gridDim.z + s) * (DD * 2) : nullptr;
   const int e0 = sp * kDecodeChunkBf16;
   if (e0 >= len) return;                  // uniform over the workgroup
   const int e1 = min(e0 + kDecodeChunkBf16, len);
@@ -247,17 +296,26 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma(
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int er = min(eb + 16 * mb + ln, last);
+        const char* kp = kbase + static_cast<size_t>(er) * ROWB;
+        if constexpr (APPEND) kp = (er == app) ? knew : kp;   // the step's token
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
-          kr[b][mb][j] = *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(er) * ROWB + (4 * j + lq) * 16);
+        for (int j = 0; j < KS; ++j) kr[b][mb][j] = *reinterpret_cast<const u32x4*>(kp + (4 * j + lq) * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bi[b][mb][r] = bbase[min(eb + 16 * mb + 4 * lq + r, last)];
+        for (int r = 0; r < 4; ++r) {
+          const int eb2 = min(eb + 16 * mb + 4 * lq + r, last);
+          // loaded in every case (the slot lies within the capacity), so
+          // that the selection below compiles to a select, not a branch
+          const float bv = bbase[eb2];
+          bi[b][mb][r] = (APPEND && eb2 == app) ? 0.f : bv;
+        }
       }
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int pc = i * 64 + l, ent = pc / CPR, ch = pc % CPR;
         const int er = min(eb + ent, last);
-        vr[b][i] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(er) * ROWB + ch * 16);
+        const char* vp = vbase + static_cast<size_t>(er) * ROWB;
+        if constexpr (APPEND) vp = (er == app) ? vnew : vp;
+        vr[b][i] = *reinterpret_cast<const u32x4*>(vp + ch * 16);
       }
     }
     // keep every load of both blocks ahead of the compute
@@ -378,17 +436,34 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma(
 // owns one feature; the partial outputs of up to PR splits per round are
 // loaded together with the split maxima and sums (staged in LDS), so a
 // round costs one memory round trip.
-template <int DD>
+template <typename T, int DD>
 __global__ __launch_bounds__(DD) void decode_merge(const float* __restrict__ part_ml, const float* __restrict__ part_o,
                                                    const int32_t* __restrict__ cache_len,
-                                                   const int32_t* __restrict__ cap_off, int Hq, int splits,
-                                                   int split_len, float* __restrict__ out) {
+                                                   const int32_t* __restrict__ cap_off, int S, int Hq, int Hkv,
+                                                   int64_t totalC, int splits, int split_len,
+                                                   float* __restrict__ out, DecAppend ap) {
   constexpr int PR = 32;             // splits per round
   __shared__ float sml[PR][2];
   const int r = blockIdx.x;          // s * Hq + qh
   const int s = r / Hq;
   const int d = threadIdx.x;
-  const int len = min(cache_len[s], cap_off[s + 1] - cap_off[s]);
+  int len;
+  if (ap.k_new) {   // the lengths the splits used (cache_len is advanced below)
+    len = ap.app[2 * s];
+    const int app = ap.app[2 * s + 1];
+    const int qh = r % Hq, g = Hq / Hkv;
+    if (app >= 0 && qh % g == 0) {   // one workgroup per (sequence, KV head) stores the token
+      const int h = qh / g;
+      const size_t src = (static_cast<size_t>(h) * S + s) * DD + d;
+      const size_t dst = (static_cast<size_t>(h) * totalC + cap_off[s] + app) * DD + d;
+      static_cast<T*>(ap.k_c)[dst] = static_cast<const T*>(ap.k_new)[src];
+      static_cast<T*>(ap.v_c)[dst] = static_cast<const T*>(ap.v_new)[src];
+      if (d == 0) ap.bias_c[static_cast<size_t>(h) * totalC + cap_off[s] + app] = 0.f;
+      if (qh == 0 && d == 0) ap.cache_len[s] = app + 1;
+    }
+  } else {
+    len = min(cache_len[s], cap_off[s + 1] - cap_off[s]);
+  }
   const int ns = max(0, min(splits, (len + split_len - 1) / split_len));
   const float* ml = part_ml + static_cast<size_t>(r) * splits * 2;
   const float* po = part_o + static_cast<size_t>(r) * splits * DD;
@@ -427,39 +502,45 @@ template <typename T, int DD>
 static hipError_t launch_decode_t(const DecodeGeom& G, int64_t totalC, const void* q, const void* k_c,
                                   const void* v_c, const float* bias_c, const int32_t* cap_off,
                                   const int32_t* cache_len, float sm_scale, float* out, void* ws,
-                                  hipStream_t st) {
+                                  hipStream_t st, DecAppend ap) {
   char* base = static_cast<char*>(ws);
   float* pml = reinterpret_cast<float*>(base + G.off_ml);
   float* po = reinterpret_cast<float*>(base + G.off_o);
+  if (ap.k_new) ap.app = reinterpret_cast<int32_t*>(base + G.off_app);
   dim3 grid(G.splits, G.Hkv, G.S);
   const int g = G.Hq / G.Hkv;
   const float c2 = sm_scale * kLog2e;
   stage_begin(ST_DECODE_SPLIT, st);
   if constexpr (std::is_same<T, uint16_t>::value) {
     (void)g;
-    hipLaunchKernelGGL((decode_split_mfma<DD>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k_c), static_cast<const uint16_t*>(v_c), bias_c, cap_off,
-                       cache_len, G.Hq, G.Hkv, totalC, G.splits, c2, pml, po);
+    if (ap.k_new)
+      hipLaunchKernelGGL((decode_split_mfma<DD, true>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(q),
+                         static_cast<const uint16_t*>(k_c), static_cast<const uint16_t*>(v_c), bias_c, cap_off,
+                         cache_len, G.Hq, G.Hkv, totalC, G.splits, c2, pml, po, ap);
+    else
+      hipLaunchKernelGGL((decode_split_mfma<DD, false>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(q),
+                         static_cast<const uint16_t*>(k_c), static_cast<const uint16_t*>(v_c), bias_c, cap_off,
+                         cache_len, G.Hq, G.Hkv, totalC, G.splits, c2, pml, po, ap);
   } else {
   if (g <= 4)
     hipLaunchKernelGGL((decode_split<T, DD, 4>), grid, dim3(256), 0, st, static_cast<const T*>(q),
                        static_cast<const T*>(k_c), static_cast<const T*>(v_c), bias_c, cap_off, cache_len,
-                       G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po);
+                       G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po, ap);
   else if (g <= 8)
     hipLaunchKernelGGL((decode_split<T, DD, 8>), grid, dim3(256), 0, st, static_cast<const T*>(q),
                        static_cast<const T*>(k_c), static_cast<const T*>(v_c), bias_c, cap_off, cache_len,
-                       G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po);
+                       G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po, ap);
   else
     hipLaunchKernelGGL((decode_split<T, DD, 16>), grid, dim3(256), 0, st, static_cast<const T*>(q),
                        static_cast<const T*>(k_c), static_cast<const T*>(v_c), bias_c, cap_off, cache_len,
-                       G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po);
+                       G.Hq, G.Hkv, totalC, G.split_len, G.splits, c2, pml, po, ap);
   }
   stage_end(ST_DECODE_SPLIT, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_DECODE_MERGE, st);
-  hipLaunchKernelGGL((decode_merge<DD>), dim3(G.S * G.Hq), dim3(DD), 0, st, pml, po, cache_len, cap_off,
-                     G.Hq, G.splits, G.split_len, out);
+  hipLaunchKernelGGL((decode_merge<T, DD>), dim3(G.S * G.Hq), dim3(DD), 0, st, pml, po, cache_len, cap_off, G.S,
+                     G.Hq, G.Hkv, totalC, G.splits, G.split_len, out, ap);
   stage_end(ST_DECODE_MERGE, st);
   return hipGetLastError();
 }
@@ -467,15 +548,26 @@ static hipError_t launch_decode_t(const DecodeGeom& G, int64_t totalC, const voi
 hipError_t launch_decode(const DecodeGeom& G, int64_t totalC, const void* q, const void* k_c,
                          const void* v_c, const float* bias_c, const int32_t* cap_off,
                          const int32_t* cache_len, float sm_scale, float* out, void* ws,
-                         hipStream_t st) {
+                         hipStream_t st, const DecodeAppendArgs* append) {
+  DecAppend ap{};
+  if (append) {
+    ap.k_new = append->k_new;
+    ap.v_new = append->v_new;
+    ap.k_c = append->k_c;
+    ap.v_c = append->v_c;
+    ap.bias_c = append->bias_c;
+    ap.cache_len = append->cache_len;
+  }
   if (G.dtype == KVE_BF16) {
     if (G.d == 64)
-      return launch_decode_t<uint16_t, 64>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st);
-    return launch_decode_t<uint16_t, 128>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st);
+      return launch_decode_t<uint16_t, 64>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st,
+                                           ap);
+    return launch_decode_t<uint16_t, 128>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st,
+                                          ap);
   }
   if (G.d == 64)
-    return launch_decode_t<float, 64>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st);
-  return launch_decode_t<float, 128>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st);
+    return launch_decode_t<float, 64>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st, ap);
+  return launch_decode_t<float, 128>(G, totalC, q, k_c, v_c, bias_c, cap_off, cache_len, sm_scale, out, ws, st, ap);
 }
 
 }  // namespace kve

@@ -49,9 +49,18 @@ hipError_t launch_compact(int S, int Hkv, int d, int esize, int T, int64_t total
 // Device address of the decode scratch array on the current device.
 hipError_t decode_scratch(void** ptr);
 
+// The decode that appends the step's token itself (NULL: the plain decode).
+struct DecodeAppendArgs {
+  const void* k_new;   // [Hkv][S][d]
+  const void* v_new;
+  void* k_c;
+  void* v_c;
+  float* bias_c;
+  int32_t* cache_len;
+};
 hipError_t launch_decode(const DecodeGeom& G, int64_t totalC, const void* q, const void* k_c,
                          const void* v_c, const float* bias_c, const int32_t* cap_off,
                          const int32_t* cache_len, float sm_scale, float* out, void* ws,
-                         hipStream_t st);
+                         hipStream_t st, const DecodeAppendArgs* append = nullptr);
 
 }  // namespace kve

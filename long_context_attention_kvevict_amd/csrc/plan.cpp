@@ -253,6 +253,7 @@ kve_status plan_decode(const kve_layout* L, const int32_t* cap_off_host, int max
   size_t off = 0;
   g.off_ml = off; off = align256(off + rows * 2 * sizeof(float));
   g.off_o = off;  off = align256(off + rows * static_cast<size_t>(g.d) * sizeof(float));
+  g.off_app = off; off = align256(off + static_cast<size_t>(g.S) * 2 * sizeof(int32_t));
   g.bytes = off;
   *G = g;
   return KVE_OK;

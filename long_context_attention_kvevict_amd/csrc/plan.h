@@ -108,6 +108,7 @@ constexpr size_t kDecodeScratchBytes = static_cast<size_t>(8) << 20;
 struct DecodeGeom {
   int S, Hq, Hkv, d, dtype, splits, split_len;
   size_t off_ml, off_o;
+  size_t off_app;                  // int [S][2]: entries attended and the appended slot (or -1), per sequence
   size_t bytes;
 };
 

@@ -25,7 +25,7 @@ EXPORTS = [
     "kvevict_select_ex", "kvevict_select_soft", "kvevict_select_literal_workspace", "kvevict_select_literal",
     "kvevict_merge_workspace", "kvevict_merge",
     "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_decode_scratch_max",
-    "kvevict_decode_snis_noalloc", "kvevict_last_error",
+    "kvevict_decode_snis_noalloc", "kvevict_decode_snis_append", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
 
@@ -94,6 +94,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_decode_scratch_max.restype = SZ
     lib.kvevict_decode_snis_noalloc.argtypes = [LP, P, P, P, P, P, P, P, I32, F32, P, P]
     lib.kvevict_decode_snis_noalloc.restype = I32
+    lib.kvevict_decode_snis_append.argtypes = [LP, P, P, P, P, P, P, P, P, P, I32, F32, P, P, SZ, P]
+    lib.kvevict_decode_snis_append.restype = I32
     lib.kvevict_last_error.argtypes = []
     lib.kvevict_last_error.restype = ctypes.c_char_p
     lib.kvevict_version.argtypes = []
@@ -341,6 +343,27 @@ class Batch:
                                              cap_host.data_ptr(), _ptr(cache_len), int(max_cache_len),
                                              float(sm_scale), _ptr(out), _ptr(ws), ws.numel(),
                                              _stream(stream)))
+        self._dec = (cap_host, cap_dev)
+        return out
+
+    def decode_append(self, q, k_new, v_new, k_c, v_c, bias_c, caps, cache_len, max_cache_len: int,
+                      sm_scale: float, out=None, stream=None, cap_offsets=None):
+        """kvevict_decode_snis_append: one decode step that attends to and
+        stores the step's token (k_new, v_new [Hkv][S][d]) at slot
+        cache_len[s] and advances cache_len (int32 device [S]) on the device.
+        Returns out [S][Hq][d] fp32."""
+        if cap_offsets is None:
+            cap_offsets = self.offsets(caps, self.device)
+        cap_host, cap_dev = cap_offsets
+        lay = ctypes.byref(self.layout)
+        nbytes = self._lib.kvevict_decode_workspace(lay, int(max_cache_len)) or 256
+        ws = self._workspace("decode", nbytes)
+        if out is None:
+            out = torch.empty((self.S, self.Hq, self.d), dtype=torch.float32, device=self.device)
+        _check(self._lib.kvevict_decode_snis_append(lay, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_c), _ptr(v_c),
+                                                    _ptr(bias_c), _ptr(cap_dev), cap_host.data_ptr(),
+                                                    _ptr(cache_len), int(max_cache_len), float(sm_scale), _ptr(out),
+                                                    _ptr(ws), ws.numel(), _stream(stream)))
         self._dec = (cap_host, cap_dev)
         return out
 

@@ -140,6 +140,16 @@ def test_compact_and_decode_reject_bad_arguments():
     r = lib.kvevict_decode_snis(ctypes.byref(lay), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, cap.data_ptr(), DUMMY,
                                 12, 0.1, DUMMY, DUMMY, 16, None)
     assert r == K.KVE_EWORKSPACE
+    # the appending decode validates the same way, and needs its new-token rows
+    r = lib.kvevict_decode_snis_append(ctypes.byref(lay), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                       cap.data_ptr(), DUMMY, 13, 0.1, DUMMY, DUMMY, 1 << 40, None)
+    assert r == K.KVE_EINVAL                            # max_cache_len > capacity
+    r = lib.kvevict_decode_snis_append(ctypes.byref(lay), DUMMY, None, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                       cap.data_ptr(), DUMMY, 12, 0.1, DUMMY, DUMMY, 1 << 40, None)
+    assert r == K.KVE_EINVAL                            # no k_new
+    r = lib.kvevict_decode_snis_append(ctypes.byref(lay), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                       cap.data_ptr(), DUMMY, 12, 0.1, DUMMY, DUMMY, 16, None)
+    assert r == K.KVE_EWORKSPACE
 
 
 def test_workspace_scales_with_shape():
