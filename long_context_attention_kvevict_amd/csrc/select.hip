@@ -1631,6 +1631,93 @@ static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bi
   hipLaunchKernelGGL((sel_write<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, cnt, rs, idx, bias);
 }
 
+// Top-k when every sequence fits one selection chunk (at most SEL_CHUNK
+// keys): one workgroup per (sequence, head) resolves the three digit levels
+// in LDS and writes the ordered output itself, in one launch (the same
+// selection as the multi-workgroup path: the B largest keys, ties to the
+// lower index, NaN below every number).  Also writes m = 0 and status OK.
+__global__ __launch_bounds__(SEL_THREADS) void sel_topk_one(const float* __restrict__ scores, SelArgs a,
+                                                            int32_t* __restrict__ idx, float* __restrict__ bias,
+                                                            double* m_out, int32_t* status_out) {
+  typedef uint32_t K;
+  const int h = blockIdx.y, s = blockIdx.z;
+  const int sh = s * a.Hkv + h;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int B = a.bud_off[s + 1] - a.bud_off[s];
+  if (threadIdx.x == 0) {
+    if (m_out) m_out[sh] = 0.0;
+    if (status_out) status_out[sh] = KVE_OK;
+  }
+  int32_t* out = idx + h * a.totalB + a.out_off[s];
+  float* bout = bias + h * a.totalB + a.out_off[s];
+  if (B <= 0) return;
+  if (B >= n) {   // everything kept, weight 0
+    for (int j = threadIdx.x; j < n; j += SEL_THREADS) {
+      out[j] = j;
+      bout[j] = 0.f;
+    }
+    return;
+  }
+  __shared__ int lh[SEL_BINS];
+  __shared__ int lds[8];
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  // thread t holds keys 4t .. 4t+3 (the ordered write's layout)
+  const int jt = SEL_PER * threadIdx.x;
+  K u[SEL_PER];
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) u[i] = (jt + i < n) ? f32_order_key(scores[row + jt + i]) : K(0);
+  K prefix = 0, mask = 0;
+  int need = B;
+#pragma unroll 1
+  for (int lv = 0; lv < Radix<K>::LEVELS; ++lv) {
+    for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+    __syncthreads();
+    const int sft = Radix<K>::shift(lv);
+    const K dm = Radix<K>::wmask(lv);
+#pragma unroll
+    for (int i = 0; i < SEL_PER; ++i)
+      if (jt + i < n && (u[i] & mask) == prefix) atomicAdd(&lh[static_cast<int>((u[i] >> sft) & dm)], 1);
+    __syncthreads();
+    int c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = lh[SEL_BINS - 1 - 8 * threadIdx.x - i];
+    int dg, ab;
+    pick_bin(c, need, lds, &dg, &ab);   // its barriers also end this level's reads of lh
+    prefix |= static_cast<K>(dg) << sft;
+    mask |= dm << sft;
+    need -= ab;
+  }
+  const K thr = prefix;   // the B-th largest key; `need` of the keys equal to it are kept
+  int neq = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) neq += (jt + i < n) && (u[i] == thr);
+  int tot;
+  int eq_rank = block_incl_scan256(neq, lds, &tot) - neq;
+  int ntake = 0;
+  uint32_t take_bits = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const bool in = jt + i < n;
+    const bool eq = in && u[i] == thr;
+    const bool take = (in && u[i] > thr) || (eq && eq_rank < need);
+    eq_rank += eq;
+    take_bits |= static_cast<uint32_t>(take) << i;
+    ntake += take;
+  }
+  int pos = block_incl_scan256(ntake, lds, &tot) - ntake;
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    if ((take_bits >> i) & 1u) {
+      if (pos < B) {
+        out[pos] = jt + i;
+        bout[pos] = 0.f;
+      }
+      ++pos;
+    }
+  }
+}
+
 // Clears the histograms and, in top-k mode, writes m = 0 and status OK.
 __global__ __launch_bounds__(256) void sel_init(int* __restrict__ p, int n, double* m_out, int32_t* status_out,
                                                 int SH) {
@@ -1672,6 +1759,12 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   // pass also writes the Gumbel keys and clears the histograms
   const bool chain = !topk && !soft && mix >= 1.0f;
   stage_begin(ST_SELECT, st);
+  if (topk && !soft && G.max_len <= SEL_CHUNK) {   // every head in one workgroup
+    hipLaunchKernelGGL(sel_topk_one, dim3(1, G.Hkv, G.S), dim3(SEL_THREADS), 0, st, scores, a, idx, bias, m_out,
+                       status_out);
+    stage_end(ST_SELECT, st);
+    return hipGetLastError();
+  }
   if (!chain)
     hipLaunchKernelGGL(sel_init, dim3((max(nzero, SH) + 255) / 256), dim3(256), 0, st, hist, nzero,
                        topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);

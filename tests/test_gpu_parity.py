@@ -454,6 +454,26 @@ def test_select_ties_nan_and_budget_edges(mode):
     _select_check(r, sc, mode, 0.5, 2.0, 12345)
 
 
+def test_select_topk_single_chunk_heads():
+    # every sequence within one 1024-key selection chunk: top-k takes the
+    # one-launch path (one workgroup per head); ties, NaN, plateaus and
+    # B in {0, n} as above
+    lens = [1, 5, 257, 1000, 1024]
+    wl = dataclasses.replace(workloads.tiny_fp32(), name="sel_one", S=5, Hq=3, Hkv=3, lens=lens, budget_frac=0.0)
+    sc = synth.random_scores(3, lens, seed=78, ties=True)
+    sc[0, 300] = np.nan
+    sc[1, 1300:1310] = np.nan
+    sc[2, 1500:1900] = sc[2, 1500]            # plateau of equal values across the threshold
+    sc[1, 2000:2100] = -np.inf
+    budgets = [1, 5, 0, 777, 1023]
+    r = type("R", (), {})()
+    r.wl = wl
+    r.b = K.Batch(lens, 3, 3, 64, 1, "f32")
+    wl.budgets = lambda: np.array(budgets, dtype=np.int32)
+    wl.bud_off = lambda: np.concatenate([[0], np.cumsum(budgets)]).astype(np.int32)
+    _select_check(r, sc, K.KVE_TOPK, 1.0, 1.0, 0)
+
+
 def test_select_sample_search_runs_out_of_newton_steps():
     # Uniform proposals with budgets of 99-99.9 % of n: the expected-distinct
     # curve E(m) is flattest there, and a safeguarded Newton iteration from
