@@ -72,6 +72,15 @@ __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
   for (int f = 0; f < F; ++f) o[f] = 0.f;
   for (int t0 = c0; t0 < c1; t0 += 64) {
     const int key = t0 + lane;
+    // the step's 64 value rows are loaded with its keys (they do not depend
+    // on the weights); rows past the chunk read its last row, with p = 0
+    float vv[64][F];
+#pragma unroll
+    for (int jj = 0; jj < 64; ++jj) {
+      const float* vr = vb + static_cast<size_t>(min(t0 + jj, c1 - 1)) * DD;
+#pragma unroll
+      for (int f = 0; f < F; ++f) vv[jj][f] = vr[64 * f + lane];
+    }
     float x = -INFINITY;
     if (key < c1 && !(a.causal && key > pos)) {
       const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<size_t>(key) * DD);
@@ -95,23 +104,12 @@ __global__ __launch_bounds__(256) void score_p1_f32(F32Args a) {
 #pragma unroll
     for (int f = 0; f < F; ++f) o[f] *= scale;
     m_run = m_new;
-    // 16 value rows' loads in flight at a time; keys past the chunk (or
-    // hidden) have p = 0 and read the chunk's last row instead
-    const int kn = min(64, c1 - t0);
-    for (int j0 = 0; j0 < kn; j0 += 16) {
-      float vv[16][F];
+    // keys past the chunk (or hidden) have p = 0
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float* vr = vb + static_cast<size_t>(min(t0 + j0 + jj, c1 - 1)) * DD;
+    for (int jj = 0; jj < 64; ++jj) {
+      const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), jj));
 #pragma unroll
-        for (int f = 0; f < F; ++f) vv[jj][f] = vr[64 * f + lane];
-      }
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j0 + jj));
-#pragma unroll
-        for (int f = 0; f < F; ++f) o[f] = fmaf(pj, vv[jj][f], o[f]);
-      }
+      for (int f = 0; f < F; ++f) o[f] = fmaf(pj, vv[jj][f], o[f]);
     }
   }
   const float lt = wave_sum(l_run);
