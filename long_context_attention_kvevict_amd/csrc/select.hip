@@ -1248,6 +1248,10 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide(SmpArgs A, int steps, 
 // 0, at least n, or past the end) is outside the histograms too.
 template <int LV, bool FIRST>
 __global__ __launch_bounds__(SEL_THREADS) void smp_search_hist(SmpArgs A, int step, int* __restrict__ hist) {
+  // per-head budgets only (never the soft budget's shared m); step 0 is
+  // the FIRST launch's, so each instance compiles only its own state update
+  __builtin_assume(A.global == 0);
+  __builtin_assume(FIRST ? step == 0 : step > 0);
   __shared__ int lds[8];
   SearchIn in;
   if (!search_load_wg(A, step, &in)) return;
@@ -1265,6 +1269,8 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search_hist(SmpArgs A, int st
 }
 template <int LV>
 __global__ __launch_bounds__(SEL_THREADS) void smp_finish_hist(SmpArgs A, int steps, int* __restrict__ hist) {
+  __builtin_assume(A.global == 0);
+  __builtin_assume(steps > 0);
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
   SearchIn in;
@@ -1275,6 +1281,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_finish_hist(SmpArgs A, int st
 template <int LV>
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide_hist(SmpArgs A, int steps, double* m_out,
                                                                int32_t* status_out, int* __restrict__ hist) {
+  __builtin_assume(A.global == 0);
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
   if (blockIdx.x == 0) smp_decide_body(A, steps, m_out, status_out, blockIdx.y, blockIdx.z);
@@ -1293,6 +1300,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_grid_hist(SmpArgs A, int* __r
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide_last(SmpArgs A, int steps, double* m_out,
                                                                int32_t* status_out, int* __restrict__ hist,
                                                                int* __restrict__ cand, int* __restrict__ cnt) {
+  __builtin_assume(A.global == 0);
   __shared__ int lh[SEL_BINS];
   __shared__ int lds[8];
   if (blockIdx.x == 0) smp_decide_body(A, steps, m_out, status_out, blockIdx.y, blockIdx.z);
