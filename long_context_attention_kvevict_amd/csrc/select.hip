@@ -655,21 +655,27 @@ __device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, 
   *hi = __umul64hi(a, b);
 }
 
-// Philox-4x64 with 10 rounds (Salmon et al., SC'11); returns output word 0.
-__device__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
-                                     uint64_t k1) {
+// Philox-4x64 with 10 rounds (Salmon et al., SC'11): the block of counter
+// c[0..3] under key (k0, k1), in place (c[i] becomes output word i).
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += W0; k1 += W1; }
     uint64_t hi0, lo0, hi1, lo1;
-    mulhilo64(M0, c0, &hi0, &lo0);
-    mulhilo64(M1, c2, &hi1, &lo1);
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    mulhilo64(M0, c[0], &hi0, &lo0);
+    mulhilo64(M1, c[2], &hi1, &lo1);
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
   }
-  return c0;
+}
+// Output word 0 of the block of counter (c0, c1, c2, c3).
+__device__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                     uint64_t k1) {
+  uint64_t c[4] = {c0, c1, c2, c3};
+  philox4x64_10(c, k0, k1);
+  return c[0];
 }
 
 constexpr double kAlphaMax = 1e12;   // upper end of the search range for m
@@ -760,14 +766,28 @@ __device__ __forceinline__ bool smp_active(const SmpArgs& A, int s, int ch, int*
 __device__ __forceinline__ double smp_logpt(const SmpArgs& A, size_t i) {
   return log(static_cast<double>(fmaxf(A.scores[i], 1.17549435e-38f))) * A.inv_tau;
 }
-// Gumbel key of key j of (sequence s, head h) with log-proposal x:
-// x - log(-log u_j), u_j = ((w >> 11) + 0.5) 2^-53 with w the Philox word 0
-// of counter (j, h, s, 0).
-__device__ __forceinline__ double smp_gumbel(const SmpArgs& A, double x, int j, int h, int s) {
-  const uint64_t w = philox4x64_10_w0(static_cast<uint64_t>(j), static_cast<uint64_t>(h), static_cast<uint64_t>(s),
-                                      0ull, A.seed, 0ull);
+// Gumbel key with log-proposal x from Philox word w:
+// x - log(-log u), u = ((w >> 11) + 0.5) 2^-53.  Key j of (sequence s,
+// head h) takes word j mod 4 of the block of counter (j / 4, h, s, 0), so
+// one block serves four consecutive keys.
+__device__ __forceinline__ double gumbel_of(double x, uint64_t w) {
   const double uu = (static_cast<double>(w >> 11) + 0.5) * 0x1.0p-53;
   return x - log(-log(uu));
+}
+__device__ __forceinline__ void smp_block(const SmpArgs& A, int j4, int h, int s, uint64_t c[4]) {
+  c[0] = static_cast<uint64_t>(j4);
+  c[1] = static_cast<uint64_t>(h);
+  c[2] = static_cast<uint64_t>(s);
+  c[3] = 0ull;
+  philox4x64_10(c, A.seed, 0ull);
+}
+// One key on its own (a whole block for one of its words).
+__device__ __forceinline__ double smp_gumbel(const SmpArgs& A, double x, int j, int h, int s) {
+  uint64_t c[4];
+  smp_block(A, j >> 2, h, s, c);
+  const int r = j & 3;
+  const uint64_t w = r == 0 ? c[0] : r == 1 ? c[1] : r == 2 ? c[2] : c[3];
+  return gumbel_of(x, w);
 }
 
 // Pass A: log pi~ = log(max(s, 2^-126)) / tau, its per-chunk maximum and
@@ -791,19 +811,34 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A, int* __restri
   __shared__ double dl[4];
   double x[SMP_PER];
   double mx = -INFINITY;
+  if constexpr (KEYS) {
+    // four consecutive keys per thread: one Philox block gives their words;
+    // log pi~ waits in the log1p(-pi) plane for the next pass
+    static_assert(SMP_PER == 4, "one Philox block per thread");
+    const int j0 = ch * SMP_CHUNK + SMP_PER * threadIdx.x;
+    uint64_t c[4] = {0ull, 0ull, 0ull, 0ull};
+    if (j0 < n) smp_block(A, j0 >> 2, h, s, c);
 #pragma unroll
-  for (int i = 0; i < SMP_PER; ++i) {
-    const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
-    x[i] = -INFINITY;
-    if (j < n) {
-      x[i] = smp_logpt(A, row + j);
-      if (KEYS) {   // log pi~ waits in the log1p(-pi) plane for the next pass
-        A.lp[row + j] = smp_gumbel(A, x[i], j, h, s);
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int j = j0 + i;
+      x[i] = -INFINITY;
+      if (j < n) {
+        x[i] = smp_logpt(A, row + j);
+        A.lp[row + j] = gumbel_of(x[i], c[i]);
         A.L[row + j] = x[i];
-      } else {
-        A.lp[row + j] = x[i];
+        mx = fmax(mx, x[i]);
       }
-      mx = fmax(mx, x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
+      x[i] = -INFINITY;
+      if (j < n) {
+        x[i] = smp_logpt(A, row + j);
+        A.lp[row + j] = x[i];
+        mx = fmax(mx, x[i]);
+      }
     }
   }
   mx = block_max_d(mx, dl);

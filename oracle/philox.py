@@ -9,8 +9,11 @@ multiplies words 0 and 2 by two odd 64-bit constants, swaps and XORs the
 high halves with the other words and a Weyl-sequence key, and the key is
 bumped by two further constants between rounds.
 
-Counter = (j, h, s, 0), key = (seed, 0).  u = ((x0 >> 11) + 0.5) * 2^-53 is
-strictly inside (0, 1), where x0 is output word 0.
+Token j of (sequence s, KV head h) takes output word j mod 4 of the block
+with counter (floor(j / 4), h, s, 0) and key (seed, 0): the tokens of one
+head read the generator's output stream in order, four words per block.
+u = ((x >> 11) + 0.5) * 2^-53 is strictly inside (0, 1), where x is that
+word.
 
 Pinned against numpy.random.Philox (numpy's independent library
 implementation of the same generator) and by a chi-square uniformity test.
@@ -62,11 +65,13 @@ def philox4x64_10(c0, c1, c2, c3, k0, k1):
 
 
 def uniform53(seed: int, s: int, h: int, j: np.ndarray) -> np.ndarray:
-    """u_j in (0, 1) for tokens j of (sequence s, KV head h)."""
+    """u_j in (0, 1) for tokens j of (sequence s, KV head h): word j mod 4 of
+    the block of counter (floor(j / 4), h, s, 0)."""
     j = np.asarray(j, dtype=np.uint64)
-    x0, _, _, _ = philox4x64_10(j, np.uint64(h), np.uint64(s), np.uint64(0),
-                                np.uint64(seed), np.uint64(0))
-    return ((x0 >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+    words = philox4x64_10(j >> np.uint64(2), np.uint64(h), np.uint64(s), np.uint64(0),
+                          np.uint64(seed), np.uint64(0))
+    x = np.choose((j & np.uint64(3)).astype(np.intp), words)
+    return ((x >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
 
 
 def uniform53_draws(seed: int, s: int, h: int, k: np.ndarray) -> np.ndarray:

@@ -124,6 +124,24 @@ def test_philox_matches_numpy_library():
     assert [int(vec[0]), int(vec[1]), int(vec[999])] == one
 
 
+def test_uniform53_reads_the_philox_stream_in_order():
+    # Token j takes word j mod 4 of counter block floor(j / 4): a head's
+    # tokens read numpy's Philox output stream word after word.  numpy starts
+    # at the block after its counter, so counter (0, h, s, 0) streams the
+    # words of tokens 4, 5, 6, ...
+    for seed, s, h in ((7, 0, 0), (2005, 3, 5), (2 ** 40 + 1, 7, 1)):
+        K = 300
+        raw = np.random.Philox(counter=[0, h, s, 0], key=[seed, 0]).random_raw(4 * K)
+        ref = ((raw >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+        mine = uniform53(seed, s, h, np.arange(4, 4 * K + 4))
+        assert np.array_equal(mine, ref)
+        # the first block, word by word, from the block function
+        words = philox4x64_10(np.uint64(0), np.uint64(h), np.uint64(s), np.uint64(0),
+                              np.uint64(seed), np.uint64(0))
+        first = [((int(w) >> 11) + 0.5) * 2.0 ** -53 for w in words]
+        assert list(uniform53(seed, s, h, np.arange(4))) == first
+
+
 def test_uniform_chi_square():
     u = uniform53(12345, 0, 0, np.arange(1 << 20))
     assert u.min() > 0 and u.max() < 1
