@@ -99,6 +99,28 @@ def test_score_window_equals_length():
     check_scores(got, ref, "w=n")
 
 
+@pytest.mark.parametrize("Hq,Hkv,w,lens", [
+    (8, 2, 1, [1, 300, 2049]),    # one window row per q-head; a one-token sequence
+    (16, 2, 64, [64, 1500]),      # 512 rows per KV head (four full row groups); n = w
+    (2, 2, 64, [3000]),           # one q-head per KV head: 64 rows, half a row group
+])
+def test_score_bf16_window_and_group_extremes(Hq, Hkv, w, lens):
+    wl = dataclasses.replace(workloads.llama8b_32k(), name=f"bf16_g{Hq // Hkv}_w{w}", S=len(lens), Hq=Hq,
+                             Hkv=Hkv, w=w, lens=lens, sinks=2, needles=2, data_seed=77 + w)
+    r = Run(wl)
+    say(f"[gpu] score extremes Hq={Hq} Hkv={Hkv} w={w} lens={lens}")
+    got = r.score().cpu().numpy()
+    ref = _oracle_scores(r)
+    off = wl.seq_off()
+    for h in range(Hkv):
+        for s in range(wl.S):
+            a, b = off[s], off[s + 1]
+            if ref[h, a:b].max() == 0.0:   # every visible key holds all of some row's weight
+                assert np.array_equal(got[h, a:b], ref[h, a:b]), f"h{h} s{s}"
+            else:
+                check_scores(got[h, a:b], ref[h, a:b], f"extremes h{h} s{s}")
+
+
 def _plant_dominant(wl, alphas, shared_head=None, shared_alpha=0.99):
     """Inputs where one key holds a planted share a of a window row's weight
     ("DropKV" page, §3.2: the term a / (1 - a) ||o - v_j|| is steepest as a
