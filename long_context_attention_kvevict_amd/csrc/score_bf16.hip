@@ -126,8 +126,14 @@ __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :
 // block per wave).  Issued from inline assembly so that the compiler's own
 // wait insertion, which cannot tell the ring stages apart, does not drain
 // the whole pipeline before every LDS read; the kernels wait explicitly.
+// NT: non-temporal (streaming) cache policy, for tiles no other workgroup
+// reads.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "s"(lds_base) : "memory");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" :: "v"(gptr), "s"(lds_base) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "s"(lds_base) : "memory");
 }
 
 // Makes the register operand `x` ready here: the compiler places its wait for
@@ -178,6 +184,7 @@ struct RingFill {
   }
   // Keys kt0 .. kt0+63 into stage `stage`; rows past the chunk end c1 repeat
   // its last key (callers mask them).
+  template <bool NT = false>
   __device__ __forceinline__ void issue(const char* kb, const char* vb, int kt0, int c1, int stage) const {
     const size_t tbase = static_cast<size_t>(kt0) * ROWB;
     const uint32_t sb = static_cast<uint32_t>(stage) * STAGE_BYTES;
@@ -185,8 +192,8 @@ struct RingFill {
     for (int i = 0; i < NB; ++i) {
       int off = goff[i];
       if (kt0 + KT > c1 && kt0 + key[i] >= c1) off += (c1 - 1 - kt0 - key[i]) * ROWB;
-      dma16(kb + tbase + off, lds[i] + sb);
-      dma16(vb + tbase + off, lds[i] + sb + TILE_BYTES);
+      dma16<NT>(kb + tbase + off, lds[i] + sb);
+      dma16<NT>(vb + tbase + off, lds[i] + sb + TILE_BYTES);
     }
   }
   // K rows only, into stages of TILE_BYTES (the attention-weight scores).
@@ -720,6 +727,9 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
 // residual plane o - o_h, restoring an fp32-accurate distance.
 constexpr float kResidX = -6.f;   // log2 p above this <=> p > 2^-6
 
+// NT: streaming loads of the tiles (one row group per chunk, so no other
+// workgroup reads them).
+template <bool NT>
 __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   ScoreWork wk;
   if (!score_work(a, blockIdx.x, &wk)) return;
@@ -825,7 +835,7 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
   // Tiles are taken from the chunk's end back to its start: pass 1 streamed
   // each chunk front to back, so the tiles it read last are the likeliest to
   // still be in the Infinity Cache.  The ring stage follows the step count.
-  if (ntile > 0) fill.issue(kb8, vb8, c0 + (ntile - 1) * KT, c1, 0);
+  if (ntile > 0) fill.template issue<NT>(kb8, vb8, c0 + (ntile - 1) * KT, c1, 0);
 
   // One tile; EDGE tiles mask keys past the chunk end or a row's causal
   // horizon, interior tiles carry no masking code.
@@ -953,7 +963,7 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
       wait_vm<0>();
       lds_barrier();
       if (i > 0) reduce_tile(t + 1, (i - 1) & 1);
-      if (i + 1 < ntile) fill.issue(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
+      if (i + 1 < ntile) fill.template issue<NT>(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
       const bool edge = c0 + t * KT > edge_from || ((dtiles >> t) & 1u);
       if (wave_big) {
         if (edge) tile(t, i & 1, std::true_type{}, std::true_type{});
@@ -969,7 +979,7 @@ __global__ __launch_bounds__(WG, 2) void score_p2_bf16(ScoreArgs a) {
       wait_vm<0>();
       lds_barrier();
       if (i > 0) reduce_tile(t + 1, (i - 1) & 1);
-      if (i + 1 < ntile) fill.issue(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
+      if (i + 1 < ntile) fill.template issue<NT>(kb8, vb8, c0 + (t - 1) * KT, c1, (i + 1) & 1);
     }
   }
   lds_barrier();
@@ -1177,9 +1187,10 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_SCORE_P2, st);
-  if (score_kind == KVE_SCORE_PERTURB)
-    hipLaunchKernelGGL(score_p2_bf16, grid, dim3(WG), 0, st, a);
-  else if (score_kind == KVE_SCORE_MIN || score_kind == KVE_SCORE_MIN_H)
+  if (score_kind == KVE_SCORE_PERTURB) {
+    if (G.RG == 1) hipLaunchKernelGGL(score_p2_bf16<true>, grid, dim3(WG), 0, st, a);
+    else hipLaunchKernelGGL(score_p2_bf16<false>, grid, dim3(WG), 0, st, a);
+  } else if (score_kind == KVE_SCORE_MIN || score_kind == KVE_SCORE_MIN_H)
     hipLaunchKernelGGL((score_p2w_bf16<true>), grid, dim3(WG), 0, st, a, score_kind);
   else
     hipLaunchKernelGGL((score_p2w_bf16<false>), grid, dim3(WG), 0, st, a, score_kind);
