@@ -197,6 +197,7 @@ struct RingFill {
     }
   }
   // K rows only, into stages of TILE_BYTES (the attention-weight scores).
+  template <bool NT = false>
   __device__ __forceinline__ void issue_k(const char* kb, int kt0, int c1, int stage) const {
     const size_t tbase = static_cast<size_t>(kt0) * ROWB;
     const uint32_t sb = static_cast<uint32_t>(stage) * TILE_BYTES;
@@ -204,7 +205,7 @@ struct RingFill {
     for (int i = 0; i < NB; ++i) {
       int off = goff[i];
       if (kt0 + KT > c1 && kt0 + key[i] >= c1) off += (c1 - 1 - kt0 - key[i]) * ROWB;
-      dma16(kb + tbase + off, lds[i] + sb);
+      dma16<NT>(kb + tbase + off, lds[i] + sb);
     }
   }
 };
@@ -1015,7 +1016,8 @@ __device__ float score_row_weight(int kind, int wi, int w) {
   return static_cast<float>(1.0 / ((w - wi) * hw));
 }
 
-template <bool VNORM>
+// NT: streaming loads of the tiles, as in score_p2_bf16.
+template <bool VNORM, bool NT>
 __global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
   ScoreWork wk;
   if (!score_work(a, blockIdx.x, &wk)) return;
@@ -1129,13 +1131,13 @@ __global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
     }
   };
 
-  if (ntile > 0) fill.issue_k(kb8, c0, c1, 0);
+  if (ntile > 0) fill.template issue_k<NT>(kb8, c0, c1, 0);
   const int edge_from = causal ? min(c1 - KT, n - a.w - KT + 1) : c1 - KT;
   for (int t = 0; t < ntile; ++t) {
     wait_vm<0>();
     lds_barrier();
     if (t > 0) reduce_tile(t - 1);
-    if (t + 1 < ntile) fill.issue_k(kb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
+    if (t + 1 < ntile) fill.template issue_k<NT>(kb8, c0 + (t + 1) * KT, c1, (t + 1) & 1);
     if (c0 + t * KT > edge_from) tile(t, std::true_type{});
     else tile(t, std::false_type{});
   }
@@ -1190,10 +1192,13 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   if (score_kind == KVE_SCORE_PERTURB) {
     if (G.RG == 1) hipLaunchKernelGGL(score_p2_bf16<true>, grid, dim3(WG), 0, st, a);
     else hipLaunchKernelGGL(score_p2_bf16<false>, grid, dim3(WG), 0, st, a);
-  } else if (score_kind == KVE_SCORE_MIN || score_kind == KVE_SCORE_MIN_H)
-    hipLaunchKernelGGL((score_p2w_bf16<true>), grid, dim3(WG), 0, st, a, score_kind);
-  else
-    hipLaunchKernelGGL((score_p2w_bf16<false>), grid, dim3(WG), 0, st, a, score_kind);
+  } else if (score_kind == KVE_SCORE_MIN || score_kind == KVE_SCORE_MIN_H) {
+    if (G.RG == 1) hipLaunchKernelGGL((score_p2w_bf16<true, true>), grid, dim3(WG), 0, st, a, score_kind);
+    else hipLaunchKernelGGL((score_p2w_bf16<true, false>), grid, dim3(WG), 0, st, a, score_kind);
+  } else {
+    if (G.RG == 1) hipLaunchKernelGGL((score_p2w_bf16<false, true>), grid, dim3(WG), 0, st, a, score_kind);
+    else hipLaunchKernelGGL((score_p2w_bf16<false, false>), grid, dim3(WG), 0, st, a, score_kind);
+  }
   stage_end(ST_SCORE_P2, st);
   return hipGetLastError();
 }
