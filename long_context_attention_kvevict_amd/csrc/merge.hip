@@ -186,11 +186,7 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
     const float tinv = tinvs[t * MRG_TT + col];
     const float sh = tinv > 0.f ? 2.f / tinv : 1.f;
     uint32_t best = 0u;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < MRG_D / 16; ++kk) acc = mfma32(qa[rb][kk], kop[kk], acc);
+    auto post = [&](const f32x16& acc, int rb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 kv = *reinterpret_cast<const f32x4*>(&kinv[128 * wave + 32 * rb + 8 * q4 + 4 * hl]);
@@ -201,7 +197,23 @@ __global__ __launch_bounds__(MRG_THREADS, 2) void mrg_sim(MergeArgs a) {
           best = max(best, key);
         }
       }
-    }
+    };
+    // the MFMA chain of block rb runs while block rb - 1 is post-processed
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < MRG_D / 16; ++kk) acc0 = mfma32(qa[0][kk], kop[kk], acc0);
+#pragma unroll
+    for (int kk = 0; kk < MRG_D / 16; ++kk) acc1 = mfma32(qa[1][kk], kop[kk], acc1);
+    post(acc0, 0);
+    acc0 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < MRG_D / 16; ++kk) acc0 = mfma32(qa[2][kk], kop[kk], acc0);
+    post(acc1, 1);
+    acc1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < MRG_D / 16; ++kk) acc1 = mfma32(qa[3][kk], kop[kk], acc1);
+    post(acc0, 2);
+    post(acc1, 3);
     const int eb = 63 - static_cast<int>(best & 63u);
     float bv = (__uint_as_float(best & 0xffffffc0u) - sh) * tinv;   // the cosine, to about 2^-16
     int br = 128 * wave + 32 * (eb >> 4) + 8 * ((eb >> 2) & 3) + 4 * hl + (eb & 3);
