@@ -162,8 +162,9 @@ kve_status kvevict_score_ex(const kve_layout* L, const void* q_win, const void* 
  *   proposal log pi~_j = log(max(score_j, 2^-126)) / tau, pi = pi~/sum pi~;
  *   m >= 0 integer with |sum_j 1 - (1-pi_j)^m - B_s| <= 0.5 (searched in
  *   [0, 10^12]); the kept set is the B_s largest Gumbel keys
- *   log pi~_j - log(-log u_j), u_j = ((x >> 11) + 0.5) 2^-53 with x the
- *   first word of Philox-4x64-10(counter = (j, h, s, 0), key = (seed, 0));
+ *   log pi~_j - log(-log u_j), u_j = ((x >> 11) + 0.5) 2^-53 with x word
+ *   j mod 4 of Philox-4x64-10(counter = (floor(j / 4), h, s, 0),
+ *   key = (seed, 0));
  *   bias_j = -log(q_j) / tau_w with q_j = 1 - (1 - pi_j)^m.  B_s = n_s keeps
  *   all tokens with bias 0.  If no m <= 10^12 reaches the band, m = 10^12 and
  *   status_out[s][h] = KVE_ENOCONV (outputs remain valid).
