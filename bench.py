@@ -487,13 +487,24 @@ def _eviction_leg(wl, args, probe, headline=False):
            torch.empty((wl.Hkv, total_C), dtype=torch.float32, device=dev))
     score_kind = args.score_kind if headline else "perturb"
     pool_mode = args.pool_mode if headline else "max"
+    # the output-aware score with max pooling goes through the one-call
+    # eviction (kvevict_evict: the same outputs as the three calls, fewer
+    # launches); the other score kinds and mean pooling through the three
+    one_call = score_kind == "perturb" and pool_mode == "max"
+    evout = (scores, *sel, *cmp)
 
-    def step():
+    def step3():
         b.score(q, k, v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel, out=scores, score_kind=score_kind,
                 pool_mode=pool_mode)
         idx, bias, _, _ = b.select(scores, budgets, mode=mode, tau=wl.tau, tau_w=wl.tau_w, seed=wl.hash_seed,
                                    out=sel, bud_offsets=bud)
         b.compact(k, v, budgets, idx, bias, caps, out=cmp, bud_offsets=bud, cap_offsets=cap)
+
+    def step1():
+        b.evict(q, k, v, wl.sm_scale, budgets, caps, mode=mode, pool_kernel=wl.pool_kernel, tau=wl.tau,
+                tau_w=wl.tau_w, seed=wl.hash_seed, out=evout, bud_offsets=bud, cap_offsets=cap)
+
+    step = step1 if one_call else step3
 
     for _ in range(args.warmup):
         step()
@@ -559,6 +570,16 @@ def _eviction_leg(wl, args, probe, headline=False):
     torch.cuda.synchronize()
     ms_write_flushed = float(np.median([x.elapsed_time(y) for x, y in wf]))
     del scratch
+    # 6. the one call against the same step as three calls (score, select,
+    # compact), cold, alternating step by step
+    vs_three = None
+    if one_call:
+        step3()   # its workspaces
+        t1, t3 = [], []
+        for _ in range(K_):
+            t1 += _cold_times(probe, step1, 1)
+            t3 += _cold_times(probe, step3, 1)
+        vs_three = {"one_call_ms": float(np.median(t1)), "three_calls_ms": float(np.median(t3)), "pairs": K_}
     print(f"# {wl.name}: {ms:.4f} ms/step cold (median of {K_}), {ms_warm:.4f} warm; dominant {dominant} "
           f"{dom_ms * 1e3:.1f} us cold; stages {stages}", file=sys.stderr, flush=True)
 
@@ -580,6 +601,7 @@ def _eviction_leg(wl, args, probe, headline=False):
     roof["timing"] = (f"mean per-launch time over {K_} cold-cache steps, HIP events on the launch stream around "
                       f"every kernel of the step")
     roof["launch_ms_events_around_it_only"] = dom_only_ms
+    # the pooling's bytes count whether it runs as a launch or inside the selection's first pass
     step_bytes = sum(sbytes[st] for st in ("score_pass1", "score_pass2", "score_pool", "select", "compact"))
     rows = {}
     for st, rec in stages.items():
@@ -597,6 +619,8 @@ def _eviction_leg(wl, args, probe, headline=False):
         "ms_per_step_cold_min": float(np.min(cold)),
         "ms_per_step_warm": ms_warm, "tokens_per_s_warm": wl.T / (ms_warm * 1e-3),
         "ms_per_step_write_flushed_median": ms_write_flushed,
+        "step_call": "kvevict_evict" if one_call else "kvevict_score + kvevict_select + kvevict_compact",
+        "one_call_vs_three_calls": vs_three,
         "roofline": roof,
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stage_ms": {name: round(rec[0], 5) for name, rec in stages.items()},
@@ -671,7 +695,7 @@ def main():
         "roofline": roof,
     }
     for key in ("ms_per_step_cold_min", "ms_per_step_warm", "tokens_per_s_warm", "ms_per_step_write_flushed_median",
-                "step_hbm_frac", "stage_ms", "rows"):
+                "step_call", "one_call_vs_three_calls", "step_hbm_frac", "stage_ms", "rows"):
         result[key] = head[key]
     # device scratch of the scorer (the pages quote the scoring path's
     # intermediate memory at n = 128K); caller-owned, reused every step

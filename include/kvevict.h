@@ -7,6 +7,7 @@
  *   kvevict_score_ex     the same, or attention-weight scores, max/avg pool
  *   kvevict_select       per-head budgeted selection (top-k or sampling)
  *   kvevict_compact      gather of the kept K/V rows and their logit bias
+ *   kvevict_evict        score + select + compact of one layer in one call
  *   kvevict_decode_snis  decode attention over the compacted cache with a
  *                        per-entry logit bias (self-normalised importance
  *                        sampling correction); kvevict_decode_snis_append
@@ -300,6 +301,28 @@ kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v,
                            const int32_t* idx, const float* bias,
                            const int32_t* cap_off, const int32_t* cap_off_host,
                            void* k_c, void* v_c, float* bias_c, void* stream);
+
+/* ------------------------------------------------------------------ evict
+ * One layer's eviction in one call ([DK] §3.2-3.4 scoring, [PI] §4
+ * selection, [PI] §2 Eq. 3 gather): kvevict_score (output-aware scores,
+ * max pooling over pool_kernel keys), then kvevict_select in `mode`, then
+ * kvevict_compact -- the same outputs bit for bit (scores, idx, bias,
+ * m_out, status_out, k_c, v_c, bias_c), with fewer launches: for bf16
+ * inputs the pooling rides on the selection's first pass and the
+ * selection's counters are cleared by the scorer's merge launch.  Arguments
+ * as for the three calls; ws at least kvevict_evict_workspace() bytes
+ * (256-byte aligned), of which the calls use disjoint parts. */
+size_t kvevict_evict_workspace(const kve_layout* L, const int32_t* bud_off_host,
+                               int32_t mode);
+kve_status kvevict_evict(const kve_layout* L, const void* q_win, const void* k,
+                         const void* v, float sm_scale, int32_t causal,
+                         int32_t pool_kernel, const int32_t* bud_off,
+                         const int32_t* bud_off_host, int32_t mode, float tau,
+                         float tau_w, uint64_t seed, float* scores, int32_t* idx,
+                         float* bias, double* m_out, int32_t* status_out,
+                         const int32_t* cap_off, const int32_t* cap_off_host,
+                         void* k_c, void* v_c, float* bias_c, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ decode_snis
  * Corrected decode attention ([PI] §5 Definition 3-4 and Algorithm 1; GQA

@@ -236,6 +236,77 @@ kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v, co
   return KVE_OK;
 }
 
+size_t kvevict_evict_workspace(const kve_layout* L, const int32_t* bud_off_host, int32_t mode) {
+  const size_t a = kvevict_score_workspace(L);
+  const size_t b = kvevict_select_workspace(L, bud_off_host, mode);
+  if (a == 0 || b == 0) return 0;
+  return ((a + 255) & ~static_cast<size_t>(255)) + b;
+}
+
+kve_status kvevict_evict(const kve_layout* L, const void* q_win, const void* k, const void* v, float sm_scale,
+                         int32_t causal, int32_t pool_kernel, const int32_t* bud_off, const int32_t* bud_off_host,
+                         int32_t mode, float tau, float tau_w, uint64_t seed, float* scores, int32_t* idx,
+                         float* bias, double* m_out, int32_t* status_out, const int32_t* cap_off,
+                         const int32_t* cap_off_host, void* k_c, void* v_c, float* bias_c, void* ws,
+                         size_t ws_bytes, void* stream) {
+  kve::ScoreGeom Gs;
+  kve::SelectGeom Gl;
+  std::string msg;
+  kve_status st = kve::plan_score(L, &Gs, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_evict: " + msg);
+  st = kve::plan_select(L, bud_off_host, mode, &Gl, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_evict: " + msg);
+  st = kve::check_compact(L, bud_off_host, cap_off_host, &msg);
+  if (st != KVE_OK) return set_err(st, "kvevict_evict: " + msg);
+  if (!q_win || !k || !v || !scores || !bud_off || !idx || !bias || !cap_off || !k_c || !v_c || !bias_c)
+    return set_err(KVE_EINVAL, "kvevict_evict: null tensor pointer");
+  if (!(sm_scale > 0.f) || sm_scale > 1e6f) return set_err(KVE_EINVAL, "kvevict_evict: sm_scale must be in (0, 1e6]");
+  if (pool_kernel < 1 || pool_kernel > 31 || pool_kernel % 2 == 0)
+    return set_err(KVE_EINVAL, "kvevict_evict: pool_kernel must be odd and in [1, 31]");
+  if (mode == KVE_SAMPLE && (!(tau > 0.f) || !(tau_w > 0.f)))
+    return set_err(KVE_EINVAL, "kvevict_evict: tau and tau_w must be > 0");
+  const size_t off_sel = (Gs.bytes + 255) & ~static_cast<size_t>(255);
+  if (!ws || ws_bytes < off_sel + Gl.bytes)
+    return set_err(KVE_EWORKSPACE, "kvevict_evict: workspace smaller than kvevict_evict_workspace()");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_err(KVE_EINVAL, "kvevict_evict: workspace must be 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(q_win) |
+       reinterpret_cast<uintptr_t>(k_c) | reinterpret_cast<uintptr_t>(v_c)) & 15)
+    return set_err(KVE_EINVAL, "kvevict_evict: q_win, k, v, k_c and v_c must be 16-byte aligned");
+  if (k_c == k || v_c == v || k_c == v || v_c == k)
+    return set_err(KVE_EINVAL, "kvevict_evict: outputs must not alias inputs");
+  char* wsb = static_cast<char*>(ws);
+  void* ws_sel = wsb + off_sel;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // bf16, and a selection whose first pass can pool: top-k over several
+  // chunks or the sampling chain; otherwise the three calls in turn
+  const bool fuse = L->dtype == KVE_BF16 && (mode == KVE_SAMPLE || Gl.max_len > kve::kSelChunk);
+  if (!fuse) {
+    st = kvevict_score(L, q_win, k, v, sm_scale, causal, pool_kernel, scores, ws, off_sel, stream);
+    if (st != KVE_OK) return st;
+    st = kvevict_select(L, scores, bud_off, bud_off_host, mode, tau, tau_w, seed, idx, bias, m_out, status_out,
+                        ws_sel, ws_bytes - off_sel, stream);
+    if (st != KVE_OK) return st;
+    return kvevict_compact(L, k, v, bud_off, bud_off_host, idx, bias, cap_off, cap_off_host, k_c, v_c, bias_c,
+                           stream);
+  }
+  kve::ScoreZero z{};
+  if (mode == KVE_TOPK) {   // what the selection's own clearing launch would clear
+    z.p = reinterpret_cast<int*>(static_cast<char*>(ws_sel) + Gl.off_hist);
+    z.n = static_cast<int>((Gl.zero_end - Gl.off_hist) / sizeof(int));
+    z.m = m_out;
+    z.st = status_out;
+    z.nsh = L->S * L->Hkv;
+  }
+  hipError_t e = kve::launch_score_bf16(Gs, q_win, k, v, L->seq_off, sm_scale, causal ? 1 : 0, KVE_SCORE_PERTURB,
+                                        ws, s, mode == KVE_TOPK ? &z : nullptr);
+  if (e != hipSuccess) return hip_err(e, "kvevict_evict (score)");
+  const kve::PoolSrc pool{reinterpret_cast<const float*>(wsb + Gs.off_sraw), scores, Gs.pool_rg, (pool_kernel - 1) / 2};
+  e = kve::launch_select(Gl, scores, L->seq_off, bud_off, tau, tau_w, 1.f, seed, idx, bias, m_out, status_out, ws_sel,
+                         s, nullptr, &pool);
+  if (e != hipSuccess) return hip_err(e, "kvevict_evict (select)");
+  return kvevict_compact(L, k, v, bud_off, bud_off_host, idx, bias, cap_off, cap_off_host, k_c, v_c, bias_c, stream);
+}
+
 size_t kvevict_decode_workspace(const kve_layout* L, int32_t max_cache_len) {
   kve::DecodeGeom G;
   std::string msg;

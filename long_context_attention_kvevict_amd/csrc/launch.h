@@ -8,9 +8,19 @@
 
 namespace kve {
 
+// Memory a later selection needs cleared, cleared by the scorer's merge
+// launch instead of a launch of its own (one-call eviction): n ints at p, and
+// m = 0, status = KVE_OK for nsh heads (m and st may be NULL).
+struct ScoreZero {
+  int* p;
+  int n;
+  double* m;
+  int32_t* st;
+  int nsh;
+};
 hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
                              const int32_t* seq_off, float sm_scale, int causal, int score_kind, void* ws,
-                             hipStream_t st);
+                             hipStream_t st, const ScoreZero* zero = nullptr);
 hipError_t launch_score_f32(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
                             const int32_t* seq_off, float sm_scale, int causal, void* ws,
                             hipStream_t st);
@@ -26,10 +36,20 @@ struct SoftBudget {
   int64_t total_cap;        // cap_off[S]
   int32_t* kept;            // device [S*Hkv] out, or NULL
 };
+// Max pooling folded into the first selection pass (one-call eviction): the
+// pass reads the scorer's raw planes, writes the pooled plane to `out` and
+// selects on it; the selection's counters must already be clear (ScoreZero).
+struct PoolSrc {
+  const float* sraw;   // [planes][Hkv][T] raw score planes (summed in order)
+  float* out;          // [Hkv][T] pooled scores
+  int planes;
+  int radius;          // (pool kernel - 1) / 2, at most kPoolMaxRadius
+};
+constexpr int kPoolMaxRadius = 15;
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                         hipStream_t st, const SoftBudget* soft = nullptr);
+                         hipStream_t st, const SoftBudget* soft = nullptr, const PoolSrc* pool = nullptr);
 
 hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const float* scores, const double* m_in,
                           const int32_t* cap_off, int64_t total_cap, float tau, float tau_w, float mix,

@@ -92,6 +92,7 @@ struct ScoreArgs {
   float* sraw;             // [RG][Hkv][T]
   int32_t* jstar;          // [S*Hkv*RG][ROWS]  key holding over half of the row's weight, or -1
   float* cstar;            // [S*Hkv*RG][ROWS]  that pair's exact term (a / (1 - a))^2 ||o - v||^2
+  ScoreZero zero;          // cleared by the merge launch (p = NULL: nothing)
 };
 
 // Work item of a workgroup of either pass.  The RG row groups of one
@@ -554,6 +555,14 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   const int grp = gr / ROWS;
   const int rl = gr % ROWS;
   const int tid = threadIdx.x;
+  if (a.zero.p) {   // a later selection's counters (one-call eviction)
+    const int nt = gridDim.x * 256;
+    for (int i = gr * 256 + tid; i < a.zero.n; i += nt) a.zero.p[i] = 0;
+    for (int i = gr * 256 + tid; i < a.zero.nsh; i += nt) {
+      if (a.zero.m) a.zero.m[i] = 0.0;
+      if (a.zero.st) a.zero.st[i] = KVE_OK;
+    }
+  }
   const int st = tid >> 5, ln = tid & 31;
   const int s = grp / (a.Hkv * a.RG);
   const int h = (grp / a.RG) % a.Hkv;
@@ -1151,8 +1160,9 @@ __global__ __launch_bounds__(WG, 2) void score_p2w_bf16(ScoreArgs a, int kind) {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* k, const void* v,
                              const int32_t* seq_off, float sm_scale, int causal, int score_kind,
-                             void* ws, hipStream_t st) {
-  ScoreArgs a;
+                             void* ws, hipStream_t st, const ScoreZero* zero) {
+  ScoreArgs a = {};
+  if (zero) a.zero = *zero;
   a.q_win = static_cast<const uint16_t*>(q_win);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);

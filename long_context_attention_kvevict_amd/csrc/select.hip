@@ -295,6 +295,74 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(Src src, SelArgs a, int*
   sel_hist_body<Src, LV>(src, a, hist, lh, lds);
 }
 
+// Key-axis max pooling folded into a selection's first pass (one-call
+// eviction; the pooling kernel's values bit for bit): the workgroup sums
+// the raw planes of its chunk and a halo of `radius` keys, in plane order,
+// into LDS (-inf outside the sequence), and each key takes the maximum over
+// its window.  v: SEL_CHUNK + 2 * kPoolMaxRadius floats of LDS; keys
+// j0 - r .. j0 + SEL_CHUNK + r - 1 of the sequence at `base` (n keys).
+__device__ void pool_stage(const PoolSrc& P, int Hkv, int T, int h, int base, int n, int j0, float* v) {
+  const int r = P.radius;
+  for (int i = threadIdx.x; i < SEL_CHUNK + 2 * r; i += SEL_THREADS) {
+    const int j = j0 - r + i;
+    float x = -INFINITY;
+    if (j >= 0 && j < n) {
+      x = 0.f;
+      for (int p = 0; p < P.planes; ++p) x += P.sraw[(static_cast<size_t>(p) * Hkv + h) * T + base + j];
+    }
+    v[i] = x;
+  }
+  __syncthreads();
+}
+// The pooled score of key j0 + jl (window v[jl .. jl + 2r]).
+__device__ __forceinline__ float pool_at(const PoolSrc& P, const float* v, int jl) {
+  float m = -INFINITY;
+  for (int d = 0; d <= 2 * P.radius; ++d) m = fmaxf(m, v[jl + d]);
+  return m;
+}
+
+// Top-k level 0 on the pooled scores, which it also writes (for every
+// chunk of every head, selected or not).  The histograms are already clear.
+__global__ __launch_bounds__(SEL_THREADS) void sel_hist0_pool(PoolSrc P, SelArgs a, int* __restrict__ hist) {
+  typedef uint32_t K;
+  __shared__ int lh[SEL_BINS];
+  __shared__ float v[SEL_CHUNK + 2 * kPoolMaxRadius];
+  const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int base = a.seq_off[s];
+  const int n = a.seq_off[s + 1] - base;
+  const int j0 = ch * SEL_CHUNK;
+  if (j0 >= n) return;
+  pool_stage(P, a.Hkv, a.T, h, base, n, j0, v);
+  const size_t row = static_cast<size_t>(h) * a.T + base;
+  K u[SEL_PER];
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i) {
+    const int jl = i * SEL_THREADS + threadIdx.x;
+    u[i] = K(0);
+    if (j0 + jl < n) {
+      const float m = pool_at(P, v, jl);
+      P.out[row + j0 + jl] = m;
+      u[i] = f32_order_key(m);
+    }
+  }
+  const int sh = s * a.Hkv + h;
+  const int B = sel_budget(a, s, sh);
+  if (B <= 0 || B >= n) return;
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) lh[i] = 0;
+  __syncthreads();
+  const int sft = Radix<K>::shift(0);
+  const K dm = Radix<K>::wmask(0);
+#pragma unroll
+  for (int i = 0; i < SEL_PER; ++i)
+    if (j0 + i * SEL_THREADS + static_cast<int>(threadIdx.x) < n) atomicAdd(&lh[static_cast<int>((u[i] >> sft) & dm)], 1);
+  __syncthreads();
+  int* gh = hist + static_cast<size_t>(sh) * SEL_BINS;   // level 0
+  for (int i = threadIdx.x; i < SEL_BINS; i += SEL_THREADS) {
+    const int c = lh[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
 // Last digit level of the radix select, which also leaves the ordered write
 // what a separate count launch would.  Per chunk: the number of keys whose
 // leading digits (levels 0 .. LEVELS-2) exceed those of the threshold, and,
@@ -796,14 +864,38 @@ __device__ __forceinline__ double smp_gumbel(const SmpArgs& A, double x, int j, 
 // writes them in place of log pi~, and it also clears the selection's
 // histograms ([0, nzero) of `zero`: every digit level's), which no
 // workgroup of this launch touches otherwise.
-template <bool KEYS>
-__global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A, int* __restrict__ zero, int nzero) {
+// POOL (one-call eviction, KEYS only): the scores are max-pooled from the
+// scorer's raw planes here (and written to P.out for every chunk of every
+// head) instead of read from A.scores.
+template <bool KEYS, bool POOL = false>
+__global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A, int* __restrict__ zero, int nzero, PoolSrc P) {
+  static_assert(KEYS || !POOL, "pooling rides on the key pass");
   if constexpr (KEYS) {
     const int nwg = gridDim.x * gridDim.y * gridDim.z;
     const int wg = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     for (int i = wg * SEL_THREADS + threadIdx.x; i < nzero; i += nwg * SEL_THREADS) zero[i] = 0;
   }
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  float pooled[SMP_PER];
+  if constexpr (POOL) {
+    static_assert(SMP_CHUNK == SEL_CHUNK, "the pooling stage covers one selection chunk");
+    __shared__ float v[SEL_CHUNK + 2 * kPoolMaxRadius];
+    const int pbase = A.g.seq_off[s];
+    const int pn = A.g.seq_off[s + 1] - pbase;
+    const int pj0 = ch * SMP_CHUNK;
+    if (pj0 >= pn) return;
+    pool_stage(P, A.g.Hkv, A.g.T, h, pbase, pn, pj0, v);
+    const size_t prow = static_cast<size_t>(h) * A.g.T + pbase;
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int jl = SMP_PER * threadIdx.x + i;
+      pooled[i] = 0.f;
+      if (pj0 + jl < pn) {
+        pooled[i] = pool_at(P, v, jl);
+        P.out[prow + pj0 + jl] = pooled[i];
+      }
+    }
+  }
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
   const int sh = s * A.g.Hkv + h;
@@ -823,7 +915,7 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_logp(SmpArgs A, int* __restri
       const int j = j0 + i;
       x[i] = -INFINITY;
       if (j < n) {
-        x[i] = smp_logpt(A, row + j);
+        x[i] = POOL ? log(static_cast<double>(fmaxf(pooled[i], 1.17549435e-38f))) * A.inv_tau : smp_logpt(A, row + j);
         A.lp[row + j] = gumbel_of(x[i], c[i]);
         A.L[row + j] = x[i];
         mx = fmax(mx, x[i]);
@@ -1646,11 +1738,15 @@ hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const fl
 // ----------------------------------------------------------------- launch
 template <class Src, class Bias>
 static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,
-                         RState* rs, int32_t* idx, float* bias, hipStream_t st, int* cand) {
+                         RState* rs, int32_t* idx, float* bias, hipStream_t st, int* cand,
+                         const PoolSrc* pool = nullptr) {
   typedef typename Src::K K;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
   if (a.bsh == nullptr) {   // no count launch (not under a soft budget)
-    hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
+    if (pool)   // level 0 on the scores it pools (and writes)
+      hipLaunchKernelGGL(sel_hist0_pool, grid, dim3(SEL_THREADS), 0, st, *pool, a, hist);
+    else
+      hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     hipLaunchKernelGGL((sel_hist<Src, 1>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     if (Radix<K>::LEVELS > 3) {
       hipLaunchKernelGGL((sel_hist<Src, 2>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
@@ -1775,7 +1871,7 @@ __global__ __launch_bounds__(256) void sel_init(int* __restrict__ p, int n, doub
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                         hipStream_t st, const SoftBudget* soft) {
+                         hipStream_t st, const SoftBudget* soft, const PoolSrc* pool) {
   char* wsb = static_cast<char*>(ws);
   int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
   int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
@@ -1801,6 +1897,9 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   // sampling with a per-head budget and the unmixed proposal: the first
   // pass also writes the Gumbel keys and clears the histograms
   const bool chain = !topk && !soft && mix >= 1.0f;
+  // with pooling folded in: top-k over several chunks or the unmixed chain
+  // only, the counters already clear
+  if (pool && (soft || (topk && G.max_len <= SEL_CHUNK) || (!topk && !chain))) return hipErrorInvalidValue;
   stage_begin(ST_SELECT, st);
   if (topk && !soft && G.max_len <= SEL_CHUNK) {   // every head in one workgroup
     hipLaunchKernelGGL(sel_topk_one, dim3(1, G.Hkv, G.S), dim3(SEL_THREADS), 0, st, scores, a, idx, bias, m_out,
@@ -1808,12 +1907,12 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     stage_end(ST_SELECT, st);
     return hipGetLastError();
   }
-  if (!chain)
+  if (!chain && !pool)
     hipLaunchKernelGGL(sel_init, dim3((max(nzero, SH) + 255) / 256), dim3(256), 0, st, hist, nzero,
                        topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
   if (topk) {
-    launch_radix(G, a, ScoreKeys{scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st,
-                 reinterpret_cast<int*>(wsb + G.off_cand));
+    launch_radix(G, a, ScoreKeys{pool ? pool->out : scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st,
+                 reinterpret_cast<int*>(wsb + G.off_cand), pool);
   } else {
     SmpArgs A;
     A.g = a;
@@ -1840,7 +1939,12 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
     if (chain) {
       // keys first: levels 0 .. 5 ride on the grid pass, the 3 search steps,
       // the finish and the decision
-      hipLaunchKernelGGL((smp_logp<true>), sgrid, dim3(SEL_THREADS), 0, st, A, hist, nzero);
+      if (pool) {
+        A.scores = pool->out;
+        hipLaunchKernelGGL((smp_logp<true, true>), sgrid, dim3(SEL_THREADS), 0, st, A, hist, nzero, *pool);
+      } else {
+        hipLaunchKernelGGL((smp_logp<true>), sgrid, dim3(SEL_THREADS), 0, st, A, hist, nzero, PoolSrc{});
+      }
       hipLaunchKernelGGL(smp_grid_hist, sgrid, dim3(SEL_THREADS), 0, st, A, hist);
       hipLaunchKernelGGL((smp_search_hist<1, true>), sgrid, dim3(SEL_THREADS), 0, st, A, 0, hist);
       hipLaunchKernelGGL((smp_search_hist<2, false>), sgrid, dim3(SEL_THREADS), 0, st, A, 1, hist);
@@ -1853,7 +1957,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
       stage_end(ST_SELECT, st);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((smp_logp<false>), sgrid, dim3(SEL_THREADS), 0, st, A, nullptr, 0);
+    hipLaunchKernelGGL((smp_logp<false>), sgrid, dim3(SEL_THREADS), 0, st, A, nullptr, 0, PoolSrc{});
     hipLaunchKernelGGL(smp_keys, sgrid, dim3(SEL_THREADS), 0, st, A);
     if (!soft) {
       // (mixed proposal) the keys need the normaliser: levels 0 .. 4 ride

@@ -24,7 +24,7 @@ EXPORTS = [
     "kvevict_score_workspace", "kvevict_score", "kvevict_score_ex", "kvevict_select_workspace", "kvevict_select",
     "kvevict_select_ex", "kvevict_select_soft", "kvevict_select_literal_workspace", "kvevict_select_literal",
     "kvevict_merge_workspace", "kvevict_merge",
-    "kvevict_compact", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_decode_scratch_max",
+    "kvevict_compact", "kvevict_evict_workspace", "kvevict_evict", "kvevict_decode_workspace", "kvevict_decode_snis", "kvevict_decode_scratch_max",
     "kvevict_decode_snis_noalloc", "kvevict_decode_snis_append", "kvevict_last_error",
     "kvevict_version", "kvevict_timing_enable", "kvevict_timing_summary",
 ]
@@ -86,6 +86,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvevict_merge.restype = I32
     lib.kvevict_compact.argtypes = [LP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.kvevict_compact.restype = I32
+    lib.kvevict_evict_workspace.argtypes = [LP, P, I32]
+    lib.kvevict_evict_workspace.restype = SZ
+    lib.kvevict_evict.argtypes = [LP, P, P, P, F32, I32, I32, P, P, I32, F32, F32, U64, P, P, P, P, P, P, P, P, P,
+                                  P, P, SZ, P]
+    lib.kvevict_evict.restype = I32
     lib.kvevict_decode_workspace.argtypes = [LP, I32]
     lib.kvevict_decode_workspace.restype = SZ
     lib.kvevict_decode_snis.argtypes = [LP, P, P, P, P, P, P, P, I32, F32, P, P, SZ, P]
@@ -327,6 +332,38 @@ class Batch:
                                          _stream(stream)))
         self._cmp = (bud_host, bud_dev, cap_host, cap_dev)
         return k_c, v_c, b_c
+
+    def evict(self, q_win, k, v, sm_scale: float, budgets, caps, mode: int = KVE_TOPK, causal: bool = True,
+              pool_kernel: int = 7, tau: float = 1.0, tau_w: float = 1.0, seed: int = 0, out=None, stream=None,
+              bud_offsets=None, cap_offsets=None):
+        """score + select + compact in one call (max pooling, per-head
+        budgets, unmixed proposal).  out: (scores, idx, bias, m, status,
+        k_c, v_c, bias_c) to reuse, or None.  Returns that tuple (idx and
+        bias cut to the total budget)."""
+        bud_host, bud_dev = bud_offsets if bud_offsets is not None else self.offsets(budgets, self.device)
+        cap_host, cap_dev = cap_offsets if cap_offsets is not None else self.offsets(caps, self.device)
+        lay = ctypes.byref(self.layout)
+        nbytes = self._lib.kvevict_evict_workspace(lay, bud_host.data_ptr(), int(mode)) or 256
+        ws = self._workspace("evict", nbytes)
+        total, C = int(bud_host[-1]), int(cap_host[-1])
+        if out is None:
+            dev = self.device
+            out = (torch.empty((self.Hkv, self.T), dtype=torch.float32, device=dev),
+                   torch.empty((self.Hkv, max(total, 1)), dtype=torch.int32, device=dev),
+                   torch.empty((self.Hkv, max(total, 1)), dtype=torch.float32, device=dev),
+                   torch.empty((self.S, self.Hkv), dtype=torch.float64, device=dev),
+                   torch.empty((self.S, self.Hkv), dtype=torch.int32, device=dev),
+                   torch.zeros((self.Hkv, C, self.d), dtype=k.dtype, device=dev),
+                   torch.zeros((self.Hkv, C, self.d), dtype=v.dtype, device=dev),
+                   torch.zeros((self.Hkv, C), dtype=torch.float32, device=dev))
+        sc, idx, bias, m, status, k_c, v_c, b_c = out
+        _check(self._lib.kvevict_evict(lay, _ptr(q_win), _ptr(k), _ptr(v), float(sm_scale), int(bool(causal)),
+                                       int(pool_kernel), _ptr(bud_dev), bud_host.data_ptr(), int(mode), float(tau),
+                                       float(tau_w), ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(sc), _ptr(idx),
+                                       _ptr(bias), _ptr(m), _ptr(status), _ptr(cap_dev), cap_host.data_ptr(),
+                                       _ptr(k_c), _ptr(v_c), _ptr(b_c), _ptr(ws), ws.numel(), _stream(stream)))
+        self._evk = (bud_host, bud_dev, cap_host, cap_dev)   # alive until the stream has used them
+        return sc, idx[:, :total], bias[:, :total], m, status, k_c, v_c, b_c
 
     def decode(self, q, k_c, v_c, bias_c, caps, cache_len, max_cache_len: int, sm_scale: float,
                out=None, stream=None, cap_offsets=None):

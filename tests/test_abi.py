@@ -238,3 +238,27 @@ def test_noalloc_decode_rejects_batches_beyond_its_scratch():
     assert "scratch" in lib.kvevict_last_error().decode()
     # the workspace entry point takes the same batch
     assert lib.kvevict_decode_workspace(ctypes.byref(lay), 20000) > (8 << 20)
+
+
+def test_evict_rejects_bad_arguments_and_sizes_its_workspace():
+    lib = K.load_library()
+    lay, keep = _layout(Hq=8, Hkv=2, w=8, lens=(3000,))
+    bud = torch.tensor([0, 300], dtype=torch.int32)
+    cap = torch.tensor([0, 310], dtype=torch.int32)
+    seed = ctypes.c_uint64(1)
+
+    def call(pool=7, mode=K.KVE_TOPK, cap_t=cap, ws_bytes=1 << 40, tau=0.5, k_c=DUMMY + 4096):
+        return lib.kvevict_evict(ctypes.byref(lay), DUMMY, DUMMY, DUMMY, 0.1, 1, pool, DUMMY, bud.data_ptr(), mode,
+                                 tau, 1.0, seed, DUMMY, DUMMY, DUMMY, None, None, DUMMY, cap_t.data_ptr(), k_c,
+                                 DUMMY + 8192, DUMMY, DUMMY, ws_bytes, None)
+    for m in (K.KVE_TOPK, K.KVE_SAMPLE):
+        need = lib.kvevict_evict_workspace(ctypes.byref(lay), bud.data_ptr(), m)
+        parts = (lib.kvevict_score_workspace(ctypes.byref(lay))
+                 + lib.kvevict_select_workspace(ctypes.byref(lay), bud.data_ptr(), m))
+        assert parts <= need <= parts + 256
+        assert call(mode=m, ws_bytes=need - 1) == K.KVE_EWORKSPACE
+    assert call(pool=4) == K.KVE_EINVAL                     # even pooling width
+    assert call(mode=K.KVE_SAMPLE, tau=0.0) == K.KVE_EINVAL   # tau must be > 0
+    assert call(cap_t=torch.tensor([0, 299], dtype=torch.int32)) == K.KVE_EINVAL   # capacity below budget
+    assert call(k_c=DUMMY) == K.KVE_EINVAL                   # k_c aliases k
+    assert b"kvevict_evict" in lib.kvevict_last_error()
