@@ -23,6 +23,8 @@ def _cases():
         "llama_n4099_topk": (workloads.scaled(workloads.llama8b_32k(), 4099), K.KVE_TOPK, 7, None),
         # sampling chain: the key pass pools four row-group planes
         "qwen_n3001_sample": (workloads.scaled(workloads.qwen7b_128k_sample(), 3001), K.KVE_SAMPLE, 7, None),
+        # top-k level 0 over four row-group planes
+        "qwen_n3001_topk": (workloads.scaled(workloads.qwen7b_128k_sample(), 3001), K.KVE_TOPK, 7, None),
         # ragged batch, budgets 0 and n on two sequences (their scores are still written)
         "ragged3_topk_edges": (ragged, K.KVE_TOPK, 7, [0, 2049, 500]),
         "ragged3_sample_edges": (ragged, K.KVE_SAMPLE, 7, [30, 0, 5000]),
