@@ -437,7 +437,11 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
         }
       }
     };
+    // the P.V contraction at raised wave priority: the matrix cores take the
+    // MFMAs of this wave while the other wave on the SIMD does its softmax
+    __builtin_amdgcn_s_setprio(1);
     pv(pb);
+    __builtin_amdgcn_s_setprio(0);
     // A dominant weight is where the bf16 rounding of P matters: it moves o
     // by 2^-9 a v_j for a key of final weight a, against ||o - v_j|| of about
     // (1 - a) ||v_j||.  The running sum of the row (this lane's half plus its
