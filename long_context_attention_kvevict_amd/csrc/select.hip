@@ -955,6 +955,20 @@ __device__ __forceinline__ double grid_u(int k, int B) {
   return fmin(log(static_cast<double>(B)) + k * 0.69314718055994531, log(kAlphaMax));
 }
 
+// log(1 - p) for 0 <= p <= 1: below 2^-10 the series -p (1 + p/2 + p^2/3 +
+// ... + p^5/6), whose first omitted term is under 2^-60 p; log1p(-p) above.
+__device__ __forceinline__ double log1m(double p) {
+  if (p < 0x1.0p-10) {
+    double t = fma(p, 1.0 / 6.0, 0.2);
+    t = fma(p, t, 0.25);
+    t = fma(p, t, 1.0 / 3.0);
+    t = fma(p, t, 0.5);
+    t = fma(p, t, 1.0);
+    return -p * t;
+  }
+  return log1p(-p);
+}
+
 // Pass B: log1p(-pi_j) and (KEYS) the Gumbel keys of the proposal's
 // logarithm, mixed or not (smp_gumbel); without KEYS pass A already wrote
 // them and left log pi~ in the log1p(-pi) plane, which this pass overwrites.  Also the chunk's
@@ -1012,7 +1026,7 @@ __device__ void smp_keys_body(const SmpArgs& A, float (*eg)[SEL_THREADS + 1]) {
         l = log1p(-pm);
         x = log(pm);
       } else {
-        l = log1p(-exp(x - lse));
+        l = log1m(exp(x - lse));
       }
       A.L[row + j] = l;
       if (KEYS) A.lp[row + j] = smp_gumbel(A, x, j, h, s);
