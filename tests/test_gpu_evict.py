@@ -62,3 +62,27 @@ def test_evict_equals_score_select_compact(name):
             assert torch.equal(x.view(torch.uint8) if x.dtype == torch.float32 else x,
                                y.view(torch.uint8) if y.dtype == torch.float32 else y), f"{name}: {nm} differs"
     say(f"[gpu] evict {name} ok")
+
+
+@pytest.mark.parametrize("name", ["llama128k", "qwen128k", "mistral_ragged"])
+def test_evict_full_size_equals_three_calls(name):
+    # the benchmark's step at its full size: the one call against the three
+    wl = workloads.ALL[name]()
+    r = Run(wl)
+    b = r.b
+    budgets, caps = wl.budgets(), wl.caps()
+    mode = K.KVE_TOPK if wl.mode == "topk" else K.KVE_SAMPLE
+    say(f"[gpu] evict full size {wl.name} T={wl.T} mode={mode}")
+    sc = b.score(r.q, r.k, r.v, wl.sm_scale, causal=True, pool_kernel=wl.pool_kernel)
+    idx, bias, m, st = b.select(sc, budgets, mode=mode, tau=wl.tau, tau_w=wl.tau_w, seed=wl.hash_seed)
+    kc, vc, bc = b.compact(r.k, r.v, budgets, idx, bias, caps)
+    ref = [x.clone() for x in (sc, idx, bias, m, st, kc, vc, bc)]
+    del kc, vc, bc
+    torch.cuda.synchronize()
+    got = b.evict(r.q, r.k, r.v, wl.sm_scale, budgets, caps, mode=mode, pool_kernel=wl.pool_kernel, tau=wl.tau,
+                  tau_w=wl.tau_w, seed=wl.hash_seed)
+    torch.cuda.synchronize()
+    for nm, x, y in zip(("scores", "idx", "bias", "m", "status", "k_c", "v_c", "bias_c"), got, ref):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.float32 else x,
+                           y.view(torch.uint8) if y.dtype == torch.float32 else y), f"{name}: {nm} differs"
+    say(f"[gpu] evict full size {wl.name} ok")
