@@ -222,3 +222,61 @@ def test_mistral_ragged_batch_with_decode():
             err = np.abs(out.cpu().numpy() - ref).max()
             say(f"[gpu] decode step {t}: max abs err {err:.2e}")
             assert err <= DECODE_ATOL
+
+
+
+def _check_sampled_scores(r, got, s, h, keys):
+    """Keys `keys` of (sequence s, KV head h) against the oracle's pooled
+    group score: the raw score at every key of each pooling window (each
+    row's softmax still over all n keys), then the pooling maximum."""
+    from oracle.score import group_scores_at
+    wl = r.wl
+    a, b = wl.seq_off()[s], wl.seq_off()[s + 1]
+    n, rad = b - a, (wl.pool_kernel - 1) // 2
+    keys = np.unique(np.asarray(keys, dtype=np.int64))
+    near = np.unique(np.clip(keys[:, None] + np.arange(-rad, rad + 1)[None, :], 0, n - 1))
+    raw = group_scores_at(r.f64_q()[s], r.f64_kv("k", h, a, b), r.f64_kv("v", h, a, b), h, wl.g, wl.sm_scale,
+                          True, near)
+    at = dict(zip(near.tolist(), raw.tolist()))
+    ref = np.array([max(at[j] for j in range(max(0, x - rad), min(n, x + rad + 1))) for x in keys.tolist()])
+    worst, _ = check_scores(got[h, a + keys], ref, f"{wl.name} s{s} h{h} sampled")
+    say(f"[gpu] full {wl.name} s{s} h{h}: {keys.size} sampled keys, max rel err {worst:.2e}")
+
+
+def test_qwen_shape_one_head_n1m_sampling():
+    # the largest single sequence here: 2^20 tokens (512 scorer chunks and
+    # 1024 selection chunks), one KV head of the Qwen layer's shape (7
+    # q-heads, 64 window rows each), through the one-call eviction: the three
+    # calls bit for bit, sampled keys' scores against the oracle (the ten
+    # largest, the first and last 64 and 1024 at random), the sampling
+    # selection given the GPU's scores, and the compaction bit for bit
+    import dataclasses
+    wl = dataclasses.replace(workloads.qwen7b_128k_sample(), name="qwen_shape_n1m", Hq=7, Hkv=1, lens=[1 << 20])
+    say(f"[gpu] full {wl.name}: generating")
+    r = BigRun(wl)
+    budgets, caps = wl.budgets(), wl.caps()
+    say(f"[gpu] full {wl.name}: evict")
+    sc, idx, bias, m, st, kc, vc, bc = r.b.evict(r.q, r.k, r.v, wl.sm_scale, budgets, caps, mode=K.KVE_SAMPLE,
+                                                 pool_kernel=wl.pool_kernel, tau=wl.tau, tau_w=wl.tau_w,
+                                                 seed=wl.hash_seed)
+    sc3 = r.b.score(r.q, r.k, r.v, wl.sm_scale, pool_kernel=wl.pool_kernel)
+    idx3, bias3, m3, st3 = r.b.select(sc3, budgets, mode=K.KVE_SAMPLE, tau=wl.tau, tau_w=wl.tau_w,
+                                      seed=wl.hash_seed)
+    torch.cuda.synchronize()
+    assert torch.equal(sc.view(torch.uint8), sc3.view(torch.uint8))
+    assert torch.equal(idx, idx3) and torch.equal(bias.view(torch.uint8), bias3.view(torch.uint8))
+    assert torch.equal(m, m3) and torch.equal(st, st3)
+    got = sc.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    B = int(budgets[0])
+    sel = idx.cpu().numpy()[0]
+    assert np.array_equal(kc[0, :B].cpu().view(torch.int16).numpy(), r.data["k"].view(np.int16)[0, sel])
+    assert np.array_equal(vc[0, :B].cpu().view(torch.int16).numpy(), r.data["v"].view(np.int16)[0, sel])
+    n = wl.T
+    keys = np.concatenate([np.argsort(got[0])[-10:], np.arange(64), np.arange(n - 64, n),
+                           np.random.default_rng(7).choice(n, 1024, replace=False)])
+    say(f"[gpu] full {wl.name}: oracle scores of sampled keys")
+    _check_sampled_scores(r, got, 0, 0, keys)
+    say(f"[gpu] full {wl.name}: selection")
+    _, _, m, _ = _select_parity(r, got)
+    say(f"[gpu] full {wl.name}: m {m[0, 0]:.6g}")
