@@ -308,8 +308,9 @@ kve_status kvevict_compact(const kve_layout* L, const void* k, const void* v,
  * max pooling over pool_kernel keys), then kvevict_select in `mode`, then
  * kvevict_compact -- the same outputs bit for bit (scores, idx, bias,
  * m_out, status_out, k_c, v_c, bias_c), with fewer launches: for bf16
- * inputs the pooling rides on the selection's first pass and the
- * selection's counters are cleared by the scorer's merge launch.  Arguments
+ * inputs the pooling rides on the selection's first pass, the selection's
+ * counters are cleared by the scorer's merge launch, and the selection's
+ * ordered write gathers the kept rows into k_c / v_c / bias_c.  Arguments
  * as for the three calls; ws at least kvevict_evict_workspace() bytes
  * (256-byte aligned), of which the calls use disjoint parts. */
 size_t kvevict_evict_workspace(const kve_layout* L, const int32_t* bud_off_host,

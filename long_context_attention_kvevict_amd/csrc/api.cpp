@@ -277,8 +277,9 @@ kve_status kvevict_evict(const kve_layout* L, const void* q_win, const void* k, 
   char* wsb = static_cast<char*>(ws);
   void* ws_sel = wsb + off_sel;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // bf16, and a selection whose first pass can pool: top-k over several
-  // chunks or the sampling chain; otherwise the three calls in turn
+  // bf16, and a selection whose first pass can pool and whose ordered write
+  // can gather: top-k over several chunks or the sampling chain; otherwise
+  // the three calls in turn
   const bool fuse = L->dtype == KVE_BF16 && (mode == KVE_SAMPLE || Gl.max_len > kve::kSelChunk);
   if (!fuse) {
     st = kvevict_score(L, q_win, k, v, sm_scale, causal, pool_kernel, scores, ws, off_sel, stream);
@@ -301,10 +302,13 @@ kve_status kvevict_evict(const kve_layout* L, const void* q_win, const void* k, 
                                         ws, s, mode == KVE_TOPK ? &z : nullptr);
   if (e != hipSuccess) return hip_err(e, "kvevict_evict (score)");
   const kve::PoolSrc pool{reinterpret_cast<const float*>(wsb + Gs.off_sraw), scores, Gs.pool_rg, (pool_kernel - 1) / 2};
+  // the ordered write gathers the kept rows itself (bf16 rows of d values)
+  const kve::CompactDst cd{static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), static_cast<uint8_t*>(k_c),
+                           static_cast<uint8_t*>(v_c), bias_c, cap_off, cap_off_host[L->S], L->d * 2};
   e = kve::launch_select(Gl, scores, L->seq_off, bud_off, tau, tau_w, 1.f, seed, idx, bias, m_out, status_out, ws_sel,
-                         s, nullptr, &pool);
+                         s, nullptr, &pool, &cd);
   if (e != hipSuccess) return hip_err(e, "kvevict_evict (select)");
-  return kvevict_compact(L, k, v, bud_off, bud_off_host, idx, bias, cap_off, cap_off_host, k_c, v_c, bias_c, stream);
+  return KVE_OK;
 }
 
 size_t kvevict_decode_workspace(const kve_layout* L, int32_t max_cache_len) {

@@ -46,10 +46,24 @@ struct PoolSrc {
   int radius;          // (pool kernel - 1) / 2, at most kPoolMaxRadius
 };
 constexpr int kPoolMaxRadius = 15;
+// The compaction folded into the selection's ordered write (one-call
+// eviction): each workgroup gathers the K/V rows of the keys it keeps into
+// the compact cache, row cap_off[s] + slot of KV head h, with their bias.
+struct CompactDst {
+  const uint8_t* k;        // [Hkv][T] rows of row_bytes
+  const uint8_t* v;
+  uint8_t* k_c;            // [Hkv][totalC] rows of row_bytes
+  uint8_t* v_c;
+  float* bias_c;           // [Hkv][totalC]
+  const int32_t* cap_off;  // [S+1] device
+  int64_t totalC;
+  int row_bytes;           // a multiple of 16
+};
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                         hipStream_t st, const SoftBudget* soft = nullptr, const PoolSrc* pool = nullptr);
+                         hipStream_t st, const SoftBudget* soft = nullptr, const PoolSrc* pool = nullptr,
+                         const CompactDst* compact = nullptr);
 
 hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const float* scores, const double* m_in,
                           const int32_t* cap_off, int64_t total_cap, float tau, float tau_w, float mix,

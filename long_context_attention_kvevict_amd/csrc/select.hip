@@ -620,13 +620,48 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
 // keys with the same leading digits and a larger last digit, and the keys
 // equal to it are those with the same last digit (from the chunk's list or
 // suffix sums).  The rest is sel_write's; the output is the same.
-template <class Src, class Bias>
+//
+// With CP the workgroup also gathers the rows of the keys it keeps (listed
+// in LDS, so no re-read of idx) into the compact cache: it owns the
+// consecutive output slots from the count of kept keys in earlier chunks on.
+__device__ __forceinline__ void gather_kept(const CompactDst& cd, const int* ckey, const float* cbias, int nrow,
+                                            int slot0, size_t src_row0, int h, int s) {
+  const int chunks = cd.row_bytes >> 4;
+  const int64_t dst0 = h * cd.totalC + cd.cap_off[s] + slot0;
+  constexpr int U = 8;   // items in flight per thread
+  for (int it0 = threadIdx.x; it0 < nrow * chunks; it0 += U * SEL_THREADS) {
+    u32x4 kv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * SEL_THREADS;
+      if (it < nrow * chunks) {
+        const int r = it / chunks, q = it - r * chunks;
+        const size_t src = (src_row0 + static_cast<size_t>(ckey ? ckey[r] : r)) * cd.row_bytes + 16 * q;
+        kv[u] = *reinterpret_cast<const u32x4*>(cd.k + src);
+        vv[u] = *reinterpret_cast<const u32x4*>(cd.v + src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * SEL_THREADS;
+      if (it < nrow * chunks) {
+        const int r = it / chunks, q = it - r * chunks;
+        const size_t dst = static_cast<size_t>(dst0 + r) * cd.row_bytes + 16 * q;
+        *reinterpret_cast<u32x4*>(cd.k_c + dst) = kv[u];
+        *reinterpret_cast<u32x4*>(cd.v_c + dst) = vv[u];
+        if (q == 0) cd.bias_c[dst0 + r] = cbias ? cbias[r] : 0.f;
+      }
+    }
+  }
+}
+
+template <class Src, class Bias, bool CP>
 __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bias_of, SelArgs a,
                                                                 const int* __restrict__ hist,
                                                                 const int* __restrict__ cnt,
                                                                 const int* __restrict__ cand,
                                                                 int32_t* __restrict__ idx,
-                                                                float* __restrict__ bias) {
+                                                                float* __restrict__ bias, CompactDst cd) {
   typedef typename Src::K K;
   constexpr int NLV = Radix<K>::LEVELS;
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -639,15 +674,16 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bi
   int32_t* out = idx + h * a.totalB + a.out_off[s];
   float* bout = bias + h * a.totalB + a.out_off[s];
   if (B <= 0) return;
+  const size_t row = static_cast<size_t>(h) * a.T + base;
   if (B >= n) {   // everything kept, weight 1
     for (int i = threadIdx.x; i < SEL_CHUNK; i += SEL_THREADS) {
       const int j = j0 + i;
       if (j < n) { out[j] = j; bout[j] = 0.f; }
     }
+    if constexpr (CP) gather_kept(cd, nullptr, nullptr, min(SEL_CHUNK, n - j0), j0, row + j0, h, s);
     return;
   }
   __shared__ int lds[8];
-  const size_t row = static_cast<size_t>(h) * a.T + base;
   const int jt = j0 + SEL_PER * threadIdx.x;
   K u[SEL_PER];
 #pragma unroll
@@ -698,16 +734,28 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bi
     ntake += take;
   }
   int take_tot;
-  int pos = gt_b + min(eq_b, need) + block_incl_scan256(ntake, lds, &take_tot) - ntake;
+  const int wbase = gt_b + min(eq_b, need);   // slots of earlier chunks' kept keys
+  int lpos = block_incl_scan256(ntake, lds, &take_tot) - ntake;
+  __shared__ int ckey[CP ? SEL_CHUNK : 1];
+  __shared__ float cbias[CP ? SEL_CHUNK : 1];
 #pragma unroll
   for (int i = 0; i < SEL_PER; ++i) {
     if ((take_bits >> i) & 1u) {
-      if (pos < B) {   // bounded even if the counts were inconsistent
-        out[pos] = jt + i;
-        bout[pos] = bias_of(sh, row + jt + i);
+      if (wbase + lpos < B) {   // bounded even if the counts were inconsistent
+        const float b = bias_of(sh, row + jt + i);
+        out[wbase + lpos] = jt + i;
+        bout[wbase + lpos] = b;
+        if constexpr (CP) {
+          ckey[lpos] = jt + i - j0;
+          cbias[lpos] = b;
+        }
       }
-      ++pos;
+      ++lpos;
     }
+  }
+  if constexpr (CP) {
+    __syncthreads();
+    gather_kept(cd, ckey, cbias, max(0, min(take_tot, B - wbase)), wbase, row + j0, h, s);
   }
 }
 
@@ -1753,7 +1801,7 @@ hipError_t launch_literal(const LiteralGeom& G, const int32_t* seq_off, const fl
 template <class Src, class Bias>
 static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bias_of, int* hist, int* cnt,
                          RState* rs, int32_t* idx, float* bias, hipStream_t st, int* cand,
-                         const PoolSrc* pool = nullptr) {
+                         const PoolSrc* pool = nullptr, const CompactDst* compact = nullptr) {
   typedef typename Src::K K;
   const dim3 grid(G.nchunk, G.Hkv, G.S);
   if (a.bsh == nullptr) {   // no count launch (not under a soft budget)
@@ -1768,8 +1816,12 @@ static void launch_radix(const SelectGeom& G, const SelArgs& a, Src src, Bias bi
       hipLaunchKernelGGL((sel_hist<Src, 4>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
     }
     hipLaunchKernelGGL((sel_hist_last<Src>), grid, dim3(SEL_THREADS), 0, st, src, a, hist, cand, cnt);
-    hipLaunchKernelGGL((sel_write_listed<Src, Bias>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, hist, cnt,
-                       cand, idx, bias);
+    if (compact)
+      hipLaunchKernelGGL((sel_write_listed<Src, Bias, true>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, hist,
+                         cnt, cand, idx, bias, *compact);
+    else
+      hipLaunchKernelGGL((sel_write_listed<Src, Bias, false>), grid, dim3(SEL_THREADS), 0, st, src, bias_of, a, hist,
+                         cnt, cand, idx, bias, CompactDst{});
     return;
   }
   hipLaunchKernelGGL((sel_hist<Src, 0>), grid, dim3(SEL_THREADS), 0, st, src, a, hist);
@@ -1885,7 +1937,8 @@ __global__ __launch_bounds__(256) void sel_init(int* __restrict__ p, int n, doub
 hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t* seq_off,
                          const int32_t* bud_off, float tau, float tau_w, float mix, uint64_t seed,
                          int32_t* idx, float* bias, double* m_out, int32_t* status_out, void* ws,
-                         hipStream_t st, const SoftBudget* soft, const PoolSrc* pool) {
+                         hipStream_t st, const SoftBudget* soft, const PoolSrc* pool,
+                         const CompactDst* compact) {
   char* wsb = static_cast<char*>(ws);
   int* hist = reinterpret_cast<int*>(wsb + G.off_hist);
   int* cnt = reinterpret_cast<int*>(wsb + G.off_cnt);
@@ -1914,6 +1967,9 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
   // with pooling folded in: top-k over several chunks or the unmixed chain
   // only, the counters already clear
   if (pool && (soft || (topk && G.max_len <= SEL_CHUNK) || (!topk && !chain))) return hipErrorInvalidValue;
+  // the gather rides on the listed ordered write: no soft budget, no
+  // single-chunk top-k
+  if (compact && (soft || (topk && G.max_len <= SEL_CHUNK))) return hipErrorInvalidValue;
   stage_begin(ST_SELECT, st);
   if (topk && !soft && G.max_len <= SEL_CHUNK) {   // every head in one workgroup
     hipLaunchKernelGGL(sel_topk_one, dim3(1, G.Hkv, G.S), dim3(SEL_THREADS), 0, st, scores, a, idx, bias, m_out,
@@ -1926,7 +1982,7 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
                        topk ? m_out : nullptr, topk ? status_out : nullptr, topk ? SH : 0);
   if (topk) {
     launch_radix(G, a, ScoreKeys{pool ? pool->out : scores}, ZeroBias{}, hist, cnt, rs, idx, bias, st,
-                 reinterpret_cast<int*>(wsb + G.off_cand), pool);
+                 reinterpret_cast<int*>(wsb + G.off_cand), pool, compact);
   } else {
     SmpArgs A;
     A.g = a;
@@ -1966,8 +2022,12 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
       hipLaunchKernelGGL((smp_finish_hist<4>), sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, hist);
       hipLaunchKernelGGL(smp_decide_last, sgrid, dim3(SEL_THREADS), 0, st, A, kSelSearchSteps, m_out, status_out,
                          hist, cand, cnt);
-      hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias>), sgrid, dim3(SEL_THREADS), 0, st,
-                         GumbelKeys{A.lp}, bias_of, a, hist, cnt, cand, idx, bias);
+      if (compact)
+        hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias, true>), sgrid, dim3(SEL_THREADS), 0, st,
+                           GumbelKeys{A.lp}, bias_of, a, hist, cnt, cand, idx, bias, *compact);
+      else
+        hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias, false>), sgrid, dim3(SEL_THREADS), 0, st,
+                           GumbelKeys{A.lp}, bias_of, a, hist, cnt, cand, idx, bias, CompactDst{});
       stage_end(ST_SELECT, st);
       return hipGetLastError();
     }
@@ -1985,8 +2045,12 @@ hipError_t launch_select(const SelectGeom& G, const float* scores, const int32_t
       const dim3 grid(G.nchunk, G.Hkv, G.S);
       hipLaunchKernelGGL((sel_hist_last<GumbelKeys>), grid, dim3(SEL_THREADS), 0, st, GumbelKeys{A.lp}, a, hist,
                          cand, cnt);
-      hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias>), grid, dim3(SEL_THREADS), 0, st, GumbelKeys{A.lp},
-                         bias_of, a, hist, cnt, cand, idx, bias);
+      if (compact)
+        hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias, true>), grid, dim3(SEL_THREADS), 0, st,
+                           GumbelKeys{A.lp}, bias_of, a, hist, cnt, cand, idx, bias, *compact);
+      else
+        hipLaunchKernelGGL((sel_write_listed<GumbelKeys, SnisBias, false>), grid, dim3(SEL_THREADS), 0, st,
+                           GumbelKeys{A.lp}, bias_of, a, hist, cnt, cand, idx, bias, CompactDst{});
     } else {
       // a soft budget decides each head's kept count first (its radix
       // levels need it)
