@@ -259,7 +259,9 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   const bool row_ok = row < R;
   // A wave of the last row group can hold no window row (R not a multiple
   // of 128, e.g. 7 query heads x 64 rows): it still loads its share of the
-  // tiles and forms its keys' ||v||^2, but skips the attention arithmetic.
+  // tiles (and in row group 0 forms its keys' ||v||^2, which the other row
+  // groups of the chunk leave to that one), but skips the attention
+  // arithmetic.
   const bool wave_rows = __builtin_amdgcn_readfirstlane(rg * ROWS + wave * 32 < R ? 1 : 0) != 0;
   const int qh = h * g + (row_ok ? row / a.w : 0);
   const int wi = row_ok ? row % a.w : 0;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
     const int kt0 = c0 + t * KT;
     const char* Kt = ring + (t & 1) * STAGE_BYTES;
     const char* Vt = Kt + TILE_BYTES;
-    {
+    if (rg == 0) {   // one row group forms the tile's ||v||^2
       f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) {
@@ -504,7 +506,8 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
   lds_barrier();   // vn complete
 
   // ||v||^2 of the chunk
-  for (int i = tid; i < c1 - c0; i += WG) a.vnorm[static_cast<size_t>(h) * a.T + base + c0 + i] = vn[i];
+  if (rg == 0)
+    for (int i = tid; i < c1 - c0; i += WG) a.vnorm[static_cast<size_t>(h) * a.T + base + c0 + i] = vn[i];
 
   // The row's candidate is the larger weight of its two halves' (the lower
   // key on equal weights); the other half's candidate joins the other keys.
