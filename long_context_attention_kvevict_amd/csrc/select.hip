@@ -93,25 +93,37 @@ __device__ __forceinline__ void block_sum3_d(double* a, double* b, double* c, do
   __syncthreads();
 }
 
-// Block sums of G values per thread (G * 8 == 256 threads): every thread
-// writes its G values, then 8 threads per value each sum 32 entries and
-// combine in a fixed tree.  Returns the total of value threadIdx.x / 8 on
-// the thread with threadIdx.x % 8 == 0 (0 elsewhere).  lds: [G][257].
-template <int G>
-__device__ __forceinline__ float block_sum_many(const float (&v)[G], float (*lds)[257]) {
-  static_assert(G * 8 == 256, "eight threads per value");
+// Workgroup sums (256 threads) of 32 values per thread.  Within a wave,
+// five exchange steps each hand half of the lane's remaining values to the
+// partner lane (xor 32, 16, 8, 4, 2) and add the half it keeps, and a sixth
+// adds the neighbour's (xor 1): lanes 2k and 2k+1 then hold value k's wave
+// sum.  The four waves' sums are added in wave order.  On return every
+// thread reads value k's total in red[128 + k] (red: 160 floats of LDS).
+constexpr int kRed32 = 160;
+template <int N>
+__device__ __forceinline__ void fold_half(const float (&v)[2 * N], float (&o)[N], int mask) {
+  const bool hi = (threadIdx.x & mask) != 0;
 #pragma unroll
-  for (int k = 0; k < G; ++k) lds[k][threadIdx.x] = v[k];
+  for (int i = 0; i < N; ++i) {
+    const float keep = hi ? v[N + i] : v[i];
+    const float give = hi ? v[i] : v[N + i];
+    o[i] = keep + __shfl_xor(give, mask);
+  }
+}
+__device__ __forceinline__ void block_sum32(const float (&v)[32], float* red) {
+  float a[16], b[8], c[4], d[2], e[1];
+  fold_half<16>(v, a, 32);
+  fold_half<8>(a, b, 16);
+  fold_half<4>(b, c, 8);
+  fold_half<2>(c, d, 4);
+  fold_half<1>(d, e, 2);
+  const float t = e[0] + __shfl_xor(e[0], 1);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((lane & 1) == 0) red[wave * 32 + (lane >> 1)] = t;
   __syncthreads();
-  const int k = threadIdx.x >> 3, part = threadIdx.x & 7;
-  float t = 0.f;
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) t += lds[k][part * 32 + i];
-  t += __shfl_xor(t, 1, 8);
-  t += __shfl_xor(t, 2, 8);
-  t += __shfl_xor(t, 4, 8);
+  if (threadIdx.x < 32)
+    red[128 + threadIdx.x] = ((red[threadIdx.x] + red[32 + threadIdx.x]) + red[64 + threadIdx.x]) + red[96 + threadIdx.x];
   __syncthreads();
-  return part == 0 ? t : 0.f;
 }
 
 __device__ __forceinline__ double block_max_d(double v, double* lds) {
@@ -1024,7 +1036,7 @@ __device__ __forceinline__ double log1m(double p) {
 // the search; every value the search accepts is fp64).
 // eg: kSelGrid x 257 floats of LDS.
 template <bool KEYS>
-__device__ void smp_keys_body(const SmpArgs& A, float (*eg)[SEL_THREADS + 1]) {
+__device__ void smp_keys_body(const SmpArgs& A, float* red) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -1087,13 +1099,13 @@ __device__ void smp_keys_body(const SmpArgs& A, float (*eg)[SEL_THREADS + 1]) {
     }
   }
   // per grid point, the chunk sum in a fixed order
-  const float t = block_sum_many<kSelGrid>(e, eg);
-  if ((threadIdx.x & 7) == 0)
-    A.grid[(static_cast<size_t>(sh) * A.nsmp + ch) * kSelGrid + (threadIdx.x >> 3)] = t;
+  static_assert(kSelGrid == 32, "the grid sums fold 32 values");
+  block_sum32(e, red);
+  if (threadIdx.x < kSelGrid) A.grid[(static_cast<size_t>(sh) * A.nsmp + ch) * kSelGrid + threadIdx.x] = red[128 + threadIdx.x];
 }
 __global__ __launch_bounds__(SEL_THREADS) void smp_keys(SmpArgs A) {
-  __shared__ float eg[kSelGrid][SEL_THREADS + 1];
-  smp_keys_body<true>(A, eg);
+  __shared__ float red[kRed32];
+  smp_keys_body<true>(A, red);
 }
 
 // What a search step (or the finish) reads, loaded at the start of its
@@ -1146,7 +1158,7 @@ __device__ __forceinline__ void search_load(const SmpArgs& A, int step, int sh, 
 // when the step leaves it), or stop once |E - B| <= 0.5, or -- on step 1,
 // from E(10^12) -- stop with the target out of reach.
 __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int B, double* dl,
-                               float (*eg)[257], const SearchIn& in) {
+                               float* red, const SearchIn& in) {
   if (step == 0) {
     // start from the grid: the first point whose E reaches B, and a bracket
     // one grid cell wider on each side than the crossing (the grid sums are
@@ -1172,13 +1184,11 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
 #pragma unroll
       for (int k = 0; k < kSelGrid; ++k) v[k] = static_cast<float>(acc[k]);
     }
-    const float t = block_sum_many<kSelGrid>(v, eg);
-    if ((threadIdx.x & 7) == 0) eg[0][256 - kSelGrid + (threadIdx.x >> 3)] = t;   // totals, in a free column
-    __syncthreads();
+    block_sum32(v, red);
     int kx = kSelGrid;   // first grid point with E >= B
     double Ek = 0.0, Ep = 0.0;
     for (int k = 0; k < kSelGrid; ++k) {
-      const double e = static_cast<double>(eg[0][256 - kSelGrid + k]) / nh;
+      const double e = static_cast<double>(red[128 + k]) / nh;
       if (e >= target) { kx = k; Ek = e; break; }
       Ep = e;
     }
@@ -1235,9 +1245,9 @@ __device__ Search search_state(const SmpArgs& A, int step, int sh, int nch, int 
 // One step of the expected-samples search: brings the state up to date,
 // then (if still searching) writes the chunk's E(m), dE/dm at m = e^u, and
 // on the first step also E(10^12).
-// eg: kSelGrid x 257 floats of LDS, used on step 0 only (may be NULL after);
+// red: kRed32 floats of LDS, used on step 0 only (may be NULL after);
 // in: search_load's values for this workgroup.
-__device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257], const SearchIn& in) {
+__device__ void smp_search_body(const SmpArgs& A, int step, float* red, const SearchIn& in) {
   const int ch = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   int n, B, base;
   if (!smp_active(A, s, ch, &n, &B, &base)) return;
@@ -1245,7 +1255,7 @@ __device__ void smp_search_body(const SmpArgs& A, int step, float (*eg)[257], co
   const int nch = (n + SMP_CHUNK - 1) / SMP_CHUNK;
   const size_t SH = static_cast<size_t>(A.g.S) * A.g.Hkv;
   __shared__ double dl[12];
-  const Search st = search_state(A, step, sh, nch, B, dl, eg, in);
+  const Search st = search_state(A, step, sh, nch, B, dl, red, in);
   if (ch == 0 && threadIdx.x == 0) A.state[((step + 1) & 1) * SH + sh] = st;
   if (st.done > 0.0) return;
   const bool want_eh = step == 0 && st.done == 0.0;
@@ -1410,10 +1420,10 @@ __device__ __forceinline__ bool search_load_wg(const SmpArgs& A, int step, Searc
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void smp_search(SmpArgs A, int step) {
-  __shared__ float eg[kSelGrid][257];
+  __shared__ float red[kRed32];
   SearchIn in;
   if (!search_load_wg(A, step, &in)) return;
-  smp_search_body(A, step, eg, in);
+  smp_search_body(A, step, red, in);
 }
 __global__ __launch_bounds__(SEL_THREADS) void smp_finish(SmpArgs A, int steps) {
   SearchIn in;
@@ -1445,11 +1455,10 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_search_hist(SmpArgs A, int st
   SearchIn in;
   if (!search_load_wg(A, step, &in)) return;
   if constexpr (FIRST) {
-    __shared__ __align__(16) float eg[kSelGrid][257];
-    static_assert(sizeof(eg) >= SEL_BINS * sizeof(int), "the grid block holds the histogram");
-    sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, reinterpret_cast<int*>(&eg[0][0]), lds);
-    __syncthreads();   // the histogram's LDS is the grid's
-    smp_search_body(A, step, eg, in);
+    __shared__ int lh[SEL_BINS];
+    __shared__ float red[kRed32];
+    sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
+    smp_search_body(A, step, red, in);
   } else {
     __shared__ int lh[SEL_BINS];
     sel_hist_body<GumbelKeys, LV>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
@@ -1479,11 +1488,10 @@ __global__ __launch_bounds__(SEL_THREADS) void smp_decide_hist(SmpArgs A, int st
 // Pass B without the keys (pass A wrote them), with the keys' level 0.
 __global__ __launch_bounds__(SEL_THREADS) void smp_grid_hist(SmpArgs A, int* __restrict__ hist) {
   __shared__ int lds[8];
-  __shared__ __align__(16) float eg[kSelGrid][SEL_THREADS + 1];
-  static_assert(sizeof(eg) >= SEL_BINS * sizeof(int), "the grid block holds the histogram");
-  smp_keys_body<false>(A, eg);
-  __syncthreads();
-  sel_hist_body<GumbelKeys, 0>(GumbelKeys{A.lp}, A.g, hist, reinterpret_cast<int*>(&eg[0][0]), lds);
+  __shared__ int lh[SEL_BINS];
+  __shared__ float red[kRed32];
+  smp_keys_body<false>(A, red);
+  sel_hist_body<GumbelKeys, 0>(GumbelKeys{A.lp}, A.g, hist, lh, lds);
 }
 // The decision with the keys' last level (its candidate list and counts).
 __global__ __launch_bounds__(SEL_THREADS) void smp_decide_last(SmpArgs A, int steps, double* m_out,
