@@ -1071,13 +1071,14 @@ __device__ void smp_keys_body(const SmpArgs& A, float* red) {
     }
   }
   const double lse = M + log(block_sum_d(zp, dl));
-  // per grid point, this thread's share of the chunk's E(m_k)
-  float e[kSelGrid];
-#pragma unroll
-  for (int k = 0; k < kSelGrid; ++k) e[k] = 0.f;
+  // the keys' fp64 terms first, then (with those temporaries dead) each
+  // key's run over the grid points: this thread's share of the chunk's
+  // E(m_k), accumulated key by key
+  float d0[SMP_PER];
 #pragma unroll 2
   for (int i = 0; i < SMP_PER; ++i) {
     const int j = ch * SMP_CHUNK + i * SEL_THREADS + threadIdx.x;
+    d0[i] = 0.f;
     if (j < n) {
       double x = xin[i];
       double l;
@@ -1090,7 +1091,16 @@ __device__ void smp_keys_body(const SmpArgs& A, float* red) {
       }
       A.L[row + j] = l;
       if (KEYS) A.lp[row + j] = smp_gumbel(A, x, j, h, s);
-      float dk = -expm1f(static_cast<float>(static_cast<double>(B) * l));
+      d0[i] = -expm1f(static_cast<float>(static_cast<double>(B) * l));
+    }
+  }
+  float e[kSelGrid];
+#pragma unroll
+  for (int k = 0; k < kSelGrid; ++k) e[k] = 0.f;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    if (ch * SMP_CHUNK + i * SEL_THREADS + static_cast<int>(threadIdx.x) < n) {
+      float dk = d0[i];
 #pragma unroll
       for (int k = 0; k < kSelGrid; ++k) {
         e[k] += dk;
