@@ -1,7 +1,9 @@
 """GPU tier at full workload sizes, in the launch configuration the benchmark
 times.  The oracle scores every key of two KV heads per workload (all
 window rows, all n keys), checks every head's selection given the GPU's
-scores, and sampled decode steps."""
+scores, and sampled decode steps.  One KV head at n = 2^20 (the longest
+sequence tested) checks sampled keys and their pooling windows, each
+against every row's full softmax."""
 import numpy as np
 import pytest
 import torch
