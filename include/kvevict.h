@@ -38,7 +38,13 @@
  *  - Execution: each call validates its arguments on the host, then
  *    enqueues kernels on `stream` (a hipStream_t; NULL = default stream)
  *    and returns without synchronising.  Faults during execution surface
- *    at the caller's next synchronisation.
+ *    at the caller's next synchronisation.  The calls enqueue kernels only
+ *    (scratch that must start at zero is cleared by a kernel, never by a
+ *    memset or copy), so a caller may capture them in a HIP graph and
+ *    replay it.  Grid sizes are fixed at capture from the host-side
+ *    arrays, so a replay computes the captured sizes: the device buffers
+ *    (offsets, inputs, outputs, workspace) must stay allocated, and the
+ *    device offset arrays unchanged, while the graph is replayed.
  *  - Errors: argument errors return KVE_EINVAL / KVE_ENOTSUP /
  *    KVE_EWORKSPACE before anything is launched or written; a failed launch
  *    returns KVE_EHIP.  kvevict_last_error() describes the last failure of
