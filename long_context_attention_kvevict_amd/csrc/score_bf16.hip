@@ -541,9 +541,9 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup per window row: 8 streams of 32 lanes take every 8th chunk
-// (lane = DD/32 consecutive features), then combine through LDS in a fixed
-// order.  Chunks wholly beyond a row's causal horizon carry max = -inf and
+// One workgroup per window row: NSTR streams of 32 lanes take every
+// NSTR-th chunk (lane = DD/32 consecutive features), then combine through
+// LDS in a fixed order.  Chunks wholly beyond a row's causal horizon carry max = -inf and
 // weight 0.
 //
 // A row whose best candidate key (largest weight over the chunks'
@@ -554,18 +554,19 @@ __global__ __launch_bounds__(WG, 2) void score_p1_bf16(ScoreArgs a) {
 // and ||o - v_j||^2 is summed from the explicit difference.  Any key with a
 // weight above one half has the row's unique largest weight and was
 // recorded as a candidate on its tile, so this covers every such row.
-template <int DD, bool BF16OUT>
-__global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
+template <int DD, bool BF16OUT, int NSTR>
+__global__ __launch_bounds__(NSTR * 32) void score_merge(ScoreArgs a, float* o32) {
   constexpr int F = DD / 32;
-  constexpr int NSTR = 8;
+  constexpr int NT = NSTR * 32;   // threads: NSTR streams of 32 lanes
+  static_assert(NT % 64 == 0 && NT <= 256, "whole waves, at most four");
   const int gr = blockIdx.x;   // grp * ROWS + rl
   const int grp = gr / ROWS;
   const int rl = gr % ROWS;
   const int tid = threadIdx.x;
   if (a.zero.p) {   // a later selection's counters (one-call eviction)
-    const int nt = gridDim.x * 256;
-    for (int i = gr * 256 + tid; i < a.zero.n; i += nt) a.zero.p[i] = 0;
-    for (int i = gr * 256 + tid; i < a.zero.nsh; i += nt) {
+    const int nt = gridDim.x * NT;
+    for (int i = gr * NT + tid; i < a.zero.n; i += nt) a.zero.p[i] = 0;
+    for (int i = gr * NT + tid; i < a.zero.nsh; i += nt) {
       if (a.zero.m) a.zero.m[i] = 0.0;
       if (a.zero.st) a.zero.st[i] = KVE_OK;
     }
@@ -600,17 +601,19 @@ __global__ __launch_bounds__(256) void score_merge(ScoreArgs a, float* o32) {
   }
   __shared__ float red_o[NSTR][DD];
   __shared__ float red_l[NSTR][4];   // others' sum, candidate weight, key, chunk
-  __shared__ float red_m[4];
+  __shared__ float red_m[NT / 64];
   const size_t cstride_ml = static_cast<size_t>(ROWS) * kScoreRec;
   const size_t cstride_o = static_cast<size_t>(ROWS) * DD;
   const float* ml = a.part_ml + (static_cast<size_t>(grp) * a.P * ROWS + rl) * kScoreRec;
   const float* po = a.part_o + (static_cast<size_t>(grp) * a.P * ROWS + rl) * DD + ln * F;
   float M = -INFINITY;
-  for (int c = tid; c < nch; c += 256) M = fmaxf(M, ml[c * cstride_ml]);
+  for (int c = tid; c < nch; c += NT) M = fmaxf(M, ml[c * cstride_ml]);
   M = wave_max(M);
   if ((tid & 63) == 0) red_m[tid >> 6] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red_m[w]);
   // per stream: sum of the non-candidate weights (the candidates that lose
   // to a better one included) and the best candidate (weight, key, chunk),
   // all scaled to the reference M
@@ -1200,8 +1203,15 @@ hipError_t launch_score_bf16(const ScoreGeom& G, const void* q_win, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   stage_begin(ST_SCORE_MERGE, st);
-  hipLaunchKernelGGL((score_merge<D, true>), dim3(G.S * G.Hkv * G.RG * ROWS), dim3(256), 0, st, a,
-                     static_cast<float*>(nullptr));
+  // a row with at most 32 chunks (a batch of many rows, such as a ragged
+  // batch of 64K-token sequences) takes 2 streams in a one-wave workgroup,
+  // so that the rows fit the CUs in fewer rounds; otherwise 8
+  if (G.P <= 32)
+    hipLaunchKernelGGL((score_merge<D, true, 2>), dim3(G.S * G.Hkv * G.RG * ROWS), dim3(64), 0, st, a,
+                       static_cast<float*>(nullptr));
+  else
+    hipLaunchKernelGGL((score_merge<D, true, 8>), dim3(G.S * G.Hkv * G.RG * ROWS), dim3(256), 0, st, a,
+                       static_cast<float*>(nullptr));
   stage_end(ST_SCORE_MERGE, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1232,8 +1242,8 @@ hipError_t launch_merge_f32(const ScoreGeom& G, const int32_t* seq_off, void* ws
   a.no2 = reinterpret_cast<float*>(base + G.off_no2);
   float* o32 = reinterpret_cast<float*>(base + G.off_ohi);
   dim3 grid(G.S * G.Hkv * G.RG * ROWS);
-  if (G.d == 64) hipLaunchKernelGGL((score_merge<64, false>), grid, dim3(256), 0, st, a, o32);
-  else hipLaunchKernelGGL((score_merge<128, false>), grid, dim3(256), 0, st, a, o32);
+  if (G.d == 64) hipLaunchKernelGGL((score_merge<64, false, 8>), grid, dim3(256), 0, st, a, o32);
+  else hipLaunchKernelGGL((score_merge<128, false, 8>), grid, dim3(256), 0, st, a, o32);
   return hipGetLastError();
 }
 
