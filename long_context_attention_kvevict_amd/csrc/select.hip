@@ -626,16 +626,11 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_write(Src src, Bias bias_of, 
   }
 }
 
-// Ordered write from sel_hist_last's counts: the threshold is resolved here
-// from the finished histograms (as sel_count does); the keys above it in an
-// earlier chunk are that chunk's count of larger leading digits plus its
-// keys with the same leading digits and a larger last digit, and the keys
-// equal to it are those with the same last digit (from the chunk's list or
-// suffix sums).  The rest is sel_write's; the output is the same.
-//
-// With CP the workgroup also gathers the rows of the keys it keeps (listed
-// in LDS, so no re-read of idx) into the compact cache: it owns the
-// consecutive output slots from the count of kept keys in earlier chunks on.
+// The gather of a workgroup's kept rows into the compact cache (one-call
+// eviction, [PI] §2 Eq. 3): rows ckey[r] (chunk-relative; r itself when
+// ckey is NULL) of the sequence's K and V go to slots slot0 + r of KV head
+// h, with their bias (0 when cbias is NULL), eight 16-byte pieces in flight
+// per thread.
 __device__ __forceinline__ void gather_kept(const CompactDst& cd, const int* ckey, const float* cbias, int nrow,
                                             int slot0, size_t src_row0, int h, int s) {
   const int chunks = cd.row_bytes >> 4;
@@ -667,6 +662,16 @@ __device__ __forceinline__ void gather_kept(const CompactDst& cd, const int* cke
   }
 }
 
+// Ordered write from sel_hist_last's counts: the threshold is resolved here
+// from the finished histograms (as sel_count does); the keys above it in an
+// earlier chunk are that chunk's count of larger leading digits plus its
+// keys with the same leading digits and a larger last digit, and the keys
+// equal to it are those with the same last digit (from the chunk's list or
+// suffix sums).  The rest is sel_write's; the output is the same.
+//
+// With CP the workgroup also gathers the rows of the keys it keeps (listed
+// in LDS, so no re-read of idx) into the compact cache: it owns the
+// consecutive output slots from the count of kept keys in earlier chunks on.
 template <class Src, class Bias, bool CP>
 __global__ __launch_bounds__(SEL_THREADS) void sel_write_listed(Src src, Bias bias_of, SelArgs a,
                                                                 const int* __restrict__ hist,
