@@ -31,6 +31,13 @@ def _cases():
         # widest and narrowest pooling
         "ragged3_topk_pool31": (ragged, K.KVE_TOPK, 31, None),
         "llama_n4099_sample_pool1": (workloads.scaled(workloads.llama8b_32k(), 4099), K.KVE_SAMPLE, 1, None),
+        # sequences exactly as long as the window (n = w = 32) and one longer by
+        # a key, beside one that spans several chunks: pooling windows and
+        # gathers that meet sequence ends
+        "ragged_min_topk": (dataclasses.replace(ragged, name="ragged_min", lens=[32, 5000, 33], needles=0),
+                            K.KVE_TOPK, 7, None),
+        "ragged_min_sample": (dataclasses.replace(ragged, name="ragged_min", lens=[32, 5000, 33], needles=0),
+                              K.KVE_SAMPLE, 31, [3, 500, 32]),
         # paths that run the three calls in turn: one chunk per head, fp32
         "ragged_short_topk": (dataclasses.replace(ragged, name="short", lens=[300, 1024, 777]), K.KVE_TOPK, 7, None),
         "tiny_fp32_topk": (workloads.tiny_fp32(), K.KVE_TOPK, 5, None),
